@@ -1,0 +1,177 @@
+"""Pins of the oracle's attention, mode schedule and causal prefill (CPU only).
+
+Attention is pinned against torch's scaled_dot_product_attention (CPU, fp64,
+scale 1), and by special cases: K equal to the pool size reproduces dense
+attention over the pool, one key returns that key, a zero query returns the
+mean key, the LSE merge equals one softmax over the concatenation, and a pool
+permutation with remapped indices leaves the output unchanged.
+The schedule is pinned by invariants: Reuse reproduces its source layer's
+indices, Reindex with the Full layer's own indexer inputs equals Full, a
+candidate pool as large as the pool equals the flat path, and the
+hierarchical Full layer's Top-K equals the flat Top-K.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as TF
+
+from oracle import csa2 as O
+from oracle import formats as F
+from fp4_kv_cache_score_amd import synth
+from fp4_kv_cache_score_amd.configs import CONFIGS, FULL, REINDEX, REUSE
+
+
+def _sdpa(q_bits, keys):
+    q = torch.from_numpy(F.bf16_value(q_bits))[None, :, None, :]          # [1,H,1,D]
+    k = torch.from_numpy(keys)[None, None].expand(1, q.shape[1], -1, -1)  # [1,H,N,D]
+    return TF.scaled_dot_product_attention(q, k, k, scale=1.0)[0, :, 0].numpy()
+
+
+def _small_case(M=256, K=16, W=8, modes=(FULL,), P=0, seed=11, B=1):
+    cfg = CONFIGS[0].scaled(name="t", seed=seed, B=B, M=M, K=K, W=W, modes=tuple(modes), P=P)
+    return synth.make_case(cfg)
+
+
+def _layers(case, b=0):
+    return [dict(mode=L.mode,
+                 q_idx=None if L.q_idx is None else L.q_idx[b, 0],
+                 w_idx=None if L.w_idx is None else L.w_idx[b, 0],
+                 q=L.q[b, 0], swa=L.swa[b]) for L in case.layers]
+
+
+def test_attend_matches_torch_sdpa():
+    case = _small_case()
+    p = case.pool
+    idx = np.arange(0, 256, 9)
+    keys = O.gather_keys(p.latent[0], p.scale[0], idx, case.layers[0].swa[0])
+    o, lse = O.attend(case.layers[0].q[0, 0], keys)
+    assert np.allclose(o, _sdpa(case.layers[0].q[0, 0], keys), rtol=1e-12, atol=1e-14)
+    q = F.bf16_value(case.layers[0].q[0, 0])
+    ref_lse = np.log(np.exp(q @ keys.T).sum(1))
+    assert np.allclose(lse, ref_lse, rtol=1e-12)
+
+
+def test_k_equal_pool_size_is_dense_attention():
+    case = _small_case(M=128, K=128, W=0)
+    p = case.pool
+    rec = O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], _layers(case), K=128)[0]
+    assert rec["idx"].tolist() == list(range(128))
+    dense = F.dequant_latent(p.latent[0], p.scale[0])
+    assert np.allclose(rec["o"], _sdpa(case.layers[0].q[0, 0], dense), rtol=1e-12, atol=1e-14)
+
+
+def test_single_key_and_zero_query():
+    case = _small_case()
+    p = case.pool
+    key = O.gather_keys(p.latent[0], p.scale[0], np.array([17, -1, -1]))
+    o, lse = O.attend(case.layers[0].q[0, 0], key)
+    assert np.array_equal(o, np.broadcast_to(key[0], o.shape))
+    keys = O.gather_keys(p.latent[0], p.scale[0], np.arange(10), case.layers[0].swa[0])
+    o, lse = O.attend(np.zeros((16, 512), np.uint16), keys)
+    assert np.allclose(o, keys.mean(0)[None], rtol=1e-13, atol=1e-15)
+    assert np.allclose(lse, np.log(len(keys)))
+    o, lse = O.attend(case.layers[0].q[0, 0], np.zeros((0, 512)))
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+def test_lse_merge_equals_union_softmax():
+    case = _small_case()
+    p = case.pool
+    q = case.layers[0].q[0, 0]
+    g = O.gather_keys(p.latent[0], p.scale[0], np.arange(5, 60, 3))
+    o1, l1 = O.attend(q, g)
+    o, l = O.swa_merge(q, case.layers[0].swa[0], o1, l1)
+    ou, lu = O.attend(q, O.gather_keys(p.latent[0], p.scale[0], np.arange(5, 60, 3),
+                                       case.layers[0].swa[0]))
+    assert np.allclose(o, ou, rtol=1e-12, atol=1e-15) and np.allclose(l, lu, rtol=1e-13)
+
+
+def test_pool_permutation_invariance():
+    case = _small_case(M=200, K=24, W=4, seed=5)
+    p = case.pool
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(200)        # new row r holds old row perm[r]
+    inv = np.argsort(perm)
+    L = _layers(case)
+    a = O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], L, K=24)[0]
+    b = O.decode_sequence(p.latent[0][perm], p.scale[0][perm], p.idx_key[0][perm], L, K=24)[0]
+    assert a["gap"] > 1e-9
+    assert sorted(perm[b["idx"]].tolist()) == a["idx"].tolist()
+    assert np.allclose(a["o"], b["o"], rtol=1e-12, atol=1e-15)
+    assert np.allclose(a["lse"], b["lse"], rtol=1e-13)
+    assert sorted(inv[a["idx"]].tolist()) == b["idx"].tolist()
+
+
+def test_reuse_reproduces_source_and_reindex_with_same_query_equals_full():
+    case = _small_case(M=300, K=20, modes=(FULL, REUSE, REINDEX, REUSE, REUSE))
+    p = case.pool
+    L = _layers(case)
+    recs = O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], L, K=20)
+    assert np.array_equal(recs[1]["idx"], recs[0]["idx"])
+    assert np.array_equal(recs[3]["idx"], recs[2]["idx"])
+    assert np.array_equal(recs[4]["idx"], recs[2]["idx"])
+    assert not np.array_equal(recs[2]["idx"], recs[0]["idx"])
+    L2 = [dict(x) for x in L]
+    L2[2]["q_idx"], L2[2]["w_idx"] = L[0]["q_idx"], L[0]["w_idx"]
+    recs2 = O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], L2, K=20)
+    assert np.array_equal(recs2[2]["idx"], recs[0]["idx"])
+
+
+def test_hierarchical_pool_invariants():
+    case = _small_case(M=512, K=16, modes=(FULL, REINDEX, REINDEX), P=64, seed=7)
+    p = case.pool
+    L = _layers(case)
+    flat = O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], L, K=16)
+    hier = O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], L, K=16, P=64)
+    # the Full layer's Top-K is the same with or without the candidate pool
+    assert np.array_equal(hier[0]["idx"], flat[0]["idx"])
+    cand = hier[0]["cand"]
+    assert np.array_equal(cand, O.topk(flat[0]["scores"], 64)[0])
+    for r in hier[1:]:
+        assert set(r["idx"].tolist()) <= set(cand.tolist())
+        # Reindex inside the pool = Top-K of the flat scores restricted to the pool
+        fs = O.index_scores(p.idx_key[0], L[1]["q_idx"], L[1]["w_idx"])
+    want = O.map_positions(O.topk(fs[cand], 16)[0], cand)
+    assert np.array_equal(hier[1]["idx"], want)
+    # a candidate pool covering the whole pool is the flat path
+    full = O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], L, K=16, P=512)
+    for a, b in zip(full, flat):
+        assert np.array_equal(a["idx"], b["idx"])
+        assert np.allclose(a["o"], b["o"], rtol=0, atol=0)
+
+
+def test_schedule_must_start_with_full():
+    case = _small_case(modes=(REINDEX,))
+    p = case.pool
+    with pytest.raises(ValueError):
+        O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], _layers(case), K=4)
+    case = _small_case(modes=(FULL,))
+    L = _layers(case)
+    L[0] = dict(L[0], mode=REUSE)
+    with pytest.raises(ValueError):
+        O.decode_sequence(p.latent[0], p.scale[0], p.idx_key[0], L, K=4)
+
+
+def test_visible_entries_bruteforce():
+    for ratio in (1, 4):
+        for M in (1, 5, 9):
+            for pos in range(-1, 4 * M + 6):
+                want = sum(1 for j in range(M) if ratio * j + ratio - 1 <= pos)
+                assert O.visible_entries(M, pos, ratio) == want
+
+
+def test_prefill_last_query_sees_all_and_matches_truncated_decode():
+    cfg = CONFIGS[4].scaled(M=96, Q=24, K=8, W=5)
+    case = synth.make_case(cfg)
+    p, L = case.pool, case.layers[0]
+    assert cfg.pos0 == 4 * 96 - 24
+    for t in (0, 7, 23):
+        r = O.prefill_query(p.latent[0], p.scale[0], p.idx_key[0], L.q_idx[0, t], L.w_idx[0, t],
+                            L.q[0, t], L.swa[0], t, cfg.pos0, cfg.ratio, cfg.K, cfg.W)
+        vis = r["vis"]
+        assert vis == min(96, (cfg.pos0 + t + 1) // 4)
+        d = O.decode_sequence(p.latent[0][:vis], p.scale[0][:vis], p.idx_key[0][:vis],
+                              [dict(mode=FULL, q_idx=L.q_idx[0, t], w_idx=L.w_idx[0, t],
+                                    q=L.q[0, t], swa=L.swa[0, t:t + cfg.W])], K=cfg.K)[0]
+        assert np.array_equal(r["idx"], d["idx"]) and np.array_equal(r["o"], d["o"])
+    assert (cfg.pos0 + 23 + 1) // 4 == 96
