@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""CSA2 decode benchmark on one MI355X: query-tokens/s and achieved HBM bandwidth.
+
+A step is one decode token for every sequence of the batch through the whole
+layer schedule (csa2_decode_layers: indexer scan, Top-K, FP4 gather +
+attention, FP8 window merge per layer) with all inputs resident in HBM.
+The default workload is the 128K-context decode (batch 32, pool M = 32768,
+K = 512, W = 128, layers Full / Reindex / Reuse / Reuse); the 1M-context
+hierarchical decode (batch 8, M = 262144, P = 8192, Full + 3 Reindex) is
+measured too and reported under "extra".
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the indexer
+scan): algorithmic bytes per launch / its mean duration, timed with HIP
+events on the stream it runs on; `traffic` is the counter-measured HBM bytes
+per launch recorded under profiles/ for the same kernel source (null when the
+kernel changed since).  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload on one host core.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_traffic.json")
+SCORE_SRC = os.path.join(ROOT, "fp4_kv_cache_score_amd", "csrc", "index_score.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload)
+    if not e or e.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def time_decode(dc, steps: int, warmup: int):
+    import torch
+    dc.prepare_decode(idx_for_reuse=False)
+    for _ in range(warmup):
+        dc.decode_layers()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        dc.decode_layers()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_score_kernel(dc, launches: int):
+    """Mean duration of the scan kernel as decode launches it (flat, histogram on)."""
+    import torch
+    from fp4_kv_cache_score_amd import _lib as C
+    cfg = dc.cfg
+    d = dc.layers[0]
+    scores = torch.empty((cfg.B, cfg.M), dtype=torch.float32, device="cuda")
+    hist = torch.zeros((cfg.B, 4096), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        C.csa2_index_score(dc.pool, d["q_idx"], d["w_idx"], 1, -1, 1, None, 0, scores, hist, stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        C.csa2_index_score(dc.pool, d["q_idx"], d["w_idx"], 1, -1, 1, None, 0, scores, hist, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ms)), float(np.min(ms))
+
+
+def cpu_baseline(case, budget_s: float = 15.0):
+    """The CPU oracle, single-threaded, on whole sequences until the budget is used."""
+    from threadpoolctl import threadpool_limits
+    from oracle import csa2 as O
+    cfg = case.cfg
+    p = case.pool
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b in range(cfg.B):
+            layers = [dict(mode=L.mode,
+                           q_idx=None if L.q_idx is None else L.q_idx[b, 0],
+                           w_idx=None if L.w_idx is None else L.w_idx[b, 0],
+                           q=L.q[b, 0], swa=L.swa[b]) for L in case.layers]
+            O.decode_sequence(p.latent[b], p.scale[b], p.idx_key[b], layers, cfg.K, cfg.P)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    el = time.perf_counter() - t0
+    return dict(value=done / el, unit="query-tokens/s", cores=1, kind="oracle",
+                sample="%d of %d sequences of %s through all %d layers (%.1f s, NumPy fp64, "
+                       "BLAS limited to 1 thread)" % (done, cfg.B, cfg.name, cfg.L, el))
+
+
+def measure(ci: int, steps: int, warmup: int, score_launches: int):
+    import torch
+    from fp4_kv_cache_score_amd import synth
+    from fp4_kv_cache_score_amd.configs import CONFIGS, algorithmic_bytes
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[ci]
+    t0 = time.perf_counter()
+    case = synth.make_case(cfg)
+    log("generated %s in %.1f s" % (cfg.name, time.perf_counter() - t0))
+    dc = DeviceCase(case)
+    torch.cuda.synchronize()
+    ms, wall = time_decode(dc, steps, warmup)
+    log("%s: %.3f ms/step (wall %.3f s for %d steps)" % (cfg.name, ms, wall, steps))
+    ab = algorithmic_bytes(cfg)
+    k_ms, k_min = time_score_kernel(dc, score_launches)
+    per_launch = cfg.B * cfg.M * cfg.HI * cfg.DI + cfg.B * (cfg.HI * cfg.DI + cfg.HI * 4)
+    log("%s: scan kernel mean %.3f ms (min %.3f) per launch" % (cfg.name, k_ms, k_min))
+    res = dict(cfg=cfg, case=case, ms=ms, wall=wall, bytes=ab, k_ms=k_ms, per_launch=per_launch)
+    del dc
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="headline workload (config index)")
+    ap.add_argument("--extra", type=int, nargs="*", default=[2],
+                    help="further decode configs measured into 'extra'")
+    ap.add_argument("--score-launches", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(decode shards by sequence; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    from fp4_kv_cache_score_amd import _lib
+    _lib.lib()
+
+    head = measure(args.config, args.steps, args.warmup, args.score_launches)
+    cfg = head["cfg"]
+    value = cfg.B / (head["ms"] * 1e-3)
+    achieved = head["per_launch"] / (head["k_ms"] * 1e-3) / 1e9
+    traffic = recorded_traffic(cfg.name)
+    step_gbs = head["bytes"]["total"] / (head["ms"] * 1e-3) / 1e9
+    extra = {}
+    for ci in args.extra:
+        if ci == args.config:
+            continue
+        r = measure(ci, args.steps, args.warmup, args.score_launches)
+        c = r["cfg"]
+        extra[c.name] = dict(
+            query_tokens_per_s=c.B / (r["ms"] * 1e-3), ms_per_step=r["ms"],
+            step_hbm_gbs=r["bytes"]["total"] / (r["ms"] * 1e-3) / 1e9,
+            step_frac_of_peak=r["bytes"]["total"] / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            algorithmic_bytes_per_step=r["bytes"]["total"],
+            scan_kernel_ms=r["k_ms"],
+            scan_kernel_gbs=r["per_launch"] / (r["k_ms"] * 1e-3) / 1e9)
+        del r
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head["case"], args.cpu_budget)
+
+    out = {
+        "metric": "CSA2 decode query-tokens/s at 128K ctx (achieved HBM GB/s vs peak)",
+        "value": value,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3/fp4e2m1 inputs, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) pool and queries, MXFP4 / E4M3 encoded)",
+        "config": {"workload": cfg.name, "batch": cfg.B, "pool_entries": cfg.M, "K": cfg.K,
+                   "P": cfg.P, "W": cfg.W, "heads": cfg.H, "d": cfg.D,
+                   "layers": "/".join({0: "Full", 1: "Reindex", 2: "Reuse"}[m] for m in cfg.modes)},
+        "step_hbm_gbs": step_gbs,
+        "step_frac_of_peak": step_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": head["bytes"]["total"],
+        "roofline": {"bound": "hbm", "kernel": "k_index_score (indexer scan, histogram fused)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "bytes_per_launch": head["per_launch"], "mean_launch_ms": head["k_ms"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

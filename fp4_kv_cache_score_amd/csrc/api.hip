@@ -1,0 +1,298 @@
+// Host side of the C ABI: argument validation, workspace carving and the
+// per-layer Full / Reindex / Reuse dispatch.  Every check runs before the
+// first HIP call, so argument errors never touch the device.
+#include "csa2.h"
+#include "csa2_internal.h"
+
+using namespace csa2;
+
+namespace {
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+csa2_status check_pool(const csa2_pool* p) {
+  if (!p || !p->latent || !p->scale || !p->idx_key) return CSA2_ERR_NULL;
+  if (p->B <= 0 || p->M <= 0 || p->M > kMaxTopkN) return CSA2_ERR_SHAPE;
+  if (p->D != kD || p->HI != kHI || p->DI != kDI) return CSA2_ERR_SHAPE;
+  if (!al16(p->latent) || !al16(p->scale) || !al16(p->idx_key)) return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
+
+csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+constexpr int32_t kMaxW = 4096;
+constexpr int32_t kMaxRows = 65535;  // grid.y limit for row-indexed launches
+
+size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
+  const int64_t N = P > M ? P : M;
+  const int64_t Kmax = P > K ? P : K;
+  const int64_t splits = attn_splits_global((int32_t)K) + attn_splits_window((int32_t)W);
+  return align256(B * N * 4) + topk_ws_bytes(B, N, Kmax) + align256(B * (P > 0 ? P : 1) * 4) +
+         attn_ws_bytes(B, splits > 0 ? splits : 1);
+}
+
+// Top-K on already-written scores whose histogram is ready in ws.hist.
+csa2_status select_rows(const float* scores, int32_t R, int32_t N, const int32_t* n_valid,
+                        int32_t n_all, const int32_t* cand, int32_t K, int32_t* out,
+                        const TopkWs& t, hipStream_t s) {
+  return hip_status(launch_topk_select(scores, R, N, n_valid, n_all, cand, K, out, t, s));
+}
+
+// Zero the histogram and the per-row counters (adjacent in the workspace).
+csa2_status zero_hist_counters(const TopkWs& t, int64_t R, hipStream_t s) {
+  const int64_t words = (int64_t)((char*)t.counters - (char*)t.hist) / 4 + R * kCounterWords;
+  return hip_status(launch_fill_zero(t.hist, words, s));
+}
+
+csa2_status zero_counters(const TopkWs& t, int64_t R, hipStream_t s) {
+  return hip_status(launch_fill_zero(t.counters, R * kCounterWords, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_NULL: return "required pointer is NULL";
+    case CSA2_ERR_SHAPE: return "size out of range or unsupported";
+    case CSA2_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case CSA2_ERR_SCHEDULE: return "invalid layer mode schedule";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+const char* csa2_version(void) { return "csa2-mi355x 0.1.0 gfx950"; }
+
+size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K, int32_t P,
+                            int32_t W, int32_t H) {
+  if (B <= 0 || Q <= 0) return 0;
+  switch (op) {
+    case CSA2_OP_TOPK:
+      if (M <= 0 || K <= 0 || K > kMaxK || M > kMaxTopkN) return 0;
+      return topk_ws_bytes(B, M, K);
+    case CSA2_OP_SPARSE_ATTN:
+      if (K <= 0 || K > kMaxK || H != kH) return 0;
+      return attn_ws_bytes((int64_t)B * Q, attn_splits_global(K));
+    case CSA2_OP_SWA_MERGE:
+      if (W < 0 || W > kMaxW || H != kH) return 0;
+      return attn_ws_bytes((int64_t)B * Q, attn_splits_window(W) > 0 ? attn_splits_window(W) : 1);
+    case CSA2_OP_DECODE_LAYERS:
+      if (M <= 0 || K <= 0 || K > kMaxK || P < 0 || P > kMaxK || (P > 0 && P < K) ||
+          W < 0 || W > kMaxW || H != kH)
+        return 0;
+      return decode_ws_bytes(B, M, K, P, W);
+  }
+  return 0;
+}
+
+csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx, const float* w_idx,
+                             int32_t Q, int64_t pos0, int32_t ratio, const int32_t* cand,
+                             int32_t P, float* scores, uint32_t* hist, hipStream_t stream) {
+  csa2_status st = check_pool(pool);
+  if (st != CSA2_OK) return st;
+  if (!q_idx || !w_idx || !scores) return CSA2_ERR_NULL;
+  if (Q <= 0 || (int64_t)pool->B * Q > kMaxRows) return CSA2_ERR_SHAPE;
+  if (pos0 >= 0 && ratio <= 0) return CSA2_ERR_SHAPE;
+  if (cand && (P <= 0 || P > kMaxTopkN)) return CSA2_ERR_SHAPE;
+  if (!al16(q_idx) || !al4(w_idx) || !al4(scores) || (hist && !al4(hist)) || (cand && !al4(cand)))
+    return CSA2_ERR_ALIGN;
+  const int32_t N = cand ? P : pool->M;
+  return hip_status(launch_index_score(pool->idx_key, pool->B, pool->M, q_idx, w_idx, Q, pos0,
+                                       pos0 >= 0 ? ratio : 1, cand, N, scores, hist, stream));
+}
+
+csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* n_valid,
+                      const int32_t* cand, int32_t K, int32_t* idx, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  if (!scores || !idx) return CSA2_ERR_NULL;
+  if (R <= 0 || R > kMaxRows || N <= 0 || N > kMaxTopkN || K <= 0 || K > kMaxK)
+    return CSA2_ERR_SHAPE;
+  if (!al4(scores) || !al4(idx) || (n_valid && !al4(n_valid)) || (cand && !al4(cand)))
+    return CSA2_ERR_ALIGN;
+  if (!ws || ws_bytes < topk_ws_bytes(R, N, K)) return CSA2_ERR_WORKSPACE;
+  if (!al16(ws)) return CSA2_ERR_ALIGN;
+  const TopkWs t = topk_ws_carve(ws, R, N, K);
+  csa2_status st = zero_hist_counters(t, R, stream);
+  if (st != CSA2_OK) return st;
+  st = hip_status(launch_topk_hist(scores, R, N, n_valid, N, t.hist, stream));
+  if (st != CSA2_OK) return st;
+  return select_rows(scores, R, N, n_valid, N, cand, K, idx, t, stream);
+}
+
+csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q, int32_t H,
+                             const int32_t* idx, int32_t K, float* o, float* lse, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  csa2_status st = check_pool(pool);
+  if (st != CSA2_OK) return st;
+  if (!q || !idx || !o || !lse) return CSA2_ERR_NULL;
+  if (Q <= 0 || H != kH || K <= 0 || K > kMaxK || (int64_t)pool->B * Q > kMaxRows)
+    return CSA2_ERR_SHAPE;
+  if (!al16(q) || !al4(idx) || !al16(o) || !al4(lse)) return CSA2_ERR_ALIGN;
+  const int64_t rows = (int64_t)pool->B * Q;
+  const int32_t Sg = attn_splits_global(K);
+  if (!ws || ws_bytes < attn_ws_bytes(rows, Sg)) return CSA2_ERR_WORKSPACE;
+  if (!al16(ws)) return CSA2_ERR_ALIGN;
+  AttnArgs a{};
+  a.latent = pool->latent;
+  a.scale = pool->scale;
+  a.M = pool->M;
+  a.idx = idx;
+  a.K = K;
+  a.swa = nullptr;
+  a.W = 0;
+  a.swa_rows = 0;
+  a.q = q;
+  a.Q = Q;
+  a.rows = (int32_t)rows;
+  a.opart = (float*)ws;
+  a.ml = (float*)((char*)ws + align256(rows * Sg * kH * kD * 4));
+  st = hip_status(launch_attn_partial(a, stream));
+  if (st != CSA2_OK) return st;
+  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, Sg, nullptr, nullptr, o, lse, stream));
+}
+
+csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t D,
+                           const uint8_t* swa, int32_t W, float* o, float* lse, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!q || !o || !lse) return CSA2_ERR_NULL;
+  if (B <= 0 || Q <= 0 || H != kH || D != kD || W < 0 || W > kMaxW ||
+      (int64_t)B * Q > kMaxRows)
+    return CSA2_ERR_SHAPE;
+  if (W > 0 && !swa) return CSA2_ERR_NULL;
+  if (!al16(q) || !al16(o) || !al4(lse) || (swa && !al16(swa))) return CSA2_ERR_ALIGN;
+  const int64_t rows = (int64_t)B * Q;
+  const int32_t Sw = attn_splits_window(W);
+  if (!ws || ws_bytes < attn_ws_bytes(rows, Sw > 0 ? Sw : 1)) return CSA2_ERR_WORKSPACE;
+  if (!al16(ws)) return CSA2_ERR_ALIGN;
+  if (W == 0) return CSA2_OK;  // nothing to merge: (o, lse) unchanged
+  AttnArgs a{};
+  a.latent = nullptr;
+  a.scale = nullptr;
+  a.M = 0;
+  a.idx = nullptr;
+  a.K = 0;
+  a.swa = swa;
+  a.W = W;
+  a.swa_rows = Q + W - 1;
+  a.q = q;
+  a.Q = Q;
+  a.rows = (int32_t)rows;
+  a.opart = (float*)ws;
+  a.ml = (float*)((char*)ws + align256(rows * Sw * kH * kD * 4));
+  csa2_status st = hip_status(launch_attn_partial(a, stream));
+  if (st != CSA2_OK) return st;
+  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, Sw, o, lse, o, lse, stream));
+}
+
+csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
+                               int32_t H, int32_t K, int32_t P, int32_t W, int32_t* src_layer,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  csa2_status st = check_pool(pool);
+  if (st != CSA2_OK) return st;
+  if (!layers) return CSA2_ERR_NULL;
+  if (L <= 0 || H != kH || K <= 0 || K > kMaxK || P < 0 || P > kMaxK || (P > 0 && P < K) ||
+      W < 0 || W > kMaxW || pool->B > kMaxRows)
+    return CSA2_ERR_SHAPE;
+  // Schedule and per-layer arguments.
+  if (layers[0].mode != CSA2_FULL) return CSA2_ERR_SCHEDULE;
+  for (int32_t l = 0; l < L; ++l) {
+    const csa2_layer& y = layers[l];
+    if (y.mode != CSA2_FULL && y.mode != CSA2_REINDEX && y.mode != CSA2_REUSE)
+      return CSA2_ERR_SCHEDULE;
+    if (!y.q || !y.o || !y.lse) return CSA2_ERR_NULL;
+    if (W > 0 && !y.swa) return CSA2_ERR_NULL;
+    if (y.mode != CSA2_REUSE && (!y.q_idx || !y.w_idx || !y.idx_out)) return CSA2_ERR_NULL;
+    if (!al16(y.q) || !al16(y.o) || !al4(y.lse) || (y.swa && !al16(y.swa)) ||
+        (y.q_idx && y.mode != CSA2_REUSE && !al16(y.q_idx)) ||
+        (y.w_idx && y.mode != CSA2_REUSE && !al4(y.w_idx)) || (y.idx_out && !al4(y.idx_out)))
+      return CSA2_ERR_ALIGN;
+  }
+  const int64_t B = pool->B, M = pool->M;
+  const size_t need = decode_ws_bytes(B, M, K, P, W);
+  if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+  if (!al16(ws)) return CSA2_ERR_ALIGN;
+
+  // Workspace: scores | Top-K scratch | candidate pool | attention partials.
+  const int64_t N = P > M ? P : M;
+  const int64_t Kmax = P > K ? P : K;
+  char* p = (char*)ws;
+  float* scores = (float*)p;
+  p += align256(B * N * 4);
+  const TopkWs t = topk_ws_carve(p, B, N, Kmax);
+  p += topk_ws_bytes(B, N, Kmax);
+  int32_t* cand = (int32_t*)p;
+  p += align256(B * (P > 0 ? P : 1) * 4);
+  const int32_t Sg = attn_splits_global(K), Sw = attn_splits_window(W);
+  float* opart = (float*)p;
+  float* ml = (float*)(p + align256(B * (Sg + Sw) * kH * kD * 4));
+
+  const int32_t* cur = nullptr;
+  int32_t cur_layer = -1;
+  const int32_t n_cand = (int32_t)(P < M ? P : M);
+  for (int32_t l = 0; l < L; ++l) {
+    const csa2_layer& y = layers[l];
+    if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
+      st = zero_hist_counters(t, B, stream);
+      if (st != CSA2_OK) return st;
+      st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
+                                         nullptr, (int32_t)M, scores, t.hist, stream));
+      if (st != CSA2_OK) return st;
+      if (y.mode == CSA2_FULL && P > 0) {
+        st = select_rows(scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P, cand, t,
+                         stream);
+        if (st != CSA2_OK) return st;
+        st = zero_counters(t, B, stream);
+        if (st != CSA2_OK) return st;
+      }
+      st = select_rows(scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, K, y.idx_out,
+                       t, stream);
+      if (st != CSA2_OK) return st;
+      cur = y.idx_out;
+      cur_layer = l;
+    } else if (y.mode == CSA2_REINDEX) {  // hierarchical: score inside the candidate pool
+      st = zero_hist_counters(t, B, stream);
+      if (st != CSA2_OK) return st;
+      st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
+                                         cand, P, scores, t.hist, stream));
+      if (st != CSA2_OK) return st;
+      st = select_rows(scores, (int32_t)B, P, nullptr, n_cand, cand, K, y.idx_out, t, stream);
+      if (st != CSA2_OK) return st;
+      cur = y.idx_out;
+      cur_layer = l;
+    } else {  // Reuse
+      if (y.idx_out && y.idx_out != cur) {
+        st = hip_status(launch_copy_i32(y.idx_out, cur, B * K, stream));
+        if (st != CSA2_OK) return st;
+      }
+    }
+    if (src_layer) src_layer[l] = cur_layer;
+
+    AttnArgs a{};
+    a.latent = pool->latent;
+    a.scale = pool->scale;
+    a.M = M;
+    a.idx = cur;
+    a.K = K;
+    a.swa = y.swa;
+    a.W = W;
+    a.swa_rows = W;
+    a.q = y.q;
+    a.Q = 1;
+    a.rows = (int32_t)B;
+    a.opart = opart;
+    a.ml = ml;
+    st = hip_status(launch_attn_partial(a, stream));
+    if (st != CSA2_OK) return st;
+    st = hip_status(launch_attn_combine(opart, ml, (int32_t)B, Sg + Sw, nullptr, nullptr, y.o,
+                                        y.lse, stream));
+    if (st != CSA2_OK) return st;
+  }
+  return CSA2_OK;
+}
+
+}  // extern "C"

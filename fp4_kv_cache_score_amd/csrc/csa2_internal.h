@@ -1,0 +1,139 @@
+// Internal definitions shared by the CSA2 HIP translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace csa2 {
+
+// Fixed shapes of this build.
+constexpr int kD = 512;          // latent width (shared K/V)
+constexpr int kLatRow = kD / 2;  // E2M1 bytes per latent row
+constexpr int kScaleRow = kD / 32;  // E8M0 scales per latent row
+constexpr int kHI = 8;           // indexer heads
+constexpr int kDI = 64;          // indexer head width
+constexpr int kKeyRow = kHI * kDI;  // E4M3 bytes per indexer key row
+constexpr int kH = 16;           // attention heads
+
+// Top-K
+constexpr int kHistBits = 12;               // first radix digit: top 12 key bits
+constexpr int kHistBins = 1 << kHistBits;   // 4096
+constexpr int kMaxK = 16384;
+constexpr int kMaxTopkN = 1 << 30;          // row length limit (composite key packs 30 bits)
+constexpr int kCounterWords = 4;            // per row: [0]=above count, [1]=candidate count
+
+// Attention
+constexpr int kKeysPerSplit = 32;           // keys staged per work-group
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Order-preserving map of a float score to uint32 (-0 folded onto +0):
+// a > b as reals  <=>  key(a) > key(b).
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Workspace carving for Top-K over R rows of N with up to K selected.
+struct TopkWs {
+  uint32_t* hist;      // [R][kHistBins]
+  uint32_t* counters;  // [R][kCounterWords]
+  int32_t* sel;        // [R][K]   positions strictly above the threshold bin
+  uint32_t* candk;     // [R][cap] keys of positions inside the threshold bin
+  int32_t* candp;      // [R][cap] their positions
+  int32_t cap;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int32_t topk_cap(int64_t R, int64_t N) {
+  // Candidate slots per row: every position for modest row counts, otherwise
+  // 16384 (the finish step re-scans the row when a threshold bin overflows).
+  int64_t c = (int64_t(1) << 25) / (R > 0 ? R : 1);
+  if (c < 16384) c = 16384;
+  if (c > N) c = N;
+  return (int32_t)(c > 0 ? c : 1);
+}
+
+inline size_t topk_ws_bytes(int64_t R, int64_t N, int64_t K) {
+  int64_t cap = topk_cap(R, N);
+  return align256(R * kHistBins * 4) + align256(R * kCounterWords * 4) +
+         align256(R * K * 4) + align256(R * cap * 4) * 2;
+}
+
+inline TopkWs topk_ws_carve(void* ws, int64_t R, int64_t N, int64_t K) {
+  TopkWs t;
+  char* p = (char*)ws;
+  t.cap = topk_cap(R, N);
+  t.hist = (uint32_t*)p;     p += align256(R * kHistBins * 4);
+  t.counters = (uint32_t*)p; p += align256(R * kCounterWords * 4);
+  t.sel = (int32_t*)p;       p += align256(R * K * 4);
+  t.candk = (uint32_t*)p;    p += align256(R * (int64_t)t.cap * 4);
+  t.candp = (int32_t*)p;
+  return t;
+}
+
+// Attention partials: per (row, split) one [kH][kD] unnormalised output and
+// kH (max, sum) pairs.
+inline size_t attn_ws_bytes(int64_t rows, int64_t splits) {
+  return align256(rows * splits * kH * kD * 4) + align256(rows * splits * kH * 2 * 4);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (each returns the hipError_t of its launch)
+// ---------------------------------------------------------------------------
+
+// Zero n 32-bit words (a kernel, so that it is safe inside captured graphs).
+hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t s);
+
+// Indexer scores; see csa2_index_score.  n_valid_rows (optional, [rows]) is
+// written with each row's count of scored positions.
+hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
+                              const uint8_t* q_idx, const float* w_idx,
+                              int32_t Q, int64_t pos0, int32_t ratio,
+                              const int32_t* cand, int32_t N, float* scores,
+                              uint32_t* hist, hipStream_t s);
+
+// Top-K pieces.  n_valid: device [R] or NULL (then n_all applies to every row).
+hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
+                            const int32_t* n_valid, int32_t n_all,
+                            uint32_t* hist, hipStream_t s);
+hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
+                              const int32_t* n_valid, int32_t n_all,
+                              const int32_t* cand, int32_t K, int32_t* out,
+                              const TopkWs& ws, hipStream_t s);
+
+// Attention over up to K gathered FP4 entries and up to W FP8 window rows per
+// query row, written as split partials; then the log-sum-exp combine (which
+// may fold in an incoming (o, lse)).
+struct AttnArgs {
+  const uint8_t* latent;  // [B][M][kLatRow]
+  const uint8_t* scale;   // [B][M][kScaleRow]
+  int64_t M;
+  const int32_t* idx;     // [rows][K]
+  int32_t K;
+  const uint8_t* swa;     // [B][swa_rows][kD]
+  int32_t W;
+  int32_t swa_rows;       // rows per sequence in swa (Q + W - 1)
+  const uint16_t* q;      // [rows][kH][kD] bf16
+  int32_t Q;              // query rows per sequence
+  int32_t rows;           // B * Q
+  float* opart;           // [rows][splits][kH][kD]
+  float* ml;              // [rows][splits][kH][2]
+};
+int32_t attn_splits_global(int32_t K);
+int32_t attn_splits_window(int32_t W);
+hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_combine(const float* opart, const float* ml,
+                               int32_t rows, int32_t splits,
+                               const float* o_in, const float* lse_in,
+                               float* o, float* lse, hipStream_t s);
+
+// Copy n int32 (Reuse layers that ask for their indices).
+hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
+
+}  // namespace csa2

@@ -1,0 +1,162 @@
+// Indexer score kernel: streams E4M3 index keys from HBM, one pass per query row.
+//
+// Reading of the pages (they give no formula, only that Full / Reindex layers
+// score the context with an indexer, "DeepSeek V4.1-Flash Cuts KV Cache by
+// 437x", paragraph on the three operating modes):
+//   s_j = sum_h w_h * ReLU(sum_i qI[h][i] * kI[j][h][i]),  8 heads x 64 E4M3.
+//
+// Work split: a pool entry's 512-byte key row is read by 32 lanes with one
+// 16-byte load each (two entries per wave64 load), so every wave load is a
+// fully coalesced 1 KiB.  Lane (sub = lane & 31) owns bytes [16*sub, 16*sub+16)
+// of the row, i.e. indexer head sub/4 and 16 of its 64 dims.  The FP8 x FP8
+// products are exact in fp32; each lane accumulates its 16 products with
+// fmaf, a 4-lane butterfly completes the head dot, then ReLU, the head weight
+// and an 8-head butterfly give the score.  Every lane holds the full query
+// slice it needs in registers, so HBM sees each key byte exactly once.
+// Optionally the kernel adds the scores' top-12-bit order keys into a
+// per-row histogram (the first radix digit of the Top-K select), built in
+// LDS per work-group and flushed with one atomic per non-empty bin.
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;                        // 16-byte loads in flight per lane
+constexpr int kEntriesPerWave = 128;
+constexpr int kEntriesPerWG = kEntriesPerWave * (kThreads / 64);   // 512
+constexpr int kIters = kEntriesPerWave / (2 * kUnroll);            // 8
+
+__device__ __forceinline__ float bfly_add(float v, int m) {
+  return v + __shfl_xor(v, m, 64);
+}
+
+template <bool kCand, bool kHist>
+__global__ __launch_bounds__(kThreads)
+void k_index_score(const uint8_t* __restrict__ key, int64_t M,
+                   const uint8_t* __restrict__ q_idx,
+                   const float* __restrict__ w_idx, int32_t Q, int64_t pos0,
+                   int32_t ratio, const int32_t* __restrict__ cand, int32_t N,
+                   float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t lh[kHist ? kHistBins : 1];
+  const int row = blockIdx.y;
+  const int b = row / Q;
+  const int t = row - b * Q;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int sub = lane & 31;
+  const int head = sub >> 2;
+
+  // Entries visible to this query (all of them when there is no causal limit).
+  int64_t vis = M;
+  if (pos0 >= 0) {
+    const int64_t v = (pos0 + t + 1) / ratio;
+    vis = v < M ? v : M;
+  }
+
+  float qf[16];
+  {
+    const u32x4 qv = *reinterpret_cast<const u32x4*>(q_idx + (size_t)row * kKeyRow + sub * 16);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)qv[d], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)qv[d], true);
+      qf[4 * d + 0] = lo.x;
+      qf[4 * d + 1] = lo.y;
+      qf[4 * d + 2] = hi.x;
+      qf[4 * d + 3] = hi.y;
+    }
+  }
+  const float wh = w_idx[(size_t)row * kHI + head];
+
+  if (kHist) {
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) lh[i] = 0u;
+    __syncthreads();
+  }
+
+  const uint8_t* kb = key + (size_t)b * (size_t)M * kKeyRow + sub * 16;
+  const int32_t* cb = kCand ? cand + (size_t)b * N : nullptr;
+  float* srow = scores + (size_t)row * N;
+  const int64_t wbase = (int64_t)blockIdx.x * kEntriesPerWG + wave * kEntriesPerWave;
+
+  for (int it = 0; it < kIters; ++it) {
+    u32x4 v[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t p = wbase + it * (2 * kUnroll) + 2 * u + half;
+      int64_t e = p;
+      bool valid = p < N;
+      if (kCand && valid) {
+        e = cb[p];
+        valid = e >= 0;
+      }
+      valid = valid && e < vis;
+      ok[u] = valid;
+      if (valid) {
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + e * kKeyRow));
+      } else {
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u][d], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u][d], true);
+        acc = fmaf(lo.x, qf[4 * d + 0], acc);
+        acc = fmaf(lo.y, qf[4 * d + 1], acc);
+        acc = fmaf(hi.x, qf[4 * d + 2], acc);
+        acc = fmaf(hi.y, qf[4 * d + 3], acc);
+      }
+      acc = bfly_add(acc, 1);
+      acc = bfly_add(acc, 2);
+      float r = acc > 0.f ? acc * wh : 0.f;
+      r = bfly_add(r, 4);
+      r = bfly_add(r, 8);
+      r = bfly_add(r, 16);
+      const int64_t p = wbase + it * (2 * kUnroll) + 2 * u + half;
+      if (sub == 0 && p < N) {
+        srow[p] = ok[u] ? r : -INFINITY;
+        if (kHist && ok[u]) atomicAdd(&lh[score_key(r) >> (32 - kHistBits)], 1u);
+      }
+    }
+  }
+
+  if (kHist) {
+    __syncthreads();
+    uint32_t* hrow = hist + (size_t)row * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) {
+      const uint32_t c = lh[i];
+      if (c) atomicAdd(&hrow[i], c);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
+                              const uint8_t* q_idx, const float* w_idx,
+                              int32_t Q, int64_t pos0, int32_t ratio,
+                              const int32_t* cand, int32_t N, float* scores,
+                              uint32_t* hist, hipStream_t s) {
+  const dim3 grid((unsigned)((N + kEntriesPerWG - 1) / kEntriesPerWG), (unsigned)(B * Q));
+  const dim3 block(kThreads);
+  if (cand) {
+    if (hist)
+      k_index_score<true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+    else
+      k_index_score<true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+  } else {
+    if (hist)
+      k_index_score<false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+    else
+      k_index_score<false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,155 @@
+"""Device buffers for a CSA2 workload and the calls that run it (torch = plumbing).
+
+`DeviceCase` uploads a host case (pool, per-layer queries and windows) to HBM
+as torch uint8 / uint16 / float32 / int32 tensors, allocates outputs and the
+workspace, and drives the C ABI through the ctypes binding.  No arithmetic
+of the method happens here.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import _lib as C
+from .configs import FULL, REINDEX, REUSE
+from .synth import HostCase
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceCase:
+    def __init__(self, case: HostCase, device: str = "cuda"):
+        cfg = case.cfg
+        self.cfg = cfg
+        self.device = device
+        p = case.pool
+        self.latent = _dev(p.latent, device)
+        self.scale = _dev(p.scale, device)
+        self.idx_key = _dev(p.idx_key, device)
+        self.pool = C.make_pool(self.latent, self.scale, self.idx_key, cfg.B, cfg.M, cfg.D,
+                                cfg.HI, cfg.DI)
+        B, Q, H, D, K = cfg.B, cfg.Q, cfg.H, cfg.D, cfg.K
+        self.layers = []
+        for L in case.layers:
+            d = dict(mode=L.mode, q=_dev(L.q, device), swa=_dev(L.swa, device),
+                     q_idx=None if L.q_idx is None else _dev(L.q_idx, device),
+                     w_idx=None if L.w_idx is None else _dev(L.w_idx, device))
+            d["o"] = torch.empty((B, Q, H, D), dtype=torch.float32, device=device)
+            d["lse"] = torch.empty((B, Q, H), dtype=torch.float32, device=device)
+            d["idx"] = torch.empty((B, Q, K), dtype=torch.int32, device=device)
+            self.layers.append(d)
+        self.ws = None
+        self.ws_bytes = 0
+        self.src_layer: Optional[List[int]] = None
+
+    # -- workspace -----------------------------------------------------------
+    def _workspace(self, nbytes: int) -> torch.Tensor:
+        if self.ws is None or self.ws_bytes < nbytes:
+            self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self.ws_bytes = nbytes
+        return self.ws
+
+    # -- decode step ---------------------------------------------------------
+    def layer_structs(self, idx_for_reuse: bool = True):
+        out = []
+        for d in self.layers:
+            reuse = d["mode"] == REUSE
+            out.append(C.csa2_layer(d["mode"], C._p(d["q_idx"]), C._p(d["w_idx"]),
+                                    C._p(d["q"]), C._p(d["swa"]), C._p(d["o"]),
+                                    C._p(d["lse"]),
+                                    C._p(d["idx"]) if (idx_for_reuse or not reuse) else None))
+        return out
+
+    def decode_workspace_bytes(self) -> int:
+        cfg = self.cfg
+        return C.csa2_workspace_bytes(C.CSA2_OP_DECODE_LAYERS, cfg.B, 1, cfg.M, cfg.K, cfg.P,
+                                      cfg.W, cfg.H)
+
+    def prepare_decode(self, idx_for_reuse: bool = True):
+        assert self.cfg.Q == 1, "decode_layers runs one query token per sequence"
+        nb = self.decode_workspace_bytes()
+        assert nb > 0
+        self._workspace(nb)
+        self._structs = self.layer_structs(idx_for_reuse)
+
+    def decode_layers(self, stream=None):
+        if getattr(self, "_structs", None) is None:
+            self.prepare_decode()
+        cfg = self.cfg
+        _, src = C.csa2_decode_layers(self.pool, self._structs, cfg.H, cfg.K, cfg.P, cfg.W,
+                                      self.ws, self.ws_bytes, stream)
+        self.src_layer = src
+        return src
+
+    # -- single-stage calls ----------------------------------------------------
+    def index_scores(self, ell: int, cand=None, P: int = 0, hist=None, stream=None):
+        cfg = self.cfg
+        d = self.layers[ell]
+        N = P if cand is not None else cfg.M
+        scores = torch.empty((cfg.B, cfg.Q, N), dtype=torch.float32, device=self.device)
+        C.csa2_index_score(self.pool, d["q_idx"], d["w_idx"], cfg.Q, cfg.pos0, cfg.ratio, cand,
+                           P, scores, hist, stream)
+        return scores
+
+    def topk(self, scores: torch.Tensor, K: int, n_valid=None, cand=None, stream=None):
+        R = scores.numel() // scores.shape[-1]
+        N = scores.shape[-1]
+        nb = C.csa2_workspace_bytes(C.CSA2_OP_TOPK, R, 1, N, K, 0, 0, 0)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        idx = torch.empty((R, K), dtype=torch.int32, device=self.device)
+        C.csa2_topk(scores, R, N, n_valid, cand, K, idx, ws, nb, stream)
+        return idx
+
+    def sparse_attn(self, ell: int, idx: torch.Tensor, stream=None):
+        cfg = self.cfg
+        d = self.layers[ell]
+        K = idx.shape[-1]
+        nb = C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, cfg.B, cfg.Q, cfg.M, K, 0, 0, cfg.H)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        o = torch.empty((cfg.B, cfg.Q, cfg.H, cfg.D), dtype=torch.float32, device=self.device)
+        lse = torch.empty((cfg.B, cfg.Q, cfg.H), dtype=torch.float32, device=self.device)
+        C.csa2_sparse_attn(self.pool, d["q"], cfg.Q, cfg.H, idx.contiguous(), K, o, lse, ws, nb,
+                           stream)
+        return o, lse
+
+    def swa_merge(self, ell: int, o: torch.Tensor, lse: torch.Tensor, stream=None):
+        cfg = self.cfg
+        d = self.layers[ell]
+        nb = C.csa2_workspace_bytes(C.CSA2_OP_SWA_MERGE, cfg.B, cfg.Q, 0, 0, 0, cfg.W, cfg.H)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        C.csa2_swa_merge(d["q"], cfg.B, cfg.Q, cfg.H, cfg.D, d["swa"], cfg.W, o, lse, ws, nb,
+                         stream)
+        return o, lse
+
+    # -- causal chunked prefill (one Full layer) ---------------------------------
+    def visible_counts(self) -> torch.Tensor:
+        cfg = self.cfg
+        t = np.arange(cfg.Q, dtype=np.int64)
+        vis = np.minimum(cfg.M, (cfg.pos0 + t + 1) // cfg.ratio) if cfg.pos0 >= 0 else \
+            np.full(cfg.Q, cfg.M)
+        return torch.from_numpy(np.tile(vis.astype(np.int32), cfg.B)).to(self.device)
+
+    def prefill(self, stream=None):
+        """index_score (Q rows, causal) -> topk (n_valid = visible) -> sparse_attn -> swa_merge."""
+        cfg = self.cfg
+        scores = self.index_scores(0, stream=stream)
+        idx = self.topk(scores, cfg.K, n_valid=self.visible_counts(), stream=stream)
+        idx = idx.view(cfg.B, cfg.Q, cfg.K)
+        o, lse = self.sparse_attn(0, idx, stream=stream)
+        o, lse = self.swa_merge(0, o, lse, stream=stream)
+        return idx, o, lse
+
+    # -- results -----------------------------------------------------------------
+    def results(self):
+        out = []
+        for d in self.layers:
+            out.append(dict(mode=d["mode"], idx=d["idx"].cpu().numpy(), o=d["o"].cpu().numpy(),
+                            lse=d["lse"].cpu().numpy()))
+        return out

@@ -1,0 +1,212 @@
+/*
+ * csa2.h - C ABI of the CSA2 (Compressed Sparse Attention 2) hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * CSA2 keeps one global KV pool for all layers and gives every layer one of
+ * three static modes (Full / Reindex / Reuse); a hierarchical candidate pool
+ * serves very long contexts; the global entries are FP4 (E2M1) restored to
+ * real values at run time and a sliding window of FP8 rows covers nearby
+ * tokens.  Sources: "DeepSeek V4.1-Flash Cuts KV Cache by 437x With New CED
+ * and CSA2 Architecture" (paragraphs on CSA2 storage, the three operating
+ * modes, sliding window attention and FP4 quantisation) and "DeepSeek V4.1
+ * Flash Architecture Breakdown" (sections "How does the cache compress along
+ * three dimensions at once?" and "How are cache precision and storage
+ * arranged?").  The pages give no formulas, sizes or layouts; the readings
+ * used here are stated per function.
+ *
+ * Conventions for every entry point
+ *  - All array pointers are DEVICE pointers unless marked "host".  Arrays are
+ *    dense, row-major, in the shapes given.  The caller owns every buffer; the
+ *    library allocates no device memory and keeps no global state.
+ *  - Work is enqueued on `stream` (0 = the null stream) and returns without
+ *    synchronising.  Outputs are fully overwritten.
+ *  - Argument and schedule errors are detected on the host and returned
+ *    before any HIP call is made.  A failed launch returns CSA2_ERR_HIP.
+ *    Faults inside kernels surface at the caller's next synchronisation.
+ *  - Device-side preconditions (not checked): no NaN E4M3 codes (0x7F, 0xFF),
+ *    E8M0 scale codes 0..252, selected indices in [-1, M), candidate lists
+ *    strictly ascending with -1 padding only at the end.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - Fixed shapes of this build: latent width D = 512, indexer HI = 8 heads of
+ *    DI = 64, attention heads H = 16.  Other values return CSA2_ERR_SHAPE.
+ *
+ * Number formats
+ *  - E4M3: OCP FP8 E4M3 (bias 7, max 448, no infinity).
+ *  - E2M1: OCP FP4, two codes per byte, element 2i in the LOW nibble of byte i.
+ *  - E8M0: OCP block scale 2^(x-127), one per 32 consecutive latent elements.
+ *  - bf16: the upper 16 bits of an IEEE binary32, passed as uint16_t.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum csa2_status {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,       /* a required pointer is NULL */
+  CSA2_ERR_SHAPE = 2,      /* a size is out of range or unsupported */
+  CSA2_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned */
+  CSA2_ERR_SCHEDULE = 4,   /* invalid per-layer mode schedule */
+  CSA2_ERR_WORKSPACE = 5,  /* workspace missing or too small */
+  CSA2_ERR_HIP = 6         /* a HIP launch or runtime call failed */
+} csa2_status;
+
+enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 };
+
+/* Which call a workspace size is asked for (csa2_workspace_bytes). */
+enum {
+  CSA2_OP_TOPK = 0,
+  CSA2_OP_SPARSE_ATTN = 1,
+  CSA2_OP_SWA_MERGE = 2,
+  CSA2_OP_DECODE_LAYERS = 3
+};
+
+/* The shared global KV pool: B sequences of M compressed entries each.
+ * Every sequence has its own M entries (structure of arrays):
+ *   latent  [B][M][D/2]     E2M1 codes of the D-wide shared K/V latent
+ *   scale   [B][M][D/32]    E8M0 block scales of the latent
+ *   idx_key [B][M][HI][DI]  E4M3 indexer keys
+ * All three pointers must be 16-byte aligned. */
+typedef struct csa2_pool {
+  const uint8_t* latent;
+  const uint8_t* scale;
+  const uint8_t* idx_key;
+  int32_t B, M, D, HI, DI;
+} csa2_pool;
+
+/* One layer of a decode step (one query token per sequence).
+ *   mode    CSA2_FULL, CSA2_REINDEX or CSA2_REUSE
+ *   q_idx   [B][HI][DI] E4M3 indexer query   (Full / Reindex; ignored for Reuse)
+ *   w_idx   [B][HI] float indexer head weights (Full / Reindex; ignored for Reuse)
+ *   q       [B][H][D] bf16 attention query (already scaled by 1/sqrt(D))
+ *   swa     [B][W][D] E4M3 sliding-window rows (may be NULL when W == 0)
+ *   o       [B][H][D] float output
+ *   lse     [B][H] float output, natural-log sum of exp of the logits
+ *   idx_out [B][K] int32 selected global entries, ascending, -1 padded.
+ *           Required for Full / Reindex; for Reuse it may be NULL, otherwise
+ *           it receives a copy of the source layer's indices. */
+typedef struct csa2_layer {
+  int32_t mode;
+  const uint8_t* q_idx;
+  const float* w_idx;
+  const uint16_t* q;
+  const uint8_t* swa;
+  float* o;
+  float* lse;
+  int32_t* idx_out;
+} csa2_layer;
+
+/* Indexer scores of pool entries.
+ * Reading (the pages give no formula): for query row r = (b, t) and pool
+ * entry j,  s = sum_h w[r][h] * ReLU(sum_i q_idx[r][h][i] * idx_key[b][j][h][i])
+ * with E4M3 operands, fp32 products (exact) and fp32 accumulation; ReLU maps
+ * x <= 0 to +0.  The pages' Full layer scores the whole context, a Reindex
+ * layer re-scores with its own indexer, and in the hierarchical case it
+ * scores only inside the candidate pool ("... Cuts KV Cache by 437x",
+ * paragraph on the three operating modes).
+ *   pool    the pool (B, M used)
+ *   q_idx   [B][Q][HI][DI] E4M3;  w_idx [B][Q][HI] float
+ *   Q       query tokens per sequence (1 for decode)
+ *   pos0    < 0: every entry is visible.  >= 0: query t sits at position
+ *           pos0 + t and sees the first min(M, (pos0 + t + 1) / ratio) entries
+ *           (an entry is visible once its last token is); scores of
+ *           invisible positions are written as -inf.
+ *   ratio   tokens per pool entry (used only when pos0 >= 0; must be >= 1)
+ *   cand    NULL: score all M entries, N = M.  Otherwise [B][P] ascending
+ *           global entry numbers, -1 padded; N = P, and position p scores
+ *           entry cand[b][p] (-inf for -1).
+ *   scores  [B][Q][N] float output
+ *   hist    NULL, or [B*Q][4096] uint32 histogram that the call ADDS the
+ *           score keys' top 12 bits to (see csa2_topk); caller zeroes it. */
+csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx,
+                             const float* w_idx, int32_t Q, int64_t pos0,
+                             int32_t ratio, const int32_t* cand, int32_t P,
+                             float* scores, uint32_t* hist, hipStream_t stream);
+
+/* Top-K selection per row.
+ * For each of R rows of N scores, select the K largest among the first
+ * n_valid[r] positions (all N when n_valid is NULL).  Equal scores are broken
+ * toward the LOWER position (= lower global entry, since candidate lists are
+ * ascending).  The selection is written as ascending entry numbers (through
+ * cand when given), padded with -1 when fewer than K positions are valid.
+ * Scores compare as real numbers (-0 == +0); NaN scores are not allowed.
+ *   scores  [R][N] float;  n_valid NULL or [R] int32
+ *   cand    NULL (output positions) or [R][N] int32 position -> entry map
+ *   idx     [R][K] int32 output
+ *   ws      workspace of at least csa2_workspace_bytes(CSA2_OP_TOPK, R, 1, N, K, 0, 0, 0)
+ * Limits: 1 <= K <= 16384, 1 <= N < 2^31. */
+csa2_status csa2_topk(const float* scores, int32_t R, int32_t N,
+                      const int32_t* n_valid, const int32_t* cand, int32_t K,
+                      int32_t* idx, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Attention over selected FP4 global entries.
+ * Per query row (b, t) and head h, the keys (= values) are the dequantised
+ * latent rows c_j[i] = E2M1(code) * 2^(scale - 127) of the selected entries
+ * (idx != -1); logits z_j = q[h] . c_j (scale 1); o[h] = sum softmax(z)_j c_j
+ * and lse[h] = log sum exp(z).  No selected entry gives o = 0, lse = -inf.
+ *   q    [B][Q][H][D] bf16;  idx [B][Q][K] int32 in [-1, M)
+ *   o    [B][Q][H][D] float;  lse [B][Q][H] float
+ *   ws   at least csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, Q, M, K, 0, 0, H) */
+csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q,
+                             int32_t Q, int32_t H, const int32_t* idx,
+                             int32_t K, float* o, float* lse, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Sliding-window attention merged into an earlier result.
+ * Query row (b, t) attends to the W E4M3 rows t .. t+W-1 of swa[b] (the
+ * window of the newest tokens including its own) and the result is merged
+ * with the incoming (o, lse) as one softmax over the union of both key sets:
+ *   lse' = log(e^lse + e^lse_w),  o' = (e^lse o + e^lse_w o_w) / e^lse'.
+ * The pages pair the sparse global entries with an FP8 sliding window for
+ * nearby tokens ("... Cuts KV Cache by 437x", paragraph on sliding window
+ * attention); merging by log-sum-exp is an exact rewrite of one softmax.
+ *   q    [B][Q][H][D] bf16;  swa [B][Q+W-1][D] E4M3
+ *   o    [B][Q][H][D] float, in/out;  lse [B][Q][H] float, in/out
+ *   ws   at least csa2_workspace_bytes(CSA2_OP_SWA_MERGE, B, Q, 0, 0, 0, W, H) */
+csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H,
+                           int32_t D, const uint8_t* swa, int32_t W, float* o,
+                           float* lse, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* One decode step through a static per-layer mode schedule over one pool.
+ * Layers run in order.  Full: score all M entries, select Top-K; with P > 0
+ * it also builds the candidate pool = Top-P of the same scores (ascending).
+ * Reindex: with P == 0 score all M with its own indexer; with P > 0 score only
+ * the candidate pool.  Reuse: no index work, take the indices of the most
+ * recent Full or Reindex layer.  Then every layer attends over its selected
+ * entries plus its W window rows (one softmax).  The first layer must be Full.
+ *   layers     host array [L]
+ *   K          selected entries per layer (1..16384); P: 0 = flat, else K <= P
+ *   W          window rows per layer (0..4096)
+ *   src_layer  NULL or host [L] output: the layer whose indices each layer
+ *              uses (itself for Full / Reindex)
+ *   ws         at least csa2_workspace_bytes(CSA2_OP_DECODE_LAYERS, B, 1, M, K, P, W, H) */
+csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers,
+                               int32_t L, int32_t H, int32_t K, int32_t P,
+                               int32_t W, int32_t* src_layer, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by an entry point (op = CSA2_OP_*).  Arguments that
+ * an op does not use are ignored.  For CSA2_OP_TOPK, B is the row count R and
+ * M the row length N.  Returns 0 for an unknown op or bad sizes. */
+size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K,
+                            int32_t P, int32_t W, int32_t H);
+
+/* Static, human-readable name of a status code. */
+const char* csa2_status_string(csa2_status s);
+
+/* Library version string (static). */
+const char* csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

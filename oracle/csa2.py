@@ -216,8 +216,9 @@ def decode_sequence(latent, scale, idx_key, layers, K: int, P: int = 0):
         if mode == FULL:
             s = index_scores(idx_key, L["q_idx"], L["w_idx"])
             if P > 0:
-                cand, _ = topk(s, P)
+                cand, cand_gap = topk(s, P)
                 rec["cand"] = cand
+                rec["cand_gap"] = cand_gap
             idx, gap = topk(s, K)
             rec.update(scores=s, gap=gap)
         elif mode == REINDEX:

@@ -1,0 +1,163 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments on the host
+before any HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_kv_cache_score_amd import _lib as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+if not os.path.exists(C.LIB_PATH):
+    pytest.skip("libcsa2.so not built (run python -m fp4_kv_cache_score_amd.build)",
+                allow_module_level=True)
+
+A = 0x10000   # a 16-byte-aligned fake device address: never dereferenced here
+A2 = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(C.EXPORTS)
+    L = ctypes.CDLL(C.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in C.csa2_version()
+
+
+def test_status_strings():
+    for s in range(7):
+        assert C.csa2_status_string(s)
+    assert C.csa2_status_string(0) == "ok"
+    assert "unknown" in C.csa2_status_string(99)
+
+
+def test_workspace_bytes():
+    ws = C.csa2_workspace_bytes
+    assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 512, 0, 0, 0) > 32 * 4096 * 4
+    assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 0, 0, 0, 0) == 0
+    assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 16385, 0, 0, 0) == 0
+    assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 16) >= 32 * 16 * 16 * 512 * 4
+    assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 8) == 0
+    assert ws(C.CSA2_OP_SWA_MERGE, 32, 1, 0, 0, 0, 128, 16) >= 32 * 4 * 16 * 512 * 4
+    d = ws(C.CSA2_OP_DECODE_LAYERS, 8, 1, 262144, 512, 8192, 128, 16)
+    assert d >= 8 * 262144 * 4
+    assert ws(C.CSA2_OP_DECODE_LAYERS, 8, 1, 262144, 512, 256, 128, 16) == 0  # P < K
+    assert ws(99, 1, 1, 1, 1, 0, 0, 16) == 0
+
+
+def _pool(**kw):
+    d = dict(latent=A, scale=A, idx_key=A, B=2, M=1024)
+    d.update(kw)
+    return C.make_pool(d["latent"], d["scale"], d["idx_key"], d["B"], d["M"],
+                       d.get("D", 512), d.get("HI", 8), d.get("DI", 64))
+
+
+def _score(pool, **kw):
+    a = dict(q_idx=A, w_idx=A, Q=1, pos0=-1, ratio=4, cand=None, P=0, scores=A, hist=None)
+    a.update(kw)
+    return C.csa2_index_score(pool, a["q_idx"], a["w_idx"], a["Q"], a["pos0"], a["ratio"],
+                              a["cand"], a["P"], a["scores"], a["hist"], 0,
+                              raise_on_error=False)
+
+
+def test_index_score_argument_errors():
+    assert _score(_pool(latent=None)) == C.CSA2_ERR_NULL
+    assert _score(_pool(), q_idx=None) == C.CSA2_ERR_NULL
+    assert _score(_pool(), scores=None) == C.CSA2_ERR_NULL
+    assert _score(_pool(B=0)) == C.CSA2_ERR_SHAPE
+    assert _score(_pool(M=0)) == C.CSA2_ERR_SHAPE
+    assert _score(_pool(D=256)) == C.CSA2_ERR_SHAPE
+    assert _score(_pool(HI=4)) == C.CSA2_ERR_SHAPE
+    assert _score(_pool(), Q=0) == C.CSA2_ERR_SHAPE
+    assert _score(_pool(B=40000), Q=2) == C.CSA2_ERR_SHAPE
+    assert _score(_pool(), pos0=10, ratio=0) == C.CSA2_ERR_SHAPE
+    assert _score(_pool(), cand=A, P=0) == C.CSA2_ERR_SHAPE
+    assert _score(_pool(idx_key=A + 4)) == C.CSA2_ERR_ALIGN
+    assert _score(_pool(), q_idx=A + 8) == C.CSA2_ERR_ALIGN
+    assert _score(_pool(), scores=A + 2) == C.CSA2_ERR_ALIGN
+
+
+def test_topk_argument_errors():
+    f = lambda **kw: C.csa2_topk(kw.get("scores", A), kw.get("R", 4), kw.get("N", 100),
+                                 kw.get("n_valid"), kw.get("cand"), kw.get("K", 8),
+                                 kw.get("idx", A2), kw.get("ws", A), kw.get("ws_bytes", 0),
+                                 0, raise_on_error=False)
+    need = C.csa2_workspace_bytes(C.CSA2_OP_TOPK, 4, 1, 100, 8, 0, 0, 0)
+    assert f(scores=None) == C.CSA2_ERR_NULL
+    assert f(idx=None) == C.CSA2_ERR_NULL
+    assert f(R=0) == C.CSA2_ERR_SHAPE
+    assert f(N=0) == C.CSA2_ERR_SHAPE
+    assert f(K=0) == C.CSA2_ERR_SHAPE
+    assert f(K=16385) == C.CSA2_ERR_SHAPE
+    assert f(ws_bytes=need - 1) == C.CSA2_ERR_WORKSPACE
+    assert f(ws=None, ws_bytes=need) == C.CSA2_ERR_WORKSPACE
+    assert f(ws=A + 4, ws_bytes=need) == C.CSA2_ERR_ALIGN
+    assert f(scores=A + 2, ws_bytes=need) == C.CSA2_ERR_ALIGN
+
+
+def test_attention_argument_errors():
+    need = C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 2, 1, 1024, 64, 0, 0, 16)
+    g = lambda pool=None, **kw: C.csa2_sparse_attn(pool or _pool(), kw.get("q", A), kw.get("Q", 1),
+                                                   kw.get("H", 16), kw.get("idx", A), kw.get("K", 64),
+                                                   kw.get("o", A), kw.get("lse", A), kw.get("ws", A),
+                                                   kw.get("ws_bytes", need - 1), 0,
+                                                   raise_on_error=False)
+    assert g(q=None) == C.CSA2_ERR_NULL
+    assert g(H=8) == C.CSA2_ERR_SHAPE
+    assert g(K=0) == C.CSA2_ERR_SHAPE
+    assert g(o=A + 4) == C.CSA2_ERR_ALIGN
+    assert g() == C.CSA2_ERR_WORKSPACE
+    needw = C.csa2_workspace_bytes(C.CSA2_OP_SWA_MERGE, 2, 1, 0, 0, 0, 128, 16)
+    h = lambda **kw: C.csa2_swa_merge(kw.get("q", A), kw.get("B", 2), 1, kw.get("H", 16),
+                                      kw.get("D", 512), kw.get("swa", A), kw.get("W", 128), A, A,
+                                      A, kw.get("ws_bytes", needw - 1), 0, raise_on_error=False)
+    assert h(q=None) == C.CSA2_ERR_NULL
+    assert h(swa=None) == C.CSA2_ERR_NULL
+    assert h(D=256) == C.CSA2_ERR_SHAPE
+    assert h(W=-1) == C.CSA2_ERR_SHAPE
+    assert h(W=5000) == C.CSA2_ERR_SHAPE
+    assert h() == C.CSA2_ERR_WORKSPACE
+
+
+def _layer(mode, **kw):
+    d = dict(q_idx=A, w_idx=A, q=A, swa=A, o=A, lse=A, idx_out=A2)
+    d.update(kw)
+    return C.csa2_layer(mode, d["q_idx"], d["w_idx"], d["q"], d["swa"], d["o"], d["lse"],
+                        d["idx_out"])
+
+
+def test_decode_layers_schedule_and_argument_errors():
+    pool = _pool()
+    need = C.csa2_workspace_bytes(C.CSA2_OP_DECODE_LAYERS, 2, 1, 1024, 64, 0, 128, 16)
+
+    def run(layers, K=64, P=0, W=128, H=16, ws=A, nb=need - 1, pool=pool):
+        st, _ = C.csa2_decode_layers(pool, layers, H, K, P, W, ws, nb, 0, raise_on_error=False)
+        return st
+
+    F, RI, RU = C.CSA2_FULL, C.CSA2_REINDEX, C.CSA2_REUSE
+    assert run([_layer(RI)]) == C.CSA2_ERR_SCHEDULE
+    assert run([_layer(RU), _layer(F)]) == C.CSA2_ERR_SCHEDULE
+    assert run([_layer(F), _layer(7)]) == C.CSA2_ERR_SCHEDULE
+    assert run([_layer(F, idx_out=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F), _layer(RI, q_idx=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F), _layer(RU, swa=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F, o=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F)], K=0) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F)], P=32) == C.CSA2_ERR_SHAPE       # P < K
+    assert run([_layer(F)], H=8) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F)], W=4097) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F, q=A + 2)]) == C.CSA2_ERR_ALIGN
+    assert run([_layer(F), _layer(RU, idx_out=None)]) == C.CSA2_ERR_WORKSPACE
+    assert run([_layer(F)], ws=None, nb=need) == C.CSA2_ERR_WORKSPACE
+    assert run([_layer(F)], pool=_pool(scale=None)) == C.CSA2_ERR_NULL
