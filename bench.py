@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 SCORE_SRC = os.path.join(ROOT, "fp4_kv_cache_score_amd", "csrc", "index_score.hip")
 
 
@@ -42,14 +43,23 @@ def kernel_hash() -> str:
 
 
 def recorded_traffic(workload: str):
+    """HBM bytes per scan launch from the counter summary of this workload.
+
+    The summary (profiles/index_score_<workload>.txt) records the scan
+    kernel's source hash; a summary taken on another version of the kernel
+    does not count (None).
+    """
     try:
-        d = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
+        text = open(os.path.join(PROFILES, "index_score_%s.txt" % workload)).read()
+    except OSError:
         return None
-    e = d.get(workload)
-    if not e or e.get("kernel_sha256_16") != kernel_hash():
+    fields = dict(m.groups() for m in re.finditer(r"^(\w+):\s*(\S+)\s*$", text, re.M))
+    if fields.get("kernel_sha256_16") != kernel_hash():
         return None
-    return e.get("bytes_per_launch")
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def time_decode(dc, steps: int, warmup: int):
@@ -153,6 +163,8 @@ def main():
     ap.add_argument("--score-launches", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="first run a 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -166,6 +178,14 @@ def main():
         sys.exit(1)
     from fp4_kv_cache_score_amd import _lib
     _lib.lib()
+    if args.copy_calib:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 3 x 1 GiB device copies done")
 
     head = measure(args.config, args.steps, args.warmup, args.score_launches)
     cfg = head["cfg"]
