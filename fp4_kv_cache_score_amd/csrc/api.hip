@@ -24,18 +24,61 @@ csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E
 constexpr int32_t kMaxW = 4096;
 constexpr int32_t kMaxRows = 65535;  // grid.y limit for row-indexed launches
 
+// Top-K workspace: nothing for rows the one-work-group select handles.
+size_t topk_call_ws_bytes(int64_t R, int64_t N, int64_t K) {
+  return N <= kRowMaxN ? 256 : topk_ws_bytes(R, N, K);
+}
+
+// decode_layers workspace: scores [B][N] | histograms [B][4096] |
+// multi-work-group Top-K scratch (only when M > kRowMaxN) | candidate pool |
+// attention partials.
+struct DecodeWs {
+  float* scores;
+  uint32_t* hist;
+  bool big;
+  TopkWs t;
+  int32_t* cand;
+  float* opart;
+  float* ml;
+};
+
 size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t N = P > M ? P : M;
   const int64_t Kmax = P > K ? P : K;
   const int64_t splits = attn_splits_global((int32_t)K) + attn_splits_window((int32_t)W);
-  return align256(B * N * 4) + topk_ws_bytes(B, N, Kmax) + align256(B * (P > 0 ? P : 1) * 4) +
+  return align256(B * N * 4) + align256(B * kHistBins * 4) +
+         (M > kRowMaxN ? topk_ws_bytes(B, M, Kmax) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
          attn_ws_bytes(B, splits > 0 ? splits : 1);
 }
 
-// Top-K on already-written scores whose histogram is ready in ws.hist.
-csa2_status select_rows(const float* scores, int32_t R, int32_t N, const int32_t* n_valid,
-                        int32_t n_all, const int32_t* cand, int32_t K, int32_t* out,
-                        const TopkWs& t, hipStream_t s) {
+DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
+  DecodeWs d{};
+  const int64_t N = P > M ? P : M;
+  const int64_t Kmax = P > K ? P : K;
+  char* p = (char*)ws;
+  d.scores = (float*)p;
+  p += align256(B * N * 4);
+  d.hist = (uint32_t*)p;
+  p += align256(B * kHistBins * 4);
+  d.big = M > kRowMaxN;
+  if (d.big) {
+    d.t = topk_ws_carve(p, B, M, Kmax);
+    p += topk_ws_bytes(B, M, Kmax);
+  }
+  d.cand = (int32_t*)p;
+  p += align256(B * (P > 0 ? P : 1) * 4);
+  const int32_t S = attn_splits_global((int32_t)K) + attn_splits_window((int32_t)W);
+  d.opart = (float*)p;
+  d.ml = (float*)(p + align256(B * (S > 0 ? S : 1) * kH * kD * 4));
+  return d;
+}
+
+// Multi-work-group Top-K on scores whose histogram is ready in t.hist.
+csa2_status select_rows_big(const float* scores, int32_t R, int32_t N, const int32_t* n_valid,
+                            int32_t n_all, const int32_t* cand, int32_t K, int32_t* out,
+                            const TopkWs& t, hipStream_t s) {
+  csa2_status st = hip_status(launch_fill_zero(t.counters, (int64_t)R * kCounterWords, s));
+  if (st != CSA2_OK) return st;
   return hip_status(launch_topk_select(scores, R, N, n_valid, n_all, cand, K, out, t, s));
 }
 
@@ -43,10 +86,6 @@ csa2_status select_rows(const float* scores, int32_t R, int32_t N, const int32_t
 csa2_status zero_hist_counters(const TopkWs& t, int64_t R, hipStream_t s) {
   const int64_t words = (int64_t)((char*)t.counters - (char*)t.hist) / 4 + R * kCounterWords;
   return hip_status(launch_fill_zero(t.hist, words, s));
-}
-
-csa2_status zero_counters(const TopkWs& t, int64_t R, hipStream_t s) {
-  return hip_status(launch_fill_zero(t.counters, R * kCounterWords, s));
 }
 
 }  // namespace
@@ -74,7 +113,7 @@ size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K, 
   switch (op) {
     case CSA2_OP_TOPK:
       if (M <= 0 || K <= 0 || K > kMaxK || M > kMaxTopkN) return 0;
-      return topk_ws_bytes(B, M, K);
+      return topk_call_ws_bytes(B, M, K);
     case CSA2_OP_SPARSE_ATTN:
       if (K <= 0 || K > kMaxK || H != kH) return 0;
       return attn_ws_bytes((int64_t)B * Q, attn_splits_global(K));
@@ -114,14 +153,17 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* 
     return CSA2_ERR_SHAPE;
   if (!al4(scores) || !al4(idx) || (n_valid && !al4(n_valid)) || (cand && !al4(cand)))
     return CSA2_ERR_ALIGN;
-  if (!ws || ws_bytes < topk_ws_bytes(R, N, K)) return CSA2_ERR_WORKSPACE;
+  if (!ws || ws_bytes < topk_call_ws_bytes(R, N, K)) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
+  if (N <= kRowMaxN)
+    return hip_status(launch_topk_rows(scores, R, N, n_valid, N, K, nullptr, false, cand, idx,
+                                       stream));
   const TopkWs t = topk_ws_carve(ws, R, N, K);
   csa2_status st = zero_hist_counters(t, R, stream);
   if (st != CSA2_OK) return st;
   st = hip_status(launch_topk_hist(scores, R, N, n_valid, N, t.hist, stream));
   if (st != CSA2_OK) return st;
-  return select_rows(scores, R, N, n_valid, N, cand, K, idx, t, stream);
+  return hip_status(launch_topk_select(scores, R, N, n_valid, N, cand, K, idx, t, stream));
 }
 
 csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q, int32_t H,
@@ -217,51 +259,62 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
 
-  // Workspace: scores | Top-K scratch | candidate pool | attention partials.
-  const int64_t N = P > M ? P : M;
-  const int64_t Kmax = P > K ? P : K;
-  char* p = (char*)ws;
-  float* scores = (float*)p;
-  p += align256(B * N * 4);
-  const TopkWs t = topk_ws_carve(p, B, N, Kmax);
-  p += topk_ws_bytes(B, N, Kmax);
-  int32_t* cand = (int32_t*)p;
-  p += align256(B * (P > 0 ? P : 1) * 4);
+  const DecodeWs d = decode_ws_carve(ws, B, M, K, P, W);
+  uint32_t* hist = d.big ? d.t.hist : d.hist;
   const int32_t Sg = attn_splits_global(K), Sw = attn_splits_window(W);
-  float* opart = (float*)p;
-  float* ml = (float*)(p + align256(B * (Sg + Sw) * kH * kD * 4));
+  float* opart = d.opart;
+  float* ml = d.ml;
+
+  // The histogram starts zeroed; every one-work-group select leaves it
+  // zeroed again, so only the multi-work-group path needs a fresh fill.
+  st = hip_status(launch_fill_zero(hist, B * kHistBins, stream));
+  if (st != CSA2_OK) return st;
+  bool hist_clean = true;
 
   const int32_t* cur = nullptr;
   int32_t cur_layer = -1;
   const int32_t n_cand = (int32_t)(P < M ? P : M);
   for (int32_t l = 0; l < L; ++l) {
     const csa2_layer& y = layers[l];
+    if (y.mode != CSA2_REUSE && !hist_clean) {
+      st = hip_status(launch_fill_zero(hist, B * kHistBins, stream));
+      if (st != CSA2_OK) return st;
+    }
     if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
-      st = zero_hist_counters(t, B, stream);
-      if (st != CSA2_OK) return st;
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         nullptr, (int32_t)M, scores, t.hist, stream));
+                                         nullptr, (int32_t)M, d.scores, hist, stream));
       if (st != CSA2_OK) return st;
-      if (y.mode == CSA2_FULL && P > 0) {
-        st = select_rows(scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P, cand, t,
-                         stream);
+      if (!d.big) {
+        if (y.mode == CSA2_FULL && P > 0) {
+          st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M,
+                                           P, hist, false, nullptr, d.cand, stream));
+          if (st != CSA2_OK) return st;
+        }
+        st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, K,
+                                         hist, true, nullptr, y.idx_out, stream));
         if (st != CSA2_OK) return st;
-        st = zero_counters(t, B, stream);
+        hist_clean = true;
+      } else {
+        if (y.mode == CSA2_FULL && P > 0) {
+          st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P,
+                               d.cand, d.t, stream);
+          if (st != CSA2_OK) return st;
+        }
+        st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, K,
+                             y.idx_out, d.t, stream);
         if (st != CSA2_OK) return st;
+        hist_clean = false;
       }
-      st = select_rows(scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, K, y.idx_out,
-                       t, stream);
-      if (st != CSA2_OK) return st;
       cur = y.idx_out;
       cur_layer = l;
     } else if (y.mode == CSA2_REINDEX) {  // hierarchical: score inside the candidate pool
-      st = zero_hist_counters(t, B, stream);
-      if (st != CSA2_OK) return st;
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         cand, P, scores, t.hist, stream));
+                                         d.cand, P, d.scores, hist, stream));
       if (st != CSA2_OK) return st;
-      st = select_rows(scores, (int32_t)B, P, nullptr, n_cand, cand, K, y.idx_out, t, stream);
+      st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, nullptr, n_cand, K, hist, true,
+                                       d.cand, y.idx_out, stream));
       if (st != CSA2_OK) return st;
+      hist_clean = true;
       cur = y.idx_out;
       cur_layer = l;
     } else {  // Reuse

@@ -21,6 +21,7 @@ constexpr int kHistBits = 12;               // first radix digit: top 12 key bit
 constexpr int kHistBins = 1 << kHistBits;   // 4096
 constexpr int kMaxK = 16384;
 constexpr int kMaxTopkN = 1 << 30;          // row length limit (composite key packs 30 bits)
+constexpr int kRowMaxN = 1 << 18;           // rows up to this length take the one-work-group select
 constexpr int kCounterWords = 4;            // per row: [0]=above count, [1]=candidate count
 
 // Attention
@@ -99,6 +100,13 @@ hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
                               uint32_t* hist, hipStream_t s);
 
 // Top-K pieces.  n_valid: device [R] or NULL (then n_all applies to every row).
+// launch_topk_rows: one work-group per row, N <= kRowMaxN.  hist: NULL (the
+// kernel builds its own) or the rows' top-12-bit histograms [R][kHistBins]
+// from the score kernel, zeroed after use when zero_hist is set.
+hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
+                            const int32_t* n_valid, int32_t n_all, int32_t K,
+                            uint32_t* hist, bool zero_hist, const int32_t* cand,
+                            int32_t* out, hipStream_t s);
 hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
                             const int32_t* n_valid, int32_t n_all,
                             uint32_t* hist, hipStream_t s);

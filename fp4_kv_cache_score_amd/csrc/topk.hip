@@ -5,22 +5,31 @@
 // on the three operating modes); equal scores going to the lower pool index
 // and the ascending output order are this library's fixed conventions.
 //
-// Every (score, position) pair maps to a unique composite order key
+// Every (score, position) pair maps to a unique 62-bit composite order key
 //   key32(score) : (n - 1 - position)
 // (key32 is the order-preserving uint32 image of the float), so the K largest
-// composites are exactly the wanted set.  The select is a radix select:
-//  1. histogram of the top 12 key bits per row (fused into the score kernel,
-//     or k_topk_hist), giving the bin b* that holds the K-th largest key;
-//  2. k_topk_collect (many work-groups per row) appends positions in bins
-//     above b* to a list and the (key, position) pairs inside b* to a
-//     candidate list, with one wave-aggregated atomic per wave;
-//  3. k_topk_finish (one work-group per row) resolves the rest of the
-//     composite with 10-bit radix passes over the candidates only, marks the
-//     chosen positions in an LDS bitmap and writes them in ascending order
-//     with a block prefix sum.  If the candidate list overflowed its slots,
-//     the same passes read the candidates straight from the score row.
-// Ties, -0 vs +0, rows with fewer than K valid positions and N up to 2^30 are
-// all handled exactly; the result is deterministic.
+// composites are exactly the wanted set, and a radix select over the
+// composite finds them.
+//
+// Rows of up to 2^18 positions (every decode and prefill shape here) use
+// k_topk_row, one 1024-thread work-group per row:
+//  1. a histogram of the top 12 key bits (taken from the score kernel, which
+//     builds it while it writes the scores, or built here) gives the digit
+//     that holds the K-th largest key;
+//  2. while that digit holds more positions than the LDS candidate slots,
+//     one more streaming pass refines the prefix by 10 bits;
+//  3. one pass marks every position strictly above the prefix in an LDS
+//     bitmap and copies the prefix's members to LDS;
+//  4. 10-bit radix passes over the LDS candidates resolve the rest (ties
+//     are broken by the position bits), and the chosen ones are marked;
+//  5. a block prefix sum over the bitmap's popcounts writes the positions in
+//     ascending order.
+// Longer rows use the multi-work-group path: k_topk_hist -> k_topk_collect
+// (positions above the threshold bin and that bin's members, appended with
+// one atomic per work-group) -> k_topk_finish (radix passes over the members
+// and an ordered extraction through bitmap segments).
+// Ties, -0 vs +0, rows with fewer than K valid positions are handled exactly;
+// the result is deterministic.
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -39,11 +48,6 @@ __device__ __forceinline__ int32_t row_count(const int32_t* n_valid, int32_t n_a
                                              int row, int32_t N) {
   int32_t n = n_valid ? n_valid[row] : n_all;
   return n < 0 ? 0 : (n > N ? N : n);
-}
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Exclusive prefix sum over the NT threads of a block; *total receives the sum.
@@ -145,47 +149,62 @@ void k_topk_collect(const float* __restrict__ scores, int32_t N,
                     const uint32_t* __restrict__ hist, uint32_t* __restrict__ counters,
                     int32_t* __restrict__ sel, uint32_t* __restrict__ candk,
                     int32_t* __restrict__ candp, int32_t cap) {
+  constexpr int PER = kChunk / kSelThreads;   // 16 positions per thread
   __shared__ uint32_t lds[kSelThreads / 64 + 3];
+  __shared__ uint32_t base_s[2];
   const int row = blockIdx.y;
   const int32_t n = row_count(n_valid, n_all, row, N);
   if (n <= K) return;
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   if (c0 >= n) return;
+  const float* sr = scores + (size_t)row * N;
+  // Issue every load of this work-group's chunk before the threshold search.
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t p = c0 + i * kSelThreads + threadIdx.x;
+    key[i] = p < n ? score_key(sr[p]) : 0u;
+  }
   int bstar;
   uint32_t above;
   threshold_bin<kSelThreads>(hist + (size_t)row * kHistBins, (uint32_t)K, lds, &bstar, &above);
-  const float* sr = scores + (size_t)row * N;
-  uint32_t* cnt = counters + (size_t)row * kCounterWords;
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t p = c0 + i * kSelThreads + threadIdx.x;
+    const int bin = (int)(key[i] >> (32 - kHistBits));
+    ngt += (p < n && bin > bstar) ? 1u : 0u;
+    neq += (p < n && bin == bstar) ? 1u : 0u;
+  }
+  // One atomic per counter per work-group; slots in any order (the finish
+  // step orders the output through a bitmap).
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<kSelThreads>((ngt << 16) | neq, lds, &tot);
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = counters + (size_t)row * kCounterWords;
+    base_s[0] = (tot >> 16) ? atomicAdd(&cnt[0], tot >> 16) : 0u;
+    base_s[1] = (tot & 0xFFFFu) ? atomicAdd(&cnt[1], tot & 0xFFFFu) : 0u;
+  }
+  __syncthreads();
+  uint32_t rg = base_s[0] + (ex >> 16);
+  uint32_t re = base_s[1] + (ex & 0xFFFFu);
   int32_t* srow = sel + (size_t)row * K;
   uint32_t* ckr = candk + (size_t)row * cap;
   int32_t* cpr = candp + (size_t)row * cap;
-  const int lane = threadIdx.x & 63;
-  for (int i = 0; i < kChunk / kSelThreads; ++i) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
     const int64_t p = c0 + i * kSelThreads + threadIdx.x;
-    const bool in = p < n;
-    const uint32_t key = in ? score_key(sr[p]) : 0u;
-    const int bin = (int)(key >> (32 - kHistBits));
-    const bool gt = in && bin > bstar;
-    const bool eq = in && bin == bstar;
-    const uint64_t mg = __ballot(gt);
-    const uint64_t me = __ballot(eq);
-    uint32_t bg = 0, be = 0;
-    if (lane == 0) {
-      if (mg) bg = atomicAdd(&cnt[0], (uint32_t)__popcll(mg));
-      if (me) be = atomicAdd(&cnt[1], (uint32_t)__popcll(me));
-    }
-    bg = __shfl(bg, 0, 64);
-    be = __shfl(be, 0, 64);
-    if (gt) {
-      const uint32_t r = bg + lanes_below(mg);
-      if (r < (uint32_t)K) srow[r] = (int32_t)p;
-    }
-    if (eq) {
-      const uint32_t r = be + lanes_below(me);
-      if (r < (uint32_t)cap) {
-        ckr[r] = key;
-        cpr[r] = (int32_t)p;
+    if (p >= n) continue;
+    const int bin = (int)(key[i] >> (32 - kHistBits));
+    if (bin > bstar) {
+      if (rg < (uint32_t)K) srow[rg] = (int32_t)p;
+      ++rg;
+    } else if (bin == bstar) {
+      if (re < (uint32_t)cap) {
+        ckr[re] = key[i];
+        cpr[re] = (int32_t)p;
       }
+      ++re;
     }
   }
 }
@@ -327,6 +346,224 @@ void k_topk_finish(const float* __restrict__ scores, int32_t N,
   for (uint32_t i = written + tid; i < (uint32_t)K; i += kFinThreads) orow[i] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// One work-group per row (rows of at most kRowMaxN positions).
+// ---------------------------------------------------------------------------
+
+constexpr int kRowThreads = 1024;
+constexpr int kRowWords = kRowMaxN / 32;   // bitmap words (8192 = 32 KiB)
+constexpr int kRowCap = 1536;              // LDS candidate slots
+constexpr int kRowUnroll = 8;              // loads in flight per thread while streaming
+
+struct RowLds {
+  uint32_t hist[kHistBins];
+  uint32_t bitmap[kRowWords];
+  uint32_t ckey[kRowCap];
+  int32_t cpos[kRowCap];
+  uint32_t scan[kRowThreads / 64 + 8];
+  uint32_t ccount;
+};
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, int32_t p, uint32_t nm1) {
+  return ((uint64_t)key << 30) | (uint64_t)(nm1 - (uint32_t)p);
+}
+
+// f(key, position) for every position p < n of the row, kRowUnroll loads in flight.
+template <typename F>
+__device__ __forceinline__ void stream_row(const float* __restrict__ sr, int32_t n, F&& f) {
+  for (int32_t base = 0; base < n; base += kRowThreads * kRowUnroll) {
+    float v[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int32_t p = base + u * kRowThreads + (int32_t)threadIdx.x;
+      v[u] = p < n ? sr[p] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int32_t p = base + u * kRowThreads + (int32_t)threadIdx.x;
+      if (p < n) f(score_key(v[u]), p);
+    }
+  }
+}
+
+// Digit holding the need-th largest member of a histogram of PER * 1024 bins
+// ordered by digit value.  Returns the digit, the number of members in higher
+// digits and the count of the digit itself (all block-uniform).
+template <int PER>
+__device__ void row_find_digit(const uint32_t* h, uint32_t need, uint32_t* scan,
+                               uint32_t* digit, uint32_t* above, uint32_t* count) {
+  const int top = PER * kRowThreads - 1 - (int)threadIdx.x * PER;
+  uint32_t c[PER];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = h[top - i];
+    s += c[i];
+  }
+  uint32_t* res = scan + kRowThreads / 64 + 1;
+  if (threadIdx.x == 0) {
+    res[0] = 0u;
+    res[1] = 0u;
+    res[2] = 0u;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<kRowThreads>(s, scan, &tot);
+  if (ex < need && need <= ex + s) {
+    uint32_t acc = ex;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (acc < need && need <= acc + c[i]) {
+        res[0] = (uint32_t)(top - i);
+        res[1] = acc;
+        res[2] = c[i];
+      }
+      acc += c[i];
+    }
+  }
+  __syncthreads();
+  *digit = res[0];
+  *above = res[1];
+  *count = res[2];
+  __syncthreads();
+}
+
+template <bool kHasHist>
+__global__ __launch_bounds__(kRowThreads)
+void k_topk_row(const float* __restrict__ scores, int32_t N,
+                const int32_t* __restrict__ n_valid, int32_t n_all, int32_t K,
+                uint32_t* __restrict__ hist, int32_t zero_hist,
+                const int32_t* __restrict__ cand_map, int32_t* __restrict__ out) {
+  __shared__ RowLds L;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t n = row_count(n_valid, n_all, row, N);
+  const float* sr = scores + (size_t)row * N;
+  const int32_t* mrow = cand_map ? cand_map + (size_t)row * N : nullptr;
+  int32_t* orow = out + (size_t)row * K;
+
+  // 1. Top-digit histogram: bits 61..50 of the composite = the top 12 key bits.
+  if (kHasHist) {
+    uint32_t* hr = hist + (size_t)row * kHistBins;
+    for (int i = tid; i < kHistBins; i += kRowThreads) {
+      L.hist[i] = hr[i];
+      if (zero_hist) hr[i] = 0u;   // left zeroed for the next score kernel
+    }
+  }
+  if (n <= K) {   // every valid position is selected
+    for (int i = tid; i < K; i += kRowThreads) orow[i] = i < n ? (mrow ? mrow[i] : i) : -1;
+    return;
+  }
+  if (!kHasHist) {
+    for (int i = tid; i < kHistBins; i += kRowThreads) L.hist[i] = 0u;
+    __syncthreads();
+    stream_row(sr, n, [&](uint32_t key, int32_t) {
+      atomicAdd(&L.hist[key >> (32 - kHistBits)], 1u);
+    });
+  }
+  __syncthreads();
+  const uint32_t nm1 = (uint32_t)(n - 1);
+  uint32_t d, ab, cnt;
+  row_find_digit<kHistBins / kRowThreads>(L.hist, (uint32_t)K, L.scan, &d, &ab, &cnt);
+  // Invariant: the composites whose bits above `shift` exceed `prefix` are
+  // all selected (K - need of them); `need` more come from the `cnt`
+  // composites whose bits above `shift` equal `prefix`.
+  uint64_t prefix = d;
+  uint32_t need = (uint32_t)K - ab;
+  int shift = 50;
+  bool all = cnt == need;
+
+  // 2. Refine by streaming passes until the prefix's members fit in LDS.
+  while (!all && cnt > (uint32_t)kRowCap && shift > 0) {
+    const int w = shift < kDigit ? shift : kDigit;
+    shift -= w;
+    for (int i = tid; i < (1 << kDigit); i += kRowThreads) L.hist[i] = 0u;
+    __syncthreads();
+    const int sh = shift;
+    stream_row(sr, n, [&](uint32_t key, int32_t p) {
+      const uint64_t c = composite(key, p, nm1);
+      if ((c >> (sh + w)) == prefix) atomicAdd(&L.hist[(uint32_t)(c >> sh) & ((1u << w) - 1u)], 1u);
+    });
+    __syncthreads();
+    row_find_digit<(1 << kDigit) / kRowThreads>(L.hist, need, L.scan, &d, &ab, &cnt);
+    prefix = (prefix << w) | d;
+    need -= ab;
+    all = cnt == need;
+  }
+
+  // 3. Mark everything above the prefix; copy the prefix's members to LDS.
+  for (int i = tid; i < kRowWords; i += kRowThreads) L.bitmap[i] = 0u;
+  if (tid == 0) L.ccount = 0u;
+  __syncthreads();
+  {
+    const int sh = shift;
+    const bool take_eq = all;
+    stream_row(sr, n, [&](uint32_t key, int32_t p) {
+      const uint64_t hi = composite(key, p, nm1) >> sh;
+      if (hi > prefix || (take_eq && hi == prefix)) {
+        atomicOr(&L.bitmap[p >> 5], 1u << (p & 31));
+      } else if (hi == prefix) {
+        const uint32_t slot = atomicAdd(&L.ccount, 1u);
+        if (slot < (uint32_t)kRowCap) {
+          L.ckey[slot] = key;
+          L.cpos[slot] = p;
+        }
+      }
+    });
+  }
+  __syncthreads();
+
+  // 4. Radix passes over the LDS members, then mark the chosen ones.
+  if (!all) {
+    const uint32_t C = L.ccount;   // == cnt <= kRowCap
+    while (!all && shift > 0) {
+      const int w = shift < kDigit ? shift : kDigit;
+      shift -= w;
+      for (int i = tid; i < (1 << kDigit); i += kRowThreads) L.hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < C; i += kRowThreads) {
+        const uint64_t c = composite(L.ckey[i], L.cpos[i], nm1);
+        if ((c >> (shift + w)) == prefix)
+          atomicAdd(&L.hist[(uint32_t)(c >> shift) & ((1u << w) - 1u)], 1u);
+      }
+      __syncthreads();
+      row_find_digit<(1 << kDigit) / kRowThreads>(L.hist, need, L.scan, &d, &ab, &cnt);
+      prefix = (prefix << w) | d;
+      need -= ab;
+      all = cnt == need;
+    }
+    for (uint32_t i = tid; i < C; i += kRowThreads) {
+      const int32_t p = L.cpos[i];
+      if ((composite(L.ckey[i], p, nm1) >> shift) >= prefix)
+        atomicOr(&L.bitmap[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+  }
+
+  // 5. Ascending output through the bitmap.
+  constexpr int WPT = kRowWords / kRowThreads;   // 8 words per thread
+  uint32_t wv[WPT];
+  uint32_t c = 0;
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) {
+    wv[w] = L.bitmap[tid * WPT + w];
+    c += __popc(wv[w]);
+  }
+  uint32_t tot;
+  uint32_t pos = block_excl_scan<kRowThreads>(c, L.scan, &tot);
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) {
+    uint32_t m = wv[w];
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      const int32_t p = (tid * WPT + w) * 32 + bit;
+      if (pos < (uint32_t)K) orow[pos] = mrow ? mrow[p] : p;
+      ++pos;
+    }
+  }
+  for (uint32_t i = tot + tid; i < (uint32_t)K; i += kRowThreads) orow[i] = -1;
+}
+
 __global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -354,6 +591,20 @@ hipError_t launch_copy_i32(int32_t* d, const int32_t* src, int64_t n, hipStream_
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   k_copy_i32<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(d, src, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
+                            const int32_t* n_valid, int32_t n_all, int32_t K,
+                            uint32_t* hist, bool zero_hist, const int32_t* cand,
+                            int32_t* out, hipStream_t s) {
+  if (N > kRowMaxN) return hipErrorInvalidValue;
+  if (hist)
+    k_topk_row<true><<<dim3((unsigned)R), dim3(kRowThreads), 0, s>>>(
+        scores, N, n_valid, n_all, K, hist, zero_hist ? 1 : 0, cand, out);
+  else
+    k_topk_row<false><<<dim3((unsigned)R), dim3(kRowThreads), 0, s>>>(
+        scores, N, n_valid, n_all, K, nullptr, 0, cand, out);
   return hipGetLastError();
 }
 

@@ -44,7 +44,8 @@ def test_status_strings():
 
 def test_workspace_bytes():
     ws = C.csa2_workspace_bytes
-    assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 512, 0, 0, 0) > 32 * 4096 * 4
+    assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 512, 0, 0, 0) > 0
+    assert ws(C.CSA2_OP_TOPK, 4, 1, 300001, 512, 0, 0, 0) > 4 * 4096 * 4
     assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 0, 0, 0, 0) == 0
     assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 16385, 0, 0, 0) == 0
     assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 16) >= 32 * 16 * 16 * 512 * 4
