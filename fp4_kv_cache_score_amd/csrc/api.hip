@@ -45,7 +45,7 @@ struct DecodeWs {
 size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t N = P > M ? P : M;
   const int64_t Kmax = P > K ? P : K;
-  const int64_t splits = attn_splits_global((int32_t)K) + attn_splits_window((int32_t)W);
+  const int64_t splits = attn_chunks((int32_t)K, (int32_t)W);
   return align256(B * N * 4) + align256(B * kHistBins * 4) +
          (M > kRowMaxN ? topk_ws_bytes(B, M, Kmax) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
          attn_ws_bytes(B, splits > 0 ? splits : 1);
@@ -67,7 +67,7 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   }
   d.cand = (int32_t*)p;
   p += align256(B * (P > 0 ? P : 1) * 4);
-  const int32_t S = attn_splits_global((int32_t)K) + attn_splits_window((int32_t)W);
+  const int32_t S = attn_chunks((int32_t)K, (int32_t)W);
   d.opart = (float*)p;
   d.ml = (float*)(p + align256(B * (S > 0 ? S : 1) * kH * kD * 4));
   return d;
@@ -116,10 +116,10 @@ size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K, 
       return topk_call_ws_bytes(B, M, K);
     case CSA2_OP_SPARSE_ATTN:
       if (K <= 0 || K > kMaxK || H != kH) return 0;
-      return attn_ws_bytes((int64_t)B * Q, attn_splits_global(K));
+      return attn_ws_bytes((int64_t)B * Q, attn_chunks(K, 0));
     case CSA2_OP_SWA_MERGE:
       if (W < 0 || W > kMaxW || H != kH) return 0;
-      return attn_ws_bytes((int64_t)B * Q, attn_splits_window(W) > 0 ? attn_splits_window(W) : 1);
+      return attn_ws_bytes((int64_t)B * Q, W > 0 ? attn_chunks(0, W) : 1);
     case CSA2_OP_DECODE_LAYERS:
       if (M <= 0 || K <= 0 || K > kMaxK || P < 0 || P > kMaxK || (P > 0 && P < K) ||
           W < 0 || W > kMaxW || H != kH)
@@ -176,8 +176,8 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
     return CSA2_ERR_SHAPE;
   if (!al16(q) || !al4(idx) || !al16(o) || !al4(lse)) return CSA2_ERR_ALIGN;
   const int64_t rows = (int64_t)pool->B * Q;
-  const int32_t Sg = attn_splits_global(K);
-  if (!ws || ws_bytes < attn_ws_bytes(rows, Sg)) return CSA2_ERR_WORKSPACE;
+  const int32_t chunks = attn_chunks(K, 0);
+  if (!ws || ws_bytes < attn_ws_bytes(rows, chunks)) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
   AttnArgs a{};
   a.latent = pool->latent;
@@ -192,10 +192,13 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   a.Q = Q;
   a.rows = (int32_t)rows;
   a.opart = (float*)ws;
-  a.ml = (float*)((char*)ws + align256(rows * Sg * kH * kD * 4));
-  st = hip_status(launch_attn_partial(a, stream));
-  if (st != CSA2_OK) return st;
-  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, Sg, nullptr, nullptr, o, lse, stream));
+  a.ml = (float*)((char*)ws + align256(rows * chunks * kH * kD * 4));
+  a.o = o;
+  a.lse = lse;
+  const int32_t S = attn_splits(rows, chunks);
+  st = hip_status(launch_attn_partial(a, S, true, stream));
+  if (st != CSA2_OK || S == 1) return st;
+  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, S, nullptr, nullptr, o, lse, stream));
 }
 
 csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t D,
@@ -208,8 +211,8 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   if (W > 0 && !swa) return CSA2_ERR_NULL;
   if (!al16(q) || !al16(o) || !al4(lse) || (swa && !al16(swa))) return CSA2_ERR_ALIGN;
   const int64_t rows = (int64_t)B * Q;
-  const int32_t Sw = attn_splits_window(W);
-  if (!ws || ws_bytes < attn_ws_bytes(rows, Sw > 0 ? Sw : 1)) return CSA2_ERR_WORKSPACE;
+  const int32_t chunks = W > 0 ? attn_chunks(0, W) : 1;
+  if (!ws || ws_bytes < attn_ws_bytes(rows, chunks)) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
   if (W == 0) return CSA2_OK;  // nothing to merge: (o, lse) unchanged
   AttnArgs a{};
@@ -225,10 +228,13 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   a.Q = Q;
   a.rows = (int32_t)rows;
   a.opart = (float*)ws;
-  a.ml = (float*)((char*)ws + align256(rows * Sw * kH * kD * 4));
-  csa2_status st = hip_status(launch_attn_partial(a, stream));
+  a.ml = (float*)((char*)ws + align256(rows * chunks * kH * kD * 4));
+  a.o = o;
+  a.lse = lse;
+  const int32_t S = attn_splits(rows, chunks);
+  csa2_status st = hip_status(launch_attn_partial(a, S, false, stream));
   if (st != CSA2_OK) return st;
-  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, Sw, o, lse, o, lse, stream));
+  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, S, o, lse, o, lse, stream));
 }
 
 csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
@@ -261,7 +267,7 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
 
   const DecodeWs d = decode_ws_carve(ws, B, M, K, P, W);
   uint32_t* hist = d.big ? d.t.hist : d.hist;
-  const int32_t Sg = attn_splits_global(K), Sw = attn_splits_window(W);
+  const int32_t S = attn_splits(B, attn_chunks(K, W));
   float* opart = d.opart;
   float* ml = d.ml;
 
@@ -339,11 +345,15 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     a.rows = (int32_t)B;
     a.opart = opart;
     a.ml = ml;
-    st = hip_status(launch_attn_partial(a, stream));
+    a.o = y.o;
+    a.lse = y.lse;
+    st = hip_status(launch_attn_partial(a, S, true, stream));
     if (st != CSA2_OK) return st;
-    st = hip_status(launch_attn_combine(opart, ml, (int32_t)B, Sg + Sw, nullptr, nullptr, y.o,
-                                        y.lse, stream));
-    if (st != CSA2_OK) return st;
+    if (S > 1) {
+      st = hip_status(launch_attn_combine(opart, ml, (int32_t)B, S, nullptr, nullptr, y.o, y.lse,
+                                          stream));
+      if (st != CSA2_OK) return st;
+    }
   }
   return CSA2_OK;
 }

@@ -79,9 +79,9 @@ inline TopkWs topk_ws_carve(void* ws, int64_t R, int64_t N, int64_t K) {
 }
 
 // Attention partials: per (row, split) one [kH][kD] unnormalised output and
-// kH (max, sum) pairs.
-inline size_t attn_ws_bytes(int64_t rows, int64_t splits) {
-  return align256(rows * splits * kH * kD * 4) + align256(rows * splits * kH * 2 * 4);
+// kH (max, sum) pairs.  `chunks` bounds the number of splits.
+inline size_t attn_ws_bytes(int64_t rows, int64_t chunks) {
+  return align256(rows * chunks * kH * kD * 4) + align256(rows * chunks * kH * 2 * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -116,8 +116,11 @@ hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
                               const TopkWs& ws, hipStream_t s);
 
 // Attention over up to K gathered FP4 entries and up to W FP8 window rows per
-// query row, written as split partials; then the log-sum-exp combine (which
-// may fold in an incoming (o, lse)).
+// query row.  The row's keys are cut into chunks of kKeysPerSplit (global
+// chunks first, then window chunks) and the chunks into `splits` contiguous
+// runs, one work-group each.  With one split per row and no incoming (o, lse)
+// the kernel writes o and lse itself; otherwise it writes partials that
+// launch_attn_combine merges (optionally with an incoming (o, lse)).
 struct AttnArgs {
   const uint8_t* latent;  // [B][M][kLatRow]
   const uint8_t* scale;   // [B][M][kScaleRow]
@@ -132,13 +135,15 @@ struct AttnArgs {
   int32_t rows;           // B * Q
   float* opart;           // [rows][splits][kH][kD]
   float* ml;              // [rows][splits][kH][2]
+  float* o;               // [rows][kH][kD]  (written directly when splits == 1)
+  float* lse;             // [rows][kH]
 };
-int32_t attn_splits_global(int32_t K);
-int32_t attn_splits_window(int32_t W);
-hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_combine(const float* opart, const float* ml,
-                               int32_t rows, int32_t splits,
-                               const float* o_in, const float* lse_in,
+int32_t attn_chunks(int32_t K, int32_t W);          // chunks of one row's keys
+int32_t attn_splits(int64_t rows, int32_t chunks);  // work-groups per row
+// final_out: write o / lse directly when the row has one split.
+hipError_t launch_attn_partial(const AttnArgs& a, int32_t splits, bool final_out, hipStream_t s);
+hipError_t launch_attn_combine(const float* opart, const float* ml, int32_t rows,
+                               int32_t splits, const float* o_in, const float* lse_in,
                                float* o, float* lse, hipStream_t s);
 
 // Copy n int32 (Reuse layers that ask for their indices).

@@ -7,8 +7,9 @@
 //
 // Work split: a pool entry's 512-byte key row is read by 32 lanes with one
 // 16-byte load each (two entries per wave64 load), so every wave load is a
-// fully coalesced 1 KiB.  Lane (sub = lane & 31) owns bytes [16*sub, 16*sub+16)
-// of the row, i.e. indexer head sub/4 and 16 of its 64 dims.  The FP8 x FP8
+// fully coalesced 1 KiB; each lane keeps 8 such loads in flight.  Lane
+// (sub = lane & 31) owns bytes [16*sub, 16*sub+16) of the row, i.e. indexer
+// head sub/4 and 16 of its 64 dims.  The FP8 x FP8
 // products are exact in fp32; each lane accumulates its 16 products with
 // fmaf, a 4-lane butterfly completes the head dot, then ReLU, the head weight
 // and an 8-head butterfly give the score.  Every lane holds the full query
@@ -23,22 +24,26 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;                        // 16-byte loads in flight per lane
-constexpr int kEntriesPerWave = 128;
-constexpr int kEntriesPerWG = kEntriesPerWave * (kThreads / 64);   // 512
-constexpr int kIters = kEntriesPerWave / (2 * kUnroll);            // 8
 
 __device__ __forceinline__ float bfly_add(float v, int m) {
   return v + __shfl_xor(v, m, 64);
 }
 
-template <bool kCand, bool kHist>
+// EPW pool entries per wave, 4 waves per work-group.  With a candidate list
+// the work-group first copies its EPW * 4 entry numbers to LDS (one round
+// trip), so that every key load of the streaming loop is independent.
+template <int EPW, bool kCand, bool kHist>
 __global__ __launch_bounds__(kThreads)
 void k_index_score(const uint8_t* __restrict__ key, int64_t M,
                    const uint8_t* __restrict__ q_idx,
                    const float* __restrict__ w_idx, int32_t Q, int64_t pos0,
                    int32_t ratio, const int32_t* __restrict__ cand, int32_t N,
                    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  constexpr int kEntriesPerWG = EPW * (kThreads / 64);
+  constexpr int kIters = EPW / (2 * kUnroll);
+  static_assert(EPW % (2 * kUnroll) == 0, "EPW must be a multiple of 16");
   __shared__ uint32_t lh[kHist ? kHistBins : 1];
+  __shared__ int32_t ce[kCand ? kEntriesPerWG : 1];
   const int row = blockIdx.y;
   const int b = row / Q;
   const int t = row - b * Q;
@@ -55,6 +60,14 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
     vis = v < M ? v : M;
   }
 
+  const int64_t g0 = (int64_t)blockIdx.x * kEntriesPerWG;
+  if (kCand) {
+    const int32_t* cb = cand + (size_t)b * N;
+    for (int i = threadIdx.x; i < kEntriesPerWG; i += kThreads) {
+      const int64_t p = g0 + i;
+      ce[i] = p < N ? cb[p] : -1;
+    }
+  }
   float qf[16];
   {
     const u32x4 qv = *reinterpret_cast<const u32x4*>(q_idx + (size_t)row * kKeyRow + sub * 16);
@@ -70,26 +83,25 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
   }
   const float wh = w_idx[(size_t)row * kHI + head];
 
-  if (kHist) {
+  if (kHist)
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) lh[i] = 0u;
-    __syncthreads();
-  }
+  if (kHist || kCand) __syncthreads();
 
   const uint8_t* kb = key + (size_t)b * (size_t)M * kKeyRow + sub * 16;
-  const int32_t* cb = kCand ? cand + (size_t)b * N : nullptr;
   float* srow = scores + (size_t)row * N;
-  const int64_t wbase = (int64_t)blockIdx.x * kEntriesPerWG + wave * kEntriesPerWave;
+  const int wofs = wave * EPW;
 
   for (int it = 0; it < kIters; ++it) {
     u32x4 v[kUnroll];
     bool ok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t p = wbase + it * (2 * kUnroll) + 2 * u + half;
+      const int lp = wofs + it * (2 * kUnroll) + 2 * u + half;   // position within the work-group
+      const int64_t p = g0 + lp;
       int64_t e = p;
       bool valid = p < N;
-      if (kCand && valid) {
-        e = cb[p];
+      if (kCand) {
+        e = ce[lp];
         valid = e >= 0;
       }
       valid = valid && e < vis;
@@ -118,7 +130,7 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
       r = bfly_add(r, 4);
       r = bfly_add(r, 8);
       r = bfly_add(r, 16);
-      const int64_t p = wbase + it * (2 * kUnroll) + 2 * u + half;
+      const int64_t p = g0 + wofs + it * (2 * kUnroll) + 2 * u + half;
       if (sub == 0 && p < N) {
         srow[p] = ok[u] ? r : -INFINITY;
         if (kHist && ok[u]) atomicAdd(&lh[score_key(r) >> (32 - kHistBits)], 1u);
@@ -136,6 +148,25 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
   }
 }
 
+template <int EPW>
+void launch_epw(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
+                const float* w_idx, int32_t Q, int64_t pos0, int32_t ratio, const int32_t* cand,
+                int32_t N, float* scores, uint32_t* hist, hipStream_t s) {
+  const dim3 grid((unsigned)((N + EPW * 4 - 1) / (EPW * 4)), (unsigned)(B * Q));
+  const dim3 block(kThreads);
+  if (cand) {
+    if (hist)
+      k_index_score<EPW, true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+    else
+      k_index_score<EPW, true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+  } else {
+    if (hist)
+      k_index_score<EPW, false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+    else
+      k_index_score<EPW, false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
@@ -143,19 +174,14 @@ hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
                               int32_t Q, int64_t pos0, int32_t ratio,
                               const int32_t* cand, int32_t N, float* scores,
                               uint32_t* hist, hipStream_t s) {
-  const dim3 grid((unsigned)((N + kEntriesPerWG - 1) / kEntriesPerWG), (unsigned)(B * Q));
-  const dim3 block(kThreads);
-  if (cand) {
-    if (hist)
-      k_index_score<true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
-    else
-      k_index_score<true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
-  } else {
-    if (hist)
-      k_index_score<false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
-    else
-      k_index_score<false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
-  }
+  // 64 entries per wave (256 per work-group) keep enough loads in flight on
+  // long rows; short rows (candidate pools) take 32 so that the launch still
+  // has >= 1024 work-groups.
+  const int64_t rows = (int64_t)B * Q;
+  if (rows * ((N + 255) / 256) >= 1024)
+    launch_epw<64>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, s);
+  else
+    launch_epw<32>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, s);
   return hipGetLastError();
 }
 

@@ -17,10 +17,10 @@
 //     builds it while it writes the scores, or built here) gives the digit
 //     that holds the K-th largest key;
 //  2. while that digit holds more positions than the LDS candidate slots,
-//     one more streaming pass refines the prefix by 10 bits;
+//     one more streaming pass refines the prefix by 12 bits;
 //  3. one pass marks every position strictly above the prefix in an LDS
 //     bitmap and copies the prefix's members to LDS;
-//  4. 10-bit radix passes over the LDS candidates resolve the rest (ties
+//  4. 12-bit radix passes over the LDS candidates resolve the rest (ties
 //     are broken by the position bits), and the chosen ones are marked;
 //  5. a block prefix sum over the bitmap's popcounts writes the positions in
 //     ascending order.
@@ -42,7 +42,8 @@ constexpr int kSegBits = 18;              // bitmap segment of 2^18 positions (3
 constexpr int kSeg = 1 << kSegBits;
 constexpr int kSegWords = kSeg / 32;      // 8192
 constexpr int kCompBits = 50;             // 20 low key bits + 30 position bits
-constexpr int kDigit = 10;
+constexpr int kDigit = 10;                // multi-work-group finish: 10-bit digits
+constexpr int kRowDigit = 12;             // one-work-group select: 12-bit digits
 
 __device__ __forceinline__ int32_t row_count(const int32_t* n_valid, int32_t n_all,
                                              int row, int32_t N) {
@@ -51,9 +52,11 @@ __device__ __forceinline__ int32_t row_count(const int32_t* n_valid, int32_t n_a
 }
 
 // Exclusive prefix sum over the NT threads of a block; *total receives the sum.
-// lds must hold NT/64 + 1 words and is free again on return.
+// lds must hold NT/64 + 1 words and is free again on return.  Waves scan with
+// shuffles; wave 0 scans the wave totals.
 template <int NT>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -64,18 +67,20 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t* total) 
   }
   if (lane == 63) lds[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t acc = 0;
-    for (int w = 0; w < NT / 64; ++w) {
-      const uint32_t c = lds[w];
-      lds[w] = acc;
-      acc += c;
+  if (wave == 0) {
+    const uint32_t c = lane < NW ? lds[lane] : 0u;
+    uint32_t s = c;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) {
+      const uint32_t y = __shfl_up(s, o, 64);
+      if (lane >= o) s += y;
     }
-    lds[NT / 64] = acc;
+    if (lane < NW) lds[lane] = s - c;
+    if (lane == NW - 1) lds[NW] = s;
   }
   __syncthreads();
   const uint32_t r = lds[wave] + x - v;
-  *total = lds[NT / 64];
+  *total = lds[NW];
   __syncthreads();
   return r;
 }
@@ -368,10 +373,35 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, int32_t p, uint32_t 
   return ((uint64_t)key << 30) | (uint64_t)(nm1 - (uint32_t)p);
 }
 
-// f(key, position) for every position p < n of the row, kRowUnroll loads in flight.
+// f(key, position) for every position p < n of the row.  16-byte loads, 8 in
+// flight per thread, when the row is 16-byte aligned; otherwise 4-byte loads.
 template <typename F>
 __device__ __forceinline__ void stream_row(const float* __restrict__ sr, int32_t n, F&& f) {
-  for (int32_t base = 0; base < n; base += kRowThreads * kRowUnroll) {
+  int32_t done = 0;
+  if (((uintptr_t)sr & 15u) == 0) {
+    const float4* s4 = reinterpret_cast<const float4*>(sr);
+    const int32_t n4 = n >> 2;
+    for (int32_t base = 0; base < n4; base += kRowThreads * kRowUnroll) {
+      float4 v[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int32_t i = base + u * kRowThreads + (int32_t)threadIdx.x;
+        v[u] = i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int32_t i = base + u * kRowThreads + (int32_t)threadIdx.x;
+        if (i < n4) {
+          f(score_key(v[u].x), 4 * i);
+          f(score_key(v[u].y), 4 * i + 1);
+          f(score_key(v[u].z), 4 * i + 2);
+          f(score_key(v[u].w), 4 * i + 3);
+        }
+      }
+    }
+    done = n4 << 2;
+  }
+  for (int32_t base = done; base < n; base += kRowThreads * kRowUnroll) {
     float v[kRowUnroll];
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
@@ -441,6 +471,8 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   const int32_t* mrow = cand_map ? cand_map + (size_t)row * N : nullptr;
   int32_t* orow = out + (size_t)row * K;
 
+  auto visit = [&](auto&& f) { stream_row(sr, n, f); };
+
   // 1. Top-digit histogram: bits 61..50 of the composite = the top 12 key bits.
   if (kHasHist) {
     uint32_t* hr = hist + (size_t)row * kHistBins;
@@ -456,7 +488,7 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   if (!kHasHist) {
     for (int i = tid; i < kHistBins; i += kRowThreads) L.hist[i] = 0u;
     __syncthreads();
-    stream_row(sr, n, [&](uint32_t key, int32_t) {
+    visit([&](uint32_t key, int32_t) {
       atomicAdd(&L.hist[key >> (32 - kHistBits)], 1u);
     });
   }
@@ -473,18 +505,29 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   bool all = cnt == need;
 
   // 2. Refine by streaming passes until the prefix's members fit in LDS.
+  //    While the digit lies in the score bits (shift >= 30) every test is a
+  //    32-bit compare of the score key.
   while (!all && cnt > (uint32_t)kRowCap && shift > 0) {
-    const int w = shift < kDigit ? shift : kDigit;
+    const int w = shift < kRowDigit ? shift : kRowDigit;
     shift -= w;
-    for (int i = tid; i < (1 << kDigit); i += kRowThreads) L.hist[i] = 0u;
+    for (int i = tid; i < (1 << kRowDigit); i += kRowThreads) L.hist[i] = 0u;
     __syncthreads();
     const int sh = shift;
-    stream_row(sr, n, [&](uint32_t key, int32_t p) {
-      const uint64_t c = composite(key, p, nm1);
-      if ((c >> (sh + w)) == prefix) atomicAdd(&L.hist[(uint32_t)(c >> sh) & ((1u << w) - 1u)], 1u);
-    });
+    const uint32_t mask = (1u << w) - 1u;
+    if (sh >= 30) {
+      const int ks = sh - 30;
+      const uint32_t pre = (uint32_t)prefix;
+      visit([&](uint32_t key, int32_t) {
+        if ((key >> (ks + w)) == pre) atomicAdd(&L.hist[(key >> ks) & mask], 1u);
+      });
+    } else {
+      visit([&](uint32_t key, int32_t p) {
+        const uint64_t c = composite(key, p, nm1);
+        if ((c >> (sh + w)) == prefix) atomicAdd(&L.hist[(uint32_t)(c >> sh) & mask], 1u);
+      });
+    }
     __syncthreads();
-    row_find_digit<(1 << kDigit) / kRowThreads>(L.hist, need, L.scan, &d, &ab, &cnt);
+    row_find_digit<(1 << kRowDigit) / kRowThreads>(L.hist, need, L.scan, &d, &ab, &cnt);
     prefix = (prefix << w) | d;
     need -= ab;
     all = cnt == need;
@@ -497,18 +540,30 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   {
     const int sh = shift;
     const bool take_eq = all;
-    stream_row(sr, n, [&](uint32_t key, int32_t p) {
-      const uint64_t hi = composite(key, p, nm1) >> sh;
-      if (hi > prefix || (take_eq && hi == prefix)) {
+    auto hit = [&](uint32_t key, int32_t p, bool above, bool equal) {
+      if (above || (take_eq && equal)) {
         atomicOr(&L.bitmap[p >> 5], 1u << (p & 31));
-      } else if (hi == prefix) {
+      } else if (equal) {
         const uint32_t slot = atomicAdd(&L.ccount, 1u);
         if (slot < (uint32_t)kRowCap) {
           L.ckey[slot] = key;
           L.cpos[slot] = p;
         }
       }
-    });
+    };
+    if (sh >= 30) {
+      const int ks = sh - 30;
+      const uint32_t pre = (uint32_t)prefix;
+      visit([&](uint32_t key, int32_t p) {
+        const uint32_t hi = key >> ks;
+        if (hi >= pre) hit(key, p, hi > pre, hi == pre);
+      });
+    } else {
+      visit([&](uint32_t key, int32_t p) {
+        const uint64_t hi = composite(key, p, nm1) >> sh;
+        if (hi >= prefix) hit(key, p, hi > prefix, hi == prefix);
+      });
+    }
   }
   __syncthreads();
 
@@ -516,9 +571,9 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   if (!all) {
     const uint32_t C = L.ccount;   // == cnt <= kRowCap
     while (!all && shift > 0) {
-      const int w = shift < kDigit ? shift : kDigit;
+      const int w = shift < kRowDigit ? shift : kRowDigit;
       shift -= w;
-      for (int i = tid; i < (1 << kDigit); i += kRowThreads) L.hist[i] = 0u;
+      for (int i = tid; i < (1 << kRowDigit); i += kRowThreads) L.hist[i] = 0u;
       __syncthreads();
       for (uint32_t i = tid; i < C; i += kRowThreads) {
         const uint64_t c = composite(L.ckey[i], L.cpos[i], nm1);
@@ -526,7 +581,7 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
           atomicAdd(&L.hist[(uint32_t)(c >> shift) & ((1u << w) - 1u)], 1u);
       }
       __syncthreads();
-      row_find_digit<(1 << kDigit) / kRowThreads>(L.hist, need, L.scan, &d, &ab, &cnt);
+      row_find_digit<(1 << kRowDigit) / kRowThreads>(L.hist, need, L.scan, &d, &ab, &cnt);
       prefix = (prefix << w) | d;
       need -= ab;
       all = cnt == need;
@@ -599,12 +654,12 @@ hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
                             uint32_t* hist, bool zero_hist, const int32_t* cand,
                             int32_t* out, hipStream_t s) {
   if (N > kRowMaxN) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)R), block(kRowThreads);
   if (hist)
-    k_topk_row<true><<<dim3((unsigned)R), dim3(kRowThreads), 0, s>>>(
-        scores, N, n_valid, n_all, K, hist, zero_hist ? 1 : 0, cand, out);
+    k_topk_row<true><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, hist,
+                                            zero_hist ? 1 : 0, cand, out);
   else
-    k_topk_row<false><<<dim3((unsigned)R), dim3(kRowThreads), 0, s>>>(
-        scores, N, n_valid, n_all, K, nullptr, 0, cand, out);
+    k_topk_row<false><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, nullptr, 0, cand, out);
   return hipGetLastError();
 }
 
