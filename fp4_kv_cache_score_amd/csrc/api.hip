@@ -116,10 +116,10 @@ size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K, 
       return topk_call_ws_bytes(B, M, K);
     case CSA2_OP_SPARSE_ATTN:
       if (K <= 0 || K > kMaxK || H != kH) return 0;
-      return attn_ws_bytes((int64_t)B * Q, attn_chunks(K, 0));
+      return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, attn_chunks(K, 0));
     case CSA2_OP_SWA_MERGE:
       if (W < 0 || W > kMaxW || H != kH) return 0;
-      return attn_ws_bytes((int64_t)B * Q, W > 0 ? attn_chunks(0, W) : 1);
+      return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, W > 0 ? attn_chunks(0, W) : 1);
     case CSA2_OP_DECODE_LAYERS:
       if (M <= 0 || K <= 0 || K > kMaxK || P < 0 || P > kMaxK || (P > 0 && P < K) ||
           W < 0 || W > kMaxW || H != kH)
@@ -140,6 +140,11 @@ csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx, const 
   if (cand && (P <= 0 || P > kMaxTopkN)) return CSA2_ERR_SHAPE;
   if (!al16(q_idx) || !al4(w_idx) || !al4(scores) || (hist && !al4(hist)) || (cand && !al4(cand)))
     return CSA2_ERR_ALIGN;
+  if (Q > 1 && !cand) {   // chunked prefill: matrix-core contraction
+    if (hist) return CSA2_ERR_SHAPE;
+    return hip_status(launch_prefill_score(pool->idx_key, pool->B, pool->M, q_idx, w_idx, Q, pos0,
+                                           pos0 >= 0 ? ratio : 1, scores, stream));
+  }
   const int32_t N = cand ? P : pool->M;
   return hip_status(launch_index_score(pool->idx_key, pool->B, pool->M, q_idx, w_idx, Q, pos0,
                                        pos0 >= 0 ? ratio : 1, cand, N, scores, hist, stream));
@@ -177,7 +182,8 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   if (!al16(q) || !al4(idx) || !al16(o) || !al4(lse)) return CSA2_ERR_ALIGN;
   const int64_t rows = (int64_t)pool->B * Q;
   const int32_t chunks = attn_chunks(K, 0);
-  if (!ws || ws_bytes < attn_ws_bytes(rows, chunks)) return CSA2_ERR_WORKSPACE;
+  const size_t need = Q > 1 ? 256 : attn_ws_bytes(rows, chunks);
+  if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
   AttnArgs a{};
   a.latent = pool->latent;
@@ -195,6 +201,7 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   a.ml = (float*)((char*)ws + align256(rows * chunks * kH * kD * 4));
   a.o = o;
   a.lse = lse;
+  if (Q > 1) return hip_status(launch_prefill_attn(a, nullptr, nullptr, stream));
   const int32_t S = attn_splits(rows, chunks);
   st = hip_status(launch_attn_partial(a, S, true, stream));
   if (st != CSA2_OK || S == 1) return st;
@@ -212,7 +219,7 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   if (!al16(q) || !al16(o) || !al4(lse) || (swa && !al16(swa))) return CSA2_ERR_ALIGN;
   const int64_t rows = (int64_t)B * Q;
   const int32_t chunks = W > 0 ? attn_chunks(0, W) : 1;
-  if (!ws || ws_bytes < attn_ws_bytes(rows, chunks)) return CSA2_ERR_WORKSPACE;
+  if (!ws || ws_bytes < (Q > 1 ? 256 : attn_ws_bytes(rows, chunks))) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
   if (W == 0) return CSA2_OK;  // nothing to merge: (o, lse) unchanged
   AttnArgs a{};
@@ -231,6 +238,7 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   a.ml = (float*)((char*)ws + align256(rows * chunks * kH * kD * 4));
   a.o = o;
   a.lse = lse;
+  if (Q > 1) return hip_status(launch_prefill_attn(a, o, lse, stream));
   const int32_t S = attn_splits(rows, chunks);
   csa2_status st = hip_status(launch_attn_partial(a, S, false, stream));
   if (st != CSA2_OK) return st;

@@ -146,6 +146,18 @@ hipError_t launch_attn_combine(const float* opart, const float* ml, int32_t rows
                                int32_t splits, const float* o_in, const float* lse_in,
                                float* o, float* lse, hipStream_t s);
 
+// Chunked prefill (Q > 1 query tokens per sequence), matrix-core kernels.
+// Scores of every pool entry for every query (no candidate list, no
+// histogram); invisible entries get -inf.
+hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
+                                const float* w_idx, int32_t Q, int64_t pos0, int32_t ratio,
+                                float* scores, hipStream_t s);
+// One work-group per query row over its K selected entries and W window rows;
+// writes a.o / a.lse, merged with (o_in, lse_in) when lse_in is given (they
+// may alias a.o / a.lse).
+hipError_t launch_prefill_attn(const AttnArgs& a, const float* o_in, const float* lse_in,
+                               hipStream_t s);
+
 // Copy n int32 (Reuse layers that ask for their indices).
 hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 
