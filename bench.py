@@ -105,6 +105,48 @@ def time_score_kernel(dc, launches: int):
     return float(np.mean(ms)), float(np.min(ms))
 
 
+def measure_prefill(ci: int, steps: int, warmup: int):
+    """Chunked prefill (Q tokens, one Full layer): step time and per-stage kernel times."""
+    import torch
+    from fp4_kv_cache_score_amd import synth
+    from fp4_kv_cache_score_amd.configs import CONFIGS
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[ci]
+    case = synth.make_case(cfg)
+    dc = DeviceCase(case)
+    dc.prepare_prefill()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dc.prefill()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(4)] for _ in range(steps)]
+    for k in range(steps):
+        for st in range(4):
+            ev[k][st][0].record(stream)
+            dc.prefill_stage(st)
+            ev[k][st][1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = [float(np.mean([ev[k][st][0].elapsed_time(ev[k][st][1]) for k in range(steps)]))
+                for st in range(4)]
+    ms = sum(stage_ms)
+    t = np.arange(cfg.Q)
+    vis = np.minimum(cfg.M, (cfg.pos0 + t + 1) // cfg.ratio)
+    idx_flop = 2.0 * cfg.B * float(vis.sum()) * cfg.HI * cfg.DI
+    # S = q C^T and O = P C (P as bf16 hi + lo, two products) over K + W keys
+    attn_flop = 2.0 * cfg.B * cfg.Q * cfg.H * cfg.D * (cfg.K + cfg.W) * 3
+    del dc
+    torch.cuda.empty_cache()
+    return dict(workload=cfg.name, query_tokens_per_s=cfg.B * cfg.Q / (ms * 1e-3), ms_per_step=ms,
+                stage_ms={"index_score_mfma": stage_ms[0], "topk": stage_ms[1],
+                          "sparse_attn_mfma": stage_ms[2], "swa_merge_mfma": stage_ms[3]},
+                index_score_tflops=idx_flop / (stage_ms[0] * 1e-3) / 1e12,
+                index_score_frac_of_bf16_mfma_peak=idx_flop / (stage_ms[0] * 1e-3) / 2.5e15,
+                attention_tflops=attn_flop / ((stage_ms[2] + stage_ms[3]) * 1e-3) / 1e12,
+                attention_frac_of_bf16_mfma_peak=attn_flop / ((stage_ms[2] + stage_ms[3]) * 1e-3)
+                / 2.5e15)
+
+
 def cpu_baseline(case, budget_s: float = 15.0):
     """The CPU oracle, single-threaded, on whole sequences until the budget is used."""
     from threadpoolctl import threadpool_limits
@@ -160,6 +202,8 @@ def main():
     ap.add_argument("--config", type=int, default=1, help="headline workload (config index)")
     ap.add_argument("--extra", type=int, nargs="*", default=[2],
                     help="further decode configs measured into 'extra'")
+    ap.add_argument("--prefill", type=int, nargs="*", default=[4],
+                    help="chunked-prefill configs measured into 'extra'")
     ap.add_argument("--score-launches", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -207,6 +251,10 @@ def main():
             scan_kernel_ms=r["k_ms"],
             scan_kernel_gbs=r["per_launch"] / (r["k_ms"] * 1e-3) / 1e9)
         del r
+    for ci in args.prefill:
+        r = measure_prefill(ci, max(3, args.steps // 5), 2)
+        extra[r.pop("workload")] = r
+        log("prefill: %.3f ms/step %s" % (r["ms_per_step"], r["stage_ms"]))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head["case"], args.cpu_budget)

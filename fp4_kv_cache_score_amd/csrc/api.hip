@@ -202,10 +202,11 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   a.o = o;
   a.lse = lse;
   if (Q > 1) return hip_status(launch_prefill_attn(a, nullptr, nullptr, stream));
-  const int32_t S = attn_splits(rows, chunks);
-  st = hip_status(launch_attn_partial(a, S, true, stream));
-  if (st != CSA2_OK || S == 1) return st;
-  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, S, nullptr, nullptr, o, lse, stream));
+  const AttnPlan plan = attn_plan(rows, chunks);
+  st = hip_status(launch_attn_partial(a, plan, true, stream));
+  if (st != CSA2_OK || plan.splits == 1) return st;
+  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, plan.splits, nullptr, nullptr, o, lse,
+                                        stream));
 }
 
 csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t D,
@@ -239,10 +240,10 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   a.o = o;
   a.lse = lse;
   if (Q > 1) return hip_status(launch_prefill_attn(a, o, lse, stream));
-  const int32_t S = attn_splits(rows, chunks);
-  csa2_status st = hip_status(launch_attn_partial(a, S, false, stream));
+  const AttnPlan plan = attn_plan(rows, chunks);
+  csa2_status st = hip_status(launch_attn_partial(a, plan, false, stream));
   if (st != CSA2_OK) return st;
-  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, S, o, lse, o, lse, stream));
+  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, plan.splits, o, lse, o, lse, stream));
 }
 
 csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
@@ -275,7 +276,8 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
 
   const DecodeWs d = decode_ws_carve(ws, B, M, K, P, W);
   uint32_t* hist = d.big ? d.t.hist : d.hist;
-  const int32_t S = attn_splits(B, attn_chunks(K, W));
+  const AttnPlan plan = attn_plan(B, attn_chunks(K, W));
+  const int32_t S = plan.splits;
   float* opart = d.opart;
   float* ml = d.ml;
 
@@ -355,7 +357,7 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     a.ml = ml;
     a.o = y.o;
     a.lse = y.lse;
-    st = hip_status(launch_attn_partial(a, S, true, stream));
+    st = hip_status(launch_attn_partial(a, plan, true, stream));
     if (st != CSA2_OK) return st;
     if (S > 1) {
       st = hip_status(launch_attn_combine(opart, ml, (int32_t)B, S, nullptr, nullptr, y.o, y.lse,

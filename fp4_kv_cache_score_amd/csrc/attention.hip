@@ -42,7 +42,7 @@ constexpr int kCsStrideU = kD / 2 + 4;       // staged key row stride in u32: 16
 constexpr int kQU = kD / 2 + 4;              // q row stride in u32 (padded like the key rows)
 constexpr int kZS = KS + 4;                  // logit row stride (4 heads of a wave in 4 bank groups)
 constexpr int kMaxChunksPerSplit = 32;       // entry numbers staged per work-group: 1024
-constexpr int kTargetGroups = 512;           // work-groups per launch the split count aims at
+constexpr int kGroupsPerRound = 256;         // work-groups that run at once, one per compute unit
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
@@ -156,20 +156,31 @@ __device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& 
   }
 }
 
+// G heads per work-group (16 or 8): grid (splits, rows, 16 / G).
+template <int G>
 __global__ __launch_bounds__(kThreads, 2)
 void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t final_out) {
-  __shared__ __attribute__((aligned(16))) uint32_t qs[kH * kQU];          // 16 KiB
+  static_assert(G == 16 || G == 8, "heads per work-group");
+  constexpr int NHG = G / 4;               // groups of 4 heads
+  constexpr int KG = 64 / NHG;             // logits: key lanes per head group
+  constexpr int NK = 32 / KG;              // logits: keys per lane
+  constexpr int SPH = kThreads / G;        // softmax: threads per head
+  constexpr int SK = KS / SPH;             // softmax: keys per thread
+  constexpr int DP = 4 / NHG;              // P x V: dim parts
+  constexpr int LD = kD / DP / 64;         // P x V: dims per lane
+  __shared__ __attribute__((aligned(16))) uint32_t qs[G * kQU];
   __shared__ __attribute__((aligned(16))) uint32_t cs[KS * kCsStrideU];   // 33 KiB
-  __shared__ __attribute__((aligned(16))) float zp[4][kH][kZS];           // 9 KiB
-  __shared__ __attribute__((aligned(16))) float ps[KS][kH];               // 2 KiB
+  __shared__ __attribute__((aligned(16))) float zp[4][G][kZS];
+  __shared__ __attribute__((aligned(16))) float ps[KS][G];
   __shared__ int32_t idx_s[kMaxChunksPerSplit * KS];                      // 4 KiB
   __shared__ int valid_s[KS];
-  __shared__ float mh[kH], lh[kH];
-  __shared__ __attribute__((aligned(16))) float ah[kH];
+  __shared__ float mh[G], lh[G];
+  __shared__ __attribute__((aligned(16))) float ah[G];
 
   const int row = blockIdx.y;
   const int split = blockIdx.x;
   const int S = gridDim.x;
+  const int hb = blockIdx.z * G;           // first head of this work-group
   const int b = row / a.Q;
   const int t = row - b * a.Q;
   const int tid = threadIdx.x;
@@ -178,9 +189,9 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t fina
   const int c0 = split * cps;
   const int c1 = (c0 + cps < C) ? c0 + cps : C;
 
-  {  // q -> LDS
-    const u32x4* qg = reinterpret_cast<const u32x4*>(a.q + (size_t)row * kH * kD);
-    for (int i = tid; i < kH * kD / 8; i += kThreads)   // 64 16-byte pieces per head row
+  {  // q of the G heads -> LDS
+    const u32x4* qg = reinterpret_cast<const u32x4*>(a.q + ((size_t)row * kH + hb) * kD);
+    for (int i = tid; i < G * kD / 8; i += kThreads)   // 64 16-byte pieces per head row
       *reinterpret_cast<u32x4*>(qs + (i >> 6) * kQU + (i & 63) * 4) = qg[i];
   }
   // entry numbers of this split's global keys -> LDS
@@ -188,7 +199,7 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t fina
   const int gend = (c1 < Cg ? c1 : Cg) * KS;
   const int key1 = gend < a.K ? gend : a.K;
   for (int k = key0 + tid; k < key1; k += kThreads) idx_s[k - key0] = a.idx[(size_t)row * a.K + k];
-  if (tid < kH) {
+  if (tid < G) {
     mh[tid] = -INFINITY;
     lh[tid] = 0.f;
   }
@@ -197,79 +208,87 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t fina
   ChunkRegs r;
   load_chunk(a, c0, Cg, b, t, idx_s, key0, r);
 
-  // P x V accumulators: wave = 4 heads, lane = 8 dims
-  const int h0 = wave * 4;
-  const int d0 = lane * 8;
-  float acc[4][8];
+  // P x V accumulators: wave = (4 heads, 1/DP of the dims), lane = LD dims
+  const int h0 = 4 * (wave % NHG);
+  const int d0 = (wave / NHG) * (kD / DP) + lane * LD;
+  float acc[4][LD];
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+    for (int i = 0; i < LD; ++i) acc[h][i] = 0.f;
 
   for (int c = c0; c < c1; ++c) {
     stage_chunk(c, Cg, r, cs, valid_s);
     __syncthreads();
     if (c + 1 < c1) load_chunk(a, c + 1, Cg, b, t, idx_s, key0, r);
 
-    {  // logits: wave = quarter of the dims; lane = 4 heads x 2 keys
-      const int hg = lane >> 4;
-      const int kg = lane & 15;
+    {  // logits: wave = quarter of the dims; lane = 4 heads x NK keys
+      const int hg = lane / KG;
+      const int kg = lane % KG;
       const int u0 = wave * (kD / 8);          // first u32 of this wave's 128 dims
-      float z[4][2];
+      float z[4][NK];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) z[h][0] = z[h][1] = 0.f;
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int k = 0; k < NK; ++k) z[h][k] = 0.f;
 #pragma unroll 4
       for (int du = 0; du < kD / 8; du += 4) {
-        u32x4 qv[4], cv[2];
+        u32x4 qv[4], cv[NK];
 #pragma unroll
         for (int h = 0; h < 4; ++h)
           qv[h] = *reinterpret_cast<const u32x4*>(qs + (4 * hg + h) * kQU + u0 + du);
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
-          cv[k] = *reinterpret_cast<const u32x4*>(cs + (kg + 16 * k) * kCsStrideU + u0 + du);
+        for (int k = 0; k < NK; ++k)
+          cv[k] = *reinterpret_cast<const u32x4*>(cs + (kg + KG * k) * kCsStrideU + u0 + du);
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
-          for (int k = 0; k < 2; ++k)
+          for (int k = 0; k < NK; ++k)
 #pragma unroll
             for (int w = 0; w < 4; ++w)
               z[h][k] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[h][w]), as_bf16x2(cv[k][w]),
                                                         z[h][k], false);
       }
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        zp[wave][4 * hg + h][kg] = z[h][0];
-        zp[wave][4 * hg + h][kg + 16] = z[h][1];
-      }
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int k = 0; k < NK; ++k) zp[wave][4 * hg + h][kg + KG * k] = z[h][k];
     }
     __syncthreads();
 
-    {  // online softmax statistics: thread = (head, 2 keys)
-      const int h = tid >> 4;
-      const int j0 = tid & 15;
-      float z[2];
+    {  // online softmax statistics: thread = (head, SK keys)
+      const int h = tid / SPH;
+      const int j0 = tid % SPH;
+      float z[SK];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int j = j0 + 16 * k;
+      for (int k = 0; k < SK; ++k) {
+        const int j = j0 + SPH * k;
         const float s = ((zp[0][h][j] + zp[1][h][j]) + zp[2][h][j]) + zp[3][h][j];
         z[k] = valid_s[j] ? s : -INFINITY;
       }
-      float m = fmaxf(z[0], z[1]);
+      float m = z[0];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      for (int k = 1; k < SK; ++k) m = fmaxf(m, z[k]);
+#pragma unroll
+      for (int o = 1; o < SPH; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       const float m_old = mh[h];
       const float m_new = fmaxf(m_old, m);
-      float p0 = 0.f, p1 = 0.f, alpha = 1.f;
+      float p[SK];
+      float alpha = 1.f;
+#pragma unroll
+      for (int k = 0; k < SK; ++k) p[k] = 0.f;
       if (m_new != -INFINITY) {
-        p0 = __expf(z[0] - m_new);
-        p1 = __expf(z[1] - m_new);
+#pragma unroll
+        for (int k = 0; k < SK; ++k) p[k] = __expf(z[k] - m_new);
         alpha = __expf(m_old - m_new);
       }
-      float l = p0 + p1;
+      float l = p[0];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
-      ps[j0][h] = p0;
-      ps[j0 + 16][h] = p1;
+      for (int k = 1; k < SK; ++k) l += p[k];
+#pragma unroll
+      for (int o = 1; o < SPH; o <<= 1) l += __shfl_xor(l, o, 64);
+#pragma unroll
+      for (int k = 0; k < SK; ++k) ps[j0 + SPH * k][h] = p[k];
       if (j0 == 0) {
         mh[h] = m_new;
         lh[h] = lh[h] * alpha + l;
@@ -284,22 +303,29 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t fina
 #pragma unroll
       for (int h = 0; h < 4; ++h)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] *= alv[h];
+        for (int i = 0; i < LD; ++i) acc[h][i] *= alv[h];
 #pragma unroll 4
       for (int j = 0; j < KS; ++j) {
         const float4 p = *reinterpret_cast<const float4*>(&ps[j][h0]);
-        const u32x4 cv = *reinterpret_cast<const u32x4*>(cs + j * kCsStrideU + d0 / 2);
-        float cf[8];
+        uint32_t cw[LD / 2];
+        if constexpr (LD == 8) {
+          const u32x4 cv = *reinterpret_cast<const u32x4*>(cs + j * kCsStrideU + d0 / 2);
+          cw[0] = cv[0]; cw[1] = cv[1]; cw[2] = cv[2]; cw[3] = cv[3];
+        } else {
+          const uint2 cv = *reinterpret_cast<const uint2*>(cs + j * kCsStrideU + d0 / 2);
+          cw[0] = cv.x; cw[1] = cv.y;
+        }
+        float cf[LD];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          cf[2 * w + 0] = __uint_as_float(cv[w] << 16);
-          cf[2 * w + 1] = __uint_as_float(cv[w] & 0xFFFF0000u);
+        for (int w = 0; w < LD / 2; ++w) {
+          cf[2 * w + 0] = __uint_as_float(cw[w] << 16);
+          cf[2 * w + 1] = __uint_as_float(cw[w] & 0xFFFF0000u);
         }
         const float pv[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(pv[h], cf[i], acc[h][i]);
+          for (int i = 0; i < LD; ++i) acc[h][i] = fmaf(pv[h], cf[i], acc[h][i]);
       }
     }
     __syncthreads();
@@ -310,24 +336,26 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t fina
     for (int h = 0; h < 4; ++h) {
       const float L = lh[h0 + h];
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      float4* dst = reinterpret_cast<float4*>(a.o + ((size_t)row * kH + h0 + h) * kD + d0);
-      dst[0] = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
-      dst[1] = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+      float* dst = a.o + ((size_t)row * kH + hb + h0 + h) * kD + d0;
+#pragma unroll
+      for (int i = 0; i < LD; i += 4)
+        *reinterpret_cast<float4*>(dst + i) =
+            make_float4(acc[h][i] * inv, acc[h][i + 1] * inv, acc[h][i + 2] * inv, acc[h][i + 3] * inv);
     }
-    if (tid < kH) {
+    if (tid < G) {
       const float L = lh[tid];
-      a.lse[(size_t)row * kH + tid] = L > 0.f ? mh[tid] + logf(L) : -INFINITY;
+      a.lse[(size_t)row * kH + hb + tid] = L > 0.f ? mh[tid] + logf(L) : -INFINITY;
     }
   } else {
-    float* op = a.opart + (((size_t)row * S + split) * kH + h0) * kD + d0;
+    float* op = a.opart + (((size_t)row * S + split) * kH + hb + h0) * kD + d0;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float4* dst = reinterpret_cast<float4*>(op + (size_t)h * kD);
-      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
-    if (tid < kH) {
-      float* mlp = a.ml + (((size_t)row * S + split) * kH + tid) * 2;
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int i = 0; i < LD; i += 4)
+        *reinterpret_cast<float4*>(op + (size_t)h * kD + i) =
+            make_float4(acc[h][i], acc[h][i + 1], acc[h][i + 2], acc[h][i + 3]);
+    if (tid < G) {
+      float* mlp = a.ml + (((size_t)row * S + split) * kH + hb + tid) * 2;
       mlp[0] = mh[tid];
       mlp[1] = lh[tid];
     }
@@ -424,26 +452,47 @@ int32_t attn_chunks(int32_t K, int32_t W) {
   return (K > 0 ? (K + KS - 1) / KS : 0) + (W > 0 ? (W + KS - 1) / KS : 0);
 }
 
-int32_t attn_splits(int64_t rows, int32_t chunks) {
-  if (chunks <= 0) return 0;
-  int64_t S = (kTargetGroups + rows - 1) / (rows > 0 ? rows : 1);
-  const int64_t lo = (chunks + kMaxChunksPerSplit - 1) / kMaxChunksPerSplit;
-  if (S < lo) S = lo;
-  if (S > chunks) S = chunks;
-  if (S > kCombMaxS) S = kCombMaxS;
-  if (S < lo) S = lo;   // chunk cap wins over the combine's split cap
-  const int64_t cps = (chunks + S - 1) / S;
-  return (int32_t)((chunks + cps - 1) / cps);
+AttnPlan attn_plan(int64_t rows, int32_t chunks) {
+  // Pick heads per work-group G (16 or 8) and splits S so that the launch
+  // fills the chip without giving some compute units two work-groups while
+  // others idle: estimated time = rounds of kGroupsPerRound work-groups x
+  // (chunks per work-group x G/16 + a fixed prologue), plus a merge launch
+  // when S > 1.
+  AttnPlan best{16, 1, 0.0};
+  if (chunks <= 0) return AttnPlan{16, 0, 0.0};
+  double best_cost = 1e30;
+  for (int G = 16; G >= 8; G /= 2) {
+    const int64_t lo = (chunks + kMaxChunksPerSplit - 1) / kMaxChunksPerSplit;
+    for (int64_t S = lo; S <= chunks && S <= kCombMaxS; ++S) {
+      const int64_t cps = (chunks + S - 1) / S;
+      const int64_t Se = (chunks + cps - 1) / cps;
+      if (Se != S) continue;
+      const int64_t groups = rows * (16 / G) * S;
+      const int64_t rounds = (groups + kGroupsPerRound - 1) / kGroupsPerRound;
+      const double cost = (double)rounds * ((double)cps * G / 16.0 + 0.5) + (S > 1 ? 1.0 : 0.0);
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = AttnPlan{G, (int32_t)S, cost};
+      }
+    }
+  }
+  return best;
 }
 
-hipError_t launch_attn_partial(const AttnArgs& a, int32_t splits, bool final_out, hipStream_t s) {
+hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, bool final_out, hipStream_t s) {
   const int32_t Cg = a.K > 0 && a.latent ? (a.K + KS - 1) / KS : 0;
   const int32_t C = Cg + (a.W > 0 ? (a.W + KS - 1) / KS : 0);
+  const int32_t splits = plan.splits;
   if (C == 0 || splits <= 0) return hipSuccess;
   const int32_t cps = (C + splits - 1) / splits;
   if (cps > kMaxChunksPerSplit || (C + cps - 1) / cps != splits) return hipErrorInvalidValue;
-  k_attn_partial<<<dim3((unsigned)splits, (unsigned)a.rows), dim3(kThreads), 0, s>>>(
-      a, Cg, C, cps, final_out ? 1 : 0);
+  const dim3 block(kThreads);
+  if (plan.G == 8)
+    k_attn_partial<8><<<dim3((unsigned)splits, (unsigned)a.rows, 2), block, 0, s>>>(
+        a, Cg, C, cps, final_out ? 1 : 0);
+  else
+    k_attn_partial<16><<<dim3((unsigned)splits, (unsigned)a.rows, 1), block, 0, s>>>(
+        a, Cg, C, cps, final_out ? 1 : 0);
   return hipGetLastError();
 }
 

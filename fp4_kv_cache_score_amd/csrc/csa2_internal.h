@@ -139,9 +139,15 @@ struct AttnArgs {
   float* lse;             // [rows][kH]
 };
 int32_t attn_chunks(int32_t K, int32_t W);          // chunks of one row's keys
-int32_t attn_splits(int64_t rows, int32_t chunks);  // work-groups per row
+// Heads per work-group (16 or 8) and splits per row of a launch.
+struct AttnPlan {
+  int32_t G;
+  int32_t splits;
+  double cost;
+};
+AttnPlan attn_plan(int64_t rows, int32_t chunks);
 // final_out: write o / lse directly when the row has one split.
-hipError_t launch_attn_partial(const AttnArgs& a, int32_t splits, bool final_out, hipStream_t s);
+hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, bool final_out, hipStream_t s);
 hipError_t launch_attn_combine(const float* opart, const float* ml, int32_t rows,
                                int32_t splits, const float* o_in, const float* lse_in,
                                float* o, float* lse, hipStream_t s);

@@ -136,15 +136,51 @@ class DeviceCase:
             np.full(cfg.Q, cfg.M)
         return torch.from_numpy(np.tile(vis.astype(np.int32), cfg.B)).to(self.device)
 
+    def prepare_prefill(self):
+        """Allocate every buffer of a prefill step once (scores, indices, outputs, workspace)."""
+        cfg = self.cfg
+        dev = self.device
+        R = cfg.B * cfg.Q
+        self.pf_scores = torch.empty((cfg.B, cfg.Q, cfg.M), dtype=torch.float32, device=dev)
+        self.pf_nvalid = self.visible_counts()
+        self.pf_idx = torch.empty((R, cfg.K), dtype=torch.int32, device=dev)
+        self.pf_o = torch.empty((cfg.B, cfg.Q, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+        self.pf_lse = torch.empty((cfg.B, cfg.Q, cfg.H), dtype=torch.float32, device=dev)
+        nb = max(C.csa2_workspace_bytes(C.CSA2_OP_TOPK, R, 1, cfg.M, cfg.K, 0, 0, 0),
+                 C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, cfg.B, cfg.Q, cfg.M, cfg.K, 0, 0,
+                                        cfg.H),
+                 C.csa2_workspace_bytes(C.CSA2_OP_SWA_MERGE, cfg.B, cfg.Q, 0, 0, 0, cfg.W, cfg.H))
+        self.pf_ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.pf_ws_bytes = nb
+
+    def prefill_stage(self, stage: int, stream=None):
+        """One stage of the prefill step on the preallocated buffers:
+        0 index score (Q rows, causal), 1 Top-K over the visible entries,
+        2 sparse attention over the selected entries, 3 window merge."""
+        cfg = self.cfg
+        d = self.layers[0]
+        R = cfg.B * cfg.Q
+        if stage == 0:
+            C.csa2_index_score(self.pool, d["q_idx"], d["w_idx"], cfg.Q, cfg.pos0, cfg.ratio, None,
+                               0, self.pf_scores, None, stream)
+        elif stage == 1:
+            C.csa2_topk(self.pf_scores, R, cfg.M, self.pf_nvalid, None, cfg.K, self.pf_idx,
+                        self.pf_ws, self.pf_ws_bytes, stream)
+        elif stage == 2:
+            C.csa2_sparse_attn(self.pool, d["q"], cfg.Q, cfg.H, self.pf_idx, cfg.K, self.pf_o,
+                               self.pf_lse, self.pf_ws, self.pf_ws_bytes, stream)
+        else:
+            C.csa2_swa_merge(d["q"], cfg.B, cfg.Q, cfg.H, cfg.D, d["swa"], cfg.W, self.pf_o,
+                             self.pf_lse, self.pf_ws, self.pf_ws_bytes, stream)
+
     def prefill(self, stream=None):
         """index_score (Q rows, causal) -> topk (n_valid = visible) -> sparse_attn -> swa_merge."""
+        if getattr(self, "pf_scores", None) is None:
+            self.prepare_prefill()
+        for stage in range(4):
+            self.prefill_stage(stage, stream)
         cfg = self.cfg
-        scores = self.index_scores(0, stream=stream)
-        idx = self.topk(scores, cfg.K, n_valid=self.visible_counts(), stream=stream)
-        idx = idx.view(cfg.B, cfg.Q, cfg.K)
-        o, lse = self.sparse_attn(0, idx, stream=stream)
-        o, lse = self.swa_merge(0, o, lse, stream=stream)
-        return idx, o, lse
+        return self.pf_idx.view(cfg.B, cfg.Q, cfg.K), self.pf_o, self.pf_lse
 
     # -- results -----------------------------------------------------------------
     def results(self):
