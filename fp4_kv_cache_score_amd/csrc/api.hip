@@ -26,7 +26,7 @@ constexpr int32_t kMaxRows = 65535;  // grid.y limit for row-indexed launches
 
 // Top-K workspace: nothing for rows the one-work-group select handles.
 size_t topk_call_ws_bytes(int64_t R, int64_t N, int64_t K) {
-  return N <= kRowMaxN ? 256 : topk_ws_bytes(R, N, K);
+  return topk_multi_wg(R, N) ? topk_ws_bytes(R, N, K) : 256;
 }
 
 // decode_layers workspace: scores [B][N] | histograms [B][4096] |
@@ -47,7 +47,7 @@ size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t Kmax = P > K ? P : K;
   const int64_t splits = attn_chunks((int32_t)K, (int32_t)W);
   return align256(B * N * 4) + align256(B * kHistBins * 4) +
-         (M > kRowMaxN ? topk_ws_bytes(B, M, Kmax) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
+         (topk_multi_wg(B, M) ? topk_ws_bytes(B, M, Kmax) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
          attn_ws_bytes(B, splits > 0 ? splits : 1);
 }
 
@@ -60,7 +60,7 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   p += align256(B * N * 4);
   d.hist = (uint32_t*)p;
   p += align256(B * kHistBins * 4);
-  d.big = M > kRowMaxN;
+  d.big = topk_multi_wg(B, M);
   if (d.big) {
     d.t = topk_ws_carve(p, B, M, Kmax);
     p += topk_ws_bytes(B, M, Kmax);
@@ -73,13 +73,12 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   return d;
 }
 
-// Multi-work-group Top-K on scores whose histogram is ready in t.hist.
+// Multi-work-group Top-K on scores whose histogram is ready in t.hist (the
+// counters are zero; the finish step leaves them zero again).
 csa2_status select_rows_big(const float* scores, int32_t R, int32_t N, const int32_t* n_valid,
                             int32_t n_all, const int32_t* cand, int32_t K, int32_t* out,
-                            const TopkWs& t, hipStream_t s) {
-  csa2_status st = hip_status(launch_fill_zero(t.counters, (int64_t)R * kCounterWords, s));
-  if (st != CSA2_OK) return st;
-  return hip_status(launch_topk_select(scores, R, N, n_valid, n_all, cand, K, out, t, s));
+                            const TopkWs& t, bool zero_hist, hipStream_t s) {
+  return hip_status(launch_topk_select(scores, R, N, n_valid, n_all, cand, K, out, t, zero_hist, s));
 }
 
 // Zero the histogram and the per-row counters (adjacent in the workspace).
@@ -160,7 +159,7 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* 
     return CSA2_ERR_ALIGN;
   if (!ws || ws_bytes < topk_call_ws_bytes(R, N, K)) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
-  if (N <= kRowMaxN)
+  if (!topk_multi_wg(R, N))
     return hip_status(launch_topk_rows(scores, R, N, n_valid, N, K, nullptr, false, cand, idx,
                                        stream));
   const TopkWs t = topk_ws_carve(ws, R, N, K);
@@ -168,7 +167,7 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* 
   if (st != CSA2_OK) return st;
   st = hip_status(launch_topk_hist(scores, R, N, n_valid, N, t.hist, stream));
   if (st != CSA2_OK) return st;
-  return hip_status(launch_topk_select(scores, R, N, n_valid, N, cand, K, idx, t, stream));
+  return hip_status(launch_topk_select(scores, R, N, n_valid, N, cand, K, idx, t, false, stream));
 }
 
 csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q, int32_t H,
@@ -281,21 +280,19 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
   float* opart = d.opart;
   float* ml = d.ml;
 
-  // The histogram starts zeroed; every one-work-group select leaves it
-  // zeroed again, so only the multi-work-group path needs a fresh fill.
-  st = hip_status(launch_fill_zero(hist, B * kHistBins, stream));
+  // The histogram (and the multi-work-group counters next to it) start
+  // zeroed; every select leaves them zeroed again.
+  if (d.big)
+    st = zero_hist_counters(d.t, B, stream);
+  else
+    st = hip_status(launch_fill_zero(hist, B * kHistBins, stream));
   if (st != CSA2_OK) return st;
-  bool hist_clean = true;
 
   const int32_t* cur = nullptr;
   int32_t cur_layer = -1;
   const int32_t n_cand = (int32_t)(P < M ? P : M);
   for (int32_t l = 0; l < L; ++l) {
     const csa2_layer& y = layers[l];
-    if (y.mode != CSA2_REUSE && !hist_clean) {
-      st = hip_status(launch_fill_zero(hist, B * kHistBins, stream));
-      if (st != CSA2_OK) return st;
-    }
     if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
                                          nullptr, (int32_t)M, d.scores, hist, stream));
@@ -309,17 +306,15 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
         st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, K,
                                          hist, true, nullptr, y.idx_out, stream));
         if (st != CSA2_OK) return st;
-        hist_clean = true;
       } else {
         if (y.mode == CSA2_FULL && P > 0) {
           st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P,
-                               d.cand, d.t, stream);
+                               d.cand, d.t, false, stream);
           if (st != CSA2_OK) return st;
         }
         st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, K,
-                             y.idx_out, d.t, stream);
+                             y.idx_out, d.t, true, stream);
         if (st != CSA2_OK) return st;
-        hist_clean = false;
       }
       cur = y.idx_out;
       cur_layer = l;
@@ -330,7 +325,6 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
       st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, nullptr, n_cand, K, hist, true,
                                        d.cand, y.idx_out, stream));
       if (st != CSA2_OK) return st;
-      hist_clean = true;
       cur = y.idx_out;
       cur_layer = l;
     } else {  // Reuse

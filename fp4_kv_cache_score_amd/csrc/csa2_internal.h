@@ -21,7 +21,14 @@ constexpr int kHistBits = 12;               // first radix digit: top 12 key bit
 constexpr int kHistBins = 1 << kHistBits;   // 4096
 constexpr int kMaxK = 16384;
 constexpr int kMaxTopkN = 1 << 30;          // row length limit (composite key packs 30 bits)
-constexpr int kRowMaxN = 1 << 18;           // rows up to this length take the one-work-group select
+constexpr int kRowMaxN = 1 << 18;           // rows up to this length can take the one-work-group select
+constexpr int kRowSplitN = 32768;           // longer rows, when there are few, take the multi-work-group select
+constexpr int kRowSplitR = 256;             // "few": fewer rows than this
+
+// Which select a (rows, row length) shape takes.
+inline bool topk_multi_wg(int64_t R, int64_t N) {
+  return N > kRowMaxN || (N > kRowSplitN && R < kRowSplitR);
+}
 constexpr int kCounterWords = 4;            // per row: [0]=above count, [1]=candidate count
 
 // Attention
@@ -110,10 +117,13 @@ hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
 hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
                             const int32_t* n_valid, int32_t n_all,
                             uint32_t* hist, hipStream_t s);
+// Multi-work-group select on scores whose histogram is in ws.hist and whose
+// counters are zero; leaves the counters (and, with zero_hist, the
+// histogram) zeroed.
 hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
                               const int32_t* n_valid, int32_t n_all,
                               const int32_t* cand, int32_t K, int32_t* out,
-                              const TopkWs& ws, hipStream_t s);
+                              const TopkWs& ws, bool zero_hist, hipStream_t s);
 
 // Attention over up to K gathered FP4 entries and up to W FP8 window rows per
 // query row.  The row's keys are cut into chunks of kKeysPerSplit (global

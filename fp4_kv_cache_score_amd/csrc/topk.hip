@@ -24,10 +24,12 @@
 //     are broken by the position bits), and the chosen ones are marked;
 //  5. a block prefix sum over the bitmap's popcounts writes the positions in
 //     ascending order.
-// Longer rows use the multi-work-group path: k_topk_hist -> k_topk_collect
+// Long rows on few rows (and rows over 2^18) use the multi-work-group path:
+// k_topk_hist (unless the score kernel built the histogram) -> k_topk_collect
 // (positions above the threshold bin and that bin's members, appended with
 // one atomic per work-group) -> k_topk_finish (radix passes over the members
-// and an ordered extraction through bitmap segments).
+// and an ordered extraction through bitmap segments; it leaves the row's
+// counters, and optionally its histogram, zeroed for the next select).
 // Ties, -0 vs +0, rows with fewer than K valid positions are handled exactly;
 // the result is deterministic.
 #include "csa2_internal.h"
@@ -236,10 +238,11 @@ __device__ __forceinline__ void visit_bin(bool overflow, uint32_t C, const uint3
 __global__ __launch_bounds__(kFinThreads)
 void k_topk_finish(const float* __restrict__ scores, int32_t N,
                    const int32_t* __restrict__ n_valid, int32_t n_all, int32_t K,
-                   const uint32_t* __restrict__ hist, const uint32_t* __restrict__ counters,
+                   uint32_t* hist, uint32_t* counters,
                    const int32_t* __restrict__ sel, const uint32_t* __restrict__ candk,
                    const int32_t* __restrict__ candp, int32_t cap,
-                   const int32_t* __restrict__ cand_map, int32_t* __restrict__ out) {
+                   const int32_t* __restrict__ cand_map, int32_t* __restrict__ out,
+                   int32_t zero_hist) {
   __shared__ uint32_t lds[kFinThreads / 64 + 8];
   __shared__ uint32_t rh[1 << kDigit];
   __shared__ uint32_t bitmap[kSegWords];
@@ -248,8 +251,17 @@ void k_topk_finish(const float* __restrict__ scores, int32_t N,
   const int32_t n = row_count(n_valid, n_all, row, N);
   int32_t* orow = out + (size_t)row * K;
   const int32_t* mrow = cand_map ? cand_map + (size_t)row * N : nullptr;
+  // Leave this row's counters (and, when asked, its histogram) zeroed for the
+  // next select.  They are read and cleared through the same pointers, and
+  // every read happens before the barrier that precedes the clearing.
+  auto clean = [&]() {
+    if (tid < kCounterWords) counters[(size_t)row * kCounterWords + tid] = 0u;
+    if (zero_hist)
+      for (int i = tid; i < kHistBins; i += kFinThreads) hist[(size_t)row * kHistBins + i] = 0u;
+  };
   if (n <= K) {
     for (int i = tid; i < K; i += kFinThreads) orow[i] = i < n ? (mrow ? mrow[i] : i) : -1;
+    clean();
     return;
   }
   int bstar;
@@ -260,6 +272,8 @@ void k_topk_finish(const float* __restrict__ scores, int32_t N,
     return;
   }
   const uint32_t ccount = counters[(size_t)row * kCounterWords + 1];
+  __syncthreads();   // every thread has read the counters and the histogram
+  clean();
   const bool overflow = ccount > (uint32_t)cap;
   const uint32_t C = overflow ? 0u : ccount;
   const uint32_t* ck = candk + (size_t)row * cap;
@@ -674,7 +688,7 @@ hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
 hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
                               const int32_t* n_valid, int32_t n_all,
                               const int32_t* cand, int32_t K, int32_t* out,
-                              const TopkWs& ws, hipStream_t s) {
+                              const TopkWs& ws, bool zero_hist, hipStream_t s) {
   const dim3 grid((unsigned)((N + kChunk - 1) / kChunk), (unsigned)R);
   k_topk_collect<<<grid, dim3(kSelThreads), 0, s>>>(scores, N, n_valid, n_all, K, ws.hist,
                                                     ws.counters, ws.sel, ws.candk, ws.candp, ws.cap);
@@ -682,7 +696,7 @@ hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
   if (e != hipSuccess) return e;
   k_topk_finish<<<dim3((unsigned)R), dim3(kFinThreads), 0, s>>>(
       scores, N, n_valid, n_all, K, ws.hist, ws.counters, ws.sel, ws.candk, ws.candp, ws.cap,
-      cand, out);
+      cand, out, zero_hist ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -182,7 +182,8 @@ def _oracle_rows(scores_np, K, n_valid=None, cand=None):
 
 @pytest.mark.parametrize("R,N,K,kind", [
     (1, 1, 1, "cont"), (3, 7, 3, "ties"), (5, 100, 100, "cont"), (4, 100, 150, "ties"),
-    (8, 4097, 64, "ties"), (6, 33333, 512, "cont"), (2, 9000, 8192, "cont"),
+    (8, 4097, 64, "ties"), (6, 33333, 512, "cont"), (6, 40960, 512, "cont"), (2, 33000, 64, "ties"),
+    (2, 9000, 8192, "cont"),
     (3, 300001, 512, "cont"), (2, 300001, 8192, "ties"), (64, 4096, 1, "ties"),
     (16, 2000, 77, "zeros"), (4, 5000, 300, "negzero")])
 def test_topk_exact_vs_oracle(R, N, K, kind):
