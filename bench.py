@@ -200,7 +200,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="headline workload (config index)")
-    ap.add_argument("--extra", type=int, nargs="*", default=[2],
+    ap.add_argument("--extra", type=int, nargs="*", default=[2, 3],
                     help="further decode configs measured into 'extra'")
     ap.add_argument("--prefill", type=int, nargs="*", default=[4],
                     help="chunked-prefill configs measured into 'extra'")

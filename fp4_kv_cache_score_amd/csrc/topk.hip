@@ -53,38 +53,42 @@ __device__ __forceinline__ int32_t row_count(const int32_t* n_valid, int32_t n_a
   return n < 0 ? 0 : (n > N ? N : n);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: a scan inside each row
+// of 16 lanes with DPP row shifts, then the row totals added with readlane.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
+}
+
 // Exclusive prefix sum over the NT threads of a block; *total receives the sum.
-// lds must hold NT/64 + 1 words and is free again on return.  Waves scan with
-// shuffles; wave 0 scans the wave totals.
+// lds must hold NT/64 words and is free again on return.  Each wave scans
+// with DPP, publishes its total, and every wave then adds the totals of the
+// waves before it.
 template <int NT>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) lds[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    const uint32_t c = lane < NW ? lds[lane] : 0u;
-    uint32_t s = c;
+  uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int o = 1; o < NW; o <<= 1) {
-      const uint32_t y = __shfl_up(s, o, 64);
-      if (lane >= o) s += y;
-    }
-    if (lane < NW) lds[lane] = s - c;
-    if (lane == NW - 1) lds[NW] = s;
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = lds[w];
+    before += w < wave ? c : 0u;
+    all += c;
   }
+  *total = all;
   __syncthreads();
-  const uint32_t r = lds[wave] + x - v;
-  *total = lds[NW];
-  __syncthreads();
-  return r;
+  return before + x - v;
 }
 
 // Bin of the K-th largest key in a 4096-bin histogram (bins ordered by key).
@@ -348,15 +352,29 @@ void k_topk_finish(const float* __restrict__ scores, int32_t N,
     }
     uint32_t tot;
     uint32_t pos = written + block_excl_scan<kFinThreads>(cnt, lds, &tot);
+    if (!mrow) {   // stores only: no load in this loop (see k_topk_row)
 #pragma unroll
-    for (int w = 0; w < WPT; ++w) {
-      uint32_t m = wv[w];
-      while (m) {
-        const int bit = __ffs(m) - 1;
-        m &= m - 1;
-        const int64_t p = s0 + (int64_t)(tid * WPT + w) * 32 + bit;
-        if (pos < (uint32_t)K) orow[pos] = mrow ? mrow[p] : (int32_t)p;
-        ++pos;
+      for (int w = 0; w < WPT; ++w) {
+        uint32_t m = wv[w];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          const int64_t p = s0 + (int64_t)(tid * WPT + w) * 32 + bit;
+          if (pos < (uint32_t)K) orow[pos] = (int32_t)p;
+          ++pos;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) {
+        uint32_t m = wv[w];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          const int64_t p = s0 + (int64_t)(tid * WPT + w) * 32 + bit;
+          if (pos < (uint32_t)K) orow[pos] = mrow[p];
+          ++pos;
+        }
       }
     }
     written += tot;
@@ -373,6 +391,7 @@ constexpr int kRowThreads = 1024;
 constexpr int kRowWords = kRowMaxN / 32;   // bitmap words (8192 = 32 KiB)
 constexpr int kRowCap = 1536;              // LDS candidate slots
 constexpr int kRowUnroll = 8;              // loads in flight per thread while streaming
+constexpr int kPreF4 = 8;                  // prefetched 16-byte pieces per thread (rows up to 32768)
 
 struct RowLds {
   uint32_t hist[kHistBins];
@@ -430,6 +449,53 @@ __device__ __forceinline__ void stream_row(const float* __restrict__ sr, int32_t
   }
 }
 
+// stream_row on the float values.
+template <typename F>
+__device__ __forceinline__ void stream_row_f(const float* __restrict__ sr, int32_t n, F&& f) {
+  int32_t done = 0;
+  if (((uintptr_t)sr & 15u) == 0) {
+    const float4* s4 = reinterpret_cast<const float4*>(sr);
+    const int32_t n4 = n >> 2;
+    for (int32_t base = 0; base < n4; base += kRowThreads * kRowUnroll) {
+      float4 v[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int32_t i = base + u * kRowThreads + (int32_t)threadIdx.x;
+        v[u] = i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int32_t i = base + u * kRowThreads + (int32_t)threadIdx.x;
+        if (i < n4) {
+          f(v[u].x, 4 * i);
+          f(v[u].y, 4 * i + 1);
+          f(v[u].z, 4 * i + 2);
+          f(v[u].w, 4 * i + 3);
+        }
+      }
+    }
+    done = n4 << 2;
+  }
+  for (int32_t base = done; base < n; base += kRowThreads * kRowUnroll) {
+    float v[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int32_t p = base + u * kRowThreads + (int32_t)threadIdx.x;
+      v[u] = p < n ? sr[p] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int32_t p = base + u * kRowThreads + (int32_t)threadIdx.x;
+      if (p < n) f(v[u], p);
+    }
+  }
+}
+
+// The float whose order key (score_key) is k.
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Digit holding the need-th largest member of a histogram of PER * 1024 bins
 // ordered by digit value.  Returns the digit, the number of members in higher
 // digits and the count of the digit itself (all block-uniform).
@@ -471,7 +537,7 @@ __device__ void row_find_digit(const uint32_t* h, uint32_t need, uint32_t* scan,
   __syncthreads();
 }
 
-template <bool kHasHist>
+template <bool kHasHist, bool kPre>
 __global__ __launch_bounds__(kRowThreads)
 void k_topk_row(const float* __restrict__ scores, int32_t N,
                 const int32_t* __restrict__ n_valid, int32_t n_all, int32_t K,
@@ -485,7 +551,49 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   const int32_t* mrow = cand_map ? cand_map + (size_t)row * N : nullptr;
   int32_t* orow = out + (size_t)row * K;
 
+  // kPre (rows of at most kPreF4 * 4 * kRowThreads positions, a multiple of
+  // 4, 16-byte aligned): the row's loads are issued here, before the
+  // histogram is read, and consumed by the collection pass.
+  float4 pre[kPre ? kPreF4 : 1];
+  if (kPre && n > K) {
+    const float4* s4 = reinterpret_cast<const float4*>(sr);
+#pragma unroll
+    for (int u = 0; u < kPreF4; ++u) {
+      const int32_t i = u * kRowThreads + tid;
+      pre[u] = 4 * i < n ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
   auto visit = [&](auto&& f) { stream_row(sr, n, f); };
+  // visit_pre on the float values (the order key is computed by the caller).
+  auto visit_pre_f = [&](auto&& f) {
+    if (kPre) {
+#pragma unroll
+      for (int u = 0; u < kPreF4; ++u) {
+        const int32_t i = u * kRowThreads + tid;
+        if (4 * i + 0 < n) f(pre[u].x, 4 * i + 0);
+        if (4 * i + 1 < n) f(pre[u].y, 4 * i + 1);
+        if (4 * i + 2 < n) f(pre[u].z, 4 * i + 2);
+        if (4 * i + 3 < n) f(pre[u].w, 4 * i + 3);
+      }
+    } else {
+      stream_row_f(sr, n, f);
+    }
+  };
+
+  auto visit_pre = [&](auto&& f) {
+    if (kPre) {
+#pragma unroll
+      for (int u = 0; u < kPreF4; ++u) {
+        const int32_t i = u * kRowThreads + tid;
+        if (4 * i + 0 < n) f(score_key(pre[u].x), 4 * i + 0);
+        if (4 * i + 1 < n) f(score_key(pre[u].y), 4 * i + 1);
+        if (4 * i + 2 < n) f(score_key(pre[u].z), 4 * i + 2);
+        if (4 * i + 3 < n) f(score_key(pre[u].w), 4 * i + 3);
+      }
+    } else {
+      stream_row(sr, n, f);
+    }
+  };
 
   // 1. Top-digit histogram: bits 61..50 of the composite = the top 12 key bits.
   if (kHasHist) {
@@ -502,7 +610,7 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   if (!kHasHist) {
     for (int i = tid; i < kHistBins; i += kRowThreads) L.hist[i] = 0u;
     __syncthreads();
-    visit([&](uint32_t key, int32_t) {
+    visit_pre([&](uint32_t key, int32_t) {
       atomicAdd(&L.hist[key >> (32 - kHistBits)], 1u);
     });
   }
@@ -548,7 +656,7 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   }
 
   // 3. Mark everything above the prefix; copy the prefix's members to LDS.
-  for (int i = tid; i < kRowWords; i += kRowThreads) L.bitmap[i] = 0u;
+  for (int i = tid; i < ((n + 31) >> 5); i += kRowThreads) L.bitmap[i] = 0u;
   if (tid == 0) L.ccount = 0u;
   __syncthreads();
   {
@@ -566,14 +674,25 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
       }
     };
     if (sh >= 30) {
+      // The prefix lies in the score bits: with lo / hi the floats whose
+      // order keys are prefix << ks and (prefix + 1) << ks, a score is above
+      // the prefix iff s >= hi and inside it iff lo <= s < hi (order keys
+      // are monotone in the real value), so most elements cost two compares.
       const int ks = sh - 30;
       const uint32_t pre = (uint32_t)prefix;
-      visit([&](uint32_t key, int32_t p) {
-        const uint32_t hi = key >> ks;
-        if (hi >= pre) hit(key, p, hi > pre, hi == pre);
+      const uint32_t klo = pre << ks;
+      const bool top = (ks == 0) ? (pre == 0xFFFFFFFFu) : ((pre + 1u) >> (32 - ks)) != 0u;
+      const uint32_t khi = top ? 0xFFFFFFFFu : (pre + 1u) << ks;
+      const float flo = key_float(klo);
+      const float fhi = key_float(khi);
+      visit_pre_f([&](float s, int32_t p) {
+        if (s >= flo) {
+          const bool above = !top && s >= fhi;
+          hit(score_key(s), p, above, !above);
+        }
       });
     } else {
-      visit([&](uint32_t key, int32_t p) {
+      visit_pre([&](uint32_t key, int32_t p) {
         const uint64_t hi = composite(key, p, nm1) >> sh;
         if (hi >= prefix) hit(key, p, hi > prefix, hi == prefix);
       });
@@ -608,26 +727,64 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
     __syncthreads();
   }
 
-  // 5. Ascending output through the bitmap.
-  constexpr int WPT = kRowWords / kRowThreads;   // 8 words per thread
+  // 5. Ascending output through the bitmap.  The loop that writes positions
+  //    holds no loads (a load feeding a store in the same loop makes every
+  //    store wait for all earlier memory operations).  Up to 2 * kRowCap
+  //    positions go to LDS first and are written (mapped) with coalesced
+  //    stores afterwards.
+  // The ceil(n / 32) bitmap words in use are spread evenly over the threads
+  // (one word each for rows up to 32768), so that the per-bit loops below
+  // run on every wave instead of a few.
+  constexpr int WPT = kRowWords / kRowThreads;   // at most 8 words per thread
+  const int nwords = (n + 31) >> 5;
+  const int wpt = (nwords + kRowThreads - 1) / kRowThreads;
   uint32_t wv[WPT];
   uint32_t c = 0;
 #pragma unroll
   for (int w = 0; w < WPT; ++w) {
-    wv[w] = L.bitmap[tid * WPT + w];
+    const int wi = tid * wpt + w;
+    wv[w] = (w < wpt && wi < nwords) ? L.bitmap[wi] : 0u;
     c += __popc(wv[w]);
   }
   uint32_t tot;
-  uint32_t pos = block_excl_scan<kRowThreads>(c, L.scan, &tot);
+  const uint32_t pos0 = block_excl_scan<kRowThreads>(c, L.scan, &tot);
+  int32_t* opos = reinterpret_cast<int32_t*>(L.ckey);   // ckey and cpos: 2 * kRowCap ints
+  const bool staged = K <= 2 * kRowCap;
+  uint32_t pos = pos0;
 #pragma unroll
   for (int w = 0; w < WPT; ++w) {
     uint32_t m = wv[w];
     while (m) {
       const int bit = __ffs(m) - 1;
       m &= m - 1;
-      const int32_t p = (tid * WPT + w) * 32 + bit;
-      if (pos < (uint32_t)K) orow[pos] = mrow ? mrow[p] : p;
+      const int32_t p = (tid * wpt + w) * 32 + bit;
+      if (pos < (uint32_t)K) {
+        if (staged) opos[pos] = p;
+        else if (!mrow) orow[pos] = p;
+      }
       ++pos;
+    }
+  }
+  if (staged) {   // coalesced stores (scattered 4-byte stores issue slowly)
+    __syncthreads();
+    if (mrow)
+      for (uint32_t i = tid; i < (uint32_t)K; i += kRowThreads) orow[i] = i < tot ? mrow[opos[i]] : -1;
+    else
+      for (uint32_t i = tid; i < (uint32_t)K; i += kRowThreads) orow[i] = i < tot ? opos[i] : -1;
+    return;
+  }
+  if (mrow) {   // K > 2 * kRowCap with a map: direct mapped stores
+    pos = pos0;
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) {
+      uint32_t m = wv[w];
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        const int32_t p = (tid * wpt + w) * 32 + bit;
+        if (pos < (uint32_t)K) orow[pos] = mrow[p];
+        ++pos;
+      }
     }
   }
   for (uint32_t i = tot + tid; i < (uint32_t)K; i += kRowThreads) orow[i] = -1;
@@ -669,11 +826,19 @@ hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
                             int32_t* out, hipStream_t s) {
   if (N > kRowMaxN) return hipErrorInvalidValue;
   const dim3 grid((unsigned)R), block(kRowThreads);
-  if (hist)
-    k_topk_row<true><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, hist,
-                                            zero_hist ? 1 : 0, cand, out);
-  else
-    k_topk_row<false><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, nullptr, 0, cand, out);
+  const bool pre = (N & 3) == 0 && N <= kPreF4 * 4 * kRowThreads && ((uintptr_t)scores & 15u) == 0;
+  const int zh = zero_hist ? 1 : 0;
+  if (hist) {
+    if (pre)
+      k_topk_row<true, true><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, hist, zh, cand, out);
+    else
+      k_topk_row<true, false><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, hist, zh, cand, out);
+  } else {
+    if (pre)
+      k_topk_row<false, true><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, nullptr, 0, cand, out);
+    else
+      k_topk_row<false, false><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, nullptr, 0, cand, out);
+  }
   return hipGetLastError();
 }
 

@@ -167,7 +167,7 @@ def test_decode_is_deterministic():
             assert np.array_equal(a[k], b[k])
 
 
-@pytest.mark.parametrize("ci,seqs", [(1, (0, 17, 31)), (2, (0, 5))])
+@pytest.mark.parametrize("ci,seqs", [(1, (0, 17, 31)), (2, (0, 5)), (3, (0, 63))])
 def test_decode_full_size_sampled(ci, seqs):
     cfg = CONFIGS[ci]
     say("case: full config", ci, cfg.name, "sampled sequences", seqs)
