@@ -123,7 +123,12 @@ typedef struct csa2_layer {
  *           entry cand[b][p] (-inf for -1).
  *   scores  [B][Q][N] float output
  *   hist    NULL, or [B*Q][4096] uint32 histogram that the call ADDS the
- *           score keys' top 12 bits to (see csa2_topk); caller zeroes it. */
+ *           score keys' top 12 bits to (see csa2_topk); caller zeroes it.
+ *           Must be NULL when Q > 1 and cand is NULL (CSA2_ERR_SHAPE).
+ * With Q > 1 and no candidate list (a chunked-prefill step) the scores are
+ * computed as a matrix-core contraction of the Q queries against 128-entry
+ * tiles (E4M3 widened exactly to bf16, fp32 accumulation); the result meets
+ * the same fp32 bound as the Q == 1 path. */
 csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx,
                              const float* w_idx, int32_t Q, int64_t pos0,
                              int32_t ratio, const int32_t* cand, int32_t P,
@@ -153,7 +158,10 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N,
  * and lse[h] = log sum exp(z).  No selected entry gives o = 0, lse = -inf.
  *   q    [B][Q][H][D] bf16;  idx [B][Q][K] int32 in [-1, M)
  *   o    [B][Q][H][D] float;  lse [B][Q][H] float
- *   ws   at least csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, Q, M, K, 0, 0, H) */
+ *   ws   at least csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, Q, M, K, 0, 0, H)
+ * With Q > 1 (chunked prefill) each query token is one work-group on the
+ * matrix cores (bf16 products, fp32 accumulation, P split into two bf16
+ * halves) and the workspace is not used beyond 256 bytes. */
 csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q,
                              int32_t Q, int32_t H, const int32_t* idx,
                              int32_t K, float* o, float* lse, void* ws,
