@@ -8,23 +8,27 @@
 // are the same 512-wide latent row (shared K/V); all 16 heads share each
 // gathered row, so each row is read from HBM once per query row.
 //
-// k_attn_partial: one work-group per (query row, split).  A row's keys are cut
-// into chunks of 32 (the selected global entries first, then the window rows)
-// and a split is a run of consecutive chunks, processed with an online
-// softmax.  Per work-group:
-//   prologue  q (16 x 512 bf16) and the split's entry numbers go to LDS, the
-//             first chunk's codes are loaded into registers;
-//   per chunk 1. dequantise the registers into an LDS tile of bf16 rows: FP4
-//                with gfx950's scaled FP4->bf16 convert (exact: an E2M1 value
-//                times a power of two has at most two significant bits), FP8
-//                with the FP8->f32 convert truncated to bf16 (exact for E4M3);
-//             2. issue the next chunk's loads, so that they are in flight
-//                while this chunk is computed;
-//             3. logits with v_dot2_f32_bf16 (the bf16 products are exact in
-//                fp32): each wave takes a quarter of the 512 dims and the
-//                quarters are summed in a fixed order;
-//             4. running max / sum per head (fp32), rescale factor, exp;
-//             5. P x V in fp32 FMA (p is never rounded to bf16).
+// k_attn_partial: one work-group of 8 waves per (query row, split).  A row's
+// keys are cut into chunks of 32 (the selected global entries first, then the
+// window rows) and a split is a run of consecutive chunks.  Wave w takes the
+// 4 heads 4(w%4).. and key stream w/4: keys 16(w/4)..16(w/4)+15 of every
+// chunk, with its own online-softmax state; the two streams are merged at the
+// end.  Per chunk (double-buffered, one barrier per chunk):
+//   stage   the chunk's codes (loaded one chunk ahead into registers) are
+//           restored to bf16 - FP4 with gfx950's scaled FP4->bf16 convert,
+//           FP8 with the FP8->bf16 convert, both exact - and written to LDS
+//           twice: as rows of dim pairs (for q . c) and as key pairs per dim
+//           (for P x V);
+//   logits  q sits in registers (each lane: 4 heads x 32 dims); a lane forms
+//           4 heads x 4 keys over its 32 dims with v_dot2_f32_bf16 (exact
+//           bf16 products, fp32 sums), and the 16 lanes of a row sum their
+//           parts with 15 DPP adds: heads and keys are laid out in a
+//           lane-rotated order so that every step adds the same registers;
+//   softmax per head over the stream's 16 keys (fp32): running max, rescale
+//           factor, p = exp(z - max), running sum;
+//   P x V   each lane owns 8 dims of the 4 heads; p is split into bf16 hi +
+//           lo parts (p - hi - lo is below 2^-16 p) and every v_dot2 adds two
+//           keys of one dim, so the key pairs are used as staged.
 // With one split per row the work-group normalises and writes o and lse;
 // otherwise it writes (unnormalised o, max, sum) partials and k_attn_combine
 // merges them (and optionally an incoming (o, lse)) by log-sum-exp weights in
@@ -36,328 +40,354 @@
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int KS = kKeysPerSplit;            // 32 keys per chunk
-constexpr int kCsStrideU = kD / 2 + 4;       // staged key row stride in u32: 16 rows hit 16 bank groups
-constexpr int kQU = kD / 2 + 4;              // q row stride in u32 (padded like the key rows)
-constexpr int kZS = KS + 4;                  // logit row stride (4 heads of a wave in 4 bank groups)
-constexpr int kMaxChunksPerSplit = 32;       // entry numbers staged per work-group: 1024
-constexpr int kGroupsPerRound = 256;         // work-groups that run at once, one per compute unit
+constexpr int kThreads = 512;                   // 8 waves: 4 head groups x 2 key streams
+constexpr int KS = kKeysPerSplit;               // 32 keys per chunk, 16 per stream
+constexpr int kRowU = kD / 2;                   // staged key row: 256 u32 of dim pairs
+constexpr int kPairU = kD + 4;                  // staged key pair: 512 u32 (+ pad) of key pairs
+constexpr int kRowBufU = KS * kRowU;            // 32 KiB
+constexpr int kPairBufU = (KS / 2) * kPairU;    // 32.25 KiB
+constexpr int kMaxChunksPerSplit = 32;          // entry numbers staged per work-group: 1024
+constexpr int kGroupsPerRound = 256;            // work-groups that run at once, one per compute unit
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
+__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+
+// Value of x in the lane named by the DPP control word (within a row of 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppXor7 = 0x141;       // row_half_mirror
+constexpr int kDppXor15 = 0x140;      // row_mirror
+constexpr int kDppRor4 = 0x124;       // row_ror:4 (lane i reads lane i - 4 of its row)
+constexpr int kDppRor8 = 0x128;       // row_ror:8
+constexpr int kDppRor12 = 0x12C;      // row_ror:12 (lane i reads lane i + 4 of its row)
+
+// bf16 with round-to-nearest-even of a finite non-negative float, in the low 16 bits
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Staging unit of a thread: key pair kp (keys 2kp, 2kp+1 of the chunk) and a
+// 16-dim segment seg.  The bit assignment keeps both LDS layouts' stores to
+// at most two lanes per bank group.
+__device__ __forceinline__ int unit_kp(int tid) { return (tid & 1) | ((tid >> 2) & 0xE); }
+__device__ __forceinline__ int unit_seg(int tid) { return ((tid >> 1) & 3) | ((tid >> 4) & 0x1C); }
+
 struct ChunkRegs {
-  u32x4 v[4];       // global: 2 x 16 code bytes; window: 4 x 16 E4M3 bytes
+  u32x4 v[2];       // per key: 16 bytes (global: 32 E2M1 codes, half of them used; window: 16 E4M3)
   uint32_t sc[2];   // global: E8M0 scale codes
-  int32_t e[2];     // global: entry numbers (-1: none)
-  bool ok[4];       // window: row present
+  bool ok[2];       // key present
 };
 
+// One 16-byte load per key from a selected address, with no branch: an
+// absent key reads entry 0 or row 0 of the sequence and is masked by ok, so
+// that no register merge has to wait for the loads.  Every address read is
+// inside the inputs.
 __device__ __forceinline__ void load_chunk(const AttnArgs& a, int chunk, int Cg, int b, int t,
                                            const int32_t* idx_s, int key0, ChunkRegs& r) {
   const int tid = threadIdx.x;
-  if (chunk < Cg) {
+  const int kp = unit_kp(tid);
+  const int seg = unit_seg(tid);
+  const bool glob = chunk < Cg;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int pr = tid + i * kThreads;        // (key j, 32-element block) pair
-      const int j = pr >> 4;
-      const int blk = pr & 15;
-      const int kpos = chunk * KS + j;
-      const int32_t e = kpos < a.K ? idx_s[kpos - key0] : -1;
-      r.e[i] = e;
-      if (e >= 0) {
-        const size_t er = (size_t)b * (size_t)a.M + (size_t)e;
-        r.v[i] = *reinterpret_cast<const u32x4*>(a.latent + er * kLatRow + blk * 16);
-        r.sc[i] = a.scale[er * kScaleRow + blk];
-      }
-    }
-  } else {
-    const int wc = chunk - Cg;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pr = tid + i * kThreads;        // (row j, 16-byte segment) pair
-      const int j = pr >> 5;
-      const int seg = pr & 31;
-      const int wr = wc * KS + j;
-      r.ok[i] = wr < a.W;
-      if (r.ok[i]) {
-        const uint8_t* src = a.swa + ((size_t)b * a.swa_rows + t + wr) * kD + seg * 16;
-        r.v[i] = *reinterpret_cast<const u32x4*>(src);
-      }
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int kpos = chunk * KS + 2 * kp + i;                 // global key position
+    const int wr = (chunk - Cg) * KS + 2 * kp + i;            // window row
+    const int32_t e = idx_s[(kpos - key0) & (kMaxChunksPerSplit * KS - 1)];
+    const bool ok = glob ? (kpos < a.K && e >= 0) : (wr < a.W);
+    r.ok[i] = ok;
+    const size_t er = (size_t)b * (size_t)a.M + (size_t)(glob && ok ? e : 0);
+    const uint8_t* gsrc = a.latent + er * kLatRow + (seg >> 1) * 16;
+    const uint8_t* wsrc = a.swa + ((size_t)b * a.swa_rows + t + (!glob && ok ? wr : 0)) * kD + seg * 16;
+    r.v[i] = *reinterpret_cast<const u32x4*>(glob ? gsrc : wsrc);
+    // window chunks read a byte of q instead (the pool may be absent)
+    const uint8_t* sp = glob ? a.scale + er * kScaleRow + (seg >> 1) : reinterpret_cast<const uint8_t*>(a.q);
+    r.sc[i] = *sp;
   }
 }
 
-__device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& r, uint32_t* cs,
-                                            int* valid_s) {
+__device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& r, uint32_t* rowb,
+                                            uint32_t* pairb, int32_t* valid_s) {
   const int tid = threadIdx.x;
-  if (chunk < Cg) {
+  const int kp = unit_kp(tid);
+  const int seg = unit_seg(tid);
+  uint32_t w[2][8];   // per key: 16 bf16 of dims seg*16 .. seg*16+15 as 8 dim pairs
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int pr = tid + i * kThreads;
-      const int j = pr >> 4;
-      const int blk = pr & 15;
-      u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = o0, o2 = o0, o3 = o0;
-      if (r.e[i] >= 0) {
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) w[i][m] = 0u;
+    if (r.ok[i]) {
+      if (chunk < Cg) {
         const uint32_t sc = r.sc[i];
         const float scale = __uint_as_float(sc ? (sc << 23) : 0x00400000u);   // 2^(sc-127)
-        uint32_t w[16];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t x = (seg & 1) ? (d ? r.v[i][3] : r.v[i][2]) : (d ? r.v[i][1] : r.v[i][0]);
+          w[i][4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 0));
+          w[i][4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 1));
+          w[i][4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 2));
+          w[i][4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 3));
+        }
+      } else {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          w[4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.v[i][d], scale, 0));
-          w[4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.v[i][d], scale, 1));
-          w[4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.v[i][d], scale, 2));
-          w[4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.v[i][d], scale, 3));
+          w[i][2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, false));
+          w[i][2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, true));
         }
-        o0 = u32x4{w[0], w[1], w[2], w[3]};
-        o1 = u32x4{w[4], w[5], w[6], w[7]};
-        o2 = u32x4{w[8], w[9], w[10], w[11]};
-        o3 = u32x4{w[12], w[13], w[14], w[15]};
       }
-      // The 16 lanes of a key write its 1 KiB row; lane blk writes its four
-      // 16-byte pieces in the order rotated by blk/4, so that each store
-      // instruction covers 16 distinct bank groups.
-      u32x4* dst = reinterpret_cast<u32x4*>(cs + j * kCsStrideU + blk * 16);
-      const int rot = blk >> 2;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c = (q4 + rot) & 3;
-        const u32x4 x = c == 0 ? o0 : (c == 1 ? o1 : (c == 2 ? o2 : o3));
-        dst[c] = x;
-      }
-      if (blk == 0) valid_s[j] = r.e[i] >= 0;
     }
-  } else {
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pr = tid + i * kThreads;
-      const int j = pr >> 5;
-      const int seg = pr & 31;
-      u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = o0;
-      if (r.ok[i]) {
-        uint32_t w[8];
+  for (int i = 0; i < 2; ++i) {
+    uint32_t* dst = rowb + (2 * kp + i) * kRowU + seg * 8;
+    *reinterpret_cast<u32x4*>(dst) = u32x4{w[i][0], w[i][1], w[i][2], w[i][3]};
+    *reinterpret_cast<u32x4*>(dst + 4) = u32x4{w[i][4], w[i][5], w[i][6], w[i][7]};
+  }
+  uint32_t pr[16];    // dim seg*16 + j: (key 2kp, key 2kp+1)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[i][d], false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[i][d], true);
-          w[2 * d + 0] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
-          w[2 * d + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
-        }
-        o0 = u32x4{w[0], w[1], w[2], w[3]};
-        o1 = u32x4{w[4], w[5], w[6], w[7]};
-      }
-      // lanes seg and seg + 8 store their two pieces in opposite order
-      u32x4* dst = reinterpret_cast<u32x4*>(cs + j * kCsStrideU + seg * 8);
-      const int rot = (seg >> 3) & 1;
-      dst[rot] = rot ? o1 : o0;
-      dst[rot ^ 1] = rot ? o0 : o1;
-      if (seg == 0) valid_s[j] = r.ok[i];
-    }
+  for (int m = 0; m < 8; ++m) {
+    pr[2 * m] = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u);
+    pr[2 * m + 1] = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u);
+  }
+  uint32_t* pd = pairb + kp * kPairU + seg * 16;
+#pragma unroll
+  for (int p4 = 0; p4 < 4; ++p4)
+    *reinterpret_cast<u32x4*>(pd + 4 * p4) = u32x4{pr[4 * p4], pr[4 * p4 + 1], pr[4 * p4 + 2], pr[4 * p4 + 3]};
+  if (seg == 0) {
+    valid_s[2 * kp] = r.ok[0];
+    valid_s[2 * kp + 1] = r.ok[1];
   }
 }
 
-// G heads per work-group (16 or 8): grid (splits, rows, 16 / G).
-template <int G>
-__global__ __launch_bounds__(kThreads, 2)
+// grid (splits, rows), kThreads
+__global__ __launch_bounds__(kThreads, 1)
 void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t final_out) {
-  static_assert(G == 16 || G == 8, "heads per work-group");
-  constexpr int NHG = G / 4;               // groups of 4 heads
-  constexpr int KG = 64 / NHG;             // logits: key lanes per head group
-  constexpr int NK = 32 / KG;              // logits: keys per lane
-  constexpr int SPH = kThreads / G;        // softmax: threads per head
-  constexpr int SK = KS / SPH;             // softmax: keys per thread
-  constexpr int DP = 4 / NHG;              // P x V: dim parts
-  constexpr int LD = kD / DP / 64;         // P x V: dims per lane
-  __shared__ __attribute__((aligned(16))) uint32_t qs[G * kQU];
-  __shared__ __attribute__((aligned(16))) uint32_t cs[KS * kCsStrideU];   // 33 KiB
-  __shared__ __attribute__((aligned(16))) float zp[4][G][kZS];
-  __shared__ __attribute__((aligned(16))) float ps[KS][G];
-  __shared__ int32_t idx_s[kMaxChunksPerSplit * KS];                      // 4 KiB
-  __shared__ int valid_s[KS];
-  __shared__ float mh[G], lh[G];
-  __shared__ __attribute__((aligned(16))) float ah[G];
+  __shared__ __attribute__((aligned(16))) uint32_t rowb[2][kRowBufU];
+  __shared__ __attribute__((aligned(16))) uint32_t pairb[2][kPairBufU];
+  __shared__ __attribute__((aligned(16))) uint32_t ps[8][8][8];   // [wave][key pair][head: hi, lo]
+  __shared__ int32_t idx_s[kMaxChunksPerSplit * KS];
+  __shared__ int32_t valid_s[2][KS];
+  __shared__ float mls[4][4][2];
 
   const int row = blockIdx.y;
   const int split = blockIdx.x;
   const int S = gridDim.x;
-  const int hb = blockIdx.z * G;           // first head of this work-group
   const int b = row / a.Q;
   const int t = row - b * a.Q;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int hg = wave & 3;                 // heads 4hg .. 4hg+3
+  const int st = wave >> 2;                // key stream
   const int c0 = split * cps;
   const int c1 = (c0 + cps < C) ? c0 + cps : C;
 
-  {  // q of the G heads -> LDS
-    const u32x4* qg = reinterpret_cast<const u32x4*>(a.q + ((size_t)row * kH + hb) * kD);
-    for (int i = tid; i < G * kD / 8; i += kThreads)   // 64 16-byte pieces per head row
-      *reinterpret_cast<u32x4*>(qs + (i >> 6) * kQU + (i & 63) * 4) = qg[i];
-  }
   // entry numbers of this split's global keys -> LDS
   const int key0 = c0 * KS;
   const int gend = (c1 < Cg ? c1 : Cg) * KS;
   const int key1 = gend < a.K ? gend : a.K;
   for (int k = key0 + tid; k < key1; k += kThreads) idx_s[k - key0] = a.idx[(size_t)row * a.K + k];
-  if (tid < G) {
-    mh[tid] = -INFINITY;
-    lh[tid] = 0.f;
+
+  // logits lane: key group kb (4 keys), dim part dp (dims 8dp + 128j .. +7, j < 4).
+  // Head slot s holds head 4hg + (s ^ hx) and key slot s key 4kb + (s ^ kx).
+  const int kb = lane >> 4;
+  const int dp = lane & 15;
+  const int hx = dp & 3;
+  const int kx = (dp >> 2) & 3;
+  u32x4 qr[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint16_t* qh = a.q + ((size_t)row * kH + 4 * hg + (s ^ hx)) * kD + 8 * dp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qr[s][j] = *reinterpret_cast<const u32x4*>(qh + 128 * j);
   }
   __syncthreads();
 
   ChunkRegs r;
   load_chunk(a, c0, Cg, b, t, idx_s, key0, r);
+  stage_chunk(c0, Cg, r, rowb[0], pairb[0], valid_s[0]);
+  load_chunk(a, c0 + 1 < c1 ? c0 + 1 : c0, Cg, b, t, idx_s, key0, r);
+  __syncthreads();
 
-  // P x V accumulators: wave = (4 heads, 1/DP of the dims), lane = LD dims
-  const int h0 = 4 * (wave % NHG);
-  const int d0 = (wave / NHG) * (kD / DP) + lane * LD;
-  float acc[4][LD];
+  float acc[4][8];                         // P x V: heads 4hg.. x dims 4l..4l+3, 256+4l..
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int i = 0; i < LD; ++i) acc[h][i] = 0.f;
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+  float m_run = -INFINITY;                 // softmax state of head 4hg + hx in this stream
+  float l_run = 0.f;
 
   for (int c = c0; c < c1; ++c) {
-    stage_chunk(c, Cg, r, cs, valid_s);
-    __syncthreads();
-    if (c + 1 < c1) load_chunk(a, c + 1, Cg, b, t, idx_s, key0, r);
+    const int cur = (c - c0) & 1;
+    if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1]);
+    load_chunk(a, c + 2 < c1 ? c + 2 : c1 - 1, Cg, b, t, idx_s, key0, r);   // past the end: a harmless reload
 
-    {  // logits: wave = quarter of the dims; lane = 4 heads x NK keys
-      const int hg = lane / KG;
-      const int kg = lane % KG;
-      const int u0 = wave * (kD / 8);          // first u32 of this wave's 128 dims
-      float z[4][NK];
+    float zs;
+    {  // logits of 4 heads x 4 keys over 32 dims, then summed over the row's 16 lanes
+      const uint32_t* rb = rowb[cur] + (16 * st + 4 * kb) * kRowU + 4 * dp;
+      float z[4][4];
 #pragma unroll
       for (int h = 0; h < 4; ++h)
 #pragma unroll
-        for (int k = 0; k < NK; ++k) z[h][k] = 0.f;
-#pragma unroll 4
-      for (int du = 0; du < kD / 8; du += 4) {
-        u32x4 qv[4], cv[NK];
+        for (int k = 0; k < 4; ++k) z[h][k] = 0.f;
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-          qv[h] = *reinterpret_cast<const u32x4*>(qs + (4 * hg + h) * kQU + u0 + du);
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t* kr = rb + (k ^ kx) * kRowU;
 #pragma unroll
-        for (int k = 0; k < NK; ++k)
-          cv[k] = *reinterpret_cast<const u32x4*>(cs + (kg + KG * k) * kCsStrideU + u0 + du);
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 cv = *reinterpret_cast<const u32x4*>(kr + 64 * j);
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
+          for (int h = 0; h < 4; ++h)
 #pragma unroll
-          for (int k = 0; k < NK; ++k)
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-              z[h][k] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[h][w]), as_bf16x2(cv[k][w]),
-                                                        z[h][k], false);
+            for (int w = 0; w < 4; ++w) z[h][k] = fdot2(qr[h][j][w], cv[w], z[h][k]);
+        }
       }
+      // The partner in each step flips the lane bits that select the slot
+      // order, so the element in my slot (h, k) sits in its slot (h ^ x, k ^ y).
 #pragma unroll
       for (int h = 0; h < 4; ++h)
 #pragma unroll
-        for (int k = 0; k < NK; ++k) zp[wave][4 * hg + h][kg + KG * k] = z[h][k];
+        for (int k = 0; k < 2; ++k) z[h][k] += dpp<kDppXor15>(z[h ^ 3][k ^ 3]);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) z[h][0] += dpp<kDppXor7>(z[h ^ 3][1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) z[h][0] += dpp<kDppXor2>(z[h ^ 2][0]);
+      z[0][0] += dpp<kDppXor1>(z[1][0]);
+      zs = z[0][0];                        // head 4hg + hx, key 4kb + kx of the stream
     }
-    __syncthreads();
 
-    {  // online softmax statistics: thread = (head, SK keys)
-      const int h = tid / SPH;
-      const int j0 = tid % SPH;
-      float z[SK];
-#pragma unroll
-      for (int k = 0; k < SK; ++k) {
-        const int j = j0 + SPH * k;
-        const float s = ((zp[0][h][j] + zp[1][h][j]) + zp[2][h][j]) + zp[3][h][j];
-        z[k] = valid_s[j] ? s : -INFINITY;
-      }
-      float m = z[0];
-#pragma unroll
-      for (int k = 1; k < SK; ++k) m = fmaxf(m, z[k]);
-#pragma unroll
-      for (int o = 1; o < SPH; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      const float m_old = mh[h];
-      const float m_new = fmaxf(m_old, m);
-      float p[SK];
-      float alpha = 1.f;
-#pragma unroll
-      for (int k = 0; k < SK; ++k) p[k] = 0.f;
+    float alpha;
+    {  // online softmax of head 4hg + hx over the stream's 16 keys
+      const int kk = 4 * kb + kx;
+      const float zv = valid_s[cur][16 * st + kk] ? zs : -INFINITY;
+      float mc = fmaxf(zv, dpp<kDppRor4>(zv));
+      mc = fmaxf(mc, dpp<kDppRor8>(mc));
+      mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
+      mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+      const float m_new = fmaxf(m_run, mc);
+      float p = 0.f;
+      alpha = 1.f;
       if (m_new != -INFINITY) {
-#pragma unroll
-        for (int k = 0; k < SK; ++k) p[k] = __expf(z[k] - m_new);
-        alpha = __expf(m_old - m_new);
+        p = __expf(zv - m_new);
+        alpha = __expf(m_run - m_new);
       }
-      float l = p[0];
-#pragma unroll
-      for (int k = 1; k < SK; ++k) l += p[k];
-#pragma unroll
-      for (int o = 1; o < SPH; o <<= 1) l += __shfl_xor(l, o, 64);
-#pragma unroll
-      for (int k = 0; k < SK; ++k) ps[j0 + SPH * k][h] = p[k];
-      if (j0 == 0) {
-        mh[h] = m_new;
-        lh[h] = lh[h] * alpha + l;
-        ah[h] = alpha;
+      float ls = p + dpp<kDppRor4>(p);
+      ls += dpp<kDppRor8>(ls);
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+      // key pairs (kk, kk + 1) for kk even: the odd key is in lane dp + 4
+      const float po = dpp<kDppRor12>(p);
+      if (!(dp & 4)) {
+        const uint32_t h0 = bf16_rne(p), h1 = bf16_rne(po);
+        const uint32_t l0 = bf16_rne(p - __uint_as_float(h0 << 16));
+        const uint32_t l1 = bf16_rne(po - __uint_as_float(h1 << 16));
+        *reinterpret_cast<uint2*>(&ps[wave][kk >> 1][2 * hx]) = make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __syncthreads();
 
     {  // P x V
-      const float4 al = *reinterpret_cast<const float4*>(&ah[h0]);
-      const float alv[4] = {al.x, al.y, al.z, al.w};
+      float al[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int i = 0; i < LD; ++i) acc[h][i] *= alv[h];
-#pragma unroll 4
-      for (int j = 0; j < KS; ++j) {
-        const float4 p = *reinterpret_cast<const float4*>(&ps[j][h0]);
-        uint32_t cw[LD / 2];
-        if constexpr (LD == 8) {
-          const u32x4 cv = *reinterpret_cast<const u32x4*>(cs + j * kCsStrideU + d0 / 2);
-          cw[0] = cv[0]; cw[1] = cv[1]; cw[2] = cv[2]; cw[3] = cv[3];
-        } else {
-          const uint2 cv = *reinterpret_cast<const uint2*>(cs + j * kCsStrideU + d0 / 2);
-          cw[0] = cv.x; cw[1] = cv.y;
-        }
-        float cf[LD];
-#pragma unroll
-        for (int w = 0; w < LD / 2; ++w) {
-          cf[2 * w + 0] = __uint_as_float(cw[w] << 16);
-          cf[2 * w + 1] = __uint_as_float(cw[w] & 0xFFFF0000u);
-        }
-        const float pv[4] = {p.x, p.y, p.z, p.w};
+      for (int h = 0; h < 4; ++h) al[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+      if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
-          for (int i = 0; i < LD; ++i) acc[h][i] = fmaf(pv[h], cf[i], acc[h][i]);
+          for (int i = 0; i < 8; ++i) acc[h][i] *= al[h];
+      }
+      const uint32_t* pb = pairb[cur] + (8 * st) * kPairU + 4 * lane;
+#pragma unroll 2
+      for (int kp = 0; kp < 8; ++kp) {
+        const u32x4 pv0 = *reinterpret_cast<const u32x4*>(&ps[wave][kp][0]);
+        const u32x4 pv1 = *reinterpret_cast<const u32x4*>(&ps[wave][kp][4]);
+        const u32x4 ca = *reinterpret_cast<const u32x4*>(pb + kp * kPairU);
+        const u32x4 cb = *reinterpret_cast<const u32x4*>(pb + kp * kPairU + 256);
+        const uint32_t ph[4] = {pv0[0], pv0[2], pv1[0], pv1[2]};
+        const uint32_t pl[4] = {pv0[1], pv0[3], pv1[1], pv1[3]};
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[h][i] = fdot2(pl[h], ca[i], acc[h][i]);
+            acc[h][i] = fdot2(ph[h], ca[i], acc[h][i]);
+            acc[h][4 + i] = fdot2(pl[h], cb[i], acc[h][4 + i]);
+            acc[h][4 + i] = fdot2(ph[h], cb[i], acc[h][4 + i]);
+          }
       }
     }
     __syncthreads();
   }
 
-  if (final_out && S == 1) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float L = lh[h0 + h];
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      float* dst = a.o + ((size_t)row * kH + hb + h0 + h) * kD + d0;
-#pragma unroll
-      for (int i = 0; i < LD; i += 4)
-        *reinterpret_cast<float4*>(dst + i) =
-            make_float4(acc[h][i] * inv, acc[h][i + 1] * inv, acc[h][i + 2] * inv, acc[h][i + 3] * inv);
-    }
-    if (tid < G) {
-      const float L = lh[tid];
-      a.lse[(size_t)row * kH + hb + tid] = L > 0.f ? mh[tid] + logf(L) : -INFINITY;
-    }
-  } else {
-    float* op = a.opart + (((size_t)row * S + split) * kH + hb + h0) * kD + d0;
+  // stream 1 hands its (o, max, sum) to stream 0 through LDS
+  float* xa = reinterpret_cast<float*>(rowb[0]) + hg * 32 * 64 + lane;
+  if (st == 1) {
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
-      for (int i = 0; i < LD; i += 4)
-        *reinterpret_cast<float4*>(op + (size_t)h * kD + i) =
-            make_float4(acc[h][i], acc[h][i + 1], acc[h][i + 2], acc[h][i + 3]);
-    if (tid < G) {
-      float* mlp = a.ml + (((size_t)row * S + split) * kH + hb + tid) * 2;
-      mlp[0] = mh[tid];
-      mlp[1] = lh[tid];
+      for (int i = 0; i < 8; ++i) xa[(h * 8 + i) * 64] = acc[h][i];
+    if (lane < 4) {
+      mls[hg][lane][0] = m_run;
+      mls[hg][lane][1] = l_run;
+    }
+  }
+  __syncthreads();
+  if (st == 1) return;
+
+  float Mh[4], Lh[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), h));
+    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), h));
+    const float m1 = mls[hg][h][0];
+    const float l1 = mls[hg][h][1];
+    const float M = fmaxf(m0, m1);
+    const float w0 = m0 == -INFINITY ? 0.f : __expf(m0 - M);
+    const float w1 = m1 == -INFINITY ? 0.f : __expf(m1 - M);
+    Mh[h] = M;
+    Lh[h] = l0 * w0 + l1 * w1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * w0 + xa[(h * 8 + i) * 64] * w1;
+  }
+
+  if (final_out && S == 1) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float L = Lh[h];
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      float* dst = a.o + ((size_t)row * kH + 4 * hg + h) * kD + 4 * lane;
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+      *reinterpret_cast<float4*>(dst + 256) = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+    }
+    if (lane < 4) {
+      const float L = lane == 0 ? Lh[0] : lane == 1 ? Lh[1] : lane == 2 ? Lh[2] : Lh[3];
+      const float M = lane == 0 ? Mh[0] : lane == 1 ? Mh[1] : lane == 2 ? Mh[2] : Mh[3];
+      a.lse[(size_t)row * kH + 4 * hg + lane] = L > 0.f ? M + logf(L) : -INFINITY;
+    }
+  } else {
+    float* op = a.opart + (((size_t)row * S + split) * kH + 4 * hg) * kD + 4 * lane;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      *reinterpret_cast<float4*>(op + (size_t)h * kD) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(op + (size_t)h * kD + 256) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+    if (lane < 4) {
+      const float L = lane == 0 ? Lh[0] : lane == 1 ? Lh[1] : lane == 2 ? Lh[2] : Lh[3];
+      const float M = lane == 0 ? Mh[0] : lane == 1 ? Mh[1] : lane == 2 ? Mh[2] : Mh[3];
+      float* mlp = a.ml + (((size_t)row * S + split) * kH + 4 * hg + lane) * 2;
+      mlp[0] = M;
+      mlp[1] = L;
     }
   }
 }
@@ -453,28 +483,20 @@ int32_t attn_chunks(int32_t K, int32_t W) {
 }
 
 AttnPlan attn_plan(int64_t rows, int32_t chunks) {
-  // Pick heads per work-group G (16 or 8) and splits S so that the launch
-  // fills the chip without giving some compute units two work-groups while
-  // others idle: estimated time = rounds of kGroupsPerRound work-groups x
-  // (chunks per work-group x G/16 + a fixed prologue), plus a merge launch
-  // when S > 1.
-  AttnPlan best{16, 1, 0.0};
+  // Splits S per row so that the launch fills the chip without giving some
+  // compute units two work-groups while others idle (a work-group's LDS
+  // takes a compute unit): estimated time = rounds of kGroupsPerRound
+  // work-groups x (chunks per work-group + a fixed prologue), plus a merge
+  // launch when S > 1.
   if (chunks <= 0) return AttnPlan{16, 0, 0.0};
-  double best_cost = 1e30;
-  for (int G = 16; G >= 8; G /= 2) {
-    const int64_t lo = (chunks + kMaxChunksPerSplit - 1) / kMaxChunksPerSplit;
-    for (int64_t S = lo; S <= chunks && S <= kCombMaxS; ++S) {
-      const int64_t cps = (chunks + S - 1) / S;
-      const int64_t Se = (chunks + cps - 1) / cps;
-      if (Se != S) continue;
-      const int64_t groups = rows * (16 / G) * S;
-      const int64_t rounds = (groups + kGroupsPerRound - 1) / kGroupsPerRound;
-      const double cost = (double)rounds * ((double)cps * G / 16.0 + 0.5) + (S > 1 ? 1.0 : 0.0);
-      if (cost < best_cost - 1e-9) {
-        best_cost = cost;
-        best = AttnPlan{G, (int32_t)S, cost};
-      }
-    }
+  AttnPlan best{16, 1, 1e30};
+  const int64_t lo = (chunks + kMaxChunksPerSplit - 1) / kMaxChunksPerSplit;
+  for (int64_t S = lo; S <= chunks && S <= kCombMaxS; ++S) {
+    const int64_t cps = (chunks + S - 1) / S;
+    if ((chunks + cps - 1) / cps != S) continue;
+    const int64_t rounds = (rows * S + kGroupsPerRound - 1) / kGroupsPerRound;
+    const double cost = (double)rounds * ((double)cps + 0.5) + (S > 1 ? 1.0 : 0.0);
+    if (cost < best.cost - 1e-9) best = AttnPlan{16, (int32_t)S, cost};
   }
   return best;
 }
@@ -486,13 +508,8 @@ hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, bool fin
   if (C == 0 || splits <= 0) return hipSuccess;
   const int32_t cps = (C + splits - 1) / splits;
   if (cps > kMaxChunksPerSplit || (C + cps - 1) / cps != splits) return hipErrorInvalidValue;
-  const dim3 block(kThreads);
-  if (plan.G == 8)
-    k_attn_partial<8><<<dim3((unsigned)splits, (unsigned)a.rows, 2), block, 0, s>>>(
-        a, Cg, C, cps, final_out ? 1 : 0);
-  else
-    k_attn_partial<16><<<dim3((unsigned)splits, (unsigned)a.rows, 1), block, 0, s>>>(
-        a, Cg, C, cps, final_out ? 1 : 0);
+  k_attn_partial<<<dim3((unsigned)splits, (unsigned)a.rows), dim3(kThreads), 0, s>>>(
+      a, Cg, C, cps, final_out ? 1 : 0);
   return hipGetLastError();
 }
 
