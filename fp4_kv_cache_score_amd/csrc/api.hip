@@ -45,10 +45,10 @@ struct DecodeWs {
 size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t N = P > M ? P : M;
   const int64_t Kmax = P > K ? P : K;
-  const int64_t splits = attn_chunks((int32_t)K, (int32_t)W);
+  const int64_t chunks = attn_chunks((int32_t)K, (int32_t)W);
   return align256(B * N * 4) + align256(B * kHistBins * 4) +
          (topk_multi_wg(B, M) ? topk_ws_bytes(B, M, Kmax) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
-         attn_ws_bytes(B, splits > 0 ? splits : 1);
+         attn_ws_bytes(B, chunks > 0 ? chunks : 1);
 }
 
 DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
@@ -67,9 +67,10 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   }
   d.cand = (int32_t*)p;
   p += align256(B * (P > 0 ? P : 1) * 4);
-  const int32_t S = attn_chunks((int32_t)K, (int32_t)W);
-  d.opart = (float*)p;
-  d.ml = (float*)(p + align256(B * (S > 0 ? S : 1) * kH * kD * 4));
+  const int32_t chunks = attn_chunks((int32_t)K, (int32_t)W);
+  const AttnWs w = attn_ws_carve(p, B, chunks > 0 ? chunks : 1);
+  d.opart = w.opart;
+  d.ml = w.ml;
   return d;
 }
 
@@ -170,6 +171,15 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* 
   return hip_status(launch_topk_select(scores, R, N, n_valid, N, cand, K, idx, t, false, stream));
 }
 
+// Decode attention of `rows` query rows in the workspace of a stand-alone call.
+static csa2_status attend_rows(AttnArgs& a, void* ws, int64_t rows, int32_t chunks,
+                               hipStream_t stream) {
+  const AttnWs w = attn_ws_carve(ws, rows, chunks);
+  a.opart = w.opart;
+  a.ml = w.ml;
+  return hip_status(launch_attn_partial(a, attn_plan(rows, chunks), stream));
+}
+
 csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q, int32_t H,
                              const int32_t* idx, int32_t K, float* o, float* lse, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
@@ -196,16 +206,12 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   a.q = q;
   a.Q = Q;
   a.rows = (int32_t)rows;
-  a.opart = (float*)ws;
-  a.ml = (float*)((char*)ws + align256(rows * chunks * kH * kD * 4));
   a.o = o;
   a.lse = lse;
+  a.o_in = nullptr;
+  a.lse_in = nullptr;
   if (Q > 1) return hip_status(launch_prefill_attn(a, nullptr, nullptr, stream));
-  const AttnPlan plan = attn_plan(rows, chunks);
-  st = hip_status(launch_attn_partial(a, plan, true, stream));
-  if (st != CSA2_OK || plan.splits == 1) return st;
-  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, plan.splits, nullptr, nullptr, o, lse,
-                                        stream));
+  return attend_rows(a, ws, rows, chunks, stream);
 }
 
 csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t D,
@@ -234,15 +240,12 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   a.q = q;
   a.Q = Q;
   a.rows = (int32_t)rows;
-  a.opart = (float*)ws;
-  a.ml = (float*)((char*)ws + align256(rows * chunks * kH * kD * 4));
   a.o = o;
   a.lse = lse;
+  a.o_in = o;
+  a.lse_in = lse;
   if (Q > 1) return hip_status(launch_prefill_attn(a, o, lse, stream));
-  const AttnPlan plan = attn_plan(rows, chunks);
-  csa2_status st = hip_status(launch_attn_partial(a, plan, false, stream));
-  if (st != CSA2_OK) return st;
-  return hip_status(launch_attn_combine(a.opart, a.ml, a.rows, plan.splits, o, lse, o, lse, stream));
+  return attend_rows(a, ws, rows, chunks, stream);
 }
 
 csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
@@ -276,7 +279,6 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
   const DecodeWs d = decode_ws_carve(ws, B, M, K, P, W);
   uint32_t* hist = d.big ? d.t.hist : d.hist;
   const AttnPlan plan = attn_plan(B, attn_chunks(K, W));
-  const int32_t S = plan.splits;
   float* opart = d.opart;
   float* ml = d.ml;
 
@@ -349,15 +351,12 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     a.rows = (int32_t)B;
     a.opart = opart;
     a.ml = ml;
+    a.o_in = nullptr;
+    a.lse_in = nullptr;
     a.o = y.o;
     a.lse = y.lse;
-    st = hip_status(launch_attn_partial(a, plan, true, stream));
+    st = hip_status(launch_attn_partial(a, plan, stream));
     if (st != CSA2_OK) return st;
-    if (S > 1) {
-      st = hip_status(launch_attn_combine(opart, ml, (int32_t)B, S, nullptr, nullptr, y.o, y.lse,
-                                          stream));
-      if (st != CSA2_OK) return st;
-    }
   }
   return CSA2_OK;
 }

@@ -13,8 +13,9 @@
 // window rows) and a split is a run of consecutive chunks.  Wave w takes the
 // 4 heads 4(w%4).. and key stream w/4: keys 16(w/4)..16(w/4)+15 of every
 // chunk, with its own online-softmax state; the two streams are merged at the
-// end.  Per chunk (double-buffered, one barrier per chunk):
-//   stage   the chunk's codes (loaded one chunk ahead into registers) are
+// end.  Per chunk (double-buffered, one barrier per chunk), after computing
+// on the current buffer the next chunk is staged into the other one:
+//   stage   the chunk's codes (loaded one compute phase ahead) are
 //           restored to bf16 - FP4 with gfx950's scaled FP4->bf16 convert,
 //           FP8 with the FP8->bf16 convert, both exact - and written to LDS
 //           twice: as rows of dim pairs (for q . c) and as key pairs per dim
@@ -29,11 +30,11 @@
 //   P x V   each lane owns 8 dims of the 4 heads; p is split into bf16 hi +
 //           lo parts (p - hi - lo is below 2^-16 p) and every v_dot2 adds two
 //           keys of one dim, so the key pairs are used as staged.
-// With one split per row the work-group normalises and writes o and lse;
-// otherwise it writes (unnormalised o, max, sum) partials and k_attn_combine
-// merges them (and optionally an incoming (o, lse)) by log-sum-exp weights in
-// a fixed order, so that the result equals one softmax over the union of the
-// key sets.  All arithmetic is fp32 VALU; decode keeps the matrix cores for
+// With one split per row the work-group merges an incoming (o, lse) when
+// given, normalises and writes o and lse; otherwise it writes (unnormalised
+// o, max, sum) partials and k_attn_combine, launched right after it, merges
+// them (and the incoming result) by log-sum-exp weights in a fixed order, so
+// that the result equals one softmax over the union of the key sets.  All arithmetic is fp32 VALU; decode keeps the matrix cores for
 // the multi-query prefill contraction.
 #include "csa2_internal.h"
 
@@ -168,7 +169,7 @@ __device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& 
 
 // grid (splits, rows), kThreads
 __global__ __launch_bounds__(kThreads, 1)
-void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t final_out) {
+void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   __shared__ __attribute__((aligned(16))) uint32_t rowb[2][kRowBufU];
   __shared__ __attribute__((aligned(16))) uint32_t pairb[2][kPairBufU];
   __shared__ __attribute__((aligned(16))) uint32_t ps[8][8][8];   // [wave][key pair][head: hi, lo]
@@ -226,8 +227,6 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t fina
 
   for (int c = c0; c < c1; ++c) {
     const int cur = (c - c0) & 1;
-    if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1]);
-    load_chunk(a, c + 2 < c1 ? c + 2 : c1 - 1, Cg, b, t, idx_s, key0, r);   // past the end: a harmless reload
 
     float zs;
     {  // logits of 4 heads x 4 keys over 32 dims, then summed over the row's 16 lanes
@@ -308,25 +307,45 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t fina
           for (int i = 0; i < 8; ++i) acc[h][i] *= al[h];
       }
       const uint32_t* pb = pairb[cur] + (8 * st) * kPairU + 4 * lane;
-#pragma unroll 2
-      for (int kp = 0; kp < 8; ++kp) {
-        const u32x4 pv0 = *reinterpret_cast<const u32x4*>(&ps[wave][kp][0]);
-        const u32x4 pv1 = *reinterpret_cast<const u32x4*>(&ps[wave][kp][4]);
-        const u32x4 ca = *reinterpret_cast<const u32x4*>(pb + kp * kPairU);
-        const u32x4 cb = *reinterpret_cast<const u32x4*>(pb + kp * kPairU + 256);
-        const uint32_t ph[4] = {pv0[0], pv0[2], pv1[0], pv1[2]};
-        const uint32_t pl[4] = {pv0[1], pv0[3], pv1[1], pv1[3]};
+      const uint32_t* pw = &ps[wave][0][0];
+      // two register sets, each loaded one step before use; the scheduling
+      // barriers keep the compiler from sinking the loads to their uses
+      u32x4 A[4], Bx[4];
+      auto load_pair = [&](u32x4* x, int kp) {
+        x[0] = *reinterpret_cast<const u32x4*>(pw + kp * 8);
+        x[1] = *reinterpret_cast<const u32x4*>(pw + kp * 8 + 4);
+        x[2] = *reinterpret_cast<const u32x4*>(pb + kp * kPairU);
+        x[3] = *reinterpret_cast<const u32x4*>(pb + kp * kPairU + 256);
+      };
+      auto pv_pair = [&](const u32x4* x) {
+        const uint32_t ph[4] = {x[0][0], x[0][2], x[1][0], x[1][2]};
+        const uint32_t pl[4] = {x[0][1], x[0][3], x[1][1], x[1][3]};
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[h][i] = fdot2(pl[h], ca[i], acc[h][i]);
-            acc[h][i] = fdot2(ph[h], ca[i], acc[h][i]);
-            acc[h][4 + i] = fdot2(pl[h], cb[i], acc[h][4 + i]);
-            acc[h][4 + i] = fdot2(ph[h], cb[i], acc[h][4 + i]);
+            acc[h][i] = fdot2(pl[h], x[2][i], acc[h][i]);
+            acc[h][i] = fdot2(ph[h], x[2][i], acc[h][i]);
+            acc[h][4 + i] = fdot2(pl[h], x[3][i], acc[h][4 + i]);
+            acc[h][4 + i] = fdot2(ph[h], x[3][i], acc[h][4 + i]);
           }
+      };
+      load_pair(A, 0);
+#pragma unroll 1
+      for (int kp = 0; kp < 8; kp += 2) {
+        load_pair(Bx, kp + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        pv_pair(A);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair(A, (kp + 2) & 7);      // the last step reloads pair 0, unused
+        __builtin_amdgcn_sched_barrier(0);
+        pv_pair(Bx);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // the next chunk's codes (loaded one compute phase ago) go to the other buffer
+    if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1]);
+    load_chunk(a, c + 2 < c1 ? c + 2 : c1 - 1, Cg, b, t, idx_s, key0, r);   // past the end: a harmless reload
     __syncthreads();
   }
 
@@ -343,39 +362,55 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps, int32_t fina
     }
   }
   __syncthreads();
-  if (st == 1) return;
 
   float Mh[4], Lh[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), h));
-    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), h));
-    const float m1 = mls[hg][h][0];
-    const float l1 = mls[hg][h][1];
-    const float M = fmaxf(m0, m1);
-    const float w0 = m0 == -INFINITY ? 0.f : __expf(m0 - M);
-    const float w1 = m1 == -INFINITY ? 0.f : __expf(m1 - M);
-    Mh[h] = M;
-    Lh[h] = l0 * w0 + l1 * w1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * w0 + xa[(h * 8 + i) * 64] * w1;
-  }
-
-  if (final_out && S == 1) {
+  if (st == 0) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float L = Lh[h];
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      float* dst = a.o + ((size_t)row * kH + 4 * hg + h) * kD + 4 * lane;
-      *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
-      *reinterpret_cast<float4*>(dst + 256) = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+      const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), h));
+      const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), h));
+      const float m1 = mls[hg][h][0];
+      const float l1 = mls[hg][h][1];
+      const float M = fmaxf(m0, m1);
+      const float w0 = m0 == -INFINITY ? 0.f : __expf(m0 - M);
+      const float w1 = m1 == -INFINITY ? 0.f : __expf(m1 - M);
+      Mh[h] = M;
+      Lh[h] = l0 * w0 + l1 * w1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * w0 + xa[(h * 8 + i) * 64] * w1;
     }
-    if (lane < 4) {
-      const float L = lane == 0 ? Lh[0] : lane == 1 ? Lh[1] : lane == 2 ? Lh[2] : Lh[3];
-      const float M = lane == 0 ? Mh[0] : lane == 1 ? Mh[1] : lane == 2 ? Mh[2] : Mh[3];
-      a.lse[(size_t)row * kH + 4 * hg + lane] = L > 0.f ? M + logf(L) : -INFINITY;
+  }
+
+  if (S == 1) {   // the whole row is here: merge an incoming result, normalise, write
+    if (st == 0) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const size_t hr = (size_t)row * kH + 4 * hg + h;
+        float M = Mh[h], L = Lh[h];
+        if (a.lse_in) {     // (o, lse) in/out may alias: each lane reads its own elements first
+          const float li = a.lse_in[hr];
+          const float M2 = fmaxf(M, li);
+          const float w1 = M == -INFINITY ? 0.f : __expf(M - M2);
+          const float w2 = li == -INFINITY ? 0.f : __expf(li - M2);
+          const float4 x0 = *reinterpret_cast<const float4*>(a.o_in + hr * kD + 4 * lane);
+          const float4 x1 = *reinterpret_cast<const float4*>(a.o_in + hr * kD + 256 + 4 * lane);
+          const float xi[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * w1 + xi[i] * w2;
+          L = L * w1 + w2;
+          M = M2;
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        float* dst = a.o + hr * kD + 4 * lane;
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+        *reinterpret_cast<float4*>(dst + 256) = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+        if (lane == 0) a.lse[hr] = L > 0.f ? M + logf(L) : -INFINITY;
+      }
     }
-  } else {
+    return;
+  }
+
+  if (st == 0) {   // this split's partial: unnormalised o, max, sum
     float* op = a.opart + (((size_t)row * S + split) * kH + 4 * hg) * kD + 4 * lane;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -501,24 +536,18 @@ AttnPlan attn_plan(int64_t rows, int32_t chunks) {
   return best;
 }
 
-hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, bool final_out, hipStream_t s) {
+hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
   const int32_t Cg = a.K > 0 && a.latent ? (a.K + KS - 1) / KS : 0;
   const int32_t C = Cg + (a.W > 0 ? (a.W + KS - 1) / KS : 0);
   const int32_t splits = plan.splits;
   if (C == 0 || splits <= 0) return hipSuccess;
   const int32_t cps = (C + splits - 1) / splits;
-  if (cps > kMaxChunksPerSplit || (C + cps - 1) / cps != splits) return hipErrorInvalidValue;
-  k_attn_partial<<<dim3((unsigned)splits, (unsigned)a.rows), dim3(kThreads), 0, s>>>(
-      a, Cg, C, cps, final_out ? 1 : 0);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_combine(const float* opart, const float* ml, int32_t rows,
-                               int32_t splits, const float* o_in, const float* lse_in,
-                               float* o, float* lse, hipStream_t s) {
-  if (splits > kCombMaxS) return hipErrorInvalidValue;
-  k_attn_combine<<<dim3((unsigned)kH, (unsigned)rows), dim3(kCombThreads), 0, s>>>(
-      opart, ml, splits, o_in, lse_in, o, lse);
+  if (cps > kMaxChunksPerSplit || (C + cps - 1) / cps != splits || splits > kCombMaxS)
+    return hipErrorInvalidValue;
+  k_attn_partial<<<dim3((unsigned)splits, (unsigned)a.rows), dim3(kThreads), 0, s>>>(a, Cg, C, cps);
+  if (splits == 1) return hipGetLastError();
+  k_attn_combine<<<dim3((unsigned)kH, (unsigned)a.rows), dim3(kCombThreads), 0, s>>>(
+      a.opart, a.ml, splits, a.o_in, a.lse_in, a.o, a.lse);
   return hipGetLastError();
 }
 

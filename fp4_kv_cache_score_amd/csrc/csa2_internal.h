@@ -85,11 +85,6 @@ inline TopkWs topk_ws_carve(void* ws, int64_t R, int64_t N, int64_t K) {
   return t;
 }
 
-// Attention partials: per (row, split) one [kH][kD] unnormalised output and
-// kH (max, sum) pairs.  `chunks` bounds the number of splits.
-inline size_t attn_ws_bytes(int64_t rows, int64_t chunks) {
-  return align256(rows * chunks * kH * kD * 4) + align256(rows * chunks * kH * 2 * 4);
-}
 
 // ---------------------------------------------------------------------------
 // Launchers (each returns the hipError_t of its launch)
@@ -128,9 +123,10 @@ hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
 // Attention over up to K gathered FP4 entries and up to W FP8 window rows per
 // query row.  The row's keys are cut into chunks of kKeysPerSplit (global
 // chunks first, then window chunks) and the chunks into `splits` contiguous
-// runs, one work-group each.  With one split per row and no incoming (o, lse)
-// the kernel writes o and lse itself; otherwise it writes partials that
-// launch_attn_combine merges (optionally with an incoming (o, lse)).
+// runs, one work-group each.  The result, merged with an incoming (o_in,
+// lse_in) when lse_in is given (they may alias o / lse), is written to o and
+// lse: by the work-group itself when the row has one split, otherwise by a
+// merge launch over the partials.
 struct AttnArgs {
   const uint8_t* latent;  // [B][M][kLatRow]
   const uint8_t* scale;   // [B][M][kScaleRow]
@@ -145,22 +141,35 @@ struct AttnArgs {
   int32_t rows;           // B * Q
   float* opart;           // [rows][splits][kH][kD]
   float* ml;              // [rows][splits][kH][2]
-  float* o;               // [rows][kH][kD]  (written directly when splits == 1)
+  float* o;               // [rows][kH][kD]
   float* lse;             // [rows][kH]
+  const float* o_in;      // NULL or [rows][kH][kD]
+  const float* lse_in;    // NULL or [rows][kH]
 };
 int32_t attn_chunks(int32_t K, int32_t W);          // chunks of one row's keys
-// Heads per work-group (16 or 8) and splits per row of a launch.
+// Splits per row of a launch (G: heads per work-group, always kH).
 struct AttnPlan {
   int32_t G;
   int32_t splits;
   double cost;
 };
 AttnPlan attn_plan(int64_t rows, int32_t chunks);
-// final_out: write o / lse directly when the row has one split.
-hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, bool final_out, hipStream_t s);
-hipError_t launch_attn_combine(const float* opart, const float* ml, int32_t rows,
-                               int32_t splits, const float* o_in, const float* lse_in,
-                               float* o, float* lse, hipStream_t s);
+hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, hipStream_t s);
+// Attention workspace: per (row, split) one [kH][kD] unnormalised output and
+// kH (max, sum) pairs; `chunks` bounds the number of splits.
+struct AttnWs {
+  float* opart;
+  float* ml;
+};
+inline size_t attn_ws_bytes(int64_t rows, int64_t chunks) {
+  return align256(rows * chunks * kH * kD * 4) + align256(rows * chunks * kH * 2 * 4);
+}
+inline AttnWs attn_ws_carve(void* ws, int64_t rows, int64_t chunks) {
+  AttnWs w;
+  w.opart = (float*)ws;
+  w.ml = (float*)((char*)ws + align256(rows * chunks * kH * kD * 4));
+  return w;
+}
 
 // Chunked prefill (Q > 1 query tokens per sequence), matrix-core kernels.
 // Scores of every pool entry for every query (no candidate list, no
