@@ -68,12 +68,7 @@ constexpr int kDppXor15 = 0x140;      // row_mirror
 constexpr int kDppRor4 = 0x124;       // row_ror:4 (lane i reads lane i - 4 of its row)
 constexpr int kDppRor8 = 0x128;       // row_ror:8
 constexpr int kDppRor12 = 0x12C;      // row_ror:12 (lane i reads lane i + 4 of its row)
-
-// bf16 with round-to-nearest-even of a finite non-negative float, in the low 16 bits
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+constexpr float kLazyMax = 8.f;       // softmax reference slack (natural log units)
 
 // Staging unit of a thread: key pair kp (keys 2kp, 2kp+1 of the chunk) and a
 // 16-dim segment seg.  The bit assignment keeps both LDS layouts' stores to
@@ -87,11 +82,18 @@ struct ChunkRegs {
   bool ok[2];       // key present
 };
 
+// Per-sequence bases of the inputs a work-group reads.
+struct RowBase {
+  const uint8_t* lat;     // latent of entry 0 of the sequence
+  const uint8_t* sc;      // scales of entry 0 of the sequence
+  const uint8_t* win;     // window row 0 of the query row
+};
+
 // One 16-byte load per key from a selected address, with no branch: an
 // absent key reads entry 0 or row 0 of the sequence and is masked by ok, so
 // that no register merge has to wait for the loads.  Every address read is
 // inside the inputs.
-__device__ __forceinline__ void load_chunk(const AttnArgs& a, int chunk, int Cg, int b, int t,
+__device__ __forceinline__ void load_chunk(const AttnArgs& a, const RowBase& rb, int chunk, int Cg,
                                            const int32_t* idx_s, int key0, ChunkRegs& r) {
   const int tid = threadIdx.x;
   const int kp = unit_kp(tid);
@@ -104,12 +106,12 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& a, int chunk, int Cg,
     const int32_t e = idx_s[(kpos - key0) & (kMaxChunksPerSplit * KS - 1)];
     const bool ok = glob ? (kpos < a.K && e >= 0) : (wr < a.W);
     r.ok[i] = ok;
-    const size_t er = (size_t)b * (size_t)a.M + (size_t)(glob && ok ? e : 0);
-    const uint8_t* gsrc = a.latent + er * kLatRow + (seg >> 1) * 16;
-    const uint8_t* wsrc = a.swa + ((size_t)b * a.swa_rows + t + (!glob && ok ? wr : 0)) * kD + seg * 16;
+    const size_t er = (size_t)(glob && ok ? e : 0);
+    const uint8_t* gsrc = rb.lat + er * kLatRow + (seg >> 1) * 16;
+    const uint8_t* wsrc = rb.win + (size_t)(!glob && ok ? wr : 0) * kD + seg * 16;
     r.v[i] = *reinterpret_cast<const u32x4*>(glob ? gsrc : wsrc);
     // window chunks read a byte of q instead (the pool may be absent)
-    const uint8_t* sp = glob ? a.scale + er * kScaleRow + (seg >> 1) : reinterpret_cast<const uint8_t*>(a.q);
+    const uint8_t* sp = glob ? rb.sc + er * kScaleRow + (seg >> 1) : reinterpret_cast<const uint8_t*>(a.q);
     r.sc[i] = *sp;
   }
 }
@@ -119,31 +121,34 @@ __device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& 
   const int tid = threadIdx.x;
   const int kp = unit_kp(tid);
   const int seg = unit_seg(tid);
+  // Absent keys are converted like the others (their codes are finite data
+  // of entry 0 or row 0): their logits are masked and their p is 0.
   uint32_t w[2][8];   // per key: 16 bf16 of dims seg*16 .. seg*16+15 as 8 dim pairs
+  if (chunk < Cg) {
+    const bool hi = seg & 1;             // the 8 code bytes are the upper half of the 16 loaded
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int m = 0; m < 8; ++m) w[i][m] = 0u;
-    if (r.ok[i]) {
-      if (chunk < Cg) {
-        const uint32_t sc = r.sc[i];
-        const float scale = __uint_as_float(sc ? (sc << 23) : 0x00400000u);   // 2^(sc-127)
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const uint32_t x = (seg & 1) ? (d ? r.v[i][3] : r.v[i][2]) : (d ? r.v[i][1] : r.v[i][0]);
-          w[i][4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 0));
-          w[i][4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 1));
-          w[i][4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 2));
-          w[i][4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 3));
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          w[i][2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, false));
-          w[i][2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, true));
-        }
-      }
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t sc = r.sc[i];
+      const float scale = __uint_as_float(sc ? (sc << 23) : 0x00400000u);   // 2^(sc-127)
+      const uint32_t x0 = hi ? r.v[i][2] : r.v[i][0];
+      const uint32_t x1 = hi ? r.v[i][3] : r.v[i][1];
+      w[i][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, 0));
+      w[i][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, 1));
+      w[i][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, 2));
+      w[i][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, 3));
+      w[i][4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, 0));
+      w[i][5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, 1));
+      w[i][6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, 2));
+      w[i][7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, 3));
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        w[i][2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, false));
+        w[i][2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, true));
+      }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -211,10 +216,14 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   }
   __syncthreads();
 
+  RowBase rbase;
+  rbase.lat = a.latent + (size_t)b * (size_t)a.M * kLatRow;
+  rbase.sc = a.scale + (size_t)b * (size_t)a.M * kScaleRow;
+  rbase.win = a.swa + ((size_t)b * a.swa_rows + t) * kD;
   ChunkRegs r;
-  load_chunk(a, c0, Cg, b, t, idx_s, key0, r);
+  load_chunk(a, rbase, c0, Cg, idx_s, key0, r);
   stage_chunk(c0, Cg, r, rowb[0], pairb[0], valid_s[0]);
-  load_chunk(a, c0 + 1 < c1 ? c0 + 1 : c0, Cg, b, t, idx_s, key0, r);
+  load_chunk(a, rbase, c0 + 1 < c1 ? c0 + 1 : c0, Cg, idx_s, key0, r);
   __syncthreads();
 
   float acc[4][8];                         // P x V: heads 4hg.. x dims 4l..4l+3, 256+4l..
@@ -270,7 +279,10 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
       mc = fmaxf(mc, dpp<kDppRor8>(mc));
       mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
       mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
-      const float m_new = fmaxf(m_run, mc);
+      // The reference m_run moves only when the chunk's max passes it by
+      // more than kLazyMax, so that p <= e^kLazyMax and most chunks need no
+      // rescaling; o / l and m + log l are the same for any reference.
+      const float m_new = mc > m_run + kLazyMax ? mc : m_run;
       float p = 0.f;
       alpha = 1.f;
       if (m_new != -INFINITY) {
@@ -283,14 +295,15 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
       ls += __shfl_xor(ls, 32, 64);
       l_run = l_run * alpha + ls;
       m_run = m_new;
-      // key pairs (kk, kk + 1) for kk even: the odd key is in lane dp + 4
+      // key pairs (kk, kk + 1) for kk even: the odd key is in lane dp + 4;
+      // p = hi + lo in bf16 (round to nearest even), residual below 2^-16 p
       const float po = dpp<kDppRor12>(p);
-      if (!(dp & 4)) {
-        const uint32_t h0 = bf16_rne(p), h1 = bf16_rne(po);
-        const uint32_t l0 = bf16_rne(p - __uint_as_float(h0 << 16));
-        const uint32_t l1 = bf16_rne(po - __uint_as_float(h1 << 16));
-        *reinterpret_cast<uint2*>(&ps[wave][kk >> 1][2 * hx]) = make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
-      }
+      const bf16x2 hb = __builtin_convertvector((f32x2){p, po}, bf16x2);
+      const uint32_t hu = __builtin_bit_cast(uint32_t, hb);
+      const bf16x2 lb = __builtin_convertvector(
+          (f32x2){p - __uint_as_float(hu << 16), po - __uint_as_float(hu & 0xFFFF0000u)}, bf16x2);
+      if (!(dp & 4))
+        *reinterpret_cast<uint2*>(&ps[wave][kk >> 1][2 * hx]) = make_uint2(hu, __builtin_bit_cast(uint32_t, lb));
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -345,7 +358,7 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
     }
     // the next chunk's codes (loaded one compute phase ago) go to the other buffer
     if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1]);
-    load_chunk(a, c + 2 < c1 ? c + 2 : c1 - 1, Cg, b, t, idx_s, key0, r);   // past the end: a harmless reload
+    load_chunk(a, rbase, c + 2 < c1 ? c + 2 : c1 - 1, Cg, idx_s, key0, r);   // past the end: a harmless reload
     __syncthreads();
   }
 
