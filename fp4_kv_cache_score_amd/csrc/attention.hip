@@ -440,11 +440,14 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   }
 }
 
-// One work-group (128 lanes x 4 dims) per (head, query row).  Every split's
-// (max, sum) pair is loaded at once, then the partial rows in unrolled groups
-// of independent loads.
+// One work-group (128 lanes x 4 dims) per (head, query row).  The partial
+// rows of up to kCombBatch splits are loaded together with every split's
+// (max, sum) pair, so that the merge waits on one round trip to memory; the
+// weights are formed in LDS by the first wave, and the rows are summed in
+// split order, then the incoming result.
 constexpr int kCombThreads = 128;
 constexpr int kCombMaxS = 63;            // splits per row (lane kCombMaxS holds an incoming result)
+constexpr int kCombBatch = 8;            // partial rows in flight per lane
 
 __global__ __launch_bounds__(kCombThreads)
 void k_attn_combine(const float* __restrict__ opart, const float* __restrict__ ml,
@@ -455,6 +458,12 @@ void k_attn_combine(const float* __restrict__ opart, const float* __restrict__ m
   const int h = blockIdx.x;
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
+  const int d0 = tid * 4;
+  const float* src = opart + ((size_t)row * S * kH + h) * kD + d0;
+  float4 x[kCombBatch];
+#pragma unroll
+  for (int u = 0; u < kCombBatch; ++u)
+    if (u < S) x[u] = *reinterpret_cast<const float4*>(src + (size_t)u * kH * kD);
   const float* mlr = ml + (size_t)row * S * kH * 2;
   if (tid < 64) {
     // lanes 0..S-1 hold one split each (S <= 63), lane S the incoming result
@@ -484,39 +493,33 @@ void k_attn_combine(const float* __restrict__ opart, const float* __restrict__ m
   }
   __syncthreads();
   const float L = L_s;
-  const int d0 = tid * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* src = opart + ((size_t)row * S * kH + h) * kD + d0;
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    float4 x[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4*>(src + (size_t)(s + u) * kH * kD);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = wgt_s[s + u];
+  for (int u = 0; u < kCombBatch; ++u) {
+    if (u < S) {
+      const float w = wgt_s[u];
       acc.x = fmaf(w, x[u].x, acc.x);
       acc.y = fmaf(w, x[u].y, acc.y);
       acc.z = fmaf(w, x[u].z, acc.z);
       acc.w = fmaf(w, x[u].w, acc.w);
     }
   }
-  for (; s < S; ++s) {
-    const float4 x = *reinterpret_cast<const float4*>(src + (size_t)s * kH * kD);
+  for (int s = kCombBatch; s < S; ++s) {
+    const float4 y = *reinterpret_cast<const float4*>(src + (size_t)s * kH * kD);
     const float w = wgt_s[s];
-    acc.x = fmaf(w, x.x, acc.x);
-    acc.y = fmaf(w, x.y, acc.y);
-    acc.z = fmaf(w, x.z, acc.z);
-    acc.w = fmaf(w, x.w, acc.w);
+    acc.x = fmaf(w, y.x, acc.x);
+    acc.y = fmaf(w, y.y, acc.y);
+    acc.z = fmaf(w, y.z, acc.z);
+    acc.w = fmaf(w, y.w, acc.w);
   }
   if (lse_in) {
     const float w = wgt_s[S];
     if (w > 0.f) {
-      const float4 x = *reinterpret_cast<const float4*>(o_in + ((size_t)row * kH + h) * kD + d0);
-      acc.x = fmaf(w, x.x, acc.x);
-      acc.y = fmaf(w, x.y, acc.y);
-      acc.z = fmaf(w, x.z, acc.z);
-      acc.w = fmaf(w, x.w, acc.w);
+      const float4 y = *reinterpret_cast<const float4*>(o_in + ((size_t)row * kH + h) * kD + d0);
+      acc.x = fmaf(w, y.x, acc.x);
+      acc.y = fmaf(w, y.y, acc.y);
+      acc.z = fmaf(w, y.z, acc.z);
+      acc.w = fmaf(w, y.w, acc.w);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
