@@ -29,12 +29,13 @@ size_t topk_call_ws_bytes(int64_t R, int64_t N, int64_t K) {
   return topk_multi_wg(R, N) ? topk_ws_bytes(R, N, K) : 256;
 }
 
-// decode_layers workspace: scores [B][N] | histograms [B][4096] |
-// multi-work-group Top-K scratch (only when M > kRowMaxN) | candidate pool |
-// attention partials.
+// decode_layers workspace: scores [B][N] | multi-work-group Top-K scratch
+// (only when M > kRowMaxN) | candidate pool | attention partials.  The scans
+// build no histogram: a fused one costs more in cross-XCD atomics than the
+// 4 bytes per entry a Top-K pass reads (the row kernel builds its own from
+// the row it holds; the multi-work-group select gets one histogram pass).
 struct DecodeWs {
   float* scores;
-  uint32_t* hist;
   bool big;
   TopkWs t;
   int32_t* cand;
@@ -46,9 +47,8 @@ size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t N = P > M ? P : M;
   const int64_t Kmax = P > K ? P : K;
   const int64_t chunks = attn_chunks((int32_t)K, (int32_t)W);
-  return align256(B * N * 4) + align256(B * kHistBins * 4) +
-         (topk_multi_wg(B, M) ? topk_ws_bytes(B, M, Kmax) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
-         attn_ws_bytes(B, chunks > 0 ? chunks : 1);
+  return align256(B * N * 4) + (topk_multi_wg(B, M) ? topk_ws_bytes(B, M, Kmax) : 0) +
+         align256(B * (P > 0 ? P : 1) * 4) + attn_ws_bytes(B, chunks > 0 ? chunks : 1);
 }
 
 DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
@@ -58,8 +58,6 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   char* p = (char*)ws;
   d.scores = (float*)p;
   p += align256(B * N * 4);
-  d.hist = (uint32_t*)p;
-  p += align256(B * kHistBins * 4);
   d.big = topk_multi_wg(B, M);
   if (d.big) {
     d.t = topk_ws_carve(p, B, M, Kmax);
@@ -277,18 +275,16 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
   if (!al16(ws)) return CSA2_ERR_ALIGN;
 
   const DecodeWs d = decode_ws_carve(ws, B, M, K, P, W);
-  uint32_t* hist = d.big ? d.t.hist : d.hist;
   const AttnPlan plan = attn_plan(B, attn_chunks(K, W));
   float* opart = d.opart;
   float* ml = d.ml;
 
-  // The histogram (and the multi-work-group counters next to it) start
-  // zeroed; every select leaves them zeroed again.
-  if (d.big)
+  // The multi-work-group select's histogram and counters start zeroed; every
+  // select leaves them zeroed again.
+  if (d.big) {
     st = zero_hist_counters(d.t, B, stream);
-  else
-    st = hip_status(launch_fill_zero(hist, B * kHistBins, stream));
-  if (st != CSA2_OK) return st;
+    if (st != CSA2_OK) return st;
+  }
 
   const int32_t* cur = nullptr;
   int32_t cur_layer = -1;
@@ -297,18 +293,21 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     const csa2_layer& y = layers[l];
     if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         nullptr, (int32_t)M, d.scores, hist, stream));
+                                         nullptr, (int32_t)M, d.scores, nullptr, stream));
       if (st != CSA2_OK) return st;
       if (!d.big) {
         if (y.mode == CSA2_FULL && P > 0) {
           st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M,
-                                           P, hist, false, nullptr, d.cand, stream));
+                                           P, nullptr, false, nullptr, d.cand, stream));
           if (st != CSA2_OK) return st;
         }
         st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, K,
-                                         hist, true, nullptr, y.idx_out, stream));
+                                         nullptr, false, nullptr, y.idx_out, stream));
         if (st != CSA2_OK) return st;
       } else {
+        st = hip_status(launch_topk_hist(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M,
+                                         d.t.hist, stream));
+        if (st != CSA2_OK) return st;
         if (y.mode == CSA2_FULL && P > 0) {
           st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P,
                                d.cand, d.t, false, stream);
@@ -322,9 +321,9 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
       cur_layer = l;
     } else if (y.mode == CSA2_REINDEX) {  // hierarchical: score inside the candidate pool
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         d.cand, P, d.scores, hist, stream));
+                                         d.cand, P, d.scores, nullptr, stream));
       if (st != CSA2_OK) return st;
-      st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, nullptr, n_cand, K, hist, true,
+      st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, nullptr, n_cand, K, nullptr, false,
                                        d.cand, y.idx_out, stream));
       if (st != CSA2_OK) return st;
       cur = y.idx_out;
