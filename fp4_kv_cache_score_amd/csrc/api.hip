@@ -30,7 +30,8 @@ size_t topk_call_ws_bytes(int64_t R, int64_t N, int64_t K) {
 }
 
 // decode_layers workspace: scores [B][N] | multi-work-group Top-K scratch
-// (only when M > kRowMaxN) | candidate pool | attention partials.  The scans
+// (only when the select takes several work-groups per row) | candidate pool
+// | candidate scores | attention partials.  The scans
 // build no histogram: a fused one costs more in cross-XCD atomics than the
 // 4 bytes per entry a Top-K pass reads (the row kernel builds its own from
 // the row it holds; the multi-work-group select gets one histogram pass).
@@ -39,6 +40,7 @@ struct DecodeWs {
   bool big;
   TopkWs t;
   int32_t* cand;
+  float* cscore;
   float* opart;
   float* ml;
 };
@@ -48,7 +50,7 @@ size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t Kmax = P > K ? P : K;
   const int64_t chunks = attn_chunks((int32_t)K, (int32_t)W);
   return align256(B * N * 4) + (topk_multi_wg(B, M) ? topk_ws_bytes(B, M, Kmax) : 0) +
-         align256(B * (P > 0 ? P : 1) * 4) + attn_ws_bytes(B, chunks > 0 ? chunks : 1);
+         2 * align256(B * (P > 0 ? P : 1) * 4) + attn_ws_bytes(B, chunks > 0 ? chunks : 1);
 }
 
 DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
@@ -64,6 +66,8 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
     p += topk_ws_bytes(B, M, Kmax);
   }
   d.cand = (int32_t*)p;
+  p += align256(B * (P > 0 ? P : 1) * 4);
+  d.cscore = (float*)p;
   p += align256(B * (P > 0 ? P : 1) * 4);
   const int32_t chunks = attn_chunks((int32_t)K, (int32_t)W);
   const AttnWs w = attn_ws_carve(p, B, chunks > 0 ? chunks : 1);
@@ -308,14 +312,28 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
         st = hip_status(launch_topk_hist(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M,
                                          d.t.hist, stream));
         if (st != CSA2_OK) return st;
-        if (y.mode == CSA2_FULL && P > 0) {
+        if (y.mode == CSA2_FULL && P > 0 && n_cand <= kRowMaxN) {
+          // Top-P over the row, then Top-K over the P candidates' scores: the
+          // candidates hold the Top-K (same order, K <= P), and their list is
+          // ascending, so the lower-index tie-break is kept.
           st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P,
-                               d.cand, d.t, false, stream);
+                               d.cand, d.t, true, stream);
+          if (st != CSA2_OK) return st;
+          st = hip_status(launch_gather_scores(d.scores, (int32_t)B, M, d.cand, P, d.cscore, stream));
+          if (st != CSA2_OK) return st;
+          st = hip_status(launch_topk_rows(d.cscore, (int32_t)B, P, nullptr, n_cand, K, nullptr,
+                                           false, d.cand, y.idx_out, stream));
+          if (st != CSA2_OK) return st;
+        } else {
+          if (y.mode == CSA2_FULL && P > 0) {
+            st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P,
+                                 d.cand, d.t, false, stream);
+            if (st != CSA2_OK) return st;
+          }
+          st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, K,
+                               y.idx_out, d.t, true, stream);
           if (st != CSA2_OK) return st;
         }
-        st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, K,
-                             y.idx_out, d.t, true, stream);
-        if (st != CSA2_OK) return st;
       }
       cur = y.idx_out;
       cur_layer = l;

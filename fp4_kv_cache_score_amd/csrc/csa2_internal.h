@@ -185,5 +185,8 @@ hipError_t launch_prefill_attn(const AttnArgs& a, const float* o_in, const float
 
 // Copy n int32 (Reuse layers that ask for their indices).
 hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
+// out[r][i] = scores[r][idx[r][i]], -inf where idx is -1 (idx in [-1, N)).
+hipError_t launch_gather_scores(const float* scores, int32_t R, int64_t N, const int32_t* idx,
+                                int32_t P, float* out, hipStream_t s);
 
 }  // namespace csa2

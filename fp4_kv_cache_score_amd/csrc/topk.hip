@@ -802,7 +802,25 @@ __global__ void k_copy_i32(int32_t* __restrict__ d, const int32_t* __restrict__ 
   for (int64_t k = i; k < n; k += stride) d[k] = s[k];
 }
 
+// out[r][i] = scores[r][idx[r][i]] (-inf for idx -1): the scores of a
+// candidate list, so that a later select can run over the list alone.
+__global__ void k_gather_scores(const float* __restrict__ scores, int64_t N,
+                                const int32_t* __restrict__ idx, int32_t P, float* __restrict__ out) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = blockIdx.y;
+  if (i >= P) return;
+  const int32_t e = idx[(size_t)row * P + i];
+  out[(size_t)row * P + i] = e >= 0 ? scores[(size_t)row * N + e] : -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_gather_scores(const float* scores, int32_t R, int64_t N, const int32_t* idx,
+                                int32_t P, float* out, hipStream_t s) {
+  if (R <= 0 || P <= 0) return hipSuccess;
+  k_gather_scores<<<dim3((unsigned)((P + 255) / 256), (unsigned)R), dim3(256), 0, s>>>(scores, N, idx, P, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
