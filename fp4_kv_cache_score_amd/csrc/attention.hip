@@ -70,6 +70,23 @@ constexpr int kDppRor8 = 0x128;       // row_ror:8
 constexpr int kDppRor12 = 0x12C;      // row_ror:12 (lane i reads lane i + 4 of its row)
 constexpr float kLazyMax = 8.f;       // softmax reference slack (natural log units)
 
+// Max and sum over the four rows of 16 lanes: gfx950's permlane swaps
+// exchange rows 0<->1, 2<->3 and halves 0-31<->32-63 in a VALU operation
+// (both operands the same value); each lane combines the same two values
+// in the same order, so every lane gets the same result.
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Staging unit of a thread: key pair kp (keys 2kp, 2kp+1 of the chunk) and a
 // 16-dim segment seg.  The bit assignment keeps both LDS layouts' stores to
 // at most two lanes per bank group.
@@ -276,9 +293,7 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
       const int kk = 4 * kb + kx;
       const float zv = valid_s[cur][16 * st + kk] ? zs : -INFINITY;
       float mc = fmaxf(zv, dpp<kDppRor4>(zv));
-      mc = fmaxf(mc, dpp<kDppRor8>(mc));
-      mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
-      mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+      mc = rows_max(fmaxf(mc, dpp<kDppRor8>(mc)));
       // The reference m_run moves only when the chunk's max passes it by
       // more than kLazyMax, so that p <= e^kLazyMax and most chunks need no
       // rescaling; o / l and m + log l are the same for any reference.
@@ -290,9 +305,7 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
         alpha = __expf(m_run - m_new);
       }
       float ls = p + dpp<kDppRor4>(p);
-      ls += dpp<kDppRor8>(ls);
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
+      ls = rows_sum(ls + dpp<kDppRor8>(ls));
       l_run = l_run * alpha + ls;
       m_run = m_new;
       // key pairs (kk, kk + 1) for kk even: the odd key is in lane dp + 4;
