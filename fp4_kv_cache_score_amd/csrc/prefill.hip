@@ -63,7 +63,8 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
                      int32_t Q, int64_t pos0, int32_t ratio, float* __restrict__ scores) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[2][kSQ * kSRow];
   __shared__ __attribute__((aligned(16))) uint8_t ks[2][kSE * kSRow];
-  __shared__ float ws[kSQ][kHI + 1];
+  __shared__ __attribute__((aligned(16))) float ws[kHI][kSQ];   // head weights, rows contiguous
+  __shared__ int32_t vis_s[kSQ];          // entries visible to each query row of the tile
 
   const int b = blockIdx.z;
   const int q0 = blockIdx.y * kSQ;
@@ -88,22 +89,30 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
 
   for (int i = tid; i < kSQ * kHI; i += kSThreads) {
     const int r = i / kHI, h = i - r * kHI;
-    ws[r][h] = q0 + r < Q ? w_idx[((size_t)b * Q + q0 + r) * kHI + h] : 0.f;
+    ws[h][r] = q0 + r < Q ? w_idx[((size_t)b * Q + q0 + r) * kHI + h] : 0.f;
   }
+  if (tid < kSQ) vis_s[tid] = (int32_t)visible(pos0, q0 + tid, ratio, M);   // one division per row
 
-  // staging: thread -> two (row, 16-byte part) pieces of each of Q and K
+  // staging: thread -> two (row, 16-byte part) pieces of each of Q and K.
+  // Rows past Q or M load the last row instead (never written out), so the
+  // loads are unconditional.
   u32x4 rq[2], rk[2];
+  const uint8_t* qrow[2];
+  const uint8_t* krow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + i * kSThreads;
+    const int row = c >> 2, part = c & 3;
+    const int t = q0 + row < Q ? q0 + row : Q - 1;
+    const int64_t e = e0 + row < M ? e0 + row : M - 1;
+    qrow[i] = qb + (size_t)t * kKeyRow + part * 16;
+    krow[i] = kb + (size_t)e * kKeyRow + part * 16;
+  }
   auto load = [&](int h) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * kSThreads;
-      const int row = c >> 2, part = c & 3;
-      const int t = q0 + row;
-      const int64_t e = e0 + row;
-      rq[i] = t < Q ? *reinterpret_cast<const u32x4*>(qb + (size_t)t * kKeyRow + h * kDI + part * 16)
-                    : u32x4{0u, 0u, 0u, 0u};
-      rk[i] = e < M ? *reinterpret_cast<const u32x4*>(kb + (size_t)e * kKeyRow + h * kDI + part * 16)
-                    : u32x4{0u, 0u, 0u, 0u};
+      rq[i] = *reinterpret_cast<const u32x4*>(qrow[i] + h * kDI);
+      rk[i] = *reinterpret_cast<const u32x4*>(krow[i] + h * kDI);
     }
   };
   // 16 E4M3 values -> 16 bf16 (two 16-byte pieces), exact
@@ -172,14 +181,24 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
       // head weights of the 16 query rows this lane holds in each block
       float wv[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) wv[v] = ws[64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3)][h];
+      for (int j = 0; j < 4; ++j) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&ws[h][64 * wq + 32 * r + 8 * j + 4 * g]);
+        wv[4 * j] = w4.x;
+        wv[4 * j + 1] = w4.y;
+        wv[4 * j + 2] = w4.z;
+        wv[4 * j + 3] = w4.w;
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         f32x16 s = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][k], Bv[c][k], s, 0, 0, 0);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[r][c][v] = fmaf(s[v] > 0.f ? s[v] : 0.f, wv[v], acc[r][c][v]);
+        for (int v = 0; v < 16; ++v) {
+          // ReLU on the bit pattern: a signed max with 0 maps negatives and -0 to +0
+          const float rl = __int_as_float(max(__float_as_int(s[v]), 0));
+          acc[r][c][v] = fmaf(rl, wv[v], acc[r][c][v]);
+        }
       }
     }
     if (h + 1 < kHI) store(buf ^ 1);
@@ -187,18 +206,19 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
   }
 
   // write: value v of block (r, c) is query row 8*(v/4) + 4*g + v%4, entry lr
+  const int32_t ea = (int32_t)e0 + 64 * we + lr;     // entries of blocks c = 0, 1
+  const int32_t eb = ea + 32;
+  const bool oka = ea < M, okb = eb < M;
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int t = q0 + 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (t >= Q) continue;
-      const int64_t vis = visible(pos0, t, ratio, M);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int64_t e = e0 + 64 * we + 32 * c + lr;
-        if (e < M) sb[(size_t)t * M + e] = e < vis ? acc[r][c][v] : -INFINITY;
-      }
+      const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (q0 + tr >= Q) continue;
+      const int32_t vis = vis_s[tr];
+      float* srow = sb + (size_t)(q0 + tr) * M;
+      if (oka) srow[ea] = ea < vis ? acc[r][0][v] : -INFINITY;
+      if (okb) srow[eb] = eb < vis ? acc[r][1][v] : -INFINITY;
     }
 }
 
