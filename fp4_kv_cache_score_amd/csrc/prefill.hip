@@ -153,15 +153,18 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[r][c][v] = 0.f;
 
+  // Per head: MFMA on the staged buffer, then the next head is staged from
+  // the registers (loaded one head's compute earlier) and the head after it
+  // is loaded into them.
   load(0);
   store(0);
+  load(1);
   __syncthreads();
   const int g = lane >> 5;       // which 32-value half of the head slice
   const int lr = lane & 31;
 #pragma unroll 1
   for (int h = 0; h < kHI; ++h) {
     const int buf = h & 1;
-    if (h + 1 < kHI) load(h + 1);
     // operands: lane holds 32 bf16 (4 k-steps of 8) of its row's half g
     bf16x8 A[2][4], Bv[2][4];
 #pragma unroll
@@ -202,6 +205,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
       }
     }
     if (h + 1 < kHI) store(buf ^ 1);
+    load(h + 2 < kHI ? h + 2 : kHI - 1);   // past the end: a harmless reload
     __syncthreads();
   }
 
