@@ -86,6 +86,77 @@ def time_decode(dc, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def time_structs(dc, structs, steps: int, warmup: int) -> float:
+    """Back-to-back mean ms of one decode_layers call over the given layer structs."""
+    import torch
+    from fp4_kv_cache_score_amd import _lib as C
+    cfg = dc.cfg
+    stream = torch.cuda.current_stream()
+
+    def run():
+        C.csa2_decode_layers(dc.pool, structs, cfg.H, cfg.K, cfg.P, cfg.W, dc.ws, dc.ws_bytes,
+                             stream)
+    for _ in range(warmup):
+        run()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def per_layer_ms(dc, steps: int):
+    """Per-layer ms (warm): the step over the schedule's first l layers, differenced.
+
+    Every prefix of a valid schedule is valid (it starts with a Full layer)."""
+    structs = dc.layer_structs(idx_for_reuse=False)
+    out, prev = [], 0.0
+    for n in range(1, len(structs) + 1):
+        t = time_structs(dc, structs[:n], steps, 2)
+        out.append(t - prev)
+        prev = t
+    return out
+
+
+def cold_step_ms(dc, steps: int) -> float:
+    """Median ms of a step that starts with the MALL evicted: a 512 MiB read-write
+    sweep runs before each timed step, outside its events."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sweep = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    dc.decode_layers()
+    for a, b in evs:
+        sweep.add_(1)
+        a.record(stream)
+        dc.decode_layers()
+        b.record(stream)
+    torch.cuda.synchronize()
+    del sweep
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def all_full_ms(dc, steps: int, warmup: int) -> float:
+    """The same layers with every layer in Full mode (each one scans and selects):
+    the per-layer indexing that Reindex / Reuse layers avoid.  Layers without an
+    indexer query of their own use the first layer's."""
+    from fp4_kv_cache_score_amd import _lib as C
+    first = next(d for d in dc.layers if d["q_idx"] is not None)
+    structs = []
+    for d in dc.layers:
+        qi = d["q_idx"] if d["q_idx"] is not None else first["q_idx"]
+        wi = d["w_idx"] if d["w_idx"] is not None else first["w_idx"]
+        structs.append(C.csa2_layer(C.CSA2_FULL, C._p(qi), C._p(wi), C._p(d["q"]),
+                                    C._p(d["swa"]), C._p(d["o"]), C._p(d["lse"]),
+                                    C._p(d["idx"])))
+    return time_structs(dc, structs, steps, warmup)
+
+
 def time_score_kernel(dc, launches: int):
     """Mean duration of the scan kernel as decode launches it (flat, no histogram)."""
     import torch
@@ -174,7 +245,7 @@ def cpu_baseline(case, budget_s: float = 15.0):
                        "BLAS limited to 1 thread)" % (done, cfg.B, cfg.name, cfg.L, el))
 
 
-def measure(ci: int, steps: int, warmup: int, score_launches: int):
+def measure(ci: int, steps: int, warmup: int, score_launches: int, detail: bool = False):
     import torch
     from fp4_kv_cache_score_amd import synth
     from fp4_kv_cache_score_amd.configs import CONFIGS, algorithmic_bytes
@@ -192,9 +263,27 @@ def measure(ci: int, steps: int, warmup: int, score_launches: int):
     per_launch = cfg.B * cfg.M * cfg.HI * cfg.DI + cfg.B * (cfg.HI * cfg.DI + cfg.HI * 4)
     log("%s: scan kernel mean %.3f ms (min %.3f) per launch" % (cfg.name, k_ms, k_min))
     res = dict(cfg=cfg, case=case, ms=ms, wall=wall, bytes=ab, k_ms=k_ms, per_launch=per_launch)
+    if detail:
+        dc.prepare_decode(idx_for_reuse=False)
+        res["per_layer_ms"] = per_layer_ms(dc, max(5, steps // 2))
+        res["cold_ms"] = cold_step_ms(dc, max(10, steps // 2))
+        res["all_full_ms"] = all_full_ms(dc, max(5, steps // 2), 2)
+        log("%s: per layer %s ms; MALL-cold step %.3f ms; all-Full schedule %.3f ms" % (
+            cfg.name, ["%.4f" % x for x in res["per_layer_ms"]], res["cold_ms"], res["all_full_ms"]))
     del dc
     torch.cuda.empty_cache()
     return res
+
+
+def step_detail(r) -> dict:
+    """Per-layer, MALL-cold and all-Full figures of a decode workload."""
+    if "per_layer_ms" not in r:
+        return {}
+    B = r["cfg"].B
+    return dict(per_layer_ms=r["per_layer_ms"],
+                cold_ms_per_step=r["cold_ms"], cold_query_tokens_per_s=B / (r["cold_ms"] * 1e-3),
+                all_full_ms_per_step=r["all_full_ms"],
+                all_full_query_tokens_per_s=B / (r["all_full_ms"] * 1e-3))
 
 
 def main():
@@ -210,6 +299,8 @@ def main():
     ap.add_argument("--score-launches", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only time --steps decode steps of --config (for a counter pass)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run a 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -234,7 +325,17 @@ def main():
         del src, dst
         log("copy calibration: 3 x 1 GiB device copies done")
 
-    head = measure(args.config, args.steps, args.warmup, args.score_launches)
+    if args.step_only:   # a counter pass over decode steps alone
+        from fp4_kv_cache_score_amd import synth
+        from fp4_kv_cache_score_amd.configs import CONFIGS
+        from fp4_kv_cache_score_amd.device import DeviceCase
+        dc = DeviceCase(synth.make_case(CONFIGS[args.config]))
+        ms, _ = time_decode(dc, args.steps, args.warmup)
+        print(json.dumps({"workload": CONFIGS[args.config].name, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": ms}), flush=True)
+        return
+
+    head = measure(args.config, args.steps, args.warmup, args.score_launches, detail=True)
     cfg = head["cfg"]
     value = cfg.B / (head["ms"] * 1e-3)
     achieved = head["per_launch"] / (head["k_ms"] * 1e-3) / 1e9
@@ -244,7 +345,7 @@ def main():
     for ci in args.extra:
         if ci == args.config:
             continue
-        r = measure(ci, args.steps, args.warmup, args.score_launches)
+        r = measure(ci, args.steps, args.warmup, args.score_launches, detail=ci in (1, 2))
         c = r["cfg"]
         extra[c.name] = dict(
             query_tokens_per_s=c.B / (r["ms"] * 1e-3), ms_per_step=r["ms"],
@@ -253,11 +354,13 @@ def main():
             algorithmic_bytes_per_step=r["bytes"]["total"],
             scan_kernel_ms=r["k_ms"],
             scan_kernel_gbs=r["per_launch"] / (r["k_ms"] * 1e-3) / 1e9)
+        extra[c.name].update(step_detail(r))
         del r
     for ci in args.prefill:
         r = measure_prefill(ci, max(3, args.steps // 5), 2)
         extra[r.pop("workload")] = r
         log("prefill: %.3f ms/step %s" % (r["ms_per_step"], r["stage_ms"]))
+    extra[cfg.name] = step_detail(head)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head["case"], args.cpu_budget)
