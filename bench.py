@@ -275,6 +275,50 @@ def measure(ci: int, steps: int, warmup: int, score_launches: int, detail: bool 
     return res
 
 
+def measure_append(ci: int, launches: int = 10):
+    """Write side at a decode workload's pool shape: a bulk append of 4096 new
+    entries per sequence (GB/s of fp32 inputs read + encoded bytes written), one
+    new entry per sequence (latency), and 4096 window rows per sequence."""
+    import torch
+    from fp4_kv_cache_score_amd import _lib as C
+    from fp4_kv_cache_score_amd.configs import CONFIGS
+    cfg = CONFIGS[ci]
+    B, M, T = cfg.B, cfg.M, 4096
+    lat = torch.zeros((B, M, cfg.D // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((B, M, cfg.D // 32), dtype=torch.uint8, device="cuda")
+    key = torch.zeros((B, M, cfg.HI, cfg.DI), dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(1)
+    xl = torch.randn((B, T, cfg.D), device="cuda", generator=g)
+    xk = torch.randn((B, T, cfg.HI, cfg.DI), device="cuda", generator=g)
+    slot = torch.arange(T, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
+    ring = torch.zeros((B, cfg.W, cfg.D), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(launches):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / launches
+
+    bulk = timed(lambda: C.csa2_pool_append(lat, sc, key, B, M, xl, xk, slot, T, stream))
+    one = timed(lambda: C.csa2_pool_append(lat, sc, key, B, M, xl, xk, slot, 1, stream))
+    win = timed(lambda: C.csa2_swa_append(ring, B, cfg.W, xl, 0, T, stream))
+    per_entry = cfg.D * 4 + cfg.HI * cfg.DI * 4 + 4 + cfg.D // 2 + cfg.D // 32 + cfg.HI * cfg.DI
+    bulk_bytes = B * T * per_entry
+    win_bytes = B * cfg.W * cfg.D * 5        # only the last W rows are encoded
+    return dict(entries=B * T, bulk_ms=bulk, bulk_gbs=bulk_bytes / (bulk * 1e-3) / 1e9,
+                bulk_frac_of_peak=bulk_bytes / (bulk * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                one_entry_per_sequence_us=one * 1e3, window_rows=B * T,
+                window_ms=win, window_gbs=win_bytes / (win * 1e-3) / 1e9)
+
+
 def step_detail(r) -> dict:
     """Per-layer, MALL-cold and all-Full figures of a decode workload."""
     if "per_layer_ms" not in r:
@@ -361,6 +405,10 @@ def main():
         extra[r.pop("workload")] = r
         log("prefill: %.3f ms/step %s" % (r["ms_per_step"], r["stage_ms"]))
     extra[cfg.name] = step_detail(head)
+    ap_res = measure_append(args.config)
+    extra["pool_append_" + cfg.name] = ap_res
+    log("pool append: %.1f GB/s bulk, %.1f us one entry per sequence" % (
+        ap_res["bulk_gbs"], ap_res["one_entry_per_sequence_us"]))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head["case"], args.cpu_budget)

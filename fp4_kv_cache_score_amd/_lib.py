@@ -23,6 +23,7 @@ CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
 CSA2_OP_TOPK, CSA2_OP_SPARSE_ATTN, CSA2_OP_SWA_MERGE, CSA2_OP_DECODE_LAYERS = 0, 1, 2, 3
 
 EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
+           "csa2_pool_append", "csa2_swa_append",
            "csa2_decode_layers", "csa2_workspace_bytes", "csa2_status_string",
            "csa2_version")
 
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.csa2_decode_layers.argtypes = [POINTER(csa2_pool), POINTER(csa2_layer), c_int32,
                                          c_int32, c_int32, c_int32, c_int32, POINTER(c_int32),
                                          c_void_p, c_size_t, c_void_p]
+        L.csa2_pool_append.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                       c_void_p, c_void_p, c_int32, c_void_p]
+        L.csa2_swa_append.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_int64, c_int32,
+                                      c_void_p]
         L.csa2_workspace_bytes.argtypes = [c_int, c_int32, c_int32, c_int32, c_int32, c_int32,
                                            c_int32, c_int32]
         L.csa2_workspace_bytes.restype = c_size_t
@@ -75,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_version.argtypes = []
         L.csa2_version.restype = c_char_p
         for fn in ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
-                   "csa2_decode_layers"):
+                   "csa2_decode_layers", "csa2_pool_append", "csa2_swa_append"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -141,6 +146,19 @@ def csa2_sparse_attn(pool: csa2_pool, q, Q: int, H: int, idx, K: int, o, lse, ws
     st = lib().csa2_sparse_attn(ctypes.byref(pool), _p(q), Q, H, _p(idx), K, _p(o), _p(lse),
                                 _p(ws), ws_bytes, _s(stream))
     return _check("csa2_sparse_attn", st, raise_on_error)
+
+
+def csa2_pool_append(latent, scale, idx_key, B: int, M: int, x_latent, x_key, slot, T: int,
+                     stream=None, raise_on_error=True) -> int:
+    st = lib().csa2_pool_append(_p(latent), _p(scale), _p(idx_key), B, M, _p(x_latent),
+                                _p(x_key), _p(slot), T, _s(stream))
+    return _check("csa2_pool_append", st, raise_on_error)
+
+
+def csa2_swa_append(swa, B: int, W: int, x, pos0: int, T: int, stream=None,
+                    raise_on_error=True) -> int:
+    st = lib().csa2_swa_append(_p(swa), B, W, _p(x), pos0, T, _s(stream))
+    return _check("csa2_swa_append", st, raise_on_error)
 
 
 def csa2_swa_merge(q, B: int, Q: int, H: int, D: int, swa, W: int, o, lse, ws,

@@ -378,4 +378,25 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
   return CSA2_OK;
 }
 
+csa2_status csa2_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key, int32_t B,
+                             int32_t M, const float* x_latent, const float* x_key,
+                             const int32_t* slot, int32_t T, hipStream_t stream) {
+  if (!latent || !scale || !idx_key || !x_latent || !x_key || !slot) return CSA2_ERR_NULL;
+  if (B <= 0 || M <= 0 || T < 0) return CSA2_ERR_SHAPE;
+  if (!al16(x_latent) || !al16(x_key) || !al4(slot) || ((uintptr_t)latent & 7u) ||
+      ((uintptr_t)idx_key & 7u))
+    return CSA2_ERR_ALIGN;
+  if (T == 0) return CSA2_OK;
+  return hip_status(launch_pool_append(latent, scale, idx_key, B, M, x_latent, x_key, slot, T, stream));
+}
+
+csa2_status csa2_swa_append(uint8_t* swa, int32_t B, int32_t W, const float* x, int64_t pos0,
+                            int32_t T, hipStream_t stream) {
+  if (!swa || !x) return CSA2_ERR_NULL;
+  if (B <= 0 || W <= 0 || T < 0 || pos0 < 0) return CSA2_ERR_SHAPE;
+  if (!al16(x) || ((uintptr_t)swa & 7u)) return CSA2_ERR_ALIGN;
+  if (T == 0) return CSA2_OK;
+  return hip_status(launch_window_append(swa, B, W, x, pos0, T, stream));
+}
+
 }  // extern "C"

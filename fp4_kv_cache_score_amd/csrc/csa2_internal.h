@@ -171,6 +171,14 @@ inline AttnWs attn_ws_carve(void* ws, int64_t rows, int64_t chunks) {
   return w;
 }
 
+// Write side: new pool entries (slot outside [0, M): skipped) and new window
+// rows into a ring of W rows (only the last W of T tokens are written).
+hipError_t launch_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key, int32_t B,
+                              int32_t M, const float* x_lat, const float* x_key, const int32_t* slot,
+                              int32_t T, hipStream_t s);
+hipError_t launch_window_append(uint8_t* swa, int32_t B, int32_t W, const float* x, int64_t pos0,
+                                int32_t T, hipStream_t s);
+
 // Chunked prefill (Q > 1 query tokens per sequence), matrix-core kernels.
 // Scores of every pool entry for every query (no candidate list, no
 // histogram); invisible entries get -inf.

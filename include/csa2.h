@@ -201,6 +201,43 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers,
                                int32_t W, int32_t* src_layer, void* ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/* New pool entries, encoded into the stored formats in place: the write side
+ * of a Full layer, which generates the global KV and the index data that
+ * later layers reuse, stored in FP4 ("... Cuts KV Cache by 437x", paragraphs
+ * on the three operating modes and FP4 quantisation).
+ * Reading (the pages give no encoding rule): each latent row becomes MXFP4 -
+ * per block of 32 elements an E8M0 scale 2^s, s = floor(log2(amax)) - 2
+ * clamped to [-127, 127] (0 for an all-zero block), elements divided by it
+ * and rounded to the nearest E2M1 value, ties to the even code, saturating at
+ * 6, signs kept; element 2i in the low nibble of byte i.  Each index key row
+ * becomes E4M3, clamped to +-448, nearest value, ties to the even code.
+ *   latent, scale, idx_key  the pool arrays [B][M][256], [B][M][16],
+ *                           [B][M][8][64] (written in place)
+ *   x_latent  [B][T][512] float;  x_key [B][T][8][64] float (finite)
+ *   slot      [B][T] int32: entry number receiving row t of sequence b;
+ *             rows whose slot is outside [0, M) are skipped.  Two rows of one
+ *             sequence naming the same slot is a caller error (race).
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (B, M <= 0, T < 0), CSA2_ERR_ALIGN
+ * (x_latent, x_key not 16-byte aligned, pool arrays not 8-byte aligned).
+ * T == 0 returns CSA2_OK without a launch. */
+csa2_status csa2_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key,
+                             int32_t B, int32_t M, const float* x_latent,
+                             const float* x_key, const int32_t* slot, int32_t T,
+                             hipStream_t stream);
+
+/* New tokens into the FP8 sliding window ("... Cuts KV Cache by 437x",
+ * paragraphs on sliding window attention and FP8 storage), kept as a ring of
+ * W rows per sequence: token position p lives in row p mod W, so the ring
+ * always holds the newest W tokens (their order does not change the window
+ * attention, one softmax over the set).  Encoding: E4M3 as for index keys.
+ *   swa   [B][W][512] E4M3 ring, written in place
+ *   x     [B][T][512] float: tokens pos0 .. pos0+T-1 (only the last W of
+ *         them are written when T > W)
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (B, W <= 0, T < 0, pos0 < 0),
+ * CSA2_ERR_ALIGN (x not 16-byte aligned, swa not 8-byte aligned). */
+csa2_status csa2_swa_append(uint8_t* swa, int32_t B, int32_t W, const float* x,
+                            int64_t pos0, int32_t T, hipStream_t stream);
+
 /* Workspace bytes needed by an entry point (op = CSA2_OP_*).  Arguments that
  * an op does not use are ignored.  For CSA2_OP_TOPK, B is the row count R and
  * M the row length N.  Returns 0 for an unknown op or bad sizes. */

@@ -131,6 +131,32 @@ def test_attention_argument_errors():
     assert h() == C.CSA2_ERR_WORKSPACE
 
 
+def test_append_argument_errors():
+    # every case returns before any HIP call, so fake aligned addresses are fine
+    f = lambda **kw: C.csa2_pool_append(kw.get("lat", A), kw.get("sc", A), kw.get("key", A),
+                                        kw.get("B", 2), kw.get("M", 100), kw.get("xl", A),
+                                        kw.get("xk", A), kw.get("slot", A), kw.get("T", 0), 0,
+                                        raise_on_error=False)
+    assert f() == C.CSA2_OK                     # T == 0: nothing to do, no launch
+    assert f(lat=None) == C.CSA2_ERR_NULL
+    assert f(slot=None) == C.CSA2_ERR_NULL
+    assert f(B=0) == C.CSA2_ERR_SHAPE
+    assert f(M=0) == C.CSA2_ERR_SHAPE
+    assert f(T=-1) == C.CSA2_ERR_SHAPE
+    assert f(xl=A + 4) == C.CSA2_ERR_ALIGN
+    assert f(key=A + 4) == C.CSA2_ERR_ALIGN
+    g = lambda **kw: C.csa2_swa_append(kw.get("swa", A), kw.get("B", 2), kw.get("W", 128),
+                                       kw.get("x", A), kw.get("pos0", 0), kw.get("T", 0), 0,
+                                       raise_on_error=False)
+    assert g() == C.CSA2_OK
+    assert g(x=None) == C.CSA2_ERR_NULL
+    assert g(W=0) == C.CSA2_ERR_SHAPE
+    assert g(pos0=-1) == C.CSA2_ERR_SHAPE
+    assert g(T=-2) == C.CSA2_ERR_SHAPE
+    assert g(x=A + 8) == C.CSA2_ERR_ALIGN
+    assert g(swa=A + 4) == C.CSA2_ERR_ALIGN
+
+
 def _layer(mode, **kw):
     d = dict(q_idx=A, w_idx=A, q=A, swa=A, o=A, lse=A, idx_out=A2)
     d.update(kw)
