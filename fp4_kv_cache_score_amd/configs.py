@@ -35,6 +35,7 @@ class CaseConfig:
     Q: int = 1                  # query tokens per sequence (1: decode)
     ratio: int = 4              # tokens per compressed pool entry
     causal: bool = False        # prefill: restrict entries to those visible
+    chunk_pos: int = -1         # prefill: first token's position (< 0: the newest Q tokens)
     plant_frac: float = 0.01    # share of planted (scaled) pool entries
     plant_mult: float = 3.0     # their pre-quantisation multiplier
 
@@ -46,9 +47,12 @@ class CaseConfig:
     def pos0(self) -> int:
         """Position of the first query token of the chunk (-1: no causal limit).
 
-        The chunk is the newest Q tokens of a context of ratio*M tokens.
+        The chunk starts at chunk_pos when that is given; otherwise it is the
+        newest Q tokens of a context of ratio*M tokens.
         """
-        return self.ratio * self.M - self.Q if self.causal else -1
+        if not self.causal:
+            return -1
+        return self.chunk_pos if self.chunk_pos >= 0 else self.ratio * self.M - self.Q
 
     def scaled(self, **kw) -> "CaseConfig":
         d = dict(self.__dict__)

@@ -39,7 +39,11 @@ Readings where the pages are silent (each is a choice, not a quotation):
 * Chunked prefill: query t of a chunk of Q sits at position pos0 + t; pool
   entry j covers tokens [ratio*j, ratio*j + ratio - 1] and is visible once its
   last token is, so the query sees the first min(M, (pos0+t+1)//ratio) entries;
-  its window is rows t .. t+W-1 of a [Q+W-1] buffer of the newest tokens.
+  its window is rows t .. t+W-1 of a [Q+W-1] buffer of the newest tokens,
+  of which rows before the context's first token do not exist (a first
+  chunk).  A chunk runs the whole layer schedule token by token; it builds no
+  candidate pool (that serves one decode token's indexing cost, while a
+  chunk's scan of the pool is shared by its Q queries).
 
 Exactness: E4M3 values are integer multiples of 2^-9 with magnitude at most
 448, so each product is a multiple of 2^-18 below 2^18 and any sum of 64 of
@@ -271,3 +275,70 @@ def prefill_query(latent, scale, idx_key, q_idx_t, w_t, q_t, swa, t: int,
     keys = gather_keys(latent, scale, idx, swa[t:t + W])
     o, lse = attend(q_t, keys)
     return dict(idx=idx, o=o, lse=lse, gap=gap, vis=vis, scores=s)
+
+
+# ---------------------------------------------------------------------------
+# Causal chunked prefill through the layer schedule (one sequence)
+# ---------------------------------------------------------------------------
+
+def window_first_row(t: int, W: int, pos0: int) -> int:
+    """First of query t's window rows t .. t+W-1 that holds a token.
+
+    Row t + r of the chunk's [Q+W-1] window buffer is token position
+    pos0 + t - (W - 1) + r; positions below 0 do not exist (the start of the
+    context).  pos0 < 0 means no causal limit: every row is a token.
+    """
+    if pos0 < 0:
+        return 0
+    return max(0, (W - 1) - (pos0 + t))
+
+
+def prefill_layers(latent, scale, idx_key, layers, Q: int, pos0: int, ratio: int,
+                   K: int, W: int):
+    """The static mode schedule for a chunk of Q query tokens of one sequence.
+
+    Every layer does what it does in decode, once per query token, with the
+    causal limits of that token: query t at position pos0 + t selects among
+    the first visible_entries(M, pos0 + t, ratio) pool entries (all M when
+    pos0 < 0) and attends to its window rows from window_first_row on.  Full
+    and Reindex layers score the visible entries with their own indexer and
+    select Top-K; a Reuse layer takes, token by token, the indices of the most
+    recent Full or Reindex layer.  (No candidate pool: see the hierarchical
+    reading, which concerns one decode token's indexing cost.)
+
+    layers: list of dicts with mode, q_idx [Q][HI][DI], w_idx [Q][HI],
+    q [Q][H][D] bf16 bits, swa [Q+W-1][D] E4M3.
+    Returns per layer a dict: idx [Q][K] (ascending, -1 padded), o [Q][H][D],
+    lse [Q][H], gap [Q] (None where no (K+1)-th entry), vis [Q].
+    """
+    M = idx_key.shape[0]
+    vis = np.array([M if pos0 < 0 else visible_entries(M, pos0 + t, ratio) for t in range(Q)])
+    out = []
+    src = None
+    for ell, L in enumerate(layers):
+        mode = L["mode"]
+        rec = dict(mode=mode, vis=vis, gap=[None] * Q)
+        if mode in (FULL, REINDEX):
+            if mode == REINDEX and src is None:
+                raise ValueError("layer %d: Reindex before any Full layer" % ell)
+            idx = np.full((Q, K), -1, np.int64)
+            for t in range(Q):
+                s = index_scores(idx_key, L["q_idx"][t], L["w_idx"][t], rows=np.arange(vis[t]))
+                idx[t], rec["gap"][t] = topk(s, K)
+            src = idx
+        elif mode == REUSE:
+            if src is None:
+                raise ValueError("layer %d: Reuse before any Full layer" % ell)
+            idx = src.copy()
+        else:
+            raise ValueError("unknown mode %r" % (mode,))
+        H, D = np.asarray(L["q"]).shape[1:]
+        o = np.zeros((Q, H, D))
+        lse = np.zeros((Q, H))
+        for t in range(Q):
+            r0 = window_first_row(t, W, pos0)
+            keys = gather_keys(latent, scale, idx[t], L["swa"][t + r0:t + W])
+            o[t], lse[t] = attend(L["q"][t], keys)
+        rec.update(idx=idx, o=o, lse=lse)
+        out.append(rec)
+    return out
