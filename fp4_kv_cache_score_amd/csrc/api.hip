@@ -90,6 +90,41 @@ csa2_status zero_hist_counters(const TopkWs& t, int64_t R, hipStream_t s) {
   return hip_status(launch_fill_zero(t.hist, words, s));
 }
 
+// Mode schedule and per-layer arguments of a layer array (decode or prefill).
+csa2_status check_layers(const csa2_layer* layers, int32_t L, int32_t W) {
+  if (layers[0].mode != CSA2_FULL) return CSA2_ERR_SCHEDULE;
+  for (int32_t l = 0; l < L; ++l) {
+    const csa2_layer& y = layers[l];
+    if (y.mode != CSA2_FULL && y.mode != CSA2_REINDEX && y.mode != CSA2_REUSE)
+      return CSA2_ERR_SCHEDULE;
+    if (!y.q || !y.o || !y.lse) return CSA2_ERR_NULL;
+    if (W > 0 && !y.swa) return CSA2_ERR_NULL;
+    if (y.mode != CSA2_REUSE && (!y.q_idx || !y.w_idx || !y.idx_out)) return CSA2_ERR_NULL;
+    if (!al16(y.q) || !al16(y.o) || !al4(y.lse) || (y.swa && !al16(y.swa)) ||
+        (y.q_idx && y.mode != CSA2_REUSE && !al16(y.q_idx)) ||
+        (y.w_idx && y.mode != CSA2_REUSE && !al4(y.w_idx)) || (y.idx_out && !al4(y.idx_out)))
+      return CSA2_ERR_ALIGN;
+  }
+  return CSA2_OK;
+}
+
+// prefill_layers workspace: scores [B*Q][M] (a chunk uses a row length N <= M)
+// | visible counts [B*Q] | multi-work-group Top-K scratch when the rows are
+// few and long.
+size_t prefill_ws_bytes(int64_t B, int64_t Q, int64_t M, int64_t K) {
+  const int64_t R = B * Q;
+  return align256(R * M * 4) + align256(R * 4) + (topk_multi_wg(R, M) ? topk_ws_bytes(R, M, K) : 0);
+}
+
+// Entries that some query of a chunk can see, rounded up to a multiple of 4
+// (at most M) so that score rows stay 16-byte aligned: the score row length.
+int64_t prefill_scan_entries(int64_t M, int32_t Q, int64_t pos0, int32_t ratio) {
+  int64_t v = pos0 < 0 ? M : (pos0 + Q) / ratio;
+  if (v > M) v = M;
+  v = (v + 3) & ~int64_t(3);
+  return v < M ? v : M;
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,6 +157,11 @@ size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K, 
     case CSA2_OP_SWA_MERGE:
       if (W < 0 || W > kMaxW || H != kH) return 0;
       return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, W > 0 ? attn_chunks(0, W) : 1);
+    case CSA2_OP_PREFILL_LAYERS:
+      if (M <= 0 || K <= 0 || K > kMaxK || W < 0 || W > kMaxW || H != kH ||
+          (int64_t)B * Q > kMaxRows)
+        return 0;
+      return prefill_ws_bytes(B, Q, M, K);
     case CSA2_OP_DECODE_LAYERS:
       if (M <= 0 || K <= 0 || K > kMaxK || P < 0 || P > kMaxK || (P > 0 && P < K) ||
           W < 0 || W > kMaxW || H != kH)
@@ -144,8 +184,9 @@ csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx, const 
     return CSA2_ERR_ALIGN;
   if (Q > 1 && !cand) {   // chunked prefill: matrix-core contraction
     if (hist) return CSA2_ERR_SHAPE;
-    return hip_status(launch_prefill_score(pool->idx_key, pool->B, pool->M, q_idx, w_idx, Q, pos0,
-                                           pos0 >= 0 ? ratio : 1, scores, stream));
+    return hip_status(launch_prefill_score(pool->idx_key, pool->B, pool->M, pool->M, q_idx, w_idx,
+                                           Q, pos0, pos0 >= 0 ? ratio : 1, scores, nullptr,
+                                           stream));
   }
   const int32_t N = cand ? P : pool->M;
   return hip_status(launch_index_score(pool->idx_key, pool->B, pool->M, q_idx, w_idx, Q, pos0,
@@ -205,6 +246,7 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   a.swa = nullptr;
   a.W = 0;
   a.swa_rows = 0;
+  a.pos0 = -1;
   a.q = q;
   a.Q = Q;
   a.rows = (int32_t)rows;
@@ -239,6 +281,7 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   a.swa = swa;
   a.W = W;
   a.swa_rows = Q + W - 1;
+  a.pos0 = -1;
   a.q = q;
   a.Q = Q;
   a.rows = (int32_t)rows;
@@ -259,20 +302,8 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
   if (L <= 0 || H != kH || K <= 0 || K > kMaxK || P < 0 || P > kMaxK || (P > 0 && P < K) ||
       W < 0 || W > kMaxW || pool->B > kMaxRows)
     return CSA2_ERR_SHAPE;
-  // Schedule and per-layer arguments.
-  if (layers[0].mode != CSA2_FULL) return CSA2_ERR_SCHEDULE;
-  for (int32_t l = 0; l < L; ++l) {
-    const csa2_layer& y = layers[l];
-    if (y.mode != CSA2_FULL && y.mode != CSA2_REINDEX && y.mode != CSA2_REUSE)
-      return CSA2_ERR_SCHEDULE;
-    if (!y.q || !y.o || !y.lse) return CSA2_ERR_NULL;
-    if (W > 0 && !y.swa) return CSA2_ERR_NULL;
-    if (y.mode != CSA2_REUSE && (!y.q_idx || !y.w_idx || !y.idx_out)) return CSA2_ERR_NULL;
-    if (!al16(y.q) || !al16(y.o) || !al4(y.lse) || (y.swa && !al16(y.swa)) ||
-        (y.q_idx && y.mode != CSA2_REUSE && !al16(y.q_idx)) ||
-        (y.w_idx && y.mode != CSA2_REUSE && !al4(y.w_idx)) || (y.idx_out && !al4(y.idx_out)))
-      return CSA2_ERR_ALIGN;
-  }
+  st = check_layers(layers, L, W);
+  if (st != CSA2_OK) return st;
   const int64_t B = pool->B, M = pool->M;
   const size_t need = decode_ws_bytes(B, M, K, P, W);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
@@ -363,6 +394,7 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     a.swa = y.swa;
     a.W = W;
     a.swa_rows = W;
+    a.pos0 = -1;
     a.q = y.q;
     a.Q = 1;
     a.rows = (int32_t)B;
@@ -373,6 +405,91 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     a.o = y.o;
     a.lse = y.lse;
     st = hip_status(launch_attn_partial(a, plan, stream));
+    if (st != CSA2_OK) return st;
+  }
+  return CSA2_OK;
+}
+
+csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
+                                int32_t Q, int64_t pos0, int32_t ratio, int32_t H, int32_t K,
+                                int32_t W, int32_t* src_layer, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  csa2_status st = check_pool(pool);
+  if (st != CSA2_OK) return st;
+  if (!layers) return CSA2_ERR_NULL;
+  if (L <= 0 || Q <= 0 || H != kH || K <= 0 || K > kMaxK || W < 0 || W > kMaxW ||
+      (int64_t)pool->B * Q > kMaxRows || (pos0 >= 0 && ratio <= 0))
+    return CSA2_ERR_SHAPE;
+  st = check_layers(layers, L, W);
+  if (st != CSA2_OK) return st;
+  const int64_t B = pool->B, M = pool->M, R = B * Q;
+  if (!ws || ws_bytes < prefill_ws_bytes(B, Q, M, K)) return CSA2_ERR_WORKSPACE;
+  if (!al16(ws)) return CSA2_ERR_ALIGN;
+
+  // A chunk scores only the entries its last query can see (early chunks of
+  // a growing pool see a prefix); none visible: no index work at all.
+  const int64_t N = prefill_scan_entries(M, Q, pos0, ratio);
+  char* p = (char*)ws;
+  float* scores = (float*)p;
+  p += align256(R * M * 4);
+  int32_t* n_valid = (int32_t*)p;
+  p += align256(R * 4);
+  const bool big = N > 0 && topk_multi_wg(R, N);
+  const TopkWs t = big ? topk_ws_carve(p, R, N, K) : TopkWs{};
+
+  const int32_t* cur = nullptr;
+  int32_t cur_layer = -1;
+  for (int32_t l = 0; l < L; ++l) {
+    const csa2_layer& y = layers[l];
+    if (y.mode == CSA2_FULL || y.mode == CSA2_REINDEX) {
+      if (N == 0) {
+        st = hip_status(launch_fill_u32((uint32_t*)y.idx_out, R * K, 0xFFFFFFFFu, stream));
+      } else {
+        st = hip_status(launch_prefill_score(pool->idx_key, (int32_t)B, M, (int32_t)N, y.q_idx,
+                                             y.w_idx, Q, pos0, pos0 >= 0 ? ratio : 1, scores,
+                                             n_valid, stream));
+        if (st != CSA2_OK) return st;
+        if (!big) {
+          st = hip_status(launch_topk_rows(scores, (int32_t)R, (int32_t)N, n_valid, (int32_t)N, K,
+                                           nullptr, false, nullptr, y.idx_out, stream));
+        } else {
+          st = zero_hist_counters(t, R, stream);
+          if (st != CSA2_OK) return st;
+          st = hip_status(launch_topk_hist(scores, (int32_t)R, (int32_t)N, n_valid, (int32_t)N,
+                                           t.hist, stream));
+          if (st != CSA2_OK) return st;
+          st = hip_status(launch_topk_select(scores, (int32_t)R, (int32_t)N, n_valid, (int32_t)N,
+                                             nullptr, K, y.idx_out, t, false, stream));
+        }
+      }
+      if (st != CSA2_OK) return st;
+      cur = y.idx_out;
+      cur_layer = l;
+    } else if (y.idx_out && y.idx_out != cur) {  // Reuse that asks for its indices
+      st = hip_status(launch_copy_i32(y.idx_out, cur, R * K, stream));
+      if (st != CSA2_OK) return st;
+    }
+    if (src_layer) src_layer[l] = cur_layer;
+
+    // the selected entries and the window rows in one pass (one softmax)
+    AttnArgs a{};
+    a.latent = pool->latent;
+    a.scale = pool->scale;
+    a.M = M;
+    a.idx = cur;
+    a.K = N > 0 ? K : 0;
+    a.swa = y.swa;
+    a.W = W;
+    a.swa_rows = Q + W - 1;
+    a.pos0 = pos0;
+    a.q = y.q;
+    a.Q = Q;
+    a.rows = (int32_t)R;
+    a.o = y.o;
+    a.lse = y.lse;
+    a.o_in = nullptr;
+    a.lse_in = nullptr;
+    st = hip_status(launch_prefill_attn(a, nullptr, nullptr, stream));
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;

@@ -136,6 +136,9 @@ struct AttnArgs {
   const uint8_t* swa;     // [B][swa_rows][kD]
   int32_t W;
   int32_t swa_rows;       // rows per sequence in swa (Q + W - 1)
+  int64_t pos0;           // prefill: position of query 0; window row t + r of query t is
+                          // position pos0 + t - (W - 1) + r, rows before 0 are skipped
+                          // (< 0: every row is a token; the decode kernels ignore it)
   const uint16_t* q;      // [rows][kH][kD] bf16
   int32_t Q;              // query rows per sequence
   int32_t rows;           // B * Q
@@ -180,17 +183,20 @@ hipError_t launch_window_append(uint8_t* swa, int32_t B, int32_t W, const float*
                                 int32_t T, hipStream_t s);
 
 // Chunked prefill (Q > 1 query tokens per sequence), matrix-core kernels.
-// Scores of every pool entry for every query (no candidate list, no
-// histogram); invisible entries get -inf.
-hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
-                                const float* w_idx, int32_t Q, int64_t pos0, int32_t ratio,
-                                float* scores, hipStream_t s);
+// Scores [B][Q][N] of pool entries 0 .. N-1 (N <= M) for every query (no
+// candidate list, no histogram); invisible entries get -inf.  n_valid
+// (optional, [B][Q]) receives each query's count of visible entries.
+hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_t N,
+                                const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
+                                int32_t ratio, float* scores, int32_t* n_valid, hipStream_t s);
 // One work-group per query row over its K selected entries and W window rows;
 // writes a.o / a.lse, merged with (o_in, lse_in) when lse_in is given (they
 // may alias a.o / a.lse).
 hipError_t launch_prefill_attn(const AttnArgs& a, const float* o_in, const float* lse_in,
                                hipStream_t s);
 
+// Fill n 32-bit words with v.
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // Copy n int32 (Reuse layers that ask for their indices).
 hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 // out[r][i] = scores[r][idx[r][i]], -inf where idx is -1 (idx in [-1, N)).

@@ -57,10 +57,13 @@ __device__ __forceinline__ int64_t visible(int64_t pos0, int32_t t, int32_t rati
   return v < M ? v : M;
 }
 
+// Scores of entries 0 .. N-1 (N <= M; also the score row length) for every
+// query; n_valid (optional, [B][Q]) receives each query's visible count.
 __global__ __launch_bounds__(kSThreads, 2)
-void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
+void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
                      const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-                     int32_t Q, int64_t pos0, int32_t ratio, float* __restrict__ scores) {
+                     int32_t Q, int64_t pos0, int32_t ratio, float* __restrict__ scores,
+                     int32_t* __restrict__ n_valid) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[2][kSQ * kSRow];
   __shared__ __attribute__((aligned(16))) uint8_t ks[2][kSE * kSRow];
   __shared__ __attribute__((aligned(16))) float ws[kHI][kSQ];   // head weights, rows contiguous
@@ -76,13 +79,15 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
   const int we = wave >> 1;               // 64-entry half of the tile
   const uint8_t* qb = q_idx + (size_t)b * Q * kKeyRow;
   const uint8_t* kb = key + (size_t)b * (size_t)M * kKeyRow;
-  float* sb = scores + (size_t)b * Q * (size_t)M;
+  float* sb = scores + (size_t)b * Q * (size_t)N;
+  if (n_valid && blockIdx.x == 0 && tid < kSQ && q0 + tid < Q)
+    n_valid[(size_t)b * Q + q0 + tid] = (int32_t)visible(pos0, q0 + tid, ratio, M);
 
   const int qlast = (q0 + kSQ < Q ? q0 + kSQ : Q) - 1;
   if (e0 >= visible(pos0, qlast, ratio, M)) {   // no query of the tile sees these entries
     for (int i = tid; i < kSQ * kSE; i += kSThreads) {
       const int r = i / kSE, c = i - r * kSE;
-      if (q0 + r < Q && e0 + c < M) sb[(size_t)(q0 + r) * M + e0 + c] = -INFINITY;
+      if (q0 + r < Q && e0 + c < N) sb[(size_t)(q0 + r) * N + e0 + c] = -INFINITY;
     }
     return;
   }
@@ -94,7 +99,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
   if (tid < kSQ) vis_s[tid] = (int32_t)visible(pos0, q0 + tid, ratio, M);   // one division per row
 
   // staging: thread -> two (row, 16-byte part) pieces of each of Q and K.
-  // Rows past Q or M load the last row instead (never written out), so the
+  // Rows past Q or N load the last row instead (never written out), so the
   // loads are unconditional.
   u32x4 rq[2], rk[2];
   const uint8_t* qrow[2];
@@ -104,7 +109,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
     const int c = tid + i * kSThreads;
     const int row = c >> 2, part = c & 3;
     const int t = q0 + row < Q ? q0 + row : Q - 1;
-    const int64_t e = e0 + row < M ? e0 + row : M - 1;
+    const int64_t e = e0 + row < N ? e0 + row : N - 1;
     qrow[i] = qb + (size_t)t * kKeyRow + part * 16;
     krow[i] = kb + (size_t)e * kKeyRow + part * 16;
   }
@@ -212,7 +217,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
   // write: value v of block (r, c) is query row 8*(v/4) + 4*g + v%4, entry lr
   const int32_t ea = (int32_t)e0 + 64 * we + lr;     // entries of blocks c = 0, 1
   const int32_t eb = ea + 32;
-  const bool oka = ea < M, okb = eb < M;
+  const bool oka = ea < N, okb = eb < N;
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -220,7 +225,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M,
       const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
       if (q0 + tr >= Q) continue;
       const int32_t vis = vis_s[tr];
-      float* srow = sb + (size_t)(q0 + tr) * M;
+      float* srow = sb + (size_t)(q0 + tr) * N;
       if (oka) srow[ea] = ea < vis ? acc[r][0][v] : -INFINITY;
       if (okb) srow[eb] = eb < vis ? acc[r][1][v] : -INFINITY;
     }
@@ -259,6 +264,10 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t C, const float* __restrict__
   const int wave = tid >> 6;
   const int ln = lane & 15;        // MFMA column / A row
   const int lg = lane >> 4;        // MFMA k-group / output row group
+  // window rows t + wr with wr < wfirst are positions before the context's
+  // first token (a first chunk): never read, never keys
+  const int64_t wgap = a.pos0 >= 0 ? (int64_t)(a.W - 1) - (a.pos0 + t) : 0;
+  const int32_t wfirst = wgap > 0 ? (int32_t)wgap : 0;
 
   // q as A operands: head ln, dims 32 s + 8 lg .. +7, for k-steps s = 0..15
   bf16x8 qa[16];
@@ -298,7 +307,7 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t C, const float* __restrict__
         const int pr = tid + i * kAThreads;      // (row j, 16-byte segment)
         const int j = pr >> 5, seg = pr & 31;
         const int wr = wc * kAC + j;
-        if (wr < a.W)
+        if (wr < a.W && wr >= wfirst)
           r.v[i] = *reinterpret_cast<const u32x4*>(a.swa + ((size_t)b * a.swa_rows + t + wr) * kD + seg * 16);
       }
     }
@@ -337,7 +346,8 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t C, const float* __restrict__
       for (int i = 0; i < 8; ++i) {
         const int pr = tid + i * kAThreads;
         const int j = pr >> 5, seg = pr & 31;
-        const bool ok = wc * kAC + j < a.W;
+        const int wr = wc * kAC + j;
+        const bool ok = wr < a.W && wr >= wfirst;
         u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = o0;
         if (ok) {
           uint32_t w[8];
@@ -512,11 +522,13 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t C, const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
-                                const float* w_idx, int32_t Q, int64_t pos0, int32_t ratio,
-                                float* scores, hipStream_t s) {
-  const dim3 grid((unsigned)((M + kSE - 1) / kSE), (unsigned)((Q + kSQ - 1) / kSQ), (unsigned)B);
-  k_prefill_score<<<grid, dim3(kSThreads), 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, scores);
+hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_t N,
+                                const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
+                                int32_t ratio, float* scores, int32_t* n_valid, hipStream_t s) {
+  if (N <= 0 || N > M || Q <= 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((N + kSE - 1) / kSE), (unsigned)((Q + kSQ - 1) / kSQ), (unsigned)B);
+  k_prefill_score<<<grid, dim3(kSThreads), 0, s>>>(key, M, N, q_idx, w_idx, Q, pos0, ratio, scores,
+                                                   n_valid);
   return hipGetLastError();
 }
 

@@ -790,10 +790,10 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   for (uint32_t i = tot + tid; i < (uint32_t)K; i += kRowThreads) orow[i] = -1;
 }
 
-__global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t k = i; k < n; k += stride) p[k] = 0u;
+  for (int64_t k = i; k < n; k += stride) p[k] = v;
 }
 
 __global__ void k_copy_i32(int32_t* __restrict__ d, const int32_t* __restrict__ s, int64_t n) {
@@ -822,13 +822,15 @@ hipError_t launch_gather_scores(const float* scores, int32_t R, int64_t N, const
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t s) {
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  k_fill_zero<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n);
+  k_fill_u32<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n, v);
   return hipGetLastError();
 }
+
+hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t s) { return launch_fill_u32(p, n, 0u, s); }
 
 hipError_t launch_copy_i32(int32_t* d, const int32_t* src, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

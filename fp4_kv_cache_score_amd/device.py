@@ -182,6 +182,29 @@ class DeviceCase:
         cfg = self.cfg
         return self.pf_idx.view(cfg.B, cfg.Q, cfg.K), self.pf_o, self.pf_lse
 
+    # -- chunked prefill through the layer schedule -------------------------------
+    def prefill_layers_workspace_bytes(self) -> int:
+        cfg = self.cfg
+        return C.csa2_workspace_bytes(C.CSA2_OP_PREFILL_LAYERS, cfg.B, cfg.Q, cfg.M, cfg.K, 0,
+                                      cfg.W, cfg.H)
+
+    def prepare_prefill_layers(self, idx_for_reuse: bool = True):
+        nb = self.prefill_layers_workspace_bytes()
+        assert nb > 0
+        self._workspace(nb)
+        self._pf_structs = self.layer_structs(idx_for_reuse)
+
+    def prefill_layers(self, pos0: Optional[int] = None, stream=None):
+        """Every layer of the schedule over the chunk (csa2_prefill_layers); outputs
+        land in self.layers[l]["idx" / "o" / "lse"].  pos0 defaults to the config's."""
+        cfg = self.cfg
+        if getattr(self, "_pf_structs", None) is None:
+            self.prepare_prefill_layers()
+        _, self.src_layer = C.csa2_prefill_layers(
+            self.pool, self._pf_structs, cfg.Q, cfg.pos0 if pos0 is None else pos0, cfg.ratio,
+            cfg.H, cfg.K, cfg.W, self.ws, self.ws_bytes, stream)
+        return self.layers
+
     # -- results -----------------------------------------------------------------
     def results(self):
         out = []

@@ -64,7 +64,8 @@ enum {
   CSA2_OP_TOPK = 0,
   CSA2_OP_SPARSE_ATTN = 1,
   CSA2_OP_SWA_MERGE = 2,
-  CSA2_OP_DECODE_LAYERS = 3
+  CSA2_OP_DECODE_LAYERS = 3,
+  CSA2_OP_PREFILL_LAYERS = 4
 };
 
 /* The shared global KV pool: B sequences of M compressed entries each.
@@ -200,6 +201,47 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers,
                                int32_t L, int32_t H, int32_t K, int32_t P,
                                int32_t W, int32_t* src_layer, void* ws,
                                size_t ws_bytes, hipStream_t stream);
+
+/* One chunk of Q tokens per sequence (chunked prefill) through the same
+ * static per-layer mode schedule as csa2_decode_layers.  The pages name
+ * prefill as the cost that CSA2's index reuse cuts and give every layer its
+ * mode there as in decode ("... Cuts KV Cache by 437x", paragraphs on prefill
+ * cost and the three operating modes).  Per query token the layer does what
+ * it does in decode, within that token's causal limits: query t sits at
+ * position pos0 + t, sees the first min(M, (pos0 + t + 1) / ratio) pool
+ * entries (an entry is visible once its last token is), and attends to its
+ * window rows of positions max(0, pos0 + t - W + 1) .. pos0 + t.  Full and
+ * Reindex score the visible entries with their own indexer (a matrix-core
+ * contraction of the chunk's queries against the pool, as in
+ * csa2_index_score) and select Top-K (csa2_topk's rules; a token that sees
+ * fewer than K entries selects all of them, -1 padded); Reuse takes the
+ * indices of the most recent Full or Reindex layer, token by token.  Each
+ * layer's selected entries and window rows form one softmax in one pass.
+ * There is no candidate pool in prefill (reading: the chunk's Q queries
+ * share one pass over the keys, which is what the candidate pool saves a
+ * single decode token).  A chunk reads only the entries its last query can
+ * see, so successive chunks over a pool that grows by csa2_pool_append cost
+ * what they can see, not M.  The first layer must be Full.
+ *   layers     host array [L]; per layer (shapes per chunk):
+ *                q_idx [B][Q][HI][DI] E4M3, w_idx [B][Q][HI] float (Full /
+ *                Reindex), q [B][Q][H][D] bf16, o [B][Q][H][D] float,
+ *                lse [B][Q][H] float, idx_out [B][Q][K] int32 (required for
+ *                Full / Reindex; optional for Reuse, then a copy),
+ *                swa [B][Q+W-1][D] E4M3: row r holds position
+ *                pos0 - (W - 1) + r; rows at positions below 0 are not read.
+ *   Q          query tokens per sequence (B * Q <= 65535)
+ *   pos0       position of the chunk's first token; < 0: no causal limit
+ *              (every entry and every window row visible)
+ *   ratio      tokens per pool entry (>= 1 when pos0 >= 0)
+ *   K          1..16384;  W  0..4096
+ *   src_layer  NULL or host [L] output, as in csa2_decode_layers
+ *   ws         at least csa2_workspace_bytes(CSA2_OP_PREFILL_LAYERS, B, Q, M, K, 0, W, H)
+ * Errors: as csa2_decode_layers (CSA2_ERR_SCHEDULE when layer 0 is not Full
+ * or a mode is unknown). */
+csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
+                                int32_t L, int32_t Q, int64_t pos0, int32_t ratio,
+                                int32_t H, int32_t K, int32_t W, int32_t* src_layer,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* New pool entries, encoded into the stored formats in place: the write side
  * of a Full layer, which generates the global KV and the index data that

@@ -188,3 +188,38 @@ def test_decode_layers_schedule_and_argument_errors():
     assert run([_layer(F), _layer(RU, idx_out=None)]) == C.CSA2_ERR_WORKSPACE
     assert run([_layer(F)], ws=None, nb=need) == C.CSA2_ERR_WORKSPACE
     assert run([_layer(F)], pool=_pool(scale=None)) == C.CSA2_ERR_NULL
+
+
+def test_prefill_layers_schedule_and_argument_errors():
+    pool = _pool()
+    need = C.csa2_workspace_bytes(C.CSA2_OP_PREFILL_LAYERS, 2, 64, 1024, 64, 0, 128, 16)
+    assert need >= 2 * 64 * 1024 * 4
+    assert C.csa2_workspace_bytes(C.CSA2_OP_PREFILL_LAYERS, 2, 64, 1024, 64, 0, 128, 8) == 0
+    assert C.csa2_workspace_bytes(C.CSA2_OP_PREFILL_LAYERS, 2, 40000, 1024, 64, 0, 128, 16) == 0
+
+    def run(layers, Q=64, pos0=0, ratio=4, K=64, W=128, H=16, ws=A, nb=need - 1, pool=pool):
+        st, _ = C.csa2_prefill_layers(pool, layers, Q, pos0, ratio, H, K, W, ws, nb, 0,
+                                      raise_on_error=False)
+        return st
+
+    F, RI, RU = C.CSA2_FULL, C.CSA2_REINDEX, C.CSA2_REUSE
+    assert run([_layer(RI)]) == C.CSA2_ERR_SCHEDULE
+    assert run([_layer(RU), _layer(F)]) == C.CSA2_ERR_SCHEDULE
+    assert run([_layer(F), _layer(5)]) == C.CSA2_ERR_SCHEDULE
+    assert run([_layer(F, idx_out=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F), _layer(RI, w_idx=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F, swa=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F, lse=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F)], Q=0) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F)], Q=40000) == C.CSA2_ERR_SHAPE      # B * Q rows above the limit
+    assert run([_layer(F)], ratio=0) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F)], K=16385) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F)], H=8) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F)], W=-1) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F, o=A + 4)]) == C.CSA2_ERR_ALIGN
+    assert run([_layer(F)]) == C.CSA2_ERR_WORKSPACE
+    assert run([_layer(F)], ws=None, nb=need) == C.CSA2_ERR_WORKSPACE
+    assert run([_layer(F)], ws=A + 8, nb=need) == C.CSA2_ERR_ALIGN
+    assert run([_layer(F)], pool=_pool(M=0)) == C.CSA2_ERR_SHAPE
+    # no causal limit: ratio is not used
+    assert run([_layer(F)], pos0=-1, ratio=0) == C.CSA2_ERR_WORKSPACE
