@@ -179,46 +179,101 @@ def time_score_kernel(dc, launches: int):
     return float(np.mean(ms)), float(np.min(ms))
 
 
-def measure_prefill(ci: int, steps: int, warmup: int):
-    """Chunked prefill (Q tokens, one Full layer): step time and per-stage kernel times."""
+def _time_calls(fn, steps: int, warmup: int) -> float:
+    """Mean milliseconds of fn() on the current stream (HIP events around each call)."""
     import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def _prefill_flops(cfg, pos0: int):
+    t = np.arange(cfg.Q)
+    vis = np.minimum(cfg.M, (pos0 + t + 1) // cfg.ratio)
+    idx_flop = 2.0 * cfg.B * float(vis.sum()) * cfg.HI * cfg.DI
+    # S = q C^T and O = P C (P as bf16 hi + lo, two products) over the selected + window keys
+    keys = np.minimum(cfg.K, vis) + np.minimum(cfg.W, pos0 + t + 1)
+    attn_flop = 2.0 * cfg.B * cfg.H * cfg.D * float(keys.sum()) * 3
+    return idx_flop, attn_flop
+
+
+def measure_prefill(ci: int, steps: int, warmup: int):
+    """Chunked prefill: csa2_prefill_layers on the chunk of `ci` (one Full layer), its
+    stages, the unfused four-call chain, a 4-layer schedule, the first chunk of a
+    context, and a whole context prefilled chunk by chunk into a growing pool."""
+    import torch
+    from fp4_kv_cache_score_amd import _lib as C
     from fp4_kv_cache_score_amd import synth
-    from fp4_kv_cache_score_amd.configs import CONFIGS
+    from fp4_kv_cache_score_amd.configs import CONFIGS, FULL, REINDEX, REUSE
     from fp4_kv_cache_score_amd.device import DeviceCase
     cfg = CONFIGS[ci]
     case = synth.make_case(cfg)
     dc = DeviceCase(case)
     dc.prepare_prefill()
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        dc.prefill()
-    torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(4)] for _ in range(steps)]
-    for k in range(steps):
-        for st in range(4):
-            ev[k][st][0].record(stream)
-            dc.prefill_stage(st)
-            ev[k][st][1].record(stream)
-    torch.cuda.synchronize()
-    stage_ms = [float(np.mean([ev[k][st][0].elapsed_time(ev[k][st][1]) for k in range(steps)]))
-                for st in range(4)]
-    ms = sum(stage_ms)
-    t = np.arange(cfg.Q)
-    vis = np.minimum(cfg.M, (cfg.pos0 + t + 1) // cfg.ratio)
-    idx_flop = 2.0 * cfg.B * float(vis.sum()) * cfg.HI * cfg.DI
-    # S = q C^T and O = P C (P as bf16 hi + lo, two products) over K + W keys
-    attn_flop = 2.0 * cfg.B * cfg.Q * cfg.H * cfg.D * (cfg.K + cfg.W) * 3
+    dc.prepare_prefill_layers()
+    ms = _time_calls(dc.prefill_layers, steps, warmup)
+    stage_ms = [_time_calls(lambda st=st: dc.prefill_stage(st), steps, warmup) for st in range(4)]
+    attn_ms = ms - stage_ms[0] - stage_ms[1]          # the fused attention pass, by difference
+    idx_flop, attn_flop = _prefill_flops(cfg, cfg.pos0)
+    res = dict(workload=cfg.name, query_tokens_per_s=cfg.B * cfg.Q / (ms * 1e-3), ms_per_step=ms,
+               path="csa2_prefill_layers (score, Top-K, one attention pass over K + W keys)",
+               stage_ms={"index_score_mfma": stage_ms[0], "topk": stage_ms[1],
+                         "attention_fused_mfma": attn_ms},
+               unfused_chain_ms=sum(stage_ms),
+               unfused_stage_ms={"sparse_attn_mfma": stage_ms[2], "swa_merge_mfma": stage_ms[3]},
+               index_score_tflops=idx_flop / (stage_ms[0] * 1e-3) / 1e12,
+               index_score_frac_of_bf16_mfma_peak=idx_flop / (stage_ms[0] * 1e-3) / 2.5e15,
+               attention_tflops=attn_flop / (attn_ms * 1e-3) / 1e12,
+               attention_frac_of_bf16_mfma_peak=attn_flop / (attn_ms * 1e-3) / 2.5e15)
+    log("prefill %s: %.3f ms (unfused chain %.3f ms)" % (cfg.name, ms, sum(stage_ms)))
+    del dc
+
+    # the same chunk through a Full, Reindex, Reuse, Reuse schedule
+    sched = (FULL, REINDEX, REUSE, REUSE)
+    c4 = cfg.scaled(modes=sched)
+    dc = DeviceCase(synth.make_case(c4))
+    ms4 = _time_calls(dc.prefill_layers, steps, warmup)
+    res["schedule_F_Ri_Ru_Ru"] = dict(ms_per_chunk=ms4,
+                                      query_tokens_per_s=c4.B * c4.Q / (ms4 * 1e-3))
+    # the first chunk of a context (positions 0 .. Q-1): it sees a prefix of the pool
+    ms0 = _time_calls(lambda: dc.prefill_layers(pos0=0), steps, warmup)
+    res["schedule_F_Ri_Ru_Ru"]["first_chunk_ms"] = ms0
+    log("prefill schedule F,Ri,Ru,Ru: %.3f ms per chunk, first chunk %.3f ms" % (ms4, ms0))
+
+    # a whole context of ratio * M tokens in chunks of Q: before each chunk the
+    # Q / ratio entries it completes are appended (MXFP4 / E4M3 encode), then the
+    # schedule runs over the chunk at its position
+    B, Q, M, ratio = c4.B, c4.Q, c4.M, c4.ratio
+    n_chunks = ratio * M // Q
+    per = Q // ratio
+    g = torch.Generator(device="cuda").manual_seed(5)
+    xl = torch.randn((B, per, c4.D), generator=g, device="cuda")
+    xk = torch.randn((B, per, c4.HI, c4.DI), generator=g, device="cuda")
+    slots = [torch.arange(c * per, (c + 1) * per, dtype=torch.int32, device="cuda")
+             .expand(B, per).contiguous() for c in range(n_chunks)]
+
+    def context():
+        for c in range(n_chunks):
+            C.csa2_pool_append(dc.latent, dc.scale, dc.idx_key, B, M, xl, xk, slots[c], per)
+            dc.prefill_layers(pos0=c * Q)
+
+    ctx_ms = _time_calls(context, 2, 1)
+    res["schedule_F_Ri_Ru_Ru"]["whole_context"] = dict(
+        tokens=ratio * M, chunks=n_chunks, ms=ctx_ms,
+        query_tokens_per_s=B * ratio * M / (ctx_ms * 1e-3))
+    log("prefill whole context %d tokens in %d chunks: %.1f ms" % (ratio * M, n_chunks, ctx_ms))
     del dc
     torch.cuda.empty_cache()
-    return dict(workload=cfg.name, query_tokens_per_s=cfg.B * cfg.Q / (ms * 1e-3), ms_per_step=ms,
-                stage_ms={"index_score_mfma": stage_ms[0], "topk": stage_ms[1],
-                          "sparse_attn_mfma": stage_ms[2], "swa_merge_mfma": stage_ms[3]},
-                index_score_tflops=idx_flop / (stage_ms[0] * 1e-3) / 1e12,
-                index_score_frac_of_bf16_mfma_peak=idx_flop / (stage_ms[0] * 1e-3) / 2.5e15,
-                attention_tflops=attn_flop / ((stage_ms[2] + stage_ms[3]) * 1e-3) / 1e12,
-                attention_frac_of_bf16_mfma_peak=attn_flop / ((stage_ms[2] + stage_ms[3]) * 1e-3)
-                / 2.5e15)
+    return res
 
 
 def cpu_baseline(case, budget_s: float = 15.0):
