@@ -22,17 +22,27 @@
 //   2^-15 relative), against ~0.4 x 2^-24 for the bf16 instruction and for
 //   sequential fp32 FMA, and the score feeds an exact Top-K.
 //
-// k_prefill_attn: one work-group per query row.  The row's keys (selected
-//   global entries, then its window rows) are taken 64 at a time, dequantised
-//   exactly into a bf16 LDS tile (as in decode), and
-//     S = q . C^T   with v_mfma_f32_16x16x32_bf16 (16 heads x 16 keys per wave)
-//     online softmax per head in fp32,
-//     O += P . C    with the same MFMA, P split into bf16 hi + lo parts so that
-//                   the rounding of P stays below 2^-16 relative.
-//   The P . C operand needs 8 consecutive keys of one dim per lane; it is read
-//   as 32-bit pairs of dims from the key-major tile and repacked with
-//   v_perm_b32, two dims feeding two output tiles.
+// k_prefill_attn: one work-group of two waves per query row; wave h owns
+//   output dims 256 h .. 256 h + 255.  The row's keys (selected global entries,
+//   then its window rows) are taken 32 per step.  Each lane loads 2 blocks of
+//   32 dims of one key (this wave's half), dequantises them exactly to bf16
+//   straight into the key operand of
+//     S^T = C . q^T   (v_mfma_f32_16x16x32_bf16, 16 keys x 16 heads, the dims
+//                      of the contraction taken in the order the lanes hold
+//                      them, q permuted to match),
+//   and stages the same bf16 rows in LDS.  The two waves' partial S^T (one per
+//   dim half) are exchanged through LDS and added in a fixed order, so both run
+//   the same online softmax per head in fp32.  S^T leaves each lane with P for
+//   4 keys of one head, which is the A-operand layout of
+//     O += P . C      (same MFMA; P split into bf16 hi + lo parts so that the
+//                      rounding of P stays below 2^-16 relative),
+//   whose B operand (8 keys of one dim per lane) comes from the staged rows with
+//   gfx950's transposing LDS read (ds_read_b64_tr_b16).  The softmax reference
+//   moves only when a logit exceeds it by more than 8 (natural log), outside the
+//   inner loop, so O stays in the matrix accumulators.  One barrier per step.
 #include "csa2_internal.h"
+
+#include <type_traits>
 
 namespace csa2 {
 namespace {
@@ -235,289 +245,324 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
 // Sparse attention (bf16 MFMA)
 // ---------------------------------------------------------------------------
 
-constexpr int kAThreads = 256;
-constexpr int kAC = 64;                      // keys per chunk
-constexpr int kARowU = kD / 2 + 4;           // key row stride in u32 (1040 B)
-constexpr int kAPRow = kAC + 8;              // P row stride in bf16 (144 B)
-constexpr int kAIdx = 1024;                  // entry numbers staged in LDS
+constexpr int kWK = 32;                        // keys per step (two MFMA sets of 16)
+constexpr int kHalf = kD / 2;                  // output dims per wave
+constexpr int kTRow = kHalf * 2 + 32;          // staged key row of one wave: 256 bf16 + 32 B pad
+constexpr float kPfLazy = 8.f;                 // softmax reference slack (natural log units)
 
-struct PfRegs {
-  u32x4 v[8];        // global: 4 x 16 code bytes; window: 8 x 16 E4M3 bytes
-  uint32_t sc[4];    // global: E8M0 scale codes, 0xFFFFFFFF for "no entry"
-};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
 
-__global__ __launch_bounds__(kAThreads, 2)
-void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t C, const float* __restrict__ o_in,
-                    const float* __restrict__ lse_in) {
-  __shared__ __attribute__((aligned(16))) uint32_t cs[kAC * kARowU];        // 65 KiB
-  __shared__ __attribute__((aligned(16))) uint16_t ph[kH * kAPRow];         // P hi
-  __shared__ __attribute__((aligned(16))) uint16_t pl[kH * kAPRow];         // P lo
-  __shared__ int32_t idx_s[kAIdx];
-  __shared__ int valid_s[kAC];
-  __shared__ float red[4][kH];
+// Max and sum over the four 16-lane rows (gfx950 permlane swaps).
+__device__ __forceinline__ float pf_rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float pf_rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
-  const int row = blockIdx.x;
+// Byte offset of (key row r, byte c) in a wave's staged tile.  With rows 544 B
+// apart, the 8 rows that half a wave's transposed read touches fall on 8
+// different 32-byte bank groups.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * kTRow + c; }
+
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const float* lse_in) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kWK * kTRow];   // 32 KiB
+  __shared__ __attribute__((aligned(16))) float xs[2][2][64 * 8];         // partial S, by step parity
+
+  // rows of one XCD are consecutive tokens (their window rows overlap in L2)
+  int row;
+  {
+    const int bid = blockIdx.x, R = a.rows;
+    const int q8 = R >> 3, r8 = R & 7, x = bid & 7, k = bid >> 3;
+    row = x * q8 + (x < r8 ? x : r8) + k;
+  }
   const int b = row / a.Q;
   const int t = row - b * a.Q;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int ln = lane & 15;        // MFMA column / A row
-  const int lg = lane >> 4;        // MFMA k-group / output row group
-  // window rows t + wr with wr < wfirst are positions before the context's
-  // first token (a first chunk): never read, never keys
+  const int hw = threadIdx.x >> 6;           // this wave's half of the dims
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
   const int64_t wgap = a.pos0 >= 0 ? (int64_t)(a.W - 1) - (a.pos0 + t) : 0;
   const int32_t wfirst = wgap > 0 ? (int32_t)wgap : 0;
 
-  // q as A operands: head ln, dims 32 s + 8 lg .. +7, for k-steps s = 0..15
-  bf16x8 qa[16];
+  // q (this half) as the B operand of S^T = C . q^T: lane (head ln, group lg)
+  // holds, for k-step s, dims 256 hw + 32 (4 (s / 4) + lg) + 8 (s % 4) .. +7,
+  // the order in which the key operand below holds them
+  bf16x8 qv[8];
   {
-    const uint16_t* qr = a.q + ((size_t)row * kH + ln) * kD + 8 * lg;
+    const uint16_t* qr = a.q + ((size_t)row * kH + ln) * kD + kHalf * hw;
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      qa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + 32 * s));
+    for (int s = 0; s < 8; ++s)
+      qv[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                             qr + 32 * (4 * (s >> 2) + lg) + 8 * (s & 3)));
   }
-  const int nst = a.K < kAIdx ? a.K : kAIdx;
-  for (int k = tid; k < nst; k += kAThreads) idx_s[k] = a.idx[(size_t)row * a.K + k];
-  __syncthreads();
+  // the last position holding an entry (-1 entries select nothing)
+  const int32_t* irow = a.idx ? a.idx + (size_t)row * a.K : nullptr;
+  int last = -1;
+  if (Cg > 0)
+    for (int k = lane; k < a.K; k += 64)
+      if (irow[k] >= 0) last = k;
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  const int cg = __builtin_amdgcn_readfirstlane(Cg > 0 ? (last + kWK) / kWK : 0);
+  const int ws0 = __builtin_amdgcn_readfirstlane(wfirst / kWK);   // window steps before position 0
+  const int n_it = cg + (Cw > ws0 ? Cw - ws0 : 0);
 
-  auto entry = [&](int kpos) -> int32_t {
-    if (kpos >= a.K) return -1;
-    return kpos < kAIdx ? idx_s[kpos] : a.idx[(size_t)row * a.K + kpos];
+  const uint8_t* lat_b = a.latent ? a.latent + (size_t)b * a.M * kLatRow + 128 * hw : nullptr;
+  const uint8_t* sc_b = a.scale ? a.scale + (size_t)b * a.M * kScaleRow : nullptr;
+  const uint8_t* swa_b = a.swa ? a.swa + ((size_t)b * a.swa_rows + t) * kD + kHalf * hw : nullptr;
+  // a readable stand-in for loads past the last step (this row's q: 16 KiB)
+  const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.q + (size_t)row * kH * kD);
+  const int kmax = a.K > 0 ? a.K - 1 : 0;
+
+  // entry number for step `it` (an unconditional load at a clamped position)
+  const int32_t* irow_s = irow ? irow : reinterpret_cast<const int32_t*>(spare);
+  auto entry = [&](int it, int u) __attribute__((always_inline)) -> int32_t {
+    return irow_s[min(it * kWK + 16 * u + ln, kmax)];
   };
-  PfRegs r;
-  auto load = [&](int chunk) {
-    if (chunk < Cg) {
+  // step `it`, set u: key 16 u + ln; lane group lg loads blocks lg and 4 + lg
+  // of this half.  Global: v0, v1 = 16 E2M1 bytes each, v2 = v3 = the entry's
+  // scale bytes.  Window: (v0, v1), (v2, v3) = 32 E4M3 bytes each.  All four
+  // loads are issued unconditionally from selected, valid addresses.
+  auto load = [&](int it, int u, int32_t e, u32x4& v0, u32x4& v1, u32x4& v2, u32x4& v3)
+      __attribute__((always_inline)) -> bool {
+    const bool g = it < cg;
+    const int kpos = it * kWK + 16 * u + ln;
+    const bool okg = kpos < a.K && e >= 0;
+    const int wr = (it - cg + ws0) * kWK + 16 * u + ln;
+    const bool okw = wr < a.W && wr >= wfirst;
+    const uint8_t *p0, *p1, *p2, *p3;
+    if (g) {
+      const int32_t ec = okg ? e : 0;                         // entry 0 exists
+      const uint8_t* gl = lat_b + (size_t)ec * kLatRow;
+      p0 = gl + 16 * lg;
+      p1 = gl + 16 * (4 + lg);
+      p2 = p3 = sc_b + (size_t)ec * kScaleRow;
+    } else {
+      const uint8_t* wp = a.W > 0 ? swa_b + (size_t)(okw ? wr : a.W - 1) * kD : spare;
+      p0 = wp + 32 * lg;
+      p1 = p0 + 16;
+      p2 = wp + 32 * (4 + lg);
+      p3 = p2 + 16;
+    }
+    v0 = *reinterpret_cast<const u32x4*>(p0);
+    v1 = *reinterpret_cast<const u32x4*>(p1);
+    v2 = *reinterpret_cast<const u32x4*>(p2);
+    v3 = *reinterpret_cast<const u32x4*>(p3);
+    return g ? okg : okw;
+  };
+
+  uint8_t* my = tile[hw];
+  // dequantise set u (k-steps 4 i + d from block 4 i + lg of this half),
+  // accumulate the partial S^T and stage the bf16 rows for P . C
+  auto score_set = [&](auto gtag, int u, const u32x4& v0, const u32x4& v1, const u32x4& v2,
+                       const u32x4& v3, f32x4& s0, f32x4& s1) __attribute__((always_inline)) {
+    constexpr bool kGlobal = decltype(gtag)::value;
+    const int r = 16 * u + ln;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pr = tid + i * kAThreads;      // (key j, 32-element block)
-        const int j = pr >> 4, blk = pr & 15;
-        const int32_t e = entry(chunk * kAC + j);
-        r.sc[i] = 0xFFFFFFFFu;
-        if (e >= 0) {
-          const size_t er = (size_t)b * (size_t)a.M + (size_t)e;
-          r.v[i] = *reinterpret_cast<const u32x4*>(a.latent + er * kLatRow + blk * 16);
-          r.sc[i] = a.scale[er * kScaleRow + blk];
+    for (int i = 0; i < 2; ++i) {
+      const int blk = 4 * i + lg;
+      u32x4 w[4];
+      if (kGlobal) {
+        const u32x4& c = i ? v1 : v0;
+        const uint32_t sw = hw ? v2[2 + i] : v2[i];          // scale bytes of blocks 8 hw + 4 i ..
+        const uint32_t scb = (sw >> (8 * lg)) & 0xFFu;
+        const float scale = __uint_as_float(scb ? (scb << 23) : 0x00400000u);   // 2^(scb-127)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          w[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 0));
+          w[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 1));
+          w[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 2));
+          w[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 3));
+        }
+      } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x4& c = i ? (d < 2 ? v2 : v3) : (d < 2 ? v0 : v1);
+          const uint32_t x0 = c[2 * (d & 1)], x1 = c[2 * (d & 1) + 1];
+          w[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.0f, false));
+          w[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.0f, true));
+          w[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.0f, false));
+          w[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.0f, true));
         }
       }
-    } else {
-      const int wc = chunk - Cg;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int pr = tid + i * kAThreads;      // (row j, 16-byte segment)
-        const int j = pr >> 5, seg = pr & 31;
-        const int wr = wc * kAC + j;
-        if (wr < a.W && wr >= wfirst)
-          r.v[i] = *reinterpret_cast<const u32x4*>(a.swa + ((size_t)b * a.swa_rows + t + wr) * kD + seg * 16);
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, w[d]);
+        if (d & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[4 * i + d], s1, 0, 0, 0);
+        else       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[4 * i + d], s0, 0, 0, 0);
+        *reinterpret_cast<u32x4*>(my + tile_off(r, 64 * blk + 16 * d)) = w[d];
       }
     }
   };
-  auto stage = [&](int chunk) {
-    if (chunk < Cg) {
+
+  // O[j][i]: head 4 lg + i, dim 256 hw + 16 j + ln
+  f32x4 O[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pr = tid + i * kAThreads;
-        const int j = pr >> 4, blk = pr & 15;
-        u32x4 o[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-        const bool present = r.sc[i] != 0xFFFFFFFFu;
-        if (present) {
-          const uint32_t sc = r.sc[i];
-          const float scale = __uint_as_float(sc ? (sc << 23) : 0x00400000u);   // 2^(sc-127)
+  for (int j = 0; j < 16; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // softmax reference of head ln
+  float l_run = 0.f;         // this lane's share of head ln's sum
+
+  u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
+  int32_t ea = -1, eb = -1;
+  bool oka = false, okb = false;
+  if (n_it > 0) {
+    oka = load(0, 0, entry(0, 0), a0, a1, a2, a3);
+    okb = load(0, 1, entry(0, 1), b0, b1, b2, b3);
+    ea = entry(1, 0);
+    eb = entry(1, 1);
+  }
+  // transposed-read rows: key 4 lg + ln / 4 (+ 16 for set 1), dims + 4 (ln % 4)
+  const int tr0 = 4 * lg + (ln >> 2), tr1 = tr0 + 16;
+
+  // one step's scores: dequantise and score both sets (the next step's loads
+  // issued as each set's registers free up), exchange the halves' partial
+  // sums; x0 / x1 = full logits of keys 4 lg + e (+16), head ln, -inf when absent
+  auto step_scores = [&](int it, f32x4& x0, f32x4& x1) __attribute__((always_inline)) -> float {
+    f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
+    const uint64_t va = __ballot(oka), vb = __ballot(okb);
+    const bool global = it < cg;
+    __asm__ volatile("" ::: "memory");       // this step's staging after the last step's reads
+    if (global) score_set(std::true_type{}, 0, a0, a1, a2, a3, sa0, sa1);
+    else        score_set(std::false_type{}, 0, a0, a1, a2, a3, sa0, sa1);
+    oka = load(it + 1, 0, ea, a0, a1, a2, a3);
+    ea = entry(it + 2, 0);
+    if (global) score_set(std::true_type{}, 1, b0, b1, b2, b3, sb0, sb1);
+    else        score_set(std::false_type{}, 1, b0, b1, b2, b3, sb0, sb1);
+    okb = load(it + 1, 1, eb, b0, b1, b2, b3);
+    eb = entry(it + 2, 1);
+    {  // the two halves' partial sums, added in a fixed order by both waves
+      float* xw = &xs[it & 1][hw][lane * 8];
+      *reinterpret_cast<f32x4*>(xw) = sa0 + sa1;
+      *reinterpret_cast<f32x4*>(xw + 4) = sb0 + sb1;
+    }
+    __syncthreads();
+    const float* x0p = &xs[it & 1][0][lane * 8];
+    const float* x1p = &xs[it & 1][1][lane * 8];
+    x0 = *reinterpret_cast<const f32x4*>(x0p) + *reinterpret_cast<const f32x4*>(x1p);
+    x1 = *reinterpret_cast<const f32x4*>(x0p + 4) + *reinterpret_cast<const f32x4*>(x1p + 4);
+    float mc = -INFINITY;
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            o[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.v[i][d], scale, 0));
-            o[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.v[i][d], scale, 1));
-            o[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.v[i][d], scale, 2));
-            o[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.v[i][d], scale, 3));
-          }
-        }
-        u32x4* dst = reinterpret_cast<u32x4*>(cs + j * kARowU + blk * 16);
-        const int rot = blk >> 2;   // 16 lanes of a key row store to 16 bank groups
+    for (int e = 0; e < 4; ++e) {
+      x0[e] = (va >> (4 * lg + e)) & 1 ? x0[e] : -INFINITY;
+      x1[e] = (vb >> (4 * lg + e)) & 1 ? x1[e] : -INFINITY;
+      mc = fmaxf(mc, fmaxf(x0[e], x1[e]));
+    }
+    return pf_rows_max(mc);
+  };
+  // one step's P . C on this half's dims, with the current reference
+  auto step_pv = [&](const f32x4& x0, const f32x4& x1) __attribute__((always_inline)) {
+    float p[8];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = (q4 + rot) & 3;
-          dst[c] = c == 0 ? o[0] : (c == 1 ? o[1] : (c == 2 ? o[2] : o[3]));
-        }
-        if (blk == 0) valid_s[j] = present;
-      }
-    } else {
-      const int wc = chunk - Cg;
+    for (int e = 0; e < 4; ++e) {
+      p[e] = x0[e] == -INFINITY ? 0.f : __expf(x0[e] - m_run);
+      p[4 + e] = x1[e] == -INFINITY ? 0.f : __expf(x1[e] - m_run);
+    }
+    // A operand: keys 4 lg + e of set 0, then of set 1 (the B reads below take
+    // the same keys); P = hi + lo in bf16
+    u32x4 ph, pl;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int pr = tid + i * kAThreads;
-        const int j = pr >> 5, seg = pr & 31;
-        const int wr = wc * kAC + j;
-        const bool ok = wr < a.W && wr >= wfirst;
-        u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = o0;
-        if (ok) {
-          uint32_t w[8];
+    for (int e = 0; e < 4; ++e) {
+      l_run += p[2 * e] + p[2 * e + 1];
+      const bf16x2 hv = __builtin_convertvector((f32x2){p[2 * e], p[2 * e + 1]}, bf16x2);
+      const f32x2 hf = __builtin_convertvector(hv, f32x2);
+      const bf16x2 lv = __builtin_convertvector((f32x2){p[2 * e] - hf[0], p[2 * e + 1] - hf[1]}, bf16x2);
+      ph[e] = __builtin_bit_cast(uint32_t, hv);
+      pl[e] = __builtin_bit_cast(uint32_t, lv);
+    }
+    const bf16x8 ahi = __builtin_bit_cast(bf16x8, ph);
+    const bf16x8 alo = __builtin_bit_cast(bf16x8, pl);
+    __asm__ volatile("" ::: "memory");       // staging stores before the transposed reads
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[i][d], false);
-            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[i][d], true);
-            w[2 * d + 0] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
-            w[2 * d + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
-          }
-          o0 = u32x4{w[0], w[1], w[2], w[3]};
-          o1 = u32x4{w[4], w[5], w[6], w[7]};
-        }
-        u32x4* dst = reinterpret_cast<u32x4*>(cs + j * kARowU + seg * 8);
-        const int rot = (seg >> 3) & 1;
-        dst[rot] = rot ? o1 : o0;
-        dst[rot ^ 1] = rot ? o0 : o1;
-        if (seg == 0) valid_s[j] = ok;
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int c = 32 * j + 8 * (ln & 3);
+      const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(my + tile_off(tr0, c)));
+      const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(my + tile_off(tr1, c)));
+      const u32x2 c0 = __builtin_bit_cast(u32x2, r0), c1 = __builtin_bit_cast(u32x2, r1);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{c0[0], c0[1], c1[0], c1[1]});
+      O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, O[j], 0, 0, 0);
+      O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, O[j], 0, 0, 0);
     }
   };
 
-  // Output accumulators: wave owns dims 128 wave .. +127 as 4 tile pairs;
-  // tile 2u column n <-> dim 128 wave + 32 u + 2 n, tile 2u+1 <-> that + 1.
-  f32x4 O[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) O[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];   // heads 4 lg + i
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.f;
-  }
-
-  if (C > 0) load(0);
+  // Steps run in an inner loop that touches O only with matrix instructions;
+  // a step whose logits exceed the reference by more than kPfLazy leaves the
+  // loop, and O is rescaled before that step's P . C.
+  int it = 0;
+  while (it < n_it) {
+    f32x4 x0, x1;
+    float mc = -INFINITY;
+    bool raise = false;
 #pragma unroll 1
-  for (int c = 0; c < C; ++c) {
-    stage(c);
-    __syncthreads();
-    if (c + 1 < C) load(c + 1);
-
-    // S = q . C^T for keys 16 wave .. +15 of the chunk
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint32_t* kr = cs + (16 * wave + ln) * kARowU + 4 * lg;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const bf16x8 bk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 16 * k));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], bk, s, 0, 0, 0);
-        if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // at most 4 key operands in flight
-      }
+    for (; it < n_it; ++it) {
+      mc = step_scores(it, x0, x1);
+      raise = mc > m_run + kPfLazy;
+      if (__ballot(raise) != 0) break;
+      step_pv(x0, x1);
     }
-    const bool kv = valid_s[16 * wave + ln] != 0;
-    float cm[4];
+    if (it >= n_it) break;
+    const float m_new = raise ? mc : m_run;
+    const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+    float al[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = kv ? s[i] : -INFINITY;
-      s[i] = x;
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-      cm[i] = x;
-    }
-    if (ln == 0) {
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][4 * lg + i] = cm[i];
-    }
-    __syncthreads();
-    float alpha[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 4 * lg + i;
-      const float mx = fmaxf(fmaxf(red[0][hh], red[1][hh]), fmaxf(red[2][hh], red[3][hh]));
-      const float m_new = fmaxf(m_run[i], mx);
-      float p = 0.f;
-      alpha[i] = 1.f;
-      if (m_new != -INFINITY) {
-        p = __expf(s[i] - m_new);
-        alpha[i] = __expf(m_run[i] - m_new);
-      }
-      m_run[i] = m_new;
-      float ps = p;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
-      l_run[i] = l_run[i] * alpha[i] + ps;
-      // P split into bf16 hi + lo (p - hi is exact in fp32)
-      const uint32_t pu = __float_as_uint(p);
-      const uint32_t hi = (pu + 0x7FFFu + ((pu >> 16) & 1u)) & 0xFFFF0000u;
-      const float lo = p - __uint_as_float(hi);
-      const uint32_t lu = __float_as_uint(lo);
-      const uint32_t lo16 = (lu + 0x7FFFu + ((lu >> 16) & 1u)) >> 16;
-      ph[hh * kAPRow + 16 * wave + ln] = (uint16_t)(hi >> 16);
-      pl[hh * kAPRow + 16 * wave + ln] = (uint16_t)lo16;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O[u][i] *= alpha[i];
-    __syncthreads();
-
-    // O += P . C: A = P[head ln][keys 32 ks + 8 lg ..], B = C[those keys][dim]
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 ahi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&ph[ln * kAPRow + 32 * ks + 8 * lg]));
-      const bf16x8 alo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pl[ln * kAPRow + 32 * ks + 8 * lg]));
-      const uint32_t* kr = cs + (32 * ks + 8 * lg) * kARowU + 64 * wave + ln;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t x[8];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) x[rr] = kr[rr * kARowU + 16 * u];
-        u32x4 be, bo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          be[i] = __builtin_amdgcn_perm(x[2 * i + 1], x[2 * i], 0x05040100u);
-          bo[i] = __builtin_amdgcn_perm(x[2 * i + 1], x[2 * i], 0x07060302u);
-        }
-        const bf16x8 bev = __builtin_bit_cast(bf16x8, be);
-        const bf16x8 bov = __builtin_bit_cast(bf16x8, bo);
-        O[2 * u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bev, O[2 * u], 0, 0, 0);
-        O[2 * u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bev, O[2 * u], 0, 0, 0);
-        O[2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bov, O[2 * u + 1], 0, 0, 0);
-        O[2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bov, O[2 * u + 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);   // one tile pair's operands live at a time
-      }
-    }
-    __syncthreads();
+      for (int i = 0; i < 4; ++i) O[j][i] *= al[i];
+    step_pv(x0, x1);
+    ++it;
   }
 
-  // total sum per head over the 4 waves' keys
-  float lin[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lin[i] = lse_in ? lse_in[(size_t)row * kH + 4 * lg + i] : -INFINITY;
-  if (ln == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][4 * lg + i] = l_run[i];
-  }
-  __syncthreads();
+  // per head: total sum, lse, merge with an incoming result; lane (ln, lg)
+  // writes dims 256 hw + 16 j + ln of heads 4 lg + i
+  const float L = pf_rows_sum(l_run);
+  const float lse_h = L > 0.f ? m_run + logf(L) : -INFINITY;   // head ln
+  float wself[4], win[4], lse4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * lg + i;
-    const float L = ((red[0][hh] + red[1][hh]) + red[2][hh]) + red[3][hh];
-    float lse = L > 0.f ? m_run[i] + logf(L) : -INFINITY;
-    float wself = L > 0.f ? 1.f / L : 0.f;
-    float win = 0.f;
-    if (lse_in) {   // merge with an incoming (o, lse) as one softmax over both key sets
-      const float li = lin[i];   // read before the barrier above: lse may alias lse_in
+    const float Li = __shfl(L, 4 * lg + i, 64);
+    float lse = __shfl(lse_h, 4 * lg + i, 64);
+    wself[i] = Li > 0.f ? 1.f / Li : 0.f;
+    win[i] = 0.f;
+    if (lse_in) {   // one softmax over both key sets
+      const float li = lse_in[(size_t)row * kH + 4 * lg + i];
       const float mx = fmaxf(li, lse);
       if (mx != -INFINITY) {
-        const float ea = li == -INFINITY ? 0.f : __expf(li - mx);
-        const float eb = lse == -INFINITY ? 0.f : __expf(lse - mx);
-        const float tot = ea + eb;
-        win = ea / tot;
-        wself *= eb / tot;
+        const float e1 = li == -INFINITY ? 0.f : __expf(li - mx);
+        const float e2 = lse == -INFINITY ? 0.f : __expf(lse - mx);
+        const float tot = e1 + e2;
+        win[i] = e1 / tot;
+        wself[i] *= e2 / tot;
         lse = mx + logf(tot);
       }
     }
-    float* orow = a.o + ((size_t)row * kH + hh) * kD + 128 * wave + 2 * ln;
-    const float* irow = lse_in ? o_in + ((size_t)row * kH + hh) * kD + 128 * wave + 2 * ln : nullptr;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float2 v = make_float2(O[2 * u][i] * wself, O[2 * u + 1][i] * wself);
-      if (irow) {
-        const float2 x = *reinterpret_cast<const float2*>(irow + 32 * u);
-        v.x = fmaf(win, x.x, v.x);
-        v.y = fmaf(win, x.y, v.y);
-      }
-      *reinterpret_cast<float2*>(orow + 32 * u) = v;
-    }
-    if (ln == 0 && wave == 0) a.lse[(size_t)row * kH + hh] = lse;
+    lse4[i] = lse;
   }
+  // the incoming lse is read by both waves before wave 0 overwrites it
+  if (lse_in) __syncthreads();
+  float* orow = a.o + (size_t)row * kH * kD + kHalf * hw;
+  const float* inrow = lse_in ? o_in + (size_t)row * kH * kD + kHalf * hw : nullptr;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t off = (size_t)(4 * lg + i) * kD + 16 * j + ln;
+      float v = O[j][i] * wself[i];
+      if (inrow) v = fmaf(win[i], inrow[off], v);
+      orow[off] = v;
+    }
+  if (hw == 0 && ln < 4)
+    a.lse[(size_t)row * kH + 4 * lg + ln] = ln == 0 ? lse4[0] : (ln == 1 ? lse4[1] : (ln == 2 ? lse4[2] : lse4[3]));
 }
 
 }  // namespace
@@ -534,9 +579,10 @@ hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_
 
 hipError_t launch_prefill_attn(const AttnArgs& a, const float* o_in, const float* lse_in,
                                hipStream_t s) {
-  const int32_t Cg = a.K > 0 && a.latent ? (a.K + kAC - 1) / kAC : 0;
-  const int32_t C = Cg + (a.W > 0 ? (a.W + kAC - 1) / kAC : 0);
-  k_prefill_attn<<<dim3((unsigned)a.rows), dim3(kAThreads), 0, s>>>(a, Cg, C, o_in, lse_in);
+  if (a.rows <= 0) return hipSuccess;
+  const int32_t Cg = a.K > 0 && a.latent ? (a.K + kWK - 1) / kWK : 0;
+  const int32_t Cw = a.W > 0 ? (a.W + kWK - 1) / kWK : 0;
+  k_prefill_attn<<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw, o_in, lse_in);
   return hipGetLastError();
 }
 
