@@ -247,7 +247,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
 
 constexpr int kWK = 32;                        // keys per step (two MFMA sets of 16)
 constexpr int kHalf = kD / 2;                  // output dims per wave
-constexpr int kTRow = kHalf * 2 + 32;          // staged key row of one wave: 256 bf16 + 32 B pad
+constexpr int kTRow = kHalf * 2;               // staged key row of one wave: 256 bf16 (512 B)
 constexpr float kPfLazy = 8.f;                 // softmax reference slack (natural log units)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -267,10 +267,14 @@ __device__ __forceinline__ float pf_rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Byte offset of (key row r, byte c) in a wave's staged tile.  With rows 544 B
-// apart, the 8 rows that half a wave's transposed read touches fall on 8
-// different 32-byte bank groups.
-__device__ __forceinline__ int tile_off(int r, int c) { return r * kTRow + c; }
+// Byte offset of (key row r, byte c) in a wave's staged tile: 32-byte units
+// XOR-swizzled by the row's low 3 bits, 16-byte halves swapped by its bit 3.
+// The 8 rows that half a wave's transposed read touches then fall on 8
+// different 32-byte bank groups, and the 16 rows of a staging store on 16
+// different 16-byte ones.
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * kTRow + ((((c >> 5) ^ (r & 7)) << 5) | ((c & 31) ^ (((r >> 3) & 1) << 4)));
+}
 
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const float* lse_in) {
@@ -304,12 +308,20 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const
       qv[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                              qr + 32 * (4 * (s >> 2) + lg) + 8 * (s & 3)));
   }
-  // the last position holding an entry (-1 entries select nothing)
+  // the last position holding an entry (-1 entries select nothing); the
+  // entry numbers are read 512 at a time, all loads in flight together
   const int32_t* irow = a.idx ? a.idx + (size_t)row * a.K : nullptr;
   int last = -1;
-  if (Cg > 0)
-    for (int k = lane; k < a.K; k += 64)
-      if (irow[k] >= 0) last = k;
+  if (Cg > 0) {
+    for (int k0 = 0; k0 < a.K; k0 += 512) {
+      int32_t e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) e[u] = irow[min(k0 + 64 * u + lane, a.K - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (e[u] >= 0 && k0 + 64 * u + lane < a.K) last = max(last, k0 + 64 * u + lane);
+    }
+  }
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
   const int cg = __builtin_amdgcn_readfirstlane(Cg > 0 ? (last + kWK) / kWK : 0);
   const int ws0 = __builtin_amdgcn_readfirstlane(wfirst / kWK);   // window steps before position 0
@@ -551,16 +563,27 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const
   // the incoming lse is read by both waves before wave 0 overwrites it
   if (lse_in) __syncthreads();
   float* orow = a.o + (size_t)row * kH * kD + kHalf * hw;
-  const float* inrow = lse_in ? o_in + (size_t)row * kH * kD + kHalf * hw : nullptr;
+  if (lse_in) {
+    // the incoming rows may be the output rows: every value this lane merges
+    // is read before any is written (one round trip, not one per value)
+    const float* inrow = o_in + (size_t)row * kH * kD + kHalf * hw;
+    f32x4 X[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t off = (size_t)(4 * lg + i) * kD + 16 * j + ln;
-      float v = O[j][i] * wself[i];
-      if (inrow) v = fmaf(win[i], inrow[off], v);
-      orow[off] = v;
-    }
+      for (int i = 0; i < 4; ++i) X[j][i] = inrow[(size_t)(4 * lg + i) * kD + 16 * j + ln];
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        orow[(size_t)(4 * lg + i) * kD + 16 * j + ln] = fmaf(win[i], X[j][i], O[j][i] * wself[i]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) orow[(size_t)(4 * lg + i) * kD + 16 * j + ln] = O[j][i] * wself[i];
+  }
   if (hw == 0 && ln < 4)
     a.lse[(size_t)row * kH + 4 * lg + ln] = ln == 0 ? lse4[0] : (ln == 1 ? lse4[1] : (ln == 2 ? lse4[2] : lse4[3]));
 }
