@@ -374,6 +374,72 @@ def measure_append(ci: int, launches: int = 10):
                 window_ms=win, window_gbs=win_bytes / (win * 1e-3) / 1e9)
 
 
+def measure_host_tier(ci: int, reps: int = 5):
+    """Host tier at a decode workload's pool shape: one sequence's whole pool
+    (M entries x 784 B) restored from / offloaded to page-locked host memory,
+    alone, and restored on a second stream while decode steps run."""
+    import torch
+    from fp4_kv_cache_score_amd import _lib as C
+    from fp4_kv_cache_score_amd import synth
+    from fp4_kv_cache_score_amd.configs import CONFIGS
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[ci]
+    dc = DeviceCase(synth.make_case(cfg))
+    dc.prepare_decode()
+    B, M = cfg.B, cfg.M
+    widths = (cfg.D // 2, cfg.D // 32, cfg.HI * cfg.DI)
+    host = [torch.empty((M, w), dtype=torch.uint8, pin_memory=True) for w in widths]
+    seq_bytes = M * sum(widths)
+    side = torch.cuda.Stream()
+
+    def copy_ms(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        fn(0)
+        side.synchronize()
+        e0.record(side)
+        for k in range(n):
+            fn(k % B)
+        e1.record(side)
+        side.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    off = copy_ms(lambda b: C.csa2_pool_offload(dc.latent, dc.scale, dc.idx_key, B, M, b, 0, M,
+                                                host[0], host[1], host[2], side), reps)
+    res = copy_ms(lambda b: C.csa2_pool_restore(dc.latent, dc.scale, dc.idx_key, B, M, b, 0, M,
+                                                host[0], host[1], host[2], side), reps)
+    # decode alone, then decode while restores stream in on the side stream
+    steps = 40
+    alone, _ = time_decode(dc, steps, 3)
+    main = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    n_res = max(1, int(round(steps * alone / max(res, 1e-3))))
+    torch.cuda.synchronize()
+    r0.record(side)
+    for k in range(n_res):
+        C.csa2_pool_restore(dc.latent, dc.scale, dc.idx_key, B, M, k % B, 0, M,
+                            host[0], host[1], host[2], side)
+    r1.record(side)
+    e0.record(main)
+    for _ in range(steps):
+        dc.decode_layers(main)
+    e1.record(main)
+    torch.cuda.synchronize()
+    busy = e0.elapsed_time(e1) / steps
+    rtime = r0.elapsed_time(r1)
+    del dc
+    torch.cuda.empty_cache()
+    return dict(sequence_bytes=seq_bytes, bytes_per_token=sum(widths) / cfg.ratio,
+                restore_ms=res, restore_gbs=seq_bytes / (res * 1e-3) / 1e9,
+                offload_ms=off, offload_gbs=seq_bytes / (off * 1e-3) / 1e9,
+                decode_ms_alone=alone, decode_ms_with_restores=busy,
+                restores_during_decode=n_res,
+                restore_gbs_during_decode=n_res * seq_bytes / (rtime * 1e-3) / 1e9)
+
+
 def step_detail(r) -> dict:
     """Per-layer, MALL-cold and all-Full figures of a decode workload."""
     if "per_layer_ms" not in r:
@@ -462,6 +528,11 @@ def main():
     extra[cfg.name] = step_detail(head)
     ap_res = measure_append(args.config)
     extra["pool_append_" + cfg.name] = ap_res
+    ht = measure_host_tier(args.config)
+    extra["host_tier_" + cfg.name] = ht
+    log("host tier: restore %.1f GB/s, offload %.1f GB/s; decode %.3f ms alone, %.3f ms beside "
+        "restores (%.1f GB/s)" % (ht["restore_gbs"], ht["offload_gbs"], ht["decode_ms_alone"],
+                                  ht["decode_ms_with_restores"], ht["restore_gbs_during_decode"]))
     log("pool append: %.1f GB/s bulk, %.1f us one entry per sequence" % (
         ap_res["bulk_gbs"], ap_res["one_entry_per_sequence_us"]))
     cpu = None

@@ -24,7 +24,8 @@ CSA2_OP_TOPK, CSA2_OP_SPARSE_ATTN, CSA2_OP_SWA_MERGE, CSA2_OP_DECODE_LAYERS = 0,
 CSA2_OP_PREFILL_LAYERS = 4
 
 EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
-           "csa2_pool_append", "csa2_swa_append",
+           "csa2_pool_append", "csa2_swa_append", "csa2_pool_restore", "csa2_pool_offload",
+           "csa2_swa_restore", "csa2_swa_offload",
            "csa2_decode_layers", "csa2_prefill_layers", "csa2_workspace_bytes",
            "csa2_status_string",
            "csa2_version")
@@ -77,6 +78,11 @@ def lib() -> ctypes.CDLL:
                                        c_void_p, c_void_p, c_int32, c_void_p]
         L.csa2_swa_append.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_int64, c_int32,
                                       c_void_p]
+        for fn in ("csa2_pool_restore", "csa2_pool_offload"):
+            getattr(L, fn).argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                       c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
+        for fn in ("csa2_swa_restore", "csa2_swa_offload"):
+            getattr(L, fn).argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]
         L.csa2_workspace_bytes.argtypes = [c_int, c_int32, c_int32, c_int32, c_int32, c_int32,
                                            c_int32, c_int32]
         L.csa2_workspace_bytes.restype = c_size_t
@@ -86,7 +92,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_version.restype = c_char_p
         for fn in ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
                    "csa2_decode_layers", "csa2_prefill_layers", "csa2_pool_append",
-                   "csa2_swa_append"):
+                   "csa2_swa_append", "csa2_pool_restore", "csa2_pool_offload",
+                   "csa2_swa_restore", "csa2_swa_offload"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -196,3 +203,27 @@ def csa2_prefill_layers(pool: csa2_pool, layers, Q: int, pos0: int, ratio: int, 
                                    _p(ws), ws_bytes, _s(stream))
     _check("csa2_prefill_layers", st, raise_on_error)
     return st, list(src)
+
+
+def csa2_pool_restore(latent, scale, idx_key, B: int, M: int, seq: int, entry0: int, n: int,
+                      h_latent, h_scale, h_key, stream=None, raise_on_error=True) -> int:
+    st = lib().csa2_pool_restore(_p(latent), _p(scale), _p(idx_key), B, M, seq, entry0, n,
+                                 _p(h_latent), _p(h_scale), _p(h_key), _s(stream))
+    return _check("csa2_pool_restore", st, raise_on_error)
+
+
+def csa2_pool_offload(latent, scale, idx_key, B: int, M: int, seq: int, entry0: int, n: int,
+                      h_latent, h_scale, h_key, stream=None, raise_on_error=True) -> int:
+    st = lib().csa2_pool_offload(_p(latent), _p(scale), _p(idx_key), B, M, seq, entry0, n,
+                                 _p(h_latent), _p(h_scale), _p(h_key), _s(stream))
+    return _check("csa2_pool_offload", st, raise_on_error)
+
+
+def csa2_swa_restore(swa, B: int, W: int, seq: int, h_swa, stream=None, raise_on_error=True) -> int:
+    st = lib().csa2_swa_restore(_p(swa), B, W, seq, _p(h_swa), _s(stream))
+    return _check("csa2_swa_restore", st, raise_on_error)
+
+
+def csa2_swa_offload(swa, B: int, W: int, seq: int, h_swa, stream=None, raise_on_error=True) -> int:
+    st = lib().csa2_swa_offload(_p(swa), B, W, seq, _p(h_swa), _s(stream))
+    return _check("csa2_swa_offload", st, raise_on_error)

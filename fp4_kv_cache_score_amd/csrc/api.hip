@@ -507,6 +507,69 @@ csa2_status csa2_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key, 
   return hip_status(launch_pool_append(latent, scale, idx_key, B, M, x_latent, x_key, slot, T, stream));
 }
 
+// Host tier: one sequence's entries (or window ring) between page-locked host
+// memory and the device arrays, by the copy engines on the caller's stream.
+static csa2_status pool_transfer(uint8_t* latent, uint8_t* scale, uint8_t* idx_key, int32_t B,
+                                 int32_t M, int32_t seq, int32_t entry0, int32_t n,
+                                 uint8_t* h_latent, uint8_t* h_scale, uint8_t* h_key, bool to_device,
+                                 hipStream_t stream) {
+  if (!latent || !scale || !idx_key || !h_latent || !h_scale || !h_key) return CSA2_ERR_NULL;
+  if (B <= 0 || M <= 0 || seq < 0 || seq >= B || entry0 < 0 || n < 0 || (int64_t)entry0 + n > M)
+    return CSA2_ERR_SHAPE;
+  if (n == 0) return CSA2_OK;
+  const size_t e0 = (size_t)seq * (size_t)M + (size_t)entry0;
+  const hipMemcpyKind kind = to_device ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+  const struct { uint8_t* dev; uint8_t* host; size_t row; } parts[3] = {
+      {latent, h_latent, (size_t)kLatRow}, {scale, h_scale, (size_t)kScaleRow},
+      {idx_key, h_key, (size_t)kKeyRow}};
+  for (const auto& q : parts) {
+    uint8_t* d = q.dev + e0 * q.row;
+    const size_t bytes = (size_t)n * q.row;
+    const hipError_t e = to_device ? hipMemcpyAsync(d, q.host, bytes, kind, stream)
+                                   : hipMemcpyAsync(q.host, d, bytes, kind, stream);
+    if (e != hipSuccess) return CSA2_ERR_HIP;
+  }
+  return CSA2_OK;
+}
+
+csa2_status csa2_pool_restore(uint8_t* latent, uint8_t* scale, uint8_t* idx_key, int32_t B,
+                              int32_t M, int32_t seq, int32_t entry0, int32_t n,
+                              const uint8_t* h_latent, const uint8_t* h_scale, const uint8_t* h_key,
+                              hipStream_t stream) {
+  return pool_transfer(latent, scale, idx_key, B, M, seq, entry0, n, const_cast<uint8_t*>(h_latent),
+                       const_cast<uint8_t*>(h_scale), const_cast<uint8_t*>(h_key), true, stream);
+}
+
+csa2_status csa2_pool_offload(const uint8_t* latent, const uint8_t* scale, const uint8_t* idx_key,
+                              int32_t B, int32_t M, int32_t seq, int32_t entry0, int32_t n,
+                              uint8_t* h_latent, uint8_t* h_scale, uint8_t* h_key,
+                              hipStream_t stream) {
+  return pool_transfer(const_cast<uint8_t*>(latent), const_cast<uint8_t*>(scale),
+                       const_cast<uint8_t*>(idx_key), B, M, seq, entry0, n, h_latent, h_scale, h_key,
+                       false, stream);
+}
+
+static csa2_status swa_transfer(uint8_t* swa, int32_t B, int32_t W, int32_t seq, uint8_t* h_swa,
+                                bool to_device, hipStream_t stream) {
+  if (!swa || !h_swa) return CSA2_ERR_NULL;
+  if (B <= 0 || W <= 0 || seq < 0 || seq >= B) return CSA2_ERR_SHAPE;
+  uint8_t* d = swa + (size_t)seq * (size_t)W * kD;
+  const size_t bytes = (size_t)W * kD;
+  const hipError_t e = to_device ? hipMemcpyAsync(d, h_swa, bytes, hipMemcpyHostToDevice, stream)
+                                 : hipMemcpyAsync(h_swa, d, bytes, hipMemcpyDeviceToHost, stream);
+  return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+csa2_status csa2_swa_restore(uint8_t* swa, int32_t B, int32_t W, int32_t seq, const uint8_t* h_swa,
+                             hipStream_t stream) {
+  return swa_transfer(swa, B, W, seq, const_cast<uint8_t*>(h_swa), true, stream);
+}
+
+csa2_status csa2_swa_offload(const uint8_t* swa, int32_t B, int32_t W, int32_t seq, uint8_t* h_swa,
+                             hipStream_t stream) {
+  return swa_transfer(const_cast<uint8_t*>(swa), B, W, seq, h_swa, false, stream);
+}
+
 csa2_status csa2_swa_append(uint8_t* swa, int32_t B, int32_t W, const float* x, int64_t pos0,
                             int32_t T, hipStream_t stream) {
   if (!swa || !x) return CSA2_ERR_NULL;

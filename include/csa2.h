@@ -280,6 +280,47 @@ csa2_status csa2_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key,
 csa2_status csa2_swa_append(uint8_t* swa, int32_t B, int32_t W, const float* x,
                             int64_t pos0, int32_t T, hipStream_t stream);
 
+/* Host tier: one sequence's pool entries between host memory and the device
+ * pool, by the copy engines on `stream`.  The pages keep the runtime copy of
+ * the KV in HBM and a longer-lived copy outside it: the sliding-window KV in a
+ * host-memory pool and the global KV in a persistent cache ("DeepSeek V4.1
+ * Flash Architecture Breakdown", section "How are cache precision and storage
+ * arranged?"; "... Cuts KV Cache by 437x", paragraph on the cache tiers).
+ * These calls move the stored bytes unchanged (the FP4 / FP8 encodings are
+ * the transfer format: 784 B per pool entry, 196 B per token at 4 tokens per
+ * entry).
+ *   latent, scale, idx_key  the device pool arrays [B][M][256], [B][M][16],
+ *                           [B][M][8][64]
+ *   seq, entry0, n          entries entry0 .. entry0+n-1 of sequence seq
+ *   h_latent, h_scale, h_key  host [n][256], [n][16], [n][8][64] (host
+ *                           pointers; page-locked memory, e.g. hipHostMalloc,
+ *                           lets the copies run asynchronously beside
+ *                           kernels on other streams; pageable memory works but
+ *                           the call may block until the copy is done)
+ * Restore copies host -> device, offload device -> host.  Errors:
+ * CSA2_ERR_NULL, CSA2_ERR_SHAPE (B, M <= 0, seq outside [0, B), entry0 < 0,
+ * n < 0, entry0 + n > M), CSA2_ERR_HIP (a copy could not be enqueued).
+ * n == 0 returns CSA2_OK without a copy. */
+csa2_status csa2_pool_restore(uint8_t* latent, uint8_t* scale, uint8_t* idx_key,
+                              int32_t B, int32_t M, int32_t seq, int32_t entry0,
+                              int32_t n, const uint8_t* h_latent,
+                              const uint8_t* h_scale, const uint8_t* h_key,
+                              hipStream_t stream);
+csa2_status csa2_pool_offload(const uint8_t* latent, const uint8_t* scale,
+                              const uint8_t* idx_key, int32_t B, int32_t M,
+                              int32_t seq, int32_t entry0, int32_t n,
+                              uint8_t* h_latent, uint8_t* h_scale, uint8_t* h_key,
+                              hipStream_t stream);
+
+/* One sequence's window ring ([W][512] E4M3, as csa2_swa_append keeps it)
+ * between host memory h_swa [W][512] and the device rings swa [B][W][512].
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (B, W <= 0, seq outside [0, B)),
+ * CSA2_ERR_HIP. */
+csa2_status csa2_swa_restore(uint8_t* swa, int32_t B, int32_t W, int32_t seq,
+                             const uint8_t* h_swa, hipStream_t stream);
+csa2_status csa2_swa_offload(const uint8_t* swa, int32_t B, int32_t W, int32_t seq,
+                             uint8_t* h_swa, hipStream_t stream);
+
 /* Workspace bytes needed by an entry point (op = CSA2_OP_*).  Arguments that
  * an op does not use are ignored.  For CSA2_OP_TOPK, B is the row count R and
  * M the row length N.  Returns 0 for an unknown op or bad sizes. */

@@ -223,3 +223,28 @@ def test_prefill_layers_schedule_and_argument_errors():
     assert run([_layer(F)], pool=_pool(M=0)) == C.CSA2_ERR_SHAPE
     # no causal limit: ratio is not used
     assert run([_layer(F)], pos0=-1, ratio=0) == C.CSA2_ERR_WORKSPACE
+
+
+def test_host_tier_argument_errors():
+    H = 0x30000   # a fake host address: never dereferenced here
+
+    def restore(**kw):
+        a = dict(latent=A, scale=A, idx_key=A, B=2, M=100, seq=1, entry0=10, n=5, h=H)
+        a.update(kw)
+        return C.csa2_pool_restore(a["latent"], a["scale"], a["idx_key"], a["B"], a["M"], a["seq"],
+                                   a["entry0"], a["n"], a["h"], a["h"], a["h"], 0,
+                                   raise_on_error=False)
+
+    assert restore(latent=None) == C.CSA2_ERR_NULL
+    assert restore(h=None) == C.CSA2_ERR_NULL
+    assert restore(seq=2) == C.CSA2_ERR_SHAPE
+    assert restore(seq=-1) == C.CSA2_ERR_SHAPE
+    assert restore(entry0=96) == C.CSA2_ERR_SHAPE           # entry0 + n > M
+    assert restore(n=-1) == C.CSA2_ERR_SHAPE
+    assert restore(M=0) == C.CSA2_ERR_SHAPE
+    assert restore(n=0) == C.CSA2_OK                        # nothing to copy, no HIP call
+    assert C.csa2_pool_offload(A, A, A, 2, 100, 0, 0, 101, H, H, H, 0,
+                               raise_on_error=False) == C.CSA2_ERR_SHAPE
+    assert C.csa2_swa_restore(A, 2, 128, 2, H, 0, raise_on_error=False) == C.CSA2_ERR_SHAPE
+    assert C.csa2_swa_restore(A, 2, 0, 0, H, 0, raise_on_error=False) == C.CSA2_ERR_SHAPE
+    assert C.csa2_swa_offload(A, 2, 128, 0, None, 0, raise_on_error=False) == C.CSA2_ERR_NULL
