@@ -374,6 +374,31 @@ def measure_append(ci: int, launches: int = 10):
                 window_ms=win, window_gbs=win_bytes / (win * 1e-3) / 1e9)
 
 
+def measure_ragged(ci: int, steps: int, warmup: int):
+    """A ragged batch at a decode workload's shape: sequence b holds a seeded
+    uniform share of the M entry slots (M/8 .. M); step time and the step's
+    algorithmic bytes (scans and candidate gathers scale with each length)."""
+    import torch
+    from fp4_kv_cache_score_amd import synth
+    from fp4_kv_cache_score_amd.configs import CONFIGS, algorithmic_bytes
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[ci]
+    rng = np.random.default_rng(cfg.seed + 1000)
+    lens = rng.integers(cfg.M // 8, cfg.M + 1, cfg.B)
+    dc = DeviceCase(synth.make_case(cfg))
+    dc.use_lengths(lens)
+    ms, _ = time_decode(dc, steps, warmup)
+    full = algorithmic_bytes(cfg)
+    frac = float(lens.sum()) / (cfg.B * cfg.M)
+    ragged_bytes = full["total"] - full["scan"] * (1.0 - frac)
+    del dc
+    torch.cuda.empty_cache()
+    return dict(lengths_mean=float(lens.mean()), lengths_min=int(lens.min()),
+                lengths_max=int(lens.max()), ms_per_step=ms,
+                query_tokens_per_s=cfg.B / (ms * 1e-3),
+                step_hbm_gbs=ragged_bytes / (ms * 1e-3) / 1e9)
+
+
 def measure_host_tier(ci: int, reps: int = 5):
     """Host tier at a decode workload's pool shape: one sequence's whole pool
     (M entries x 784 B) restored from / offloaded to page-locked host memory,
@@ -528,6 +553,10 @@ def main():
     extra[cfg.name] = step_detail(head)
     ap_res = measure_append(args.config)
     extra["pool_append_" + cfg.name] = ap_res
+    rg = measure_ragged(args.config, args.steps, args.warmup)
+    extra["ragged_" + cfg.name] = rg
+    log("ragged batch (mean length %.0f of %d): %.3f ms/step, %.1f GB/s" % (
+        rg["lengths_mean"], cfg.M, rg["ms_per_step"], rg["step_hbm_gbs"]))
     ht = measure_host_tier(args.config)
     extra["host_tier_" + cfg.name] = ht
     log("host tier: restore %.1f GB/s, offload %.1f GB/s; decode %.3f ms alone, %.3f ms beside "

@@ -34,7 +34,7 @@ EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge"
 class csa2_pool(ctypes.Structure):
     _fields_ = [("latent", c_void_p), ("scale", c_void_p), ("idx_key", c_void_p),
                 ("B", c_int32), ("M", c_int32), ("D", c_int32), ("HI", c_int32),
-                ("DI", c_int32)]
+                ("DI", c_int32), ("len", c_void_p)]
 
 
 class csa2_layer(ctypes.Structure):
@@ -123,8 +123,9 @@ def _check(fn, st, raise_on_error):
 
 
 def make_pool(latent, scale, idx_key, B: int, M: int, D: int = 512, HI: int = 8,
-              DI: int = 64) -> csa2_pool:
-    return csa2_pool(_p(latent), _p(scale), _p(idx_key), B, M, D, HI, DI)
+              DI: int = 64, len=None) -> csa2_pool:
+    """len: None, or a device int32 tensor [B] of per-sequence entry counts."""
+    return csa2_pool(_p(latent), _p(scale), _p(idx_key), B, M, D, HI, DI, _p(len))
 
 
 def csa2_status_string(status: int) -> str:

@@ -15,7 +15,8 @@ csa2_status check_pool(const csa2_pool* p) {
   if (!p || !p->latent || !p->scale || !p->idx_key) return CSA2_ERR_NULL;
   if (p->B <= 0 || p->M <= 0 || p->M > kMaxTopkN) return CSA2_ERR_SHAPE;
   if (p->D != kD || p->HI != kHI || p->DI != kDI) return CSA2_ERR_SHAPE;
-  if (!al16(p->latent) || !al16(p->scale) || !al16(p->idx_key)) return CSA2_ERR_ALIGN;
+  if (!al16(p->latent) || !al16(p->scale) || !al16(p->idx_key) || !al4(p->len))
+    return CSA2_ERR_ALIGN;
   return CSA2_OK;
 }
 
@@ -186,11 +187,12 @@ csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx, const 
     if (hist) return CSA2_ERR_SHAPE;
     return hip_status(launch_prefill_score(pool->idx_key, pool->B, pool->M, pool->M, q_idx, w_idx,
                                            Q, pos0, pos0 >= 0 ? ratio : 1, scores, nullptr,
-                                           stream));
+                                           pool->len, stream));
   }
   const int32_t N = cand ? P : pool->M;
   return hip_status(launch_index_score(pool->idx_key, pool->B, pool->M, q_idx, w_idx, Q, pos0,
-                                       pos0 >= 0 ? ratio : 1, cand, N, scores, hist, stream));
+                                       pos0 >= 0 ? ratio : 1, cand, N, scores, hist, pool->len,
+                                       stream));
 }
 
 csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* n_valid,
@@ -328,40 +330,40 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     const csa2_layer& y = layers[l];
     if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         nullptr, (int32_t)M, d.scores, nullptr, stream));
+                                         nullptr, (int32_t)M, d.scores, nullptr, pool->len, stream));
       if (st != CSA2_OK) return st;
       if (!d.big) {
         if (y.mode == CSA2_FULL && P > 0) {
-          st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M,
+          st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
                                            P, nullptr, false, nullptr, d.cand, stream));
           if (st != CSA2_OK) return st;
         }
-        st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, K,
+        st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, K,
                                          nullptr, false, nullptr, y.idx_out, stream));
         if (st != CSA2_OK) return st;
       } else {
-        st = hip_status(launch_topk_hist(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M,
+        st = hip_status(launch_topk_hist(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
                                          d.t.hist, stream));
         if (st != CSA2_OK) return st;
         if (y.mode == CSA2_FULL && P > 0 && n_cand <= kRowMaxN) {
           // Top-P over the row, then Top-K over the P candidates' scores: the
           // candidates hold the Top-K (same order, K <= P), and their list is
           // ascending, so the lower-index tie-break is kept.
-          st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P,
+          st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, nullptr, P,
                                d.cand, d.t, true, stream);
           if (st != CSA2_OK) return st;
           st = hip_status(launch_gather_scores(d.scores, (int32_t)B, M, d.cand, P, d.cscore, stream));
           if (st != CSA2_OK) return st;
-          st = hip_status(launch_topk_rows(d.cscore, (int32_t)B, P, nullptr, n_cand, K, nullptr,
+          st = hip_status(launch_topk_rows(d.cscore, (int32_t)B, P, pool->len, n_cand, K, nullptr,
                                            false, d.cand, y.idx_out, stream));
           if (st != CSA2_OK) return st;
         } else {
           if (y.mode == CSA2_FULL && P > 0) {
-            st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, P,
+            st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, nullptr, P,
                                  d.cand, d.t, false, stream);
             if (st != CSA2_OK) return st;
           }
-          st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, nullptr, (int32_t)M, nullptr, K,
+          st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, nullptr, K,
                                y.idx_out, d.t, true, stream);
           if (st != CSA2_OK) return st;
         }
@@ -370,9 +372,10 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
       cur_layer = l;
     } else if (y.mode == CSA2_REINDEX) {  // hierarchical: score inside the candidate pool
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         d.cand, P, d.scores, nullptr, stream));
+                                         d.cand, P, d.scores, nullptr, pool->len, stream));
       if (st != CSA2_OK) return st;
-      st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, nullptr, n_cand, K, nullptr, false,
+      // a ragged sequence has min(P, len) candidates (the row kernel clamps len to P)
+      st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, pool->len, n_cand, K, nullptr, false,
                                        d.cand, y.idx_out, stream));
       if (st != CSA2_OK) return st;
       cur = y.idx_out;
@@ -447,7 +450,7 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
       } else {
         st = hip_status(launch_prefill_score(pool->idx_key, (int32_t)B, M, (int32_t)N, y.q_idx,
                                              y.w_idx, Q, pos0, pos0 >= 0 ? ratio : 1, scores,
-                                             n_valid, stream));
+                                             n_valid, pool->len, stream));
         if (st != CSA2_OK) return st;
         if (!big) {
           st = hip_status(launch_topk_rows(scores, (int32_t)R, (int32_t)N, n_valid, (int32_t)N, K,

@@ -93,13 +93,13 @@ inline TopkWs topk_ws_carve(void* ws, int64_t R, int64_t N, int64_t K) {
 // Zero n 32-bit words (a kernel, so that it is safe inside captured graphs).
 hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t s);
 
-// Indexer scores; see csa2_index_score.  n_valid_rows (optional, [rows]) is
-// written with each row's count of scored positions.
+// Indexer scores; see csa2_index_score.  len (optional, [B]): sequence b has
+// len[b] <= M entries (a ragged batch); entries at or past it score -inf.
 hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
                               const uint8_t* q_idx, const float* w_idx,
                               int32_t Q, int64_t pos0, int32_t ratio,
                               const int32_t* cand, int32_t N, float* scores,
-                              uint32_t* hist, hipStream_t s);
+                              uint32_t* hist, const int32_t* len, hipStream_t s);
 
 // Top-K pieces.  n_valid: device [R] or NULL (then n_all applies to every row).
 // launch_topk_rows: one work-group per row, N <= kRowMaxN.  hist: NULL (the
@@ -188,7 +188,8 @@ hipError_t launch_window_append(uint8_t* swa, int32_t B, int32_t W, const float*
 // (optional, [B][Q]) receives each query's count of visible entries.
 hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_t N,
                                 const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
-                                int32_t ratio, float* scores, int32_t* n_valid, hipStream_t s);
+                                int32_t ratio, float* scores, int32_t* n_valid, const int32_t* len,
+                                hipStream_t s);
 // One work-group per query row over its K selected entries and W window rows;
 // writes a.o / a.lse, merged with (o_in, lse_in) when lse_in is given (they
 // may alias a.o / a.lse).

@@ -38,7 +38,8 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
                    const uint8_t* __restrict__ q_idx,
                    const float* __restrict__ w_idx, int32_t Q, int64_t pos0,
                    int32_t ratio, const int32_t* __restrict__ cand, int32_t N,
-                   float* __restrict__ scores, uint32_t* __restrict__ hist) {
+                   float* __restrict__ scores, uint32_t* __restrict__ hist,
+                   const int32_t* __restrict__ len) {
   constexpr int kEntriesPerWG = EPW * (kThreads / 64);
   constexpr int kIters = EPW / (2 * kUnroll);
   static_assert(EPW % (2 * kUnroll) == 0, "EPW must be a multiple of 16");
@@ -53,11 +54,12 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
   const int sub = lane & 31;
   const int head = sub >> 2;
 
-  // Entries visible to this query (all of them when there is no causal limit).
-  int64_t vis = M;
+  // Entries visible to this query: the sequence's length (M, or len[b] for a
+  // ragged batch), within the causal limit when there is one.
+  int64_t vis = len ? (int64_t)len[b] : M;
   if (pos0 >= 0) {
     const int64_t v = (pos0 + t + 1) / ratio;
-    vis = v < M ? v : M;
+    vis = v < vis ? v : vis;
   }
 
   const int64_t g0 = (int64_t)blockIdx.x * kEntriesPerWG;
@@ -151,19 +153,19 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
 template <int EPW>
 void launch_epw(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
                 const float* w_idx, int32_t Q, int64_t pos0, int32_t ratio, const int32_t* cand,
-                int32_t N, float* scores, uint32_t* hist, hipStream_t s) {
+                int32_t N, float* scores, uint32_t* hist, const int32_t* len, hipStream_t s) {
   const dim3 grid((unsigned)((N + EPW * 4 - 1) / (EPW * 4)), (unsigned)(B * Q));
   const dim3 block(kThreads);
   if (cand) {
     if (hist)
-      k_index_score<EPW, true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+      k_index_score<EPW, true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len);
     else
-      k_index_score<EPW, true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+      k_index_score<EPW, true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len);
   } else {
     if (hist)
-      k_index_score<EPW, false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+      k_index_score<EPW, false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len);
     else
-      k_index_score<EPW, false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist);
+      k_index_score<EPW, false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len);
   }
 }
 
@@ -173,15 +175,15 @@ hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
                               const uint8_t* q_idx, const float* w_idx,
                               int32_t Q, int64_t pos0, int32_t ratio,
                               const int32_t* cand, int32_t N, float* scores,
-                              uint32_t* hist, hipStream_t s) {
+                              uint32_t* hist, const int32_t* len, hipStream_t s) {
   // 64 entries per wave (256 per work-group) keep enough loads in flight on
   // long rows; short rows (candidate pools) take 32 so that the launch still
   // has >= 1024 work-groups.
   const int64_t rows = (int64_t)B * Q;
   if (rows * ((N + 255) / 256) >= 1024)
-    launch_epw<64>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, s);
+    launch_epw<64>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, s);
   else
-    launch_epw<32>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, s);
+    launch_epw<32>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, s);
   return hipGetLastError();
 }
 

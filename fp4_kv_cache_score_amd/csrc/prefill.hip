@@ -61,6 +61,7 @@ constexpr int kSE = 128;                 // pool entries per work-group tile
 constexpr int kSThreads = 256;
 constexpr int kSRow = 128 + 16;          // LDS bytes per staged row (64 bf16 of one head + pad)
 
+// Entries query t sees: the first M (the sequence's length), within the causal limit.
 __device__ __forceinline__ int64_t visible(int64_t pos0, int32_t t, int32_t ratio, int64_t M) {
   if (pos0 < 0) return M;
   const int64_t v = (pos0 + t + 1) / ratio;
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kSThreads, 2)
 void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
                      const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
                      int32_t Q, int64_t pos0, int32_t ratio, float* __restrict__ scores,
-                     int32_t* __restrict__ n_valid) {
+                     int32_t* __restrict__ n_valid, const int32_t* __restrict__ len) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[2][kSQ * kSRow];
   __shared__ __attribute__((aligned(16))) uint8_t ks[2][kSE * kSRow];
   __shared__ __attribute__((aligned(16))) float ws[kHI][kSQ];   // head weights, rows contiguous
@@ -90,11 +91,12 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   const uint8_t* qb = q_idx + (size_t)b * Q * kKeyRow;
   const uint8_t* kb = key + (size_t)b * (size_t)M * kKeyRow;
   float* sb = scores + (size_t)b * Q * (size_t)N;
+  const int64_t Ms = len ? (int64_t)len[b] : M;           // this sequence's entries
   if (n_valid && blockIdx.x == 0 && tid < kSQ && q0 + tid < Q)
-    n_valid[(size_t)b * Q + q0 + tid] = (int32_t)visible(pos0, q0 + tid, ratio, M);
+    n_valid[(size_t)b * Q + q0 + tid] = (int32_t)visible(pos0, q0 + tid, ratio, Ms);
 
   const int qlast = (q0 + kSQ < Q ? q0 + kSQ : Q) - 1;
-  if (e0 >= visible(pos0, qlast, ratio, M)) {   // no query of the tile sees these entries
+  if (e0 >= visible(pos0, qlast, ratio, Ms)) {   // no query of the tile sees these entries
     for (int i = tid; i < kSQ * kSE; i += kSThreads) {
       const int r = i / kSE, c = i - r * kSE;
       if (q0 + r < Q && e0 + c < N) sb[(size_t)(q0 + r) * N + e0 + c] = -INFINITY;
@@ -106,7 +108,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
     const int r = i / kHI, h = i - r * kHI;
     ws[h][r] = q0 + r < Q ? w_idx[((size_t)b * Q + q0 + r) * kHI + h] : 0.f;
   }
-  if (tid < kSQ) vis_s[tid] = (int32_t)visible(pos0, q0 + tid, ratio, M);   // one division per row
+  if (tid < kSQ) vis_s[tid] = (int32_t)visible(pos0, q0 + tid, ratio, Ms);   // one division per row
 
   // staging: thread -> two (row, 16-byte part) pieces of each of Q and K.
   // Rows past Q or N load the last row instead (never written out), so the
@@ -592,11 +594,12 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const
 
 hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_t N,
                                 const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
-                                int32_t ratio, float* scores, int32_t* n_valid, hipStream_t s) {
+                                int32_t ratio, float* scores, int32_t* n_valid, const int32_t* len,
+                                hipStream_t s) {
   if (N <= 0 || N > M || Q <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + kSE - 1) / kSE), (unsigned)((Q + kSQ - 1) / kSQ), (unsigned)B);
   k_prefill_score<<<grid, dim3(kSThreads), 0, s>>>(key, M, N, q_idx, w_idx, Q, pos0, ratio, scores,
-                                                   n_valid);
+                                                   n_valid, len);
   return hipGetLastError();
 }
 

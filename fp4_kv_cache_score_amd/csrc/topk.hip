@@ -673,18 +673,26 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
         }
       }
     };
-    if (sh >= 30) {
-      // The prefix lies in the score bits: with lo / hi the floats whose
-      // order keys are prefix << ks and (prefix + 1) << ks, a score is above
-      // the prefix iff s >= hi and inside it iff lo <= s < hi (order keys
-      // are monotone in the real value), so most elements cost two compares.
+    // The prefix lies in the score bits: with lo / hi the floats whose order
+    // keys are prefix << ks and (prefix + 1) << ks, a score is above the
+    // prefix iff s >= hi and inside it iff lo <= s < hi (order keys are
+    // monotone in the real value), so most elements cost two compares.  The
+    // lowest keys (-inf and below) have no float bound (their pattern is a
+    // NaN): there the keys themselves are compared.
+    bool fast = sh >= 30;
+    bool top = false;
+    float flo = 0.f, fhi = 0.f;
+    if (fast) {
       const int ks = sh - 30;
       const uint32_t pre = (uint32_t)prefix;
       const uint32_t klo = pre << ks;
-      const bool top = (ks == 0) ? (pre == 0xFFFFFFFFu) : ((pre + 1u) >> (32 - ks)) != 0u;
+      top = (ks == 0) ? (pre == 0xFFFFFFFFu) : ((pre + 1u) >> (32 - ks)) != 0u;
       const uint32_t khi = top ? 0xFFFFFFFFu : (pre + 1u) << ks;
-      const float flo = key_float(klo);
-      const float fhi = key_float(khi);
+      flo = key_float(klo);
+      fhi = key_float(khi);
+      fast = !__builtin_isnan(flo) && (top || !__builtin_isnan(fhi));
+    }
+    if (fast) {
       visit_pre_f([&](float s, int32_t p) {
         if (s >= flo) {
           const bool above = !top && s >= fhi;

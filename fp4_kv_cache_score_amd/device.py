@@ -49,6 +49,13 @@ class DeviceCase:
         self.ws_bytes = 0
         self.src_layer: Optional[List[int]] = None
 
+    def use_lengths(self, lens) -> None:
+        """Make the batch ragged: sequence b holds its first lens[b] entries."""
+        cfg = self.cfg
+        self.lens = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(self.device)
+        self.pool = C.make_pool(self.latent, self.scale, self.idx_key, cfg.B, cfg.M, cfg.D,
+                                cfg.HI, cfg.DI, len=self.lens)
+
     # -- workspace -----------------------------------------------------------
     def _workspace(self, nbytes: int) -> torch.Tensor:
         if self.ws is None or self.ws_bytes < nbytes:

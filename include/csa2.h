@@ -68,17 +68,23 @@ enum {
   CSA2_OP_PREFILL_LAYERS = 4
 };
 
-/* The shared global KV pool: B sequences of M compressed entries each.
- * Every sequence has its own M entries (structure of arrays):
+/* The shared global KV pool: B sequences of up to M compressed entries each.
+ * Every sequence has its own M entry slots (structure of arrays):
  *   latent  [B][M][D/2]     E2M1 codes of the D-wide shared K/V latent
  *   scale   [B][M][D/32]    E8M0 block scales of the latent
  *   idx_key [B][M][HI][DI]  E4M3 indexer keys
- * All three pointers must be 16-byte aligned. */
+ *   len     NULL: every sequence holds M entries.  Otherwise device [B]
+ *           int32 in [0, M]: sequence b holds entries 0 .. len[b]-1 (a
+ *           ragged batch, the serving shape); the scans read no key past
+ *           len[b], such entries score -inf and are never selected.  (Not
+ *           checked on the device: values outside [0, M] are not allowed.)
+ * latent, scale and idx_key must be 16-byte aligned, len 4-byte aligned. */
 typedef struct csa2_pool {
   const uint8_t* latent;
   const uint8_t* scale;
   const uint8_t* idx_key;
   int32_t B, M, D, HI, DI;
+  const int32_t* len;
 } csa2_pool;
 
 /* One layer of a decode step (one query token per sequence).

@@ -146,6 +146,8 @@ def map_positions(pos, cand) -> np.ndarray:
     """Candidate-pool positions -> global pool indices (-1 stays -1)."""
     pos = np.asarray(pos)
     cand = np.asarray(cand)
+    if cand.size == 0:                      # an empty candidate list selects nothing
+        return np.full(pos.shape, -1, np.int64)
     return np.where(pos >= 0, cand[np.maximum(pos, 0)], -1)
 
 

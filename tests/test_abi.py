@@ -248,3 +248,9 @@ def test_host_tier_argument_errors():
     assert C.csa2_swa_restore(A, 2, 128, 2, H, 0, raise_on_error=False) == C.CSA2_ERR_SHAPE
     assert C.csa2_swa_restore(A, 2, 0, 0, H, 0, raise_on_error=False) == C.CSA2_ERR_SHAPE
     assert C.csa2_swa_offload(A, 2, 128, 0, None, 0, raise_on_error=False) == C.CSA2_ERR_NULL
+
+
+def test_pool_length_array_alignment():
+    pool = _pool()
+    pool.len = A + 2
+    assert _score(pool) == C.CSA2_ERR_ALIGN

@@ -175,3 +175,19 @@ def test_prefill_last_query_sees_all_and_matches_truncated_decode():
                                     q=L.q[0, t], swa=L.swa[0, t:t + cfg.W])], K=cfg.K)[0]
         assert np.array_equal(r["idx"], d["idx"]) and np.array_equal(r["o"], d["o"])
     assert (cfg.pos0 + 23 + 1) // 4 == 96
+
+
+@pytest.mark.parametrize("P", [0, 16])
+def test_short_and_empty_pools(P):
+    # a sequence holding fewer entries than K selects all of them, in order, in
+    # every indexing layer; one holding none attends to its window rows alone
+    case = _small_case(M=64, K=8, W=4, modes=(FULL, REINDEX, REUSE), P=P, seed=12)
+    p = case.pool
+    layers = _layers(case)
+    for n in (0, 1, 5, 8):
+        recs = O.decode_sequence(p.latent[0, :n], p.scale[0, :n], p.idx_key[0, :n], layers, K=8, P=P)
+        for rec, L in zip(recs, layers):
+            assert rec["idx"].tolist() == list(range(n)) + [-1] * (8 - n), (n, rec["mode"])
+            if n == 0:
+                o, lse = O.attend(L["q"], F.e4m3_value(L["swa"]))
+                assert np.array_equal(rec["o"], o) and np.array_equal(rec["lse"], lse)
