@@ -241,6 +241,7 @@ def measure_prefill(ci: int, steps: int, warmup: int):
     sched = (FULL, REINDEX, REUSE, REUSE)
     c4 = cfg.scaled(modes=sched)
     dc = DeviceCase(synth.make_case(c4))
+    dc.prepare_prefill_layers(idx_for_reuse=False)     # Reuse layers alias their source's indices
     ms4 = _time_calls(dc.prefill_layers, steps, warmup)
     res["schedule_F_Ri_Ru_Ru"] = dict(ms_per_chunk=ms4,
                                       query_tokens_per_s=c4.B * c4.Q / (ms4 * 1e-3))
