@@ -607,11 +607,53 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
     for (int i = tid; i < K; i += kRowThreads) orow[i] = i < n ? (mrow ? mrow[i] : i) : -1;
     return;
   }
-  if (!kHasHist) {
+  // The first digit: 12 key bits from bit kbit up.  With a histogram from
+  // the score kernel, or a row streamed from memory, it is the top 12 bits.
+  // For a row held in registers it starts just below the bits that every key
+  // of the row shares (the common prefix of its smallest and largest keys,
+  // which all keys between them share too), so that the 4096 bins spread over
+  // the values the row actually holds instead of the few that share its
+  // exponent (fewer same-bin LDS atomics; no extra pass over memory).
+  int kbit = 32 - kHistBits;
+  uint32_t common = 0u;   // key bits above the first digit
+  if (!kHasHist && !kPre) {
     for (int i = tid; i < kHistBins; i += kRowThreads) L.hist[i] = 0u;
     __syncthreads();
     visit_pre([&](uint32_t key, int32_t) {
       atomicAdd(&L.hist[key >> (32 - kHistBits)], 1u);
+    });
+  } else if (!kHasHist) {
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    visit_pre([&](uint32_t key, int32_t) {
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    }
+    uint32_t* red = L.ckey;   // free until the collection step
+    if ((tid & 63) == 0) {
+      red[tid >> 6] = kmin;
+      red[kRowThreads / 64 + (tid >> 6)] = kmax;
+    }
+    for (int i = tid; i < kHistBins; i += kRowThreads) L.hist[i] = 0u;
+    __syncthreads();
+    kmin = red[0];
+    kmax = red[kRowThreads / 64];
+#pragma unroll
+    for (int w = 1; w < kRowThreads / 64; ++w) {
+      kmin = min(kmin, red[w]);
+      kmax = max(kmax, red[kRowThreads / 64 + w]);
+    }
+    const uint32_t diff = kmin ^ kmax;
+    const int h = diff ? 31 - __builtin_clz(diff) : 0;          // highest bit where keys differ
+    kbit = h >= kHistBits - 1 ? h - (kHistBits - 1) : 0;
+    common = kbit + kHistBits >= 32 ? 0u : kmax >> (kbit + kHistBits);
+    const int kb = kbit;
+    visit_pre([&](uint32_t key, int32_t) {
+      atomicAdd(&L.hist[(key >> kb) & (kHistBins - 1)], 1u);
     });
   }
   __syncthreads();
@@ -621,9 +663,9 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   // Invariant: the composites whose bits above `shift` exceed `prefix` are
   // all selected (K - need of them); `need` more come from the `cnt`
   // composites whose bits above `shift` equal `prefix`.
-  uint64_t prefix = d;
+  uint64_t prefix = ((uint64_t)common << kHistBits) | d;
   uint32_t need = (uint32_t)K - ab;
-  int shift = 50;
+  int shift = 30 + kbit;
   bool all = cnt == need;
 
   // 2. Refine by streaming passes until the prefix's members fit in LDS.
