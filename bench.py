@@ -206,7 +206,7 @@ def _prefill_flops(cfg, pos0: int):
     return idx_flop, attn_flop
 
 
-def measure_prefill(ci: int, steps: int, warmup: int):
+def measure_prefill(ci: int, steps: int, warmup: int, context: bool = True):
     """Chunked prefill: csa2_prefill_layers on the chunk of `ci` (one Full layer), its
     stages, the unfused four-call chain, a 4-layer schedule, the first chunk of a
     context, and a whole context prefilled chunk by chunk into a growing pool."""
@@ -250,6 +250,10 @@ def measure_prefill(ci: int, steps: int, warmup: int):
     res["schedule_F_Ri_Ru_Ru"]["first_chunk_ms"] = ms0
     log("prefill schedule F,Ri,Ru,Ru: %.3f ms per chunk, first chunk %.3f ms" % (ms4, ms0))
 
+    if not context:
+        del dc
+        torch.cuda.empty_cache()
+        return res
     # a whole context of ratio * M tokens in chunks of Q: before each chunk the
     # Q / ratio entries it completes are appended (MXFP4 / E4M3 encode), then the
     # schedule runs over the chunk at its position
@@ -490,6 +494,9 @@ def main():
     ap.add_argument("--score-launches", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the chunked-prefill measurement of --prefill configs, without "
+                         "the whole-context loop (for a counter pass)")
     ap.add_argument("--step-only", action="store_true",
                     help="only time --steps decode steps of --config (for a counter pass)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -515,6 +522,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("copy calibration: 3 x 1 GiB device copies done")
+
+    if args.prefill_only:   # a counter pass over prefill chunks alone
+        for ci in args.prefill:
+            r = measure_prefill(ci, args.steps, args.warmup, context=False)
+            print(json.dumps({"workload": r.pop("workload"), **r}), flush=True)
+        return
 
     if args.step_only:   # a counter pass over decode steps alone
         from fp4_kv_cache_score_amd import synth
