@@ -229,6 +229,22 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   // write: value v of block (r, c) is query row 8*(v/4) + 4*g + v%4, entry lr
   const int32_t ea = (int32_t)e0 + 64 * we + lr;     // entries of blocks c = 0, 1
   const int32_t eb = ea + 32;
+  // A tile inside the chunk and the scanned entries, all of whose entries its
+  // first (least-seeing) query sees: every value is stored, no test per value;
+  // 32-bit offsets from the sequence's score base.
+  if (q0 + kSQ <= Q && e0 + kSE <= N && e0 + kSE <= (int64_t)vis_s[0] &&
+      (uint64_t)Q * (uint64_t)N < (1ull << 31)) {
+    const uint32_t o0 = (uint32_t)(q0 + 64 * wq + 4 * g) * (uint32_t)N + (uint32_t)ea;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t off = o0 + (uint32_t)(32 * r + 8 * (v >> 2) + (v & 3)) * (uint32_t)N;
+        sb[off] = acc[r][0][v];
+        sb[off + 32] = acc[r][1][v];
+      }
+    return;
+  }
   const bool oka = ea < N, okb = eb < N;
 #pragma unroll
   for (int r = 0; r < 2; ++r)
