@@ -479,21 +479,25 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const
     x0 = *reinterpret_cast<const f32x4*>(x0p) + *reinterpret_cast<const f32x4*>(x1p);
     x1 = *reinterpret_cast<const f32x4*>(x0p + 4) + *reinterpret_cast<const f32x4*>(x1p + 4);
     float mc = -INFINITY;
+    const uint32_t ba = (uint32_t)(va >> (4 * lg)), bb = (uint32_t)(vb >> (4 * lg));   // keys 4 lg ..
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x0[e] = (va >> (4 * lg + e)) & 1 ? x0[e] : -INFINITY;
-      x1[e] = (vb >> (4 * lg + e)) & 1 ? x1[e] : -INFINITY;
+      x0[e] = (ba >> e) & 1u ? x0[e] : -INFINITY;
+      x1[e] = (bb >> e) & 1u ? x1[e] : -INFINITY;
       mc = fmaxf(mc, fmaxf(x0[e], x1[e]));
     }
     return pf_rows_max(mc);
   };
   // one step's P . C on this half's dims, with the current reference
   auto step_pv = [&](const f32x4& x0, const f32x4& x1) __attribute__((always_inline)) {
+    // absent keys are -inf: exp gives 0 (a reference of -inf only occurs while
+    // every key so far is absent, and then 0 stands in for it)
+    const float mr = m_run == -INFINITY ? 0.f : m_run;
     float p[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      p[e] = x0[e] == -INFINITY ? 0.f : __expf(x0[e] - m_run);
-      p[4 + e] = x1[e] == -INFINITY ? 0.f : __expf(x1[e] - m_run);
+      p[e] = __expf(x0[e] - mr);
+      p[4 + e] = __expf(x1[e] - mr);
     }
     // A operand: keys 4 lg + e of set 0, then of set 1 (the B reads below take
     // the same keys); P = hi + lo in bf16
