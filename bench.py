@@ -404,6 +404,25 @@ def measure_ragged(ci: int, steps: int, warmup: int):
                 step_hbm_gbs=ragged_bytes / (ms * 1e-3) / 1e9)
 
 
+def measure_paged(ci: int, steps: int, warmup: int, page_log2: int = 8):
+    """A paged pool at a decode workload's shape: every sequence's entries in
+    pages of 2^page_log2 entries at shuffled places of one shared array, read
+    through a page table; step time against the same pool laid out contiguously."""
+    import torch
+    from fp4_kv_cache_score_amd import synth
+    from fp4_kv_cache_score_amd.configs import CONFIGS, algorithmic_bytes
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[ci]
+    dc = DeviceCase(synth.make_case(cfg))
+    dc.use_pages(page_log2, seed=cfg.seed)
+    ms, _ = time_decode(dc, steps, warmup)
+    del dc
+    torch.cuda.empty_cache()
+    return dict(page_entries=1 << page_log2, ms_per_step=ms,
+                query_tokens_per_s=cfg.B / (ms * 1e-3),
+                step_hbm_gbs=algorithmic_bytes(cfg)["total"] / (ms * 1e-3) / 1e9)
+
+
 def measure_host_tier(ci: int, reps: int = 5):
     """Host tier at a decode workload's pool shape: one sequence's whole pool
     (M entries x 784 B) restored from / offloaded to page-locked host memory,
@@ -571,6 +590,10 @@ def main():
     extra["ragged_" + cfg.name] = rg
     log("ragged batch (mean length %.0f of %d): %.3f ms/step, %.1f GB/s" % (
         rg["lengths_mean"], cfg.M, rg["ms_per_step"], rg["step_hbm_gbs"]))
+    pg = measure_paged(args.config, args.steps, args.warmup)
+    extra["paged_" + cfg.name] = pg
+    log("paged pool (pages of %d entries): %.3f ms/step against %.3f contiguous" % (
+        pg["page_entries"], pg["ms_per_step"], head["ms"]))
     ht = measure_host_tier(args.config)
     extra["host_tier_" + cfg.name] = ht
     log("host tier: restore %.1f GB/s, offload %.1f GB/s; decode %.3f ms alone, %.3f ms beside "

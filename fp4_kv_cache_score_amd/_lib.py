@@ -34,7 +34,8 @@ EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge"
 class csa2_pool(ctypes.Structure):
     _fields_ = [("latent", c_void_p), ("scale", c_void_p), ("idx_key", c_void_p),
                 ("B", c_int32), ("M", c_int32), ("D", c_int32), ("HI", c_int32),
-                ("DI", c_int32), ("len", c_void_p)]
+                ("DI", c_int32), ("len", c_void_p), ("pages", c_void_p),
+                ("page_log2", c_int32)]
 
 
 class csa2_layer(ctypes.Structure):
@@ -75,7 +76,7 @@ def lib() -> ctypes.CDLL:
                                           c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
                                           POINTER(c_int32), c_void_p, c_size_t, c_void_p]
         L.csa2_pool_append.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
-                                       c_void_p, c_void_p, c_int32, c_void_p]
+                                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p]
         L.csa2_swa_append.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_int64, c_int32,
                                       c_void_p]
         for fn in ("csa2_pool_restore", "csa2_pool_offload"):
@@ -123,9 +124,11 @@ def _check(fn, st, raise_on_error):
 
 
 def make_pool(latent, scale, idx_key, B: int, M: int, D: int = 512, HI: int = 8,
-              DI: int = 64, len=None) -> csa2_pool:
-    """len: None, or a device int32 tensor [B] of per-sequence entry counts."""
-    return csa2_pool(_p(latent), _p(scale), _p(idx_key), B, M, D, HI, DI, _p(len))
+              DI: int = 64, len=None, pages=None, page_log2: int = 0) -> csa2_pool:
+    """len: None, or a device int32 tensor [B] of per-sequence entry counts;
+    pages: None (contiguous), or a device int32 page table [B][M >> page_log2]."""
+    return csa2_pool(_p(latent), _p(scale), _p(idx_key), B, M, D, HI, DI, _p(len), _p(pages),
+                     page_log2 if pages is not None else 0)
 
 
 def csa2_status_string(status: int) -> str:
@@ -163,9 +166,10 @@ def csa2_sparse_attn(pool: csa2_pool, q, Q: int, H: int, idx, K: int, o, lse, ws
 
 
 def csa2_pool_append(latent, scale, idx_key, B: int, M: int, x_latent, x_key, slot, T: int,
-                     stream=None, raise_on_error=True) -> int:
+                     stream=None, raise_on_error=True, pages=None, page_log2: int = 0) -> int:
     st = lib().csa2_pool_append(_p(latent), _p(scale), _p(idx_key), B, M, _p(x_latent),
-                                _p(x_key), _p(slot), T, _s(stream))
+                                _p(x_key), _p(slot), T, _p(pages),
+                                page_log2 if pages is not None else 0, _s(stream))
     return _check("csa2_pool_append", st, raise_on_error)
 
 

@@ -9,15 +9,28 @@ using namespace csa2;
 namespace {
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+constexpr int32_t kMinPageLog2 = 6;   // a scan wave's 64 entries lie in one page
 bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 csa2_status check_pool(const csa2_pool* p) {
   if (!p || !p->latent || !p->scale || !p->idx_key) return CSA2_ERR_NULL;
   if (p->B <= 0 || p->M <= 0 || p->M > kMaxTopkN) return CSA2_ERR_SHAPE;
   if (p->D != kD || p->HI != kHI || p->DI != kDI) return CSA2_ERR_SHAPE;
-  if (!al16(p->latent) || !al16(p->scale) || !al16(p->idx_key) || !al4(p->len))
+  if (p->pages && (p->page_log2 < kMinPageLog2 || p->page_log2 > 30 ||
+                   (p->M & ((1 << p->page_log2) - 1)) != 0))
+    return CSA2_ERR_SHAPE;
+  if (!al16(p->latent) || !al16(p->scale) || !al16(p->idx_key) || !al4(p->len) ||
+      !al4(p->pages))
     return CSA2_ERR_ALIGN;
   return CSA2_OK;
+}
+
+PoolMap pool_map(const csa2_pool* p) {
+  PoolMap m{};
+  m.pages = p->pages;
+  m.lg2 = p->pages ? p->page_log2 : 0;
+  m.np = p->pages ? p->M >> p->page_log2 : 0;
+  return m;
 }
 
 csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
@@ -187,12 +200,12 @@ csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx, const 
     if (hist) return CSA2_ERR_SHAPE;
     return hip_status(launch_prefill_score(pool->idx_key, pool->B, pool->M, pool->M, q_idx, w_idx,
                                            Q, pos0, pos0 >= 0 ? ratio : 1, scores, nullptr,
-                                           pool->len, stream));
+                                           pool->len, pool_map(pool), stream));
   }
   const int32_t N = cand ? P : pool->M;
   return hip_status(launch_index_score(pool->idx_key, pool->B, pool->M, q_idx, w_idx, Q, pos0,
                                        pos0 >= 0 ? ratio : 1, cand, N, scores, hist, pool->len,
-                                       stream));
+                                       pool_map(pool), stream));
 }
 
 csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* n_valid,
@@ -243,6 +256,7 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   a.latent = pool->latent;
   a.scale = pool->scale;
   a.M = pool->M;
+  a.map = pool_map(pool);
   a.idx = idx;
   a.K = K;
   a.swa = nullptr;
@@ -330,7 +344,8 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     const csa2_layer& y = layers[l];
     if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         nullptr, (int32_t)M, d.scores, nullptr, pool->len, stream));
+                                         nullptr, (int32_t)M, d.scores, nullptr, pool->len,
+                                         pool_map(pool), stream));
       if (st != CSA2_OK) return st;
       if (!d.big) {
         if (y.mode == CSA2_FULL && P > 0) {
@@ -372,7 +387,8 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
       cur_layer = l;
     } else if (y.mode == CSA2_REINDEX) {  // hierarchical: score inside the candidate pool
       st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         d.cand, P, d.scores, nullptr, pool->len, stream));
+                                         d.cand, P, d.scores, nullptr, pool->len,
+                                         pool_map(pool), stream));
       if (st != CSA2_OK) return st;
       // a ragged sequence has min(P, len) candidates (the row kernel clamps len to P)
       st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, pool->len, n_cand, K, nullptr, false,
@@ -392,6 +408,7 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     a.latent = pool->latent;
     a.scale = pool->scale;
     a.M = M;
+    a.map = pool_map(pool);
     a.idx = cur;
     a.K = K;
     a.swa = y.swa;
@@ -450,7 +467,7 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
       } else {
         st = hip_status(launch_prefill_score(pool->idx_key, (int32_t)B, M, (int32_t)N, y.q_idx,
                                              y.w_idx, Q, pos0, pos0 >= 0 ? ratio : 1, scores,
-                                             n_valid, pool->len, stream));
+                                             n_valid, pool->len, pool_map(pool), stream));
         if (st != CSA2_OK) return st;
         if (!big) {
           st = hip_status(launch_topk_rows(scores, (int32_t)R, (int32_t)N, n_valid, (int32_t)N, K,
@@ -479,6 +496,7 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
     a.latent = pool->latent;
     a.scale = pool->scale;
     a.M = M;
+    a.map = pool_map(pool);
     a.idx = cur;
     a.K = N > 0 ? K : 0;
     a.swa = y.swa;
@@ -500,14 +518,22 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
 
 csa2_status csa2_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key, int32_t B,
                              int32_t M, const float* x_latent, const float* x_key,
-                             const int32_t* slot, int32_t T, hipStream_t stream) {
+                             const int32_t* slot, int32_t T, const int32_t* pages,
+                             int32_t page_log2, hipStream_t stream) {
   if (!latent || !scale || !idx_key || !x_latent || !x_key || !slot) return CSA2_ERR_NULL;
   if (B <= 0 || M <= 0 || T < 0) return CSA2_ERR_SHAPE;
+  if (pages && (page_log2 < kMinPageLog2 || page_log2 > 30 || (M & ((1 << page_log2) - 1)) != 0))
+    return CSA2_ERR_SHAPE;
   if (!al16(x_latent) || !al16(x_key) || !al4(slot) || ((uintptr_t)latent & 7u) ||
-      ((uintptr_t)idx_key & 7u))
+      ((uintptr_t)idx_key & 7u) || !al4(pages))
     return CSA2_ERR_ALIGN;
   if (T == 0) return CSA2_OK;
-  return hip_status(launch_pool_append(latent, scale, idx_key, B, M, x_latent, x_key, slot, T, stream));
+  PoolMap map{};
+  map.pages = pages;
+  map.lg2 = pages ? page_log2 : 0;
+  map.np = pages ? M >> page_log2 : 0;
+  return hip_status(launch_pool_append(latent, scale, idx_key, B, M, x_latent, x_key, slot, T, map,
+                                       stream));
 }
 
 // Host tier: one sequence's entries (or window ring) between page-locked host

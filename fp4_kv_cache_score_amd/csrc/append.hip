@@ -73,14 +73,14 @@ __global__ __launch_bounds__(256)
 void k_pool_append(uint8_t* __restrict__ latent, uint8_t* __restrict__ scale,
                    uint8_t* __restrict__ idx_key, int32_t M, const float* __restrict__ x_lat,
                    const float* __restrict__ x_key, const int32_t* __restrict__ slot, int32_t T,
-                   int64_t rows) {
+                   int64_t rows, PoolMap map) {
   const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kRowLanes) + (threadIdx.x / kRowLanes);
   if (r >= rows) return;
   const int lane = threadIdx.x & (kRowLanes - 1);
   const int64_t b = r / T;
   const int32_t e = slot[r];
   if (e < 0 || e >= M) return;                       // wave-uniform
-  const size_t er = (size_t)b * (size_t)M + (size_t)e;
+  const size_t er = (size_t)pool_row(map, b, e, M);   // the entry's pool row
 
   {  // latent: 8 elements per lane, a block of 32 per 4 lanes
     const float4* src = reinterpret_cast<const float4*>(x_lat + (size_t)r * kD + 8 * lane);
@@ -133,12 +133,12 @@ void k_window_append(uint8_t* __restrict__ swa, int32_t W, const float* __restri
 
 hipError_t launch_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key, int32_t B,
                               int32_t M, const float* x_lat, const float* x_key, const int32_t* slot,
-                              int32_t T, hipStream_t s) {
+                              int32_t T, const PoolMap& map, hipStream_t s) {
   const int64_t rows = (int64_t)B * T;
   if (rows <= 0) return hipSuccess;
   const int64_t per = 256 / kRowLanes;
   k_pool_append<<<dim3((unsigned)((rows + per - 1) / per)), dim3(256), 0, s>>>(
-      latent, scale, idx_key, M, x_lat, x_key, slot, T, rows);
+      latent, scale, idx_key, M, x_lat, x_key, slot, T, rows, map);
   return hipGetLastError();
 }
 

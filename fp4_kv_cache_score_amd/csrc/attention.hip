@@ -101,8 +101,8 @@ struct ChunkRegs {
 
 // Per-sequence bases of the inputs a work-group reads.
 struct RowBase {
-  const uint8_t* lat;     // latent of entry 0 of the sequence
-  const uint8_t* sc;      // scales of entry 0 of the sequence
+  const uint8_t* lat;     // latent of pool row 0
+  const uint8_t* sc;      // scales of pool row 0
   const uint8_t* win;     // window row 0 of the query row
 };
 
@@ -216,7 +216,10 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   const int key0 = c0 * KS;
   const int gend = (c1 < Cg ? c1 : Cg) * KS;
   const int key1 = gend < a.K ? gend : a.K;
-  for (int k = key0 + tid; k < key1; k += kThreads) idx_s[k - key0] = a.idx[(size_t)row * a.K + k];
+  for (int k = key0 + tid; k < key1; k += kThreads) {   // entry -> pool row (-1 stays)
+    const int32_t e = a.idx[(size_t)row * a.K + k];
+    idx_s[k - key0] = e >= 0 ? (int32_t)pool_row(a.map, b, e, a.M) : -1;
+  }
 
   // logits lane: key group kb (4 keys), dim part dp (dims 8dp + 128j .. +7, j < 4).
   // Head slot s holds head 4hg + (s ^ hx) and key slot s key 4kb + (s ^ kx).
@@ -234,8 +237,8 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   __syncthreads();
 
   RowBase rbase;
-  rbase.lat = a.latent + (size_t)b * (size_t)a.M * kLatRow;
-  rbase.sc = a.scale + (size_t)b * (size_t)a.M * kScaleRow;
+  rbase.lat = a.latent;   // idx_s holds pool rows
+  rbase.sc = a.scale;
   rbase.win = a.swa + ((size_t)b * a.swa_rows + t) * kD;
   ChunkRegs r;
   load_chunk(a, rbase, c0, Cg, idx_s, key0, r);

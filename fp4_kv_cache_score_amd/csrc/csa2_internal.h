@@ -38,6 +38,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Where a sequence's pool entry lives.  Contiguous pools hold sequence b's
+// entry e at row b * M + e; paged pools at row page * 2^lg2 + e mod 2^lg2,
+// page = pages[b][e >> lg2] (a per-sequence page table into shared arrays).
+struct PoolMap {
+  const int32_t* pages;   // NULL: contiguous [B][M]; else [B][np] physical page numbers
+  int32_t lg2;            // entries per page = 1 << lg2
+  int32_t np;             // pages per sequence = M >> lg2
+};
+__device__ __forceinline__ int64_t pool_row(const PoolMap& m, int64_t b, int64_t e, int64_t M) {
+  if (!m.pages) return b * M + e;
+  return ((int64_t)m.pages[b * m.np + (e >> m.lg2)] << m.lg2) | (e & ((int64_t(1) << m.lg2) - 1));
+}
+
 // Order-preserving map of a float score to uint32 (-0 folded onto +0):
 // a > b as reals  <=>  key(a) > key(b).
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -99,7 +112,8 @@ hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
                               const uint8_t* q_idx, const float* w_idx,
                               int32_t Q, int64_t pos0, int32_t ratio,
                               const int32_t* cand, int32_t N, float* scores,
-                              uint32_t* hist, const int32_t* len, hipStream_t s);
+                              uint32_t* hist, const int32_t* len, const PoolMap& map,
+                              hipStream_t s);
 
 // Top-K pieces.  n_valid: device [R] or NULL (then n_all applies to every row).
 // launch_topk_rows: one work-group per row, N <= kRowMaxN.  hist: NULL (the
@@ -128,9 +142,10 @@ hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
 // lse: by the work-group itself when the row has one split, otherwise by a
 // merge launch over the partials.
 struct AttnArgs {
-  const uint8_t* latent;  // [B][M][kLatRow]
-  const uint8_t* scale;   // [B][M][kScaleRow]
+  const uint8_t* latent;  // pool rows [.][kLatRow] (see PoolMap)
+  const uint8_t* scale;   // pool rows [.][kScaleRow]
   int64_t M;
+  PoolMap map;
   const int32_t* idx;     // [rows][K]
   int32_t K;
   const uint8_t* swa;     // [B][swa_rows][kD]
@@ -178,7 +193,7 @@ inline AttnWs attn_ws_carve(void* ws, int64_t rows, int64_t chunks) {
 // rows into a ring of W rows (only the last W of T tokens are written).
 hipError_t launch_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key, int32_t B,
                               int32_t M, const float* x_lat, const float* x_key, const int32_t* slot,
-                              int32_t T, hipStream_t s);
+                              int32_t T, const PoolMap& map, hipStream_t s);
 hipError_t launch_window_append(uint8_t* swa, int32_t B, int32_t W, const float* x, int64_t pos0,
                                 int32_t T, hipStream_t s);
 
@@ -189,7 +204,7 @@ hipError_t launch_window_append(uint8_t* swa, int32_t B, int32_t W, const float*
 hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_t N,
                                 const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
                                 int32_t ratio, float* scores, int32_t* n_valid, const int32_t* len,
-                                hipStream_t s);
+                                const PoolMap& map, hipStream_t s);
 // One work-group per query row over its K selected entries and W window rows;
 // writes a.o / a.lse, merged with (o_in, lse_in) when lse_in is given (they
 // may alias a.o / a.lse).

@@ -39,7 +39,7 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
                    const float* __restrict__ w_idx, int32_t Q, int64_t pos0,
                    int32_t ratio, const int32_t* __restrict__ cand, int32_t N,
                    float* __restrict__ scores, uint32_t* __restrict__ hist,
-                   const int32_t* __restrict__ len) {
+                   const int32_t* __restrict__ len, PoolMap map) {
   constexpr int kEntriesPerWG = EPW * (kThreads / 64);
   constexpr int kIters = EPW / (2 * kUnroll);
   static_assert(EPW % (2 * kUnroll) == 0, "EPW must be a multiple of 16");
@@ -63,11 +63,12 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
   }
 
   const int64_t g0 = (int64_t)blockIdx.x * kEntriesPerWG;
-  if (kCand) {
+  if (kCand) {   // candidates -> pool rows (-1: absent or not visible to this query)
     const int32_t* cb = cand + (size_t)b * N;
     for (int i = threadIdx.x; i < kEntriesPerWG; i += kThreads) {
       const int64_t p = g0 + i;
-      ce[i] = p < N ? cb[p] : -1;
+      const int32_t c = p < N ? cb[p] : -1;
+      ce[i] = (c >= 0 && c < vis) ? (int32_t)pool_row(map, b, c, M) : -1;
     }
   }
   float qf[16];
@@ -89,9 +90,13 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) lh[i] = 0u;
   if (kHist || kCand) __syncthreads();
 
-  const uint8_t* kb = key + (size_t)b * (size_t)M * kKeyRow + sub * 16;
   float* srow = scores + (size_t)row * N;
   const int wofs = wave * EPW;
+  // the wave's EPW consecutive entries lie in one page (pages hold >= 64
+  // entries and a wave starts at a multiple of EPW): one lookup per wave
+  const int64_t w0 = g0 + wofs;
+  const int64_t roff = kCand ? 0 : (w0 < M ? pool_row(map, b, w0, M) : 0) - w0;   // row - entry
+  const uint8_t* kb = key + sub * 16;
 
   for (int it = 0; it < kIters; ++it) {
     u32x4 v[kUnroll];
@@ -100,16 +105,15 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
     for (int u = 0; u < kUnroll; ++u) {
       const int lp = wofs + it * (2 * kUnroll) + 2 * u + half;   // position within the work-group
       const int64_t p = g0 + lp;
-      int64_t e = p;
-      bool valid = p < N;
+      int64_t e = p;                       // flat: the entry; kb is offset so that e indexes it
+      bool valid = p < N && e < vis;
       if (kCand) {
-        e = ce[lp];
+        e = ce[lp];                        // candidate: its pool row
         valid = e >= 0;
       }
-      valid = valid && e < vis;
       ok[u] = valid;
       if (valid) {
-        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + e * kKeyRow));
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (roff + e) * kKeyRow));
       } else {
         v[u] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -153,19 +157,20 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
 template <int EPW>
 void launch_epw(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
                 const float* w_idx, int32_t Q, int64_t pos0, int32_t ratio, const int32_t* cand,
-                int32_t N, float* scores, uint32_t* hist, const int32_t* len, hipStream_t s) {
+                int32_t N, float* scores, uint32_t* hist, const int32_t* len, const PoolMap& map,
+                hipStream_t s) {
   const dim3 grid((unsigned)((N + EPW * 4 - 1) / (EPW * 4)), (unsigned)(B * Q));
   const dim3 block(kThreads);
   if (cand) {
     if (hist)
-      k_index_score<EPW, true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len);
+      k_index_score<EPW, true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map);
     else
-      k_index_score<EPW, true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len);
+      k_index_score<EPW, true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map);
   } else {
     if (hist)
-      k_index_score<EPW, false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len);
+      k_index_score<EPW, false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map);
     else
-      k_index_score<EPW, false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len);
+      k_index_score<EPW, false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map);
   }
 }
 
@@ -175,15 +180,16 @@ hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
                               const uint8_t* q_idx, const float* w_idx,
                               int32_t Q, int64_t pos0, int32_t ratio,
                               const int32_t* cand, int32_t N, float* scores,
-                              uint32_t* hist, const int32_t* len, hipStream_t s) {
+                              uint32_t* hist, const int32_t* len, const PoolMap& map,
+                              hipStream_t s) {
   // 64 entries per wave (256 per work-group) keep enough loads in flight on
   // long rows; short rows (candidate pools) take 32 so that the launch still
   // has >= 1024 work-groups.
   const int64_t rows = (int64_t)B * Q;
   if (rows * ((N + 255) / 256) >= 1024)
-    launch_epw<64>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, s);
+    launch_epw<64>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, s);
   else
-    launch_epw<32>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, s);
+    launch_epw<32>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, s);
   return hipGetLastError();
 }
 

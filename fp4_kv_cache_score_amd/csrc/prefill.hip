@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kSThreads, 2)
 void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
                      const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
                      int32_t Q, int64_t pos0, int32_t ratio, float* __restrict__ scores,
-                     int32_t* __restrict__ n_valid, const int32_t* __restrict__ len) {
+                     int32_t* __restrict__ n_valid, const int32_t* __restrict__ len, PoolMap map) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[2][kSQ * kSRow];
   __shared__ __attribute__((aligned(16))) uint8_t ks[2][kSE * kSRow];
   __shared__ __attribute__((aligned(16))) float ws[kHI][kSQ];   // head weights, rows contiguous
@@ -89,7 +89,6 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   const int wq = wave & 1;                // 64-query half of the tile
   const int we = wave >> 1;               // 64-entry half of the tile
   const uint8_t* qb = q_idx + (size_t)b * Q * kKeyRow;
-  const uint8_t* kb = key + (size_t)b * (size_t)M * kKeyRow;
   float* sb = scores + (size_t)b * Q * (size_t)N;
   const int64_t Ms = len ? (int64_t)len[b] : M;           // this sequence's entries
   if (n_valid && blockIdx.x == 0 && tid < kSQ && q0 + tid < Q)
@@ -123,7 +122,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
     const int t = q0 + row < Q ? q0 + row : Q - 1;
     const int64_t e = e0 + row < N ? e0 + row : N - 1;
     qrow[i] = qb + (size_t)t * kKeyRow + part * 16;
-    krow[i] = kb + (size_t)e * kKeyRow + part * 16;
+    krow[i] = key + (size_t)pool_row(map, b, e, M) * kKeyRow + part * 16;
   }
   auto load = [&](int h) {
 #pragma unroll
@@ -294,6 +293,7 @@ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * kTRow + ((((c >> 5) ^ (r & 7)) << 5) | ((c & 31) ^ (((r >> 3) & 1) << 4)));
 }
 
+template <bool kPaged>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const float* lse_in) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kWK * kTRow];   // 32 KiB
@@ -345,8 +345,8 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const
   const int ws0 = __builtin_amdgcn_readfirstlane(wfirst / kWK);   // window steps before position 0
   const int n_it = cg + (Cw > ws0 ? Cw - ws0 : 0);
 
-  const uint8_t* lat_b = a.latent ? a.latent + (size_t)b * a.M * kLatRow + 128 * hw : nullptr;
-  const uint8_t* sc_b = a.scale ? a.scale + (size_t)b * a.M * kScaleRow : nullptr;
+  const uint8_t* lat_b = a.latent ? a.latent + 128 * hw : nullptr;   // indexed by pool row
+  const uint8_t* sc_b = a.scale;
   const uint8_t* swa_b = a.swa ? a.swa + ((size_t)b * a.swa_rows + t) * kD + kHalf * hw : nullptr;
   // a readable stand-in for loads past the last step (this row's q: 16 KiB)
   const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.q + (size_t)row * kH * kD);
@@ -371,10 +371,12 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const
     const uint8_t *p0, *p1, *p2, *p3;
     if (g) {
       const int32_t ec = okg ? e : 0;                         // entry 0 exists
-      const uint8_t* gl = lat_b + (size_t)ec * kLatRow;
+      // the paged kind has its own kernel, so the contiguous loop holds no table load
+      const int64_t pr = kPaged ? pool_row(a.map, b, ec, a.M) : (int64_t)b * a.M + ec;
+      const uint8_t* gl = lat_b + (size_t)pr * kLatRow;
       p0 = gl + 16 * lg;
       p1 = gl + 16 * (4 + lg);
-      p2 = p3 = sc_b + (size_t)ec * kScaleRow;
+      p2 = p3 = sc_b + (size_t)pr * kScaleRow;
     } else {
       const uint8_t* wp = a.W > 0 ? swa_b + (size_t)(okw ? wr : a.W - 1) * kD : spare;
       p0 = wp + 32 * lg;
@@ -615,11 +617,11 @@ void k_prefill_attn(AttnArgs a, int32_t Cg, int32_t Cw, const float* o_in, const
 hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_t N,
                                 const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
                                 int32_t ratio, float* scores, int32_t* n_valid, const int32_t* len,
-                                hipStream_t s) {
+                                const PoolMap& map, hipStream_t s) {
   if (N <= 0 || N > M || Q <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + kSE - 1) / kSE), (unsigned)((Q + kSQ - 1) / kSQ), (unsigned)B);
   k_prefill_score<<<grid, dim3(kSThreads), 0, s>>>(key, M, N, q_idx, w_idx, Q, pos0, ratio, scores,
-                                                   n_valid, len);
+                                                   n_valid, len, map);
   return hipGetLastError();
 }
 
@@ -628,7 +630,10 @@ hipError_t launch_prefill_attn(const AttnArgs& a, const float* o_in, const float
   if (a.rows <= 0) return hipSuccess;
   const int32_t Cg = a.K > 0 && a.latent ? (a.K + kWK - 1) / kWK : 0;
   const int32_t Cw = a.W > 0 ? (a.W + kWK - 1) / kWK : 0;
-  k_prefill_attn<<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw, o_in, lse_in);
+  if (a.map.pages)
+    k_prefill_attn<true><<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw, o_in, lse_in);
+  else
+    k_prefill_attn<false><<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw, o_in, lse_in);
   return hipGetLastError();
 }
 

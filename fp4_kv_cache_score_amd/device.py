@@ -54,7 +54,32 @@ class DeviceCase:
         cfg = self.cfg
         self.lens = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(self.device)
         self.pool = C.make_pool(self.latent, self.scale, self.idx_key, cfg.B, cfg.M, cfg.D,
-                                cfg.HI, cfg.DI, len=self.lens)
+                                cfg.HI, cfg.DI, len=self.lens, pages=getattr(self, "pages", None),
+                                page_log2=getattr(self, "page_log2", 0))
+
+    def use_pages(self, page_log2: int, seed: int = 0, spare_pages: int = 3) -> None:
+        """Re-lay the pool out in pages of 2^page_log2 entries at shuffled
+        physical positions (plus a few unused pages), with a page table."""
+        cfg = self.cfg
+        ps = 1 << page_log2
+        assert cfg.M % ps == 0
+        npg = cfg.M // ps
+        total = cfg.B * npg + spare_pages
+        perm = np.random.default_rng(seed).permutation(total)[:cfg.B * npg].astype(np.int32)
+        table = torch.from_numpy(perm.reshape(cfg.B, npg)).to(self.device)
+        dst = torch.from_numpy(np.repeat(perm, ps) * ps + np.tile(np.arange(ps), cfg.B * npg)
+                               ).long().to(self.device)            # row of logical (b, e)
+        arrays = []
+        for t in (self.latent, self.scale, self.idx_key):
+            flat = t.reshape(cfg.B * cfg.M, -1)
+            phys = torch.zeros((total * ps, flat.shape[1]), dtype=t.dtype, device=self.device)
+            phys[dst] = flat
+            arrays.append(phys)
+        self.latent, self.scale, self.idx_key = arrays
+        self.pages, self.page_log2 = table, page_log2
+        self.pool = C.make_pool(self.latent, self.scale, self.idx_key, cfg.B, cfg.M, cfg.D,
+                                cfg.HI, cfg.DI, len=getattr(self, "lens", None), pages=table,
+                                page_log2=page_log2)
 
     # -- workspace -----------------------------------------------------------
     def _workspace(self, nbytes: int) -> torch.Tensor:

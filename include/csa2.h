@@ -68,23 +68,36 @@ enum {
   CSA2_OP_PREFILL_LAYERS = 4
 };
 
-/* The shared global KV pool: B sequences of up to M compressed entries each.
- * Every sequence has its own M entry slots (structure of arrays):
- *   latent  [B][M][D/2]     E2M1 codes of the D-wide shared K/V latent
- *   scale   [B][M][D/32]    E8M0 block scales of the latent
- *   idx_key [B][M][HI][DI]  E4M3 indexer keys
+/* The shared global KV pool: B sequences of up to M compressed entries each,
+ * stored as rows of three arrays (structure of arrays):
+ *   latent  [rows][D/2]     E2M1 codes of the D-wide shared K/V latent
+ *   scale   [rows][D/32]    E8M0 block scales of the latent
+ *   idx_key [rows][HI][DI]  E4M3 indexer keys
  *   len     NULL: every sequence holds M entries.  Otherwise device [B]
  *           int32 in [0, M]: sequence b holds entries 0 .. len[b]-1 (a
  *           ragged batch, the serving shape); the scans read no key past
  *           len[b], such entries score -inf and are never selected.  (Not
  *           checked on the device: values outside [0, M] are not allowed.)
- * latent, scale and idx_key must be 16-byte aligned, len 4-byte aligned. */
+ *   pages   NULL: contiguous, sequence b's entry e is row b * M + e (arrays
+ *           of B * M rows).  Otherwise device [B][M >> page_log2] int32: a
+ *           page table; entry e of sequence b is row
+ *           pages[b][e >> page_log2] * 2^page_log2 + (e mod 2^page_log2), so
+ *           sequences hold their entries in pages of 2^page_log2 rows of
+ *           shared arrays (a paged pool; pages need not be distinct or in
+ *           order).  page_log2 in [6, 30] and M a multiple of the page size.
+ *           (Not checked on the device: page numbers must address rows that
+ *           exist.)
+ * latent, scale and idx_key must be 16-byte aligned, len and pages 4-byte
+ * aligned.  Selected indices (idx outputs and inputs) are always entry
+ * numbers e, never rows. */
 typedef struct csa2_pool {
   const uint8_t* latent;
   const uint8_t* scale;
   const uint8_t* idx_key;
   int32_t B, M, D, HI, DI;
   const int32_t* len;
+  const int32_t* pages;
+  int32_t page_log2;
 } csa2_pool;
 
 /* One layer of a decode step (one query token per sequence).
@@ -259,18 +272,24 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
  * and rounded to the nearest E2M1 value, ties to the even code, saturating at
  * 6, signs kept; element 2i in the low nibble of byte i.  Each index key row
  * becomes E4M3, clamped to +-448, nearest value, ties to the even code.
- *   latent, scale, idx_key  the pool arrays [B][M][256], [B][M][16],
- *                           [B][M][8][64] (written in place)
+ *   latent, scale, idx_key  the pool arrays (rows of 256, 16 and 512 bytes;
+ *                           [B][M] rows when contiguous), written in place
  *   x_latent  [B][T][512] float;  x_key [B][T][8][64] float (finite)
  *   slot      [B][T] int32: entry number receiving row t of sequence b;
  *             rows whose slot is outside [0, M) are skipped.  Two rows of one
  *             sequence naming the same slot is a caller error (race).
- * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (B, M <= 0, T < 0), CSA2_ERR_ALIGN
- * (x_latent, x_key not 16-byte aligned, pool arrays not 8-byte aligned).
+ *   pages, page_log2  NULL for a contiguous pool, or its page table (as in
+ *             csa2_pool): an entry is written to the row it maps to.  Rows
+ *             written by one call must be distinct (two slots that map to
+ *             one row, through shared pages, race like a repeated slot).
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (B, M <= 0, T < 0, a page size
+ * outside [2^6, 2^30] or not dividing M), CSA2_ERR_ALIGN (x_latent, x_key
+ * not 16-byte aligned, pool arrays not 8-byte aligned).
  * T == 0 returns CSA2_OK without a launch. */
 csa2_status csa2_pool_append(uint8_t* latent, uint8_t* scale, uint8_t* idx_key,
                              int32_t B, int32_t M, const float* x_latent,
                              const float* x_key, const int32_t* slot, int32_t T,
+                             const int32_t* pages, int32_t page_log2,
                              hipStream_t stream);
 
 /* New tokens into the FP8 sliding window ("... Cuts KV Cache by 437x",

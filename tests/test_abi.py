@@ -254,3 +254,19 @@ def test_pool_length_array_alignment():
     pool = _pool()
     pool.len = A + 2
     assert _score(pool) == C.CSA2_ERR_ALIGN
+
+
+def test_paged_pool_argument_errors():
+    pool = _pool(M=1024)
+    pool.pages = A
+    pool.page_log2 = 5                                 # pages smaller than a scan wave's 64 entries
+    assert _score(pool) == C.CSA2_ERR_SHAPE
+    pool.page_log2 = 11                                # 2048 does not divide M = 1024
+    assert _score(pool) == C.CSA2_ERR_SHAPE
+    pool.page_log2 = 8
+    pool.pages = A + 2
+    assert _score(pool) == C.CSA2_ERR_ALIGN
+    f = lambda lg2, pages=A: C.csa2_pool_append(A, A, A, 2, 1024, A, A, A, 4, 0,
+                                                raise_on_error=False, pages=pages, page_log2=lg2)
+    assert f(4) == C.CSA2_ERR_SHAPE
+    assert f(8, pages=A + 1) == C.CSA2_ERR_ALIGN
