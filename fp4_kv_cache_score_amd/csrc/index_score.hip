@@ -72,8 +72,9 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
     }
   }
   float qf[16];
+  const uint8_t* qsrc = q_idx + (size_t)row * kKeyRow + sub * 16;
   {
-    const u32x4 qv = *reinterpret_cast<const u32x4*>(q_idx + (size_t)row * kKeyRow + sub * 16);
+    const u32x4 qv = *reinterpret_cast<const u32x4*>(qsrc);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)qv[d], false);
@@ -98,6 +99,7 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
   const int64_t roff = kCand ? 0 : (w0 < M ? pool_row(map, b, w0, M) : 0) - w0;   // row - entry
   const uint8_t* kb = key + sub * 16;
 
+#pragma unroll
   for (int it = 0; it < kIters; ++it) {
     u32x4 v[kUnroll];
     bool ok[kUnroll];
@@ -112,12 +114,13 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
         valid = e >= 0;
       }
       ok[u] = valid;
-      if (valid) {
-        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (roff + e) * kKeyRow));
-      } else {
-        v[u] = u32x4{0u, 0u, 0u, 0u};
-      }
+      // every lane loads (an absent entry reads the query row instead, its
+      // score is -inf whatever it holds): a load under a branch would make
+      // the compiler wait for each one before issuing the next
+      const uint8_t* src = valid ? kb + (roff + e) * kKeyRow : qsrc;
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
     }
+    __builtin_amdgcn_sched_barrier(0);     // all kUnroll loads issue before any use
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       float acc = 0.f;
