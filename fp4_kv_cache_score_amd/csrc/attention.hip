@@ -16,10 +16,13 @@
 // end.  Per chunk (double-buffered, one barrier per chunk), after computing
 // on the current buffer the next chunk is staged into the other one:
 //   stage   the chunk's codes (loaded one compute phase ahead) are
-//           restored to bf16 - FP4 with gfx950's scaled FP4->bf16 convert,
-//           FP8 with the FP8->bf16 convert, both exact - and written to LDS
-//           twice: as rows of dim pairs (for q . c) and as key pairs per dim
-//           (for P x V);
+//           restored and written to LDS twice: as bf16 rows of dim pairs
+//           with the true scale (for q . c; FP4 with gfx950's scaled
+//           FP4->bf16 convert, FP8 with the FP8->bf16 convert, both exact),
+//           and as fp16 key pairs per dim (for P x V): an FP4 value enters
+//           as E2M1 x 2^(sc - ref), ref being the largest scale code of its
+//           32-dim block among the split's entries (found by a prologue
+//           pass), exact while sc >= ref - 23; an FP8 value is exact;
 //   logits  q sits in registers (each lane: 4 heads x 32 dims); a lane forms
 //           4 heads x 4 keys over its 32 dims with v_dot2_f32_bf16 (exact
 //           bf16 products, fp32 sums), and the 16 lanes of a row sum their
@@ -27,15 +30,19 @@
 //           lane-rotated order so that every step adds the same registers;
 //   softmax per head over the stream's 16 keys (fp32): running max, rescale
 //           factor, p = exp(z - max), running sum;
-//   P x V   each lane owns 8 dims of the 4 heads; p is split into bf16 hi +
-//           lo parts (p - hi - lo is below 2^-16 p) and every v_dot2 adds two
-//           keys of one dim, so the key pairs are used as staged.
+//   P x V   each lane owns 8 dims of the 4 heads; p is rounded to fp16
+//           (relative error at most 2^-11) and every v_dot2_f32_f16 adds two
+//           keys of one dim, so the key pairs are used as staged.  The sums
+//           over global keys are in units of 2^(ref - 127) per block and are
+//           brought to units of 1 (exact powers of two) before the first
+//           window chunk or at the end.
 // With one split per row the work-group merges an incoming (o, lse) when
 // given, normalises and writes o and lse; otherwise it writes (unnormalised
 // o, max, sum) partials and k_attn_combine, launched right after it, merges
 // them (and the incoming result) by log-sum-exp weights in a fixed order, so
-// that the result equals one softmax over the union of the key sets.  All arithmetic is fp32 VALU; decode keeps the matrix cores for
-// the multi-query prefill contraction.
+// that the result equals one softmax over the union of the key sets.  All
+// arithmetic runs on the VALU with fp32 accumulation; decode keeps the matrix
+// cores for the multi-query prefill contraction.
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -54,6 +61,11 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_c
 
 __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+
+// fp16 pair dot product with fp32 accumulation (v_dot2_f32_f16)
+__device__ __forceinline__ float hdot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
 // Value of x in the lane named by the DPP control word (within a row of 16).
@@ -134,29 +146,36 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& a, const RowBase& rb,
 }
 
 __device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& r, uint32_t* rowb,
-                                            uint32_t* pairb, int32_t* valid_s) {
+                                            uint32_t* pairb, int32_t* valid_s, uint32_t ref) {
   const int tid = threadIdx.x;
   const int kp = unit_kp(tid);
   const int seg = unit_seg(tid);
   // Absent keys are converted like the others (their codes are finite data
   // of entry 0 or row 0): their logits are masked and their p is 0.
   uint32_t w[2][8];   // per key: 16 bf16 of dims seg*16 .. seg*16+15 as 8 dim pairs
+  uint32_t f[2][8];   // the same dims in fp16, in units of 2^(ref-127) for global keys
+                      // (ref: the largest scale code of this 32-dim block in the split)
   if (chunk < Cg) {
     const bool hi = seg & 1;             // the 8 code bytes are the upper half of the 16 loaded
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t sc = r.sc[i];
       const float scale = __uint_as_float(sc ? (sc << 23) : 0x00400000u);   // 2^(sc-127)
+      // 2^(sc-ref) <= 1 for a present key; an absent key (entry 0's codes,
+      // whose scale may exceed ref) stages zeros, so that 0 x p stays 0
+      const float rel = r.ok[i] ? __builtin_amdgcn_ldexpf(1.0f, (int)sc - (int)ref) : 0.f;
       const uint32_t x0 = hi ? r.v[i][2] : r.v[i][0];
       const uint32_t x1 = hi ? r.v[i][3] : r.v[i][1];
-      w[i][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, 0));
-      w[i][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, 1));
-      w[i][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, 2));
-      w[i][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, 3));
-      w[i][4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, 0));
-      w[i][5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, 1));
-      w[i][6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, 2));
-      w[i][7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, 3));
+#define CSA2_CVT_FP4(M)                                                                          \
+      w[i][M] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, M));     \
+      w[i][4 + M] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, M)); \
+      f[i][M] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x0, rel, M));        \
+      f[i][4 + M] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x1, rel, M));
+      CSA2_CVT_FP4(0)
+      CSA2_CVT_FP4(1)
+      CSA2_CVT_FP4(2)
+      CSA2_CVT_FP4(3)
+#undef CSA2_CVT_FP4
     }
   } else {
 #pragma unroll
@@ -165,6 +184,8 @@ __device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& 
       for (int d = 0; d < 4; ++d) {
         w[i][2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, false));
         w[i][2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, true));
+        f[i][2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)r.v[i][d], 1.0f, false));
+        f[i][2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)r.v[i][d], 1.0f, true));
       }
   }
 #pragma unroll
@@ -176,8 +197,8 @@ __device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& 
   uint32_t pr[16];    // dim seg*16 + j: (key 2kp, key 2kp+1)
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    pr[2 * m] = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u);
-    pr[2 * m + 1] = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u);
+    pr[2 * m] = __builtin_amdgcn_perm(f[1][m], f[0][m], 0x05040100u);
+    pr[2 * m + 1] = __builtin_amdgcn_perm(f[1][m], f[0][m], 0x07060302u);
   }
   uint32_t* pd = pairb + kp * kPairU + seg * 16;
 #pragma unroll
@@ -194,7 +215,8 @@ __global__ __launch_bounds__(kThreads, 1)
 void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   __shared__ __attribute__((aligned(16))) uint32_t rowb[2][kRowBufU];
   __shared__ __attribute__((aligned(16))) uint32_t pairb[2][kPairBufU];
-  __shared__ __attribute__((aligned(16))) uint32_t ps[8][8][8];   // [wave][key pair][head: hi, lo]
+  __shared__ __attribute__((aligned(16))) uint32_t ps[8][8][4];   // [wave][key pair][head]: fp16 p pair
+  __shared__ uint32_t ref_s[kScaleRow];   // per 32-dim block: largest scale code among the split's entries
   __shared__ int32_t idx_s[kMaxChunksPerSplit * KS];
   __shared__ int32_t valid_s[2][KS];
   __shared__ float mls[4][4][2];
@@ -216,6 +238,7 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   const int key0 = c0 * KS;
   const int gend = (c1 < Cg ? c1 : Cg) * KS;
   const int key1 = gend < a.K ? gend : a.K;
+  if (tid < kScaleRow) ref_s[tid] = 0;
   for (int k = key0 + tid; k < key1; k += kThreads) {   // entry -> pool row (-1 stays)
     const int32_t e = a.idx[(size_t)row * a.K + k];
     idx_s[k - key0] = e >= 0 ? (int32_t)pool_row(a.map, b, e, a.M) : -1;
@@ -242,7 +265,24 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   rbase.win = a.swa + ((size_t)b * a.swa_rows + t) * kD;
   ChunkRegs r;
   load_chunk(a, rbase, c0, Cg, idx_s, key0, r);
-  stage_chunk(c0, Cg, r, rowb[0], pairb[0], valid_s[0]);
+  {  // ref_s[blk] = the largest E8M0 code of 32-dim block blk among the
+     // split's entries: P x V runs on the fp16 values 2^(sc-ref) x E2M1, exact
+     // for sc >= ref - 23, and the sums take the factor 2^(ref-127) at the end.
+     // Thread tid reads block tid % 16 of entries tid / 16, tid / 16 + 32, ...
+    uint32_t mx = 0;
+    for (int k = tid; k < (key1 - key0) * kScaleRow; k += kThreads) {
+      const int32_t e = idx_s[k / kScaleRow];
+      if (e >= 0) mx = max(mx, (uint32_t)a.scale[(size_t)e * kScaleRow + (k % kScaleRow)]);
+    }
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
+    if (lane < kScaleRow && mx) atomicMax(&ref_s[lane], mx);
+  }
+  __syncthreads();
+  const uint32_t ref = ref_s[unit_seg(tid) >> 1];             // the block this thread stages
+  const float unit_lo = __builtin_amdgcn_ldexpf(1.0f, (int)ref_s[lane >> 3] - 127);        // dims 4l..
+  const float unit_hi = __builtin_amdgcn_ldexpf(1.0f, (int)ref_s[8 + (lane >> 3)] - 127);  // dims 256+4l..
+  stage_chunk(c0, Cg, r, rowb[0], pairb[0], valid_s[0], ref);
   load_chunk(a, rbase, c0 + 1 < c1 ? c0 + 1 : c0, Cg, idx_s, key0, r);
   __syncthreads();
 
@@ -312,20 +352,26 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
       l_run = l_run * alpha + ls;
       m_run = m_new;
       // key pairs (kk, kk + 1) for kk even: the odd key is in lane dp + 4;
-      // p = hi + lo in bf16 (round to nearest even), residual below 2^-16 p
+      // p in fp16 (round to nearest even, relative error below 2^-11;
+      // p <= e^kLazyMax stays far below the fp16 maximum)
       const float po = dpp<kDppRor12>(p);
-      const bf16x2 hb = __builtin_convertvector((f32x2){p, po}, bf16x2);
-      const uint32_t hu = __builtin_bit_cast(uint32_t, hb);
-      const bf16x2 lb = __builtin_convertvector(
-          (f32x2){p - __uint_as_float(hu << 16), po - __uint_as_float(hu & 0xFFFF0000u)}, bf16x2);
-      if (!(dp & 4))
-        *reinterpret_cast<uint2*>(&ps[wave][kk >> 1][2 * hx]) = make_uint2(hu, __builtin_bit_cast(uint32_t, lb));
+      const uint32_t pu = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p, po}, f16x2));
+      if (!(dp & 4)) ps[wave][kk >> 1][hx] = pu;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     {  // P x V
+      if (c == Cg && c0 < Cg) {   // first window chunk after global ones: sums to units of 1
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[h][i] *= unit_lo;
+            acc[h][4 + i] *= unit_hi;
+          }
+      }
       float al[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) al[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
@@ -339,24 +385,19 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
       const uint32_t* pw = &ps[wave][0][0];
       // two register sets, each loaded one step before use; the scheduling
       // barriers keep the compiler from sinking the loads to their uses
-      u32x4 A[4], Bx[4];
+      u32x4 A[3], Bx[3];
       auto load_pair = [&](u32x4* x, int kp) {
-        x[0] = *reinterpret_cast<const u32x4*>(pw + kp * 8);
-        x[1] = *reinterpret_cast<const u32x4*>(pw + kp * 8 + 4);
-        x[2] = *reinterpret_cast<const u32x4*>(pb + kp * kPairU);
-        x[3] = *reinterpret_cast<const u32x4*>(pb + kp * kPairU + 256);
+        x[0] = *reinterpret_cast<const u32x4*>(pw + kp * 4);
+        x[1] = *reinterpret_cast<const u32x4*>(pb + kp * kPairU);
+        x[2] = *reinterpret_cast<const u32x4*>(pb + kp * kPairU + 256);
       };
       auto pv_pair = [&](const u32x4* x) {
-        const uint32_t ph[4] = {x[0][0], x[0][2], x[1][0], x[1][2]};
-        const uint32_t pl[4] = {x[0][1], x[0][3], x[1][1], x[1][3]};
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[h][i] = fdot2(pl[h], x[2][i], acc[h][i]);
-            acc[h][i] = fdot2(ph[h], x[2][i], acc[h][i]);
-            acc[h][4 + i] = fdot2(pl[h], x[3][i], acc[h][4 + i]);
-            acc[h][4 + i] = fdot2(ph[h], x[3][i], acc[h][4 + i]);
+            acc[h][i] = hdot2(x[0][h], x[1][i], acc[h][i]);
+            acc[h][4 + i] = hdot2(x[0][h], x[2][i], acc[h][4 + i]);
           }
       };
       load_pair(A, 0);
@@ -373,11 +414,20 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
       }
     }
     // the next chunk's codes (loaded one compute phase ago) go to the other buffer
-    if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1]);
+    if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1], ref);
     load_chunk(a, rbase, c + 2 < c1 ? c + 2 : c1 - 1, Cg, idx_s, key0, r);   // past the end: a harmless reload
     __syncthreads();
   }
 
+  if (c1 <= Cg) {   // the split holds global keys only: to units of 1
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[h][i] *= unit_lo;
+        acc[h][4 + i] *= unit_hi;
+      }
+  }
   // stream 1 hands its (o, max, sum) to stream 0 through LDS
   float* xa = reinterpret_cast<float*>(rowb[0]) + hg * 32 * 64 + lane;
   if (st == 1) {

@@ -37,6 +37,7 @@ constexpr int kKeysPerSplit = 32;           // keys staged per work-group
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Where a sequence's pool entry lives.  Contiguous pools hold sequence b's
 // entry e at row b * M + e; paged pools at row page * 2^lg2 + e mod 2^lg2,

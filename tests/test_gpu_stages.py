@@ -67,6 +67,35 @@ def test_fp4_dequant_bit_exact_through_single_key_attention():
     assert np.all(np.abs(lse[0, :512] - z) <= 512 * 2.0 ** -24 * mag + 1e-30)
 
 
+def test_sparse_attn_block_scale_spread_23_binades():
+    """P x V takes fp16 values E2M1 x 2^(code - ref), ref the largest code of the
+    block among the selected entries; they are exact down to ref - 23.  Entry 0
+    sets ref = 143 in block 0 and gets weight ~e^-4000, so the output's block-0
+    dims come only from values 23 binades below it (fp16 subnormals)."""
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    say("case: sparse attention, block scales 23 binades apart")
+    cfg = CONFIGS[0].scaled(name="spread", B=1, M=64, K=64, W=0, modes=(FULL,))
+    case = synth.make_case(cfg)
+    rng = np.random.default_rng(23)
+    case.pool.latent[:] = rng.integers(0, 256, size=case.pool.latent.shape, dtype=np.uint16)
+    case.pool.scale[:] = 120
+    case.pool.scale[0, 0, 0] = 143
+    big = F.dequant_latent(case.pool.latent[0, :1], case.pool.scale[0, :1])[0, :32]
+    q = case.layers[0].q                       # bf16 bits [1][1][16][512]
+    q[0, 0, :, :32] = np.where(big > 0, 0xBA80, np.where(big < 0, 0x3A80, 0)).astype(np.uint16)
+    dc = DeviceCase(case)
+    idx = torch.arange(64, dtype=torch.int32, device="cuda").view(1, 1, 64)
+    o, lse = dc.sparse_attn(0, idx)
+    torch.cuda.synchronize()
+    keys = O.gather_keys(case.pool.latent[0], case.pool.scale[0], np.arange(64))
+    wo, wl = O.attend(q[0, 0], keys)
+    assert np.abs(wo[:, :32]).max() > 0.1 * np.abs(wo).max()    # block 0 carries the output
+    err = attn_rel_err(o[0, 0].cpu().numpy(), wo)
+    say("  rel err %.3g" % err)
+    assert err < ATTN_TOL
+    assert np.allclose(lse[0, 0].cpu().numpy(), wl, rtol=1e-5, atol=1e-5)
+
+
 def test_fp8_window_rows_bit_exact_and_merge():
     from fp4_kv_cache_score_amd.device import DeviceCase
     say("case: fp8 window, W=1 exact; W=128 merge vs oracle")
