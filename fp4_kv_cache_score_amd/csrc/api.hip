@@ -44,8 +44,9 @@ size_t topk_call_ws_bytes(int64_t R, int64_t N, int64_t K) {
 }
 
 // decode_layers workspace: scores [B][N] | multi-work-group Top-K scratch
-// (only when the select takes several work-groups per row) | candidate pool
-// | candidate scores | attention partials.  The scans
+// (only when the select takes several work-groups per row; twice with a
+// candidate pool, whose Top-P and the layer's Top-K are selected together)
+// | candidate pool | attention partials.  The scans
 // build no histogram: a fused one costs more in cross-XCD atomics than the
 // 4 bytes per entry a Top-K pass reads (the row kernel builds its own from
 // the row it holds; the multi-work-group select gets one histogram pass).
@@ -53,8 +54,8 @@ struct DecodeWs {
   float* scores;
   bool big;
   TopkWs t;
+  TopkWs t2;   // the Top-K's lists when the Top-P is selected beside it
   int32_t* cand;
-  float* cscore;
   float* opart;
   float* ml;
 };
@@ -63,8 +64,10 @@ size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t N = P > M ? P : M;
   const int64_t Kmax = P > K ? P : K;
   const int64_t chunks = attn_chunks((int32_t)K, (int32_t)W);
-  return align256(B * N * 4) + (topk_multi_wg(B, M) ? topk_ws_bytes(B, M, Kmax) : 0) +
-         2 * align256(B * (P > 0 ? P : 1) * 4) + attn_ws_bytes(B, chunks > 0 ? chunks : 1);
+  const bool big = topk_multi_wg(B, M);
+  return align256(B * N * 4) + (big ? topk_ws_bytes(B, M, Kmax) : 0) +
+         (big && P > 0 ? topk_ws_bytes(B, M, K) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
+         attn_ws_bytes(B, chunks > 0 ? chunks : 1);
 }
 
 DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
@@ -78,10 +81,12 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   if (d.big) {
     d.t = topk_ws_carve(p, B, M, Kmax);
     p += topk_ws_bytes(B, M, Kmax);
+    if (P > 0) {
+      d.t2 = topk_ws_carve(p, B, M, K);
+      p += topk_ws_bytes(B, M, K);
+    }
   }
   d.cand = (int32_t*)p;
-  p += align256(B * (P > 0 ? P : 1) * 4);
-  d.cscore = (float*)p;
   p += align256(B * (P > 0 ? P : 1) * 4);
   const int32_t chunks = attn_chunks((int32_t)K, (int32_t)W);
   const AttnWs w = attn_ws_carve(p, B, chunks > 0 ? chunks : 1);
@@ -335,6 +340,10 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
   if (d.big) {
     st = zero_hist_counters(d.t, B, stream);
     if (st != CSA2_OK) return st;
+    if (P > 0) {
+      st = zero_hist_counters(d.t2, B, stream);
+      if (st != CSA2_OK) return st;
+    }
   }
 
   const int32_t* cur = nullptr;
@@ -360,28 +369,18 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
         st = hip_status(launch_topk_hist(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
                                          d.t.hist, stream));
         if (st != CSA2_OK) return st;
-        if (y.mode == CSA2_FULL && P > 0 && n_cand <= kRowMaxN) {
-          // Top-P over the row, then Top-K over the P candidates' scores: the
-          // candidates hold the Top-K (same order, K <= P), and their list is
-          // ascending, so the lower-index tie-break is kept.
-          st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, nullptr, P,
-                               d.cand, d.t, true, stream);
-          if (st != CSA2_OK) return st;
-          st = hip_status(launch_gather_scores(d.scores, (int32_t)B, M, d.cand, P, d.cscore, stream));
-          if (st != CSA2_OK) return st;
-          st = hip_status(launch_topk_rows(d.cscore, (int32_t)B, P, pool->len, n_cand, K, nullptr,
-                                           false, d.cand, y.idx_out, stream));
-          if (st != CSA2_OK) return st;
+        if (y.mode == CSA2_FULL && P > 0) {
+          // Top-P and the layer's Top-K from one histogram, one collect pass
+          // over the scores and one finish launch (the two selects of a row
+          // run on two work-groups side by side)
+          st = hip_status(launch_topk_select2(d.scores, (int32_t)B, (int32_t)M, pool->len,
+                                              (int32_t)M, P, d.cand, d.t, K, y.idx_out, d.t2,
+                                              true, stream));
         } else {
-          if (y.mode == CSA2_FULL && P > 0) {
-            st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, nullptr, P,
-                                 d.cand, d.t, false, stream);
-            if (st != CSA2_OK) return st;
-          }
           st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, nullptr, K,
                                y.idx_out, d.t, true, stream);
-          if (st != CSA2_OK) return st;
         }
+        if (st != CSA2_OK) return st;
       }
       cur = y.idx_out;
       cur_layer = l;

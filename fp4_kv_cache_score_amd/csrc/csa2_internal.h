@@ -29,7 +29,7 @@ constexpr int kRowSplitR = 256;             // "few": fewer rows than this
 inline bool topk_multi_wg(int64_t R, int64_t N) {
   return N > kRowMaxN || (N > kRowSplitN && R < kRowSplitR);
 }
-constexpr int kCounterWords = 4;            // per row: [0]=above count, [1]=candidate count
+constexpr int kCounterWords = 4;            // per row: [0]=above count, [1]=candidate count, [2]=bin, [3]=above the bin
 
 // Attention
 constexpr int kKeysPerSplit = 32;           // keys staged per work-group
@@ -68,6 +68,20 @@ struct TopkWs {
   uint32_t* candk;     // [R][cap] keys of positions inside the threshold bin
   int32_t* candp;      // [R][cap] their positions
   int32_t cap;
+};
+
+// One select of the multi-work-group path: its K, per-row counters
+// ([0] count above the threshold bin, [1] bin members, [2] the bin, [3] the
+// count above it as found from the histogram), lists and output.
+struct SelectSet {
+  int32_t K;
+  uint32_t* counters;
+  int32_t* sel;
+  uint32_t* candk;
+  int32_t* candp;
+  int32_t cap;
+  const int32_t* cand_map;
+  int32_t* out;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -134,6 +148,15 @@ hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
                               const int32_t* n_valid, int32_t n_all,
                               const int32_t* cand, int32_t K, int32_t* out,
                               const TopkWs& ws, bool zero_hist, hipStream_t s);
+// Two selects of the same rows in one collect pass and one finish launch
+// (one work-group per row and select): K0 into out0 with ws0's lists and K1
+// into out1 with ws1's; both read ws0.hist (ws1's histogram is not used).
+// Both outputs are unmapped (global positions).
+hipError_t launch_topk_select2(const float* scores, int32_t R, int32_t N,
+                               const int32_t* n_valid, int32_t n_all,
+                               int32_t K0, int32_t* out0, const TopkWs& ws0,
+                               int32_t K1, int32_t* out1, const TopkWs& ws1,
+                               bool zero_hist, hipStream_t s);
 
 // Attention over up to K gathered FP4 entries and up to W FP8 window rows per
 // query row.  The row's keys are cut into chunks of kKeysPerSplit (global
@@ -216,8 +239,5 @@ hipError_t launch_prefill_attn(const AttnArgs& a, const float* o_in, const float
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // Copy n int32 (Reuse layers that ask for their indices).
 hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
-// out[r][i] = scores[r][idx[r][i]], -inf where idx is -1 (idx in [-1, N)).
-hipError_t launch_gather_scores(const float* scores, int32_t R, int64_t N, const int32_t* idx,
-                                int32_t P, float* out, hipStream_t s);
 
 }  // namespace csa2

@@ -91,42 +91,59 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t* total) 
   return before + x - v;
 }
 
-// Bin of the K-th largest key in a 4096-bin histogram (bins ordered by key).
-// *above = number of keys in higher bins; above < K <= above + h[bin].
-// lds: NT/64 + 3 words.  Returns bin -1 if the histogram holds fewer than K.
+// Bins of the K0-th and K1-th largest keys in a 4096-bin histogram (bins
+// ordered by key), from one read of the histogram and one block scan.
+// above[s] = number of keys in bins above bin[s]; above < K <= above + h[bin].
+// bin[s] is -1 if the histogram holds fewer than K_s keys (K1 = 0: unused).
+// lds: NT/64 + 5 words.  h is 16-byte aligned.
 template <int NT>
-__device__ void threshold_bin(const uint32_t* h, uint32_t K, uint32_t* lds,
-                              int* bin, uint32_t* above) {
-  constexpr int PER = kHistBins / NT;
-  const int top = kHistBins - 1 - (int)threadIdx.x * PER;  // thread 0 owns the highest bins
-  uint32_t c[PER];
+__device__ void threshold_bins(const uint32_t* h, uint32_t K0, uint32_t K1, uint32_t* lds,
+                               int* bin, uint32_t* above) {
+  constexpr int PER = kHistBins / NT;          // a multiple of 4
+  const int lo = kHistBins - (int)(threadIdx.x + 1) * PER;   // thread 0 owns the highest bins
+  uint32_t c[PER];                             // c[i] = h[lo + PER - 1 - i], highest first
+#pragma unroll
+  for (int j = 0; j < PER / 4; ++j) {
+    const uint4 v = *reinterpret_cast<const uint4*>(h + lo + 4 * j);
+    c[PER - 1 - 4 * j] = v.x;
+    c[PER - 2 - 4 * j] = v.y;
+    c[PER - 3 - 4 * j] = v.z;
+    c[PER - 4 - 4 * j] = v.w;
+  }
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = h[top - i];
-    s += c[i];
-  }
+  for (int i = 0; i < PER; ++i) s += c[i];
   if (threadIdx.x == 0) {
     lds[NT / 64 + 1] = 0xFFFFFFFFu;
     lds[NT / 64 + 2] = 0u;
+    lds[NT / 64 + 3] = 0xFFFFFFFFu;
+    lds[NT / 64 + 4] = 0u;
   }
   uint32_t tot;
   const uint32_t ex = block_excl_scan<NT>(s, lds, &tot);
-  if (ex < K && K <= ex + s) {
-    uint32_t acc = ex;
+  const int top = kHistBins - 1 - (int)threadIdx.x * PER;
+  const uint32_t Ks[2] = {K0, K1};
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (acc + c[i] >= K) {
-        lds[NT / 64 + 1] = (uint32_t)(top - i);
-        lds[NT / 64 + 2] = acc;
-        break;
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t K = Ks[t];
+    if (K > 0 && ex < K && K <= ex + s) {
+      uint32_t acc = ex;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (acc + c[i] >= K) {
+          lds[NT / 64 + 1 + 2 * t] = (uint32_t)(top - i);
+          lds[NT / 64 + 2 + 2 * t] = acc;
+          break;
+        }
+        acc += c[i];
       }
-      acc += c[i];
     }
   }
   __syncthreads();
-  *bin = (int)lds[NT / 64 + 1];
-  *above = lds[NT / 64 + 2];
+  bin[0] = (int)lds[NT / 64 + 1];
+  above[0] = lds[NT / 64 + 2];
+  bin[1] = (int)lds[NT / 64 + 3];
+  above[1] = lds[NT / 64 + 4];
   __syncthreads();
 }
 
@@ -154,18 +171,72 @@ void k_topk_hist(const float* __restrict__ scores, int32_t N,
   }
 }
 
+// Positions of one work-group's chunk above select t's threshold bin go to
+// t.sel, the bin's members (key, position) to t.candk / t.candp, each list
+// with one atomic per work-group; slots in any order (the finish step orders
+// the output through a bitmap).  Work-group 0 of the row also records the
+// bin and the count above it in counters [2] and [3] for the finish step.
+template <int PER>
+__device__ void collect_one(const uint32_t (&key)[PER], int64_t c0, int32_t n, int row,
+                            int bstar, uint32_t above, const SelectSet& t, uint32_t* lds,
+                            uint32_t* base_s) {
+  uint32_t* cnt = t.counters + (size_t)row * kCounterWords;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    cnt[2] = (uint32_t)bstar;
+    cnt[3] = above;
+  }
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t p = c0 + i * kSelThreads + threadIdx.x;
+    const int bin = (int)(key[i] >> (32 - kHistBits));
+    ngt += (p < n && bin > bstar) ? 1u : 0u;
+    neq += (p < n && bin == bstar) ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<kSelThreads>((ngt << 16) | neq, lds, &tot);
+  if (threadIdx.x == 0) {
+    base_s[0] = (tot >> 16) ? atomicAdd(&cnt[0], tot >> 16) : 0u;
+    base_s[1] = (tot & 0xFFFFu) ? atomicAdd(&cnt[1], tot & 0xFFFFu) : 0u;
+  }
+  __syncthreads();
+  uint32_t rg = base_s[0] + (ex >> 16);
+  uint32_t re = base_s[1] + (ex & 0xFFFFu);
+  int32_t* srow = t.sel + (size_t)row * t.K;
+  uint32_t* ckr = t.candk + (size_t)row * t.cap;
+  int32_t* cpr = t.candp + (size_t)row * t.cap;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t p = c0 + i * kSelThreads + threadIdx.x;
+    if (p >= n) continue;
+    const int bin = (int)(key[i] >> (32 - kHistBits));
+    if (bin > bstar) {
+      if (rg < (uint32_t)t.K) srow[rg] = (int32_t)p;
+      ++rg;
+    } else if (bin == bstar) {
+      if (re < (uint32_t)t.cap) {
+        ckr[re] = key[i];
+        cpr[re] = (int32_t)p;
+      }
+      ++re;
+    }
+  }
+}
+
+// One pass over the scores for up to two selects (t1.K == 0: one) that
+// share the row's top-12-bit histogram.
 __global__ __launch_bounds__(kSelThreads)
 void k_topk_collect(const float* __restrict__ scores, int32_t N,
-                    const int32_t* __restrict__ n_valid, int32_t n_all, int32_t K,
-                    const uint32_t* __restrict__ hist, uint32_t* __restrict__ counters,
-                    int32_t* __restrict__ sel, uint32_t* __restrict__ candk,
-                    int32_t* __restrict__ candp, int32_t cap) {
+                    const int32_t* __restrict__ n_valid, int32_t n_all,
+                    const uint32_t* __restrict__ hist, SelectSet t0, SelectSet t1) {
   constexpr int PER = kChunk / kSelThreads;   // 16 positions per thread
-  __shared__ uint32_t lds[kSelThreads / 64 + 3];
+  __shared__ uint32_t lds[kSelThreads / 64 + 5];
   __shared__ uint32_t base_s[2];
   const int row = blockIdx.y;
   const int32_t n = row_count(n_valid, n_all, row, N);
-  if (n <= K) return;
+  const bool go0 = n > t0.K;
+  const bool go1 = t1.K > 0 && n > t1.K;
+  if (!go0 && !go1) return;
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   if (c0 >= n) return;
   const float* sr = scores + (size_t)row * N;
@@ -176,48 +247,12 @@ void k_topk_collect(const float* __restrict__ scores, int32_t N,
     const int64_t p = c0 + i * kSelThreads + threadIdx.x;
     key[i] = p < n ? score_key(sr[p]) : 0u;
   }
-  int bstar;
-  uint32_t above;
-  threshold_bin<kSelThreads>(hist + (size_t)row * kHistBins, (uint32_t)K, lds, &bstar, &above);
-  uint32_t ngt = 0, neq = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t p = c0 + i * kSelThreads + threadIdx.x;
-    const int bin = (int)(key[i] >> (32 - kHistBits));
-    ngt += (p < n && bin > bstar) ? 1u : 0u;
-    neq += (p < n && bin == bstar) ? 1u : 0u;
-  }
-  // One atomic per counter per work-group; slots in any order (the finish
-  // step orders the output through a bitmap).
-  uint32_t tot;
-  const uint32_t ex = block_excl_scan<kSelThreads>((ngt << 16) | neq, lds, &tot);
-  if (threadIdx.x == 0) {
-    uint32_t* cnt = counters + (size_t)row * kCounterWords;
-    base_s[0] = (tot >> 16) ? atomicAdd(&cnt[0], tot >> 16) : 0u;
-    base_s[1] = (tot & 0xFFFFu) ? atomicAdd(&cnt[1], tot & 0xFFFFu) : 0u;
-  }
-  __syncthreads();
-  uint32_t rg = base_s[0] + (ex >> 16);
-  uint32_t re = base_s[1] + (ex & 0xFFFFu);
-  int32_t* srow = sel + (size_t)row * K;
-  uint32_t* ckr = candk + (size_t)row * cap;
-  int32_t* cpr = candp + (size_t)row * cap;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t p = c0 + i * kSelThreads + threadIdx.x;
-    if (p >= n) continue;
-    const int bin = (int)(key[i] >> (32 - kHistBits));
-    if (bin > bstar) {
-      if (rg < (uint32_t)K) srow[rg] = (int32_t)p;
-      ++rg;
-    } else if (bin == bstar) {
-      if (re < (uint32_t)cap) {
-        ckr[re] = key[i];
-        cpr[re] = (int32_t)p;
-      }
-      ++re;
-    }
-  }
+  int bstar[2];
+  uint32_t above[2];
+  threshold_bins<kSelThreads>(hist + (size_t)row * kHistBins, go0 ? (uint32_t)t0.K : 0u,
+                              go1 ? (uint32_t)t1.K : 0u, lds, bstar, above);
+  if (go0) collect_one<PER>(key, c0, n, row, bstar[0], above[0], t0, lds, base_s);
+  if (go1) collect_one<PER>(key, c0, n, row, bstar[1], above[1], t1, lds, base_s);
 }
 
 // Visit every member of the threshold bin: from the candidate list, or (after
@@ -239,28 +274,30 @@ __device__ __forceinline__ void visit_bin(bool overflow, uint32_t C, const uint3
   }
 }
 
+// grid (rows, selects): select blockIdx.y of t0 / t1 on its row.
 __global__ __launch_bounds__(kFinThreads)
 void k_topk_finish(const float* __restrict__ scores, int32_t N,
-                   const int32_t* __restrict__ n_valid, int32_t n_all, int32_t K,
-                   uint32_t* hist, uint32_t* counters,
-                   const int32_t* __restrict__ sel, const uint32_t* __restrict__ candk,
-                   const int32_t* __restrict__ candp, int32_t cap,
-                   const int32_t* __restrict__ cand_map, int32_t* __restrict__ out,
-                   int32_t zero_hist) {
+                   const int32_t* __restrict__ n_valid, int32_t n_all,
+                   uint32_t* hist, int32_t zero_hist, SelectSet t0, SelectSet t1) {
   __shared__ uint32_t lds[kFinThreads / 64 + 8];
   __shared__ uint32_t rh[1 << kDigit];
   __shared__ uint32_t bitmap[kSegWords];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const SelectSet& t = blockIdx.y ? t1 : t0;
+  const int32_t K = t.K;
+  uint32_t* counters = t.counters;
+  const int32_t cap = t.cap;
   const int32_t n = row_count(n_valid, n_all, row, N);
-  int32_t* orow = out + (size_t)row * K;
-  const int32_t* mrow = cand_map ? cand_map + (size_t)row * N : nullptr;
-  // Leave this row's counters (and, when asked, its histogram) zeroed for the
-  // next select.  They are read and cleared through the same pointers, and
-  // every read happens before the barrier that precedes the clearing.
+  int32_t* orow = t.out + (size_t)row * K;
+  const int32_t* mrow = t.cand_map ? t.cand_map + (size_t)row * N : nullptr;
+  // Leave this row's counters (and, when asked, its histogram: select 0's
+  // work-group, as no finish reads it) zeroed for the next select.  The
+  // counters are read and cleared through the same pointers, and every read
+  // happens before the barrier that precedes the clearing.
   auto clean = [&]() {
     if (tid < kCounterWords) counters[(size_t)row * kCounterWords + tid] = 0u;
-    if (zero_hist)
+    if (zero_hist && blockIdx.y == 0)
       for (int i = tid; i < kHistBins; i += kFinThreads) hist[(size_t)row * kHistBins + i] = 0u;
   };
   if (n <= K) {
@@ -268,20 +305,20 @@ void k_topk_finish(const float* __restrict__ scores, int32_t N,
     clean();
     return;
   }
-  int bstar;
-  uint32_t above;
-  threshold_bin<kFinThreads>(hist + (size_t)row * kHistBins, (uint32_t)K, lds, &bstar, &above);
+  // the threshold bin and the count above it, as the collect step found them
+  const int bstar = (int)counters[(size_t)row * kCounterWords + 2];
+  const uint32_t above = counters[(size_t)row * kCounterWords + 3];
+  const uint32_t ccount = counters[(size_t)row * kCounterWords + 1];
+  __syncthreads();   // every thread has read the counters
+  clean();
   if (bstar < 0) {  // inconsistent histogram: cannot happen for valid inputs
     for (int i = tid; i < K; i += kFinThreads) orow[i] = -1;
     return;
   }
-  const uint32_t ccount = counters[(size_t)row * kCounterWords + 1];
-  __syncthreads();   // every thread has read the counters and the histogram
-  clean();
   const bool overflow = ccount > (uint32_t)cap;
   const uint32_t C = overflow ? 0u : ccount;
-  const uint32_t* ck = candk + (size_t)row * cap;
-  const int32_t* cp = candp + (size_t)row * cap;
+  const uint32_t* ck = t.candk + (size_t)row * cap;
+  const int32_t* cp = t.candp + (size_t)row * cap;
   const float* sr = scores + (size_t)row * N;
   const uint64_t nm1 = (uint64_t)(n - 1);
   auto comp_of = [&](uint32_t key, int32_t p) -> uint64_t {
@@ -327,7 +364,7 @@ void k_topk_finish(const float* __restrict__ scores, int32_t N,
   const uint64_t thr = prefix << sh;   // chosen bin members: composite >= thr
 
   // Ordered extraction, one bitmap segment at a time.
-  const int32_t* srow = sel + (size_t)row * K;
+  const int32_t* srow = t.sel + (size_t)row * K;
   const uint32_t nsel = above < (uint32_t)K ? above : (uint32_t)K;
   uint32_t written = 0;
   for (int64_t s0 = 0; s0 < n; s0 += kSeg) {
@@ -852,25 +889,7 @@ __global__ void k_copy_i32(int32_t* __restrict__ d, const int32_t* __restrict__ 
   for (int64_t k = i; k < n; k += stride) d[k] = s[k];
 }
 
-// out[r][i] = scores[r][idx[r][i]] (-inf for idx -1): the scores of a
-// candidate list, so that a later select can run over the list alone.
-__global__ void k_gather_scores(const float* __restrict__ scores, int64_t N,
-                                const int32_t* __restrict__ idx, int32_t P, float* __restrict__ out) {
-  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = blockIdx.y;
-  if (i >= P) return;
-  const int32_t e = idx[(size_t)row * P + i];
-  out[(size_t)row * P + i] = e >= 0 ? scores[(size_t)row * N + e] : -INFINITY;
-}
-
 }  // namespace
-
-hipError_t launch_gather_scores(const float* scores, int32_t R, int64_t N, const int32_t* idx,
-                                int32_t P, float* out, hipStream_t s) {
-  if (R <= 0 || P <= 0) return hipSuccess;
-  k_gather_scores<<<dim3((unsigned)((P + 255) / 256), (unsigned)R), dim3(256), 0, s>>>(scores, N, idx, P, out);
-  return hipGetLastError();
-}
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
@@ -920,19 +939,40 @@ hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
   return hipGetLastError();
 }
 
+static SelectSet select_set(int32_t K, const TopkWs& ws, const int32_t* cand, int32_t* out) {
+  return SelectSet{K, ws.counters, ws.sel, ws.candk, ws.candp, ws.cap, cand, out};
+}
+
+static hipError_t launch_collect_finish(const float* scores, int32_t R, int32_t N,
+                                        const int32_t* n_valid, int32_t n_all, uint32_t* hist,
+                                        bool zero_hist, const SelectSet& t0, const SelectSet& t1,
+                                        hipStream_t s) {
+  const dim3 grid((unsigned)((N + kChunk - 1) / kChunk), (unsigned)R);
+  k_topk_collect<<<grid, dim3(kSelThreads), 0, s>>>(scores, N, n_valid, n_all, hist, t0, t1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_topk_finish<<<dim3((unsigned)R, t1.K > 0 ? 2u : 1u), dim3(kFinThreads), 0, s>>>(
+      scores, N, n_valid, n_all, hist, zero_hist ? 1 : 0, t0, t1);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_select(const float* scores, int32_t R, int32_t N,
                               const int32_t* n_valid, int32_t n_all,
                               const int32_t* cand, int32_t K, int32_t* out,
                               const TopkWs& ws, bool zero_hist, hipStream_t s) {
-  const dim3 grid((unsigned)((N + kChunk - 1) / kChunk), (unsigned)R);
-  k_topk_collect<<<grid, dim3(kSelThreads), 0, s>>>(scores, N, n_valid, n_all, K, ws.hist,
-                                                    ws.counters, ws.sel, ws.candk, ws.candp, ws.cap);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  k_topk_finish<<<dim3((unsigned)R), dim3(kFinThreads), 0, s>>>(
-      scores, N, n_valid, n_all, K, ws.hist, ws.counters, ws.sel, ws.candk, ws.candp, ws.cap,
-      cand, out, zero_hist ? 1 : 0);
-  return hipGetLastError();
+  const SelectSet none{};
+  return launch_collect_finish(scores, R, N, n_valid, n_all, ws.hist, zero_hist,
+                               select_set(K, ws, cand, out), none, s);
+}
+
+hipError_t launch_topk_select2(const float* scores, int32_t R, int32_t N,
+                               const int32_t* n_valid, int32_t n_all,
+                               int32_t K0, int32_t* out0, const TopkWs& ws0,
+                               int32_t K1, int32_t* out1, const TopkWs& ws1,
+                               bool zero_hist, hipStream_t s) {
+  return launch_collect_finish(scores, R, N, n_valid, n_all, ws0.hist, zero_hist,
+                               select_set(K0, ws0, nullptr, out0), select_set(K1, ws1, nullptr, out1),
+                               s);
 }
 
 }  // namespace csa2
