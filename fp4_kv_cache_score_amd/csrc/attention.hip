@@ -21,8 +21,9 @@
 //           FP4->bf16 convert, FP8 with the FP8->bf16 convert, both exact),
 //           and as fp16 key pairs per dim (for P x V): an FP4 value enters
 //           as E2M1 x 2^(sc - ref), ref being the largest scale code of its
-//           32-dim block among the split's entries (found by a prologue
-//           pass), exact while sc >= ref - 23; an FP8 value is exact;
+//           32-dim block among the split's entries staged so far (a running
+//           maximum, kept in LDS per staged chunk), exact while
+//           sc >= ref - 23; an FP8 value is exact;
 //   logits  q sits in registers (each lane: 4 heads x 32 dims); a lane forms
 //           4 heads x 4 keys over its 32 dims with v_dot2_f32_bf16 (exact
 //           bf16 products, fp32 sums), and the 16 lanes of a row sum their
@@ -33,9 +34,10 @@
 //   P x V   each lane owns 8 dims of the 4 heads; p is rounded to fp16
 //           (relative error at most 2^-11) and every v_dot2_f32_f16 adds two
 //           keys of one dim, so the key pairs are used as staged.  The sums
-//           over global keys are in units of 2^(ref - 127) per block and are
-//           brought to units of 1 (exact powers of two) before the first
-//           window chunk or at the end.
+//           over global keys are in units of 2^(ref - 127) per block: they
+//           are rescaled by 2^(old - new) when a chunk raises ref, and
+//           brought to units of 1 before the first window chunk or at the
+//           end (exact powers of two).
 // With one split per row the work-group merges an incoming (o, lse) when
 // given, normalises and writes o and lse; otherwise it writes (unnormalised
 // o, max, sum) partials and k_attn_combine, launched right after it, merges
@@ -145,8 +147,23 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& a, const RowBase& rb,
   }
 }
 
+// Largest of x over the 16 lanes that share lane bits 1 and 2 (the 16 key
+// pairs of one staging segment): lane bits 0, 3, 4, 5.
+__device__ __forceinline__ uint32_t kp_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppXor1, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppRor8, 0xF, 0xF, false));
+  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(b[0], b[1]);
+}
+
+// ref: this thread's block's running reference (the largest scale code of
+// the split's keys staged so far), updated here for a global chunk and
+// published in refb[block] for the compute phase.
 __device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& r, uint32_t* rowb,
-                                            uint32_t* pairb, int32_t* valid_s, uint32_t ref) {
+                                            uint32_t* pairb, int32_t* valid_s, uint32_t& ref,
+                                            uint32_t* refb) {
   const int tid = threadIdx.x;
   const int kp = unit_kp(tid);
   const int seg = unit_seg(tid);
@@ -154,9 +171,10 @@ __device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& 
   // of entry 0 or row 0): their logits are masked and their p is 0.
   uint32_t w[2][8];   // per key: 16 bf16 of dims seg*16 .. seg*16+15 as 8 dim pairs
   uint32_t f[2][8];   // the same dims in fp16, in units of 2^(ref-127) for global keys
-                      // (ref: the largest scale code of this 32-dim block in the split)
   if (chunk < Cg) {
     const bool hi = seg & 1;             // the 8 code bytes are the upper half of the 16 loaded
+    ref = max(ref, kp_max(max(r.ok[0] ? r.sc[0] : 0u, r.ok[1] ? r.sc[1] : 0u)));
+    if (kp == 0 && !hi) refb[seg >> 1] = ref;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t sc = r.sc[i];
@@ -216,7 +234,7 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   __shared__ __attribute__((aligned(16))) uint32_t rowb[2][kRowBufU];
   __shared__ __attribute__((aligned(16))) uint32_t pairb[2][kPairBufU];
   __shared__ __attribute__((aligned(16))) uint32_t ps[8][8][4];   // [wave][key pair][head]: fp16 p pair
-  __shared__ uint32_t ref_s[kScaleRow];   // per 32-dim block: largest scale code among the split's entries
+  __shared__ uint32_t refb[2][kScaleRow];   // per staged chunk and 32-dim block: the running reference
   __shared__ int32_t idx_s[kMaxChunksPerSplit * KS];
   __shared__ int32_t valid_s[2][KS];
   __shared__ float mls[4][4][2];
@@ -238,7 +256,6 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   const int key0 = c0 * KS;
   const int gend = (c1 < Cg ? c1 : Cg) * KS;
   const int key1 = gend < a.K ? gend : a.K;
-  if (tid < kScaleRow) ref_s[tid] = 0;
   for (int k = key0 + tid; k < key1; k += kThreads) {   // entry -> pool row (-1 stays)
     const int32_t e = a.idx[(size_t)row * a.K + k];
     idx_s[k - key0] = e >= 0 ? (int32_t)pool_row(a.map, b, e, a.M) : -1;
@@ -265,24 +282,8 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
   rbase.win = a.swa + ((size_t)b * a.swa_rows + t) * kD;
   ChunkRegs r;
   load_chunk(a, rbase, c0, Cg, idx_s, key0, r);
-  {  // ref_s[blk] = the largest E8M0 code of 32-dim block blk among the
-     // split's entries: P x V runs on the fp16 values 2^(sc-ref) x E2M1, exact
-     // for sc >= ref - 23, and the sums take the factor 2^(ref-127) at the end.
-     // Thread tid reads block tid % 16 of entries tid / 16, tid / 16 + 32, ...
-    uint32_t mx = 0;
-    for (int k = tid; k < (key1 - key0) * kScaleRow; k += kThreads) {
-      const int32_t e = idx_s[k / kScaleRow];
-      if (e >= 0) mx = max(mx, (uint32_t)a.scale[(size_t)e * kScaleRow + (k % kScaleRow)]);
-    }
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
-    if (lane < kScaleRow && mx) atomicMax(&ref_s[lane], mx);
-  }
-  __syncthreads();
-  const uint32_t ref = ref_s[unit_seg(tid) >> 1];             // the block this thread stages
-  const float unit_lo = __builtin_amdgcn_ldexpf(1.0f, (int)ref_s[lane >> 3] - 127);        // dims 4l..
-  const float unit_hi = __builtin_amdgcn_ldexpf(1.0f, (int)ref_s[8 + (lane >> 3)] - 127);  // dims 256+4l..
-  stage_chunk(c0, Cg, r, rowb[0], pairb[0], valid_s[0], ref);
+  uint32_t sref = 0;   // running reference of the block this thread stages
+  stage_chunk(c0, Cg, r, rowb[0], pairb[0], valid_s[0], sref, refb[0]);
   load_chunk(a, rbase, c0 + 1 < c1 ? c0 + 1 : c0, Cg, idx_s, key0, r);
   __syncthreads();
 
@@ -293,6 +294,7 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
     for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
   float m_run = -INFINITY;                 // softmax state of head 4hg + hx in this stream
   float l_run = 0.f;
+  uint32_t r_lo = 0, r_hi = 0;             // references of the blocks of dims 4l.. and 256+4l..
 
   for (int c = c0; c < c1; ++c) {
     const int cur = (c - c0) & 1;
@@ -363,23 +365,32 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
     }
 
     {  // P x V
-      if (c == Cg && c0 < Cg) {   // first window chunk after global ones: sums to units of 1
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[h][i] *= unit_lo;
-            acc[h][4 + i] *= unit_hi;
-          }
+      // unit changes of the sums: a global chunk that raised a block's
+      // reference (2^(old - new)), or the first window chunk after global
+      // ones (to units of 1)
+      float glo = 1.f, ghi = 1.f;
+      if (c < Cg) {
+        const uint32_t n_lo = refb[cur][lane >> 3];
+        const uint32_t n_hi = refb[cur][8 + (lane >> 3)];
+        glo = __builtin_amdgcn_ldexpf(1.0f, (int)r_lo - (int)n_lo);
+        ghi = __builtin_amdgcn_ldexpf(1.0f, (int)r_hi - (int)n_hi);
+        r_lo = n_lo;
+        r_hi = n_hi;
+      } else if (c == Cg && c0 < Cg) {
+        glo = __builtin_amdgcn_ldexpf(1.0f, (int)r_lo - 127);
+        ghi = __builtin_amdgcn_ldexpf(1.0f, (int)r_hi - 127);
       }
       float al[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) al[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
-      if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
+      if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f || glo != 1.f || ghi != 1.f) {
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] *= al[h];
+          for (int i = 0; i < 4; ++i) {
+            acc[h][i] *= al[h] * glo;
+            acc[h][4 + i] *= al[h] * ghi;
+          }
       }
       const uint32_t* pb = pairb[cur] + (8 * st) * kPairU + 4 * lane;
       const uint32_t* pw = &ps[wave][0][0];
@@ -414,12 +425,14 @@ void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
       }
     }
     // the next chunk's codes (loaded one compute phase ago) go to the other buffer
-    if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1], ref);
+    if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1], sref, refb[cur ^ 1]);
     load_chunk(a, rbase, c + 2 < c1 ? c + 2 : c1 - 1, Cg, idx_s, key0, r);   // past the end: a harmless reload
     __syncthreads();
   }
 
   if (c1 <= Cg) {   // the split holds global keys only: to units of 1
+    const float unit_lo = __builtin_amdgcn_ldexpf(1.0f, (int)r_lo - 127);
+    const float unit_hi = __builtin_amdgcn_ldexpf(1.0f, (int)r_hi - 127);
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
