@@ -67,22 +67,25 @@ def test_fp4_dequant_bit_exact_through_single_key_attention():
     assert np.all(np.abs(lse[0, :512] - z) <= 512 * 2.0 ** -24 * mag + 1e-30)
 
 
-def test_sparse_attn_block_scale_spread_23_binades():
+@pytest.mark.parametrize("big", [0, 40])
+def test_sparse_attn_block_scale_spread_23_binades(big):
     """P x V takes fp16 values E2M1 x 2^(code - ref), ref the largest code of the
-    block among the selected entries; they are exact down to ref - 23.  Entry 0
-    sets ref = 143 in block 0 and gets weight ~e^-4000, so the output's block-0
-    dims come only from values 23 binades below it (fp16 subnormals)."""
+    block among the entries staged so far; they are exact down to ref - 23.
+    Entry `big` sets ref = 143 in block 0 and gets weight ~e^-4000, so the
+    output's block-0 dims come only from values 23 binades below it (fp16
+    subnormals).  With big = 40 (the second 32-key chunk) the reference rises
+    after the first chunk, whose sums are rescaled by 2^-23."""
     from fp4_kv_cache_score_amd.device import DeviceCase
-    say("case: sparse attention, block scales 23 binades apart")
+    say("case: sparse attention, block scales 23 binades apart, big entry %d" % big)
     cfg = CONFIGS[0].scaled(name="spread", B=1, M=64, K=64, W=0, modes=(FULL,))
     case = synth.make_case(cfg)
     rng = np.random.default_rng(23)
     case.pool.latent[:] = rng.integers(0, 256, size=case.pool.latent.shape, dtype=np.uint16)
     case.pool.scale[:] = 120
-    case.pool.scale[0, 0, 0] = 143
-    big = F.dequant_latent(case.pool.latent[0, :1], case.pool.scale[0, :1])[0, :32]
+    case.pool.scale[0, big, 0] = 143
+    cb = F.dequant_latent(case.pool.latent[0, big:big + 1], case.pool.scale[0, big:big + 1])[0, :32]
     q = case.layers[0].q                       # bf16 bits [1][1][16][512]
-    q[0, 0, :, :32] = np.where(big > 0, 0xBA80, np.where(big < 0, 0x3A80, 0)).astype(np.uint16)
+    q[0, 0, :, :32] = np.where(cb > 0, 0xBA80, np.where(cb < 0, 0x3A80, 0)).astype(np.uint16)
     dc = DeviceCase(case)
     idx = torch.arange(64, dtype=torch.int32, device="cuda").view(1, 1, 64)
     o, lse = dc.sparse_attn(0, idx)
