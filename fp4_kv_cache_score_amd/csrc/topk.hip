@@ -574,8 +574,11 @@ __device__ void row_find_digit(const uint32_t* h, uint32_t need, uint32_t* scan,
   __syncthreads();
 }
 
+// Rows streamed from memory (not held in registers) ask for 8 waves per SIMD
+// (the SGPR budget that allows), so that two rows' work-groups share a
+// compute unit and one's barriers and loads overlap the other's work.
 template <bool kHasHist, bool kPre>
-__global__ __launch_bounds__(kRowThreads)
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(kPre ? 1 : 8, kPre ? 4 : 8)))
 void k_topk_row(const float* __restrict__ scores, int32_t N,
                 const int32_t* __restrict__ n_valid, int32_t n_all, int32_t K,
                 uint32_t* __restrict__ hist, int32_t zero_hist,
