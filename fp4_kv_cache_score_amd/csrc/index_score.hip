@@ -7,7 +7,8 @@
 //
 // Work split: a pool entry's 512-byte key row is read by 32 lanes with one
 // 16-byte load each (two entries per wave64 load), so every wave load is a
-// fully coalesced 1 KiB; each lane keeps 8 such loads in flight.  Lane
+// fully coalesced 1 KiB; each lane issues them in batches of 4, the next
+// batch in flight while the current one is computed.  Lane
 // (sub = lane & 31) owns bytes [16*sub, 16*sub+16) of the row, i.e. indexer
 // head sub/4 and 16 of its 64 dims.  The FP8 x FP8
 // products are exact in fp32; each lane accumulates its 16 products with
@@ -23,7 +24,7 @@ namespace csa2 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;                        // 16-byte loads in flight per lane
+constexpr int kUnroll = 4;                        // 16-byte loads per lane and batch (two batches in flight)
 
 __device__ __forceinline__ float bfly_add(float v, int m) {
   return v + __shfl_xor(v, m, 64);
@@ -99,10 +100,12 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
   const int64_t roff = kCand ? 0 : (w0 < M ? pool_row(map, b, w0, M) : 0) - w0;   // row - entry
   const uint8_t* kb = key + sub * 16;
 
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    u32x4 v[kUnroll];
-    bool ok[kUnroll];
+  // Batches of kUnroll loads per lane, software-pipelined: the next batch is
+  // issued before this one is consumed, so a wave keeps loads in flight while
+  // it computes.
+  u32x4 v[2][kUnroll];
+  bool ok[2][kUnroll];
+  auto issue = [&](int it, int bi) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int lp = wofs + it * (2 * kUnroll) + 2 * u + half;   // position within the work-group
@@ -113,21 +116,27 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
         e = ce[lp];                        // candidate: its pool row
         valid = e >= 0;
       }
-      ok[u] = valid;
+      ok[bi][u] = valid;
       // every lane loads (an absent entry reads the query row instead, its
       // score is -inf whatever it holds): a load under a branch would make
       // the compiler wait for each one before issuing the next
       const uint8_t* src = valid ? kb + (roff + e) * kKeyRow : qsrc;
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      v[bi][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
     }
-    __builtin_amdgcn_sched_barrier(0);     // all kUnroll loads issue before any use
+  };
+  issue(0, 0);
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int cb = it & 1;
+    if (it + 1 < kIters) issue(it + 1, cb ^ 1);
+    __builtin_amdgcn_sched_barrier(0);     // the next batch issues before this one is used
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       float acc = 0.f;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u][d], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u][d], true);
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[cb][u][d], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[cb][u][d], true);
         acc = fmaf(lo.x, qf[4 * d + 0], acc);
         acc = fmaf(lo.y, qf[4 * d + 1], acc);
         acc = fmaf(hi.x, qf[4 * d + 2], acc);
@@ -141,8 +150,8 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
       r = bfly_add(r, 16);
       const int64_t p = g0 + wofs + it * (2 * kUnroll) + 2 * u + half;
       if (sub == 0 && p < N) {
-        srow[p] = ok[u] ? r : -INFINITY;
-        if (kHist && ok[u]) atomicAdd(&lh[score_key(r) >> (32 - kHistBits)], 1u);
+        srow[p] = ok[cb][u] ? r : -INFINITY;
+        if (kHist && ok[cb][u]) atomicAdd(&lh[score_key(r) >> (32 - kHistBits)], 1u);
       }
     }
   }
