@@ -522,8 +522,8 @@ def main():
                     help="first run a 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(decode shards by sequence; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(decode would shard by sequence, one process per GPU). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

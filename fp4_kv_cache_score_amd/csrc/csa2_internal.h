@@ -7,7 +7,7 @@
 
 namespace csa2 {
 
-// Fixed shapes of this build.
+// Fixed model shapes (latent, indexer and head widths).
 constexpr int kD = 512;          // latent width (shared K/V)
 constexpr int kLatRow = kD / 2;  // E2M1 bytes per latent row
 constexpr int kScaleRow = kD / 32;  // E8M0 scales per latent row
