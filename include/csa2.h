@@ -27,7 +27,7 @@
  *    E8M0 scale codes 0..252, selected indices in [-1, M), candidate lists
  *    strictly ascending with -1 padding only at the end.
  *  - Results are deterministic: the same inputs give bit-identical outputs.
- *  - Fixed shapes of this build: latent width D = 512, indexer HI = 8 heads of
+ *  - Fixed model shapes: latent width D = 512, indexer HI = 8 heads of
  *    DI = 64, attention heads H = 16.  Other values return CSA2_ERR_SHAPE.
  *
  * Number formats
