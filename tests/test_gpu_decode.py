@@ -153,6 +153,23 @@ def test_decode_small_schedules(kw):
     stagewise_topk_exact(case, dc, res)
 
 
+def test_decode_hierarchical_all_scores_equal():
+    """Zero index keys make every score exactly 0: the joint Top-P / Top-K of
+    the Full layer (several work-groups per row, one threshold bin holding the
+    whole row) and the Reindex layer must take the lowest indices."""
+    cfg = CONFIGS[0].scaled(name="hier_ties", seed=7, B=2, M=40000, K=256, P=4096, W=64,
+                            modes=(FULL, REINDEX, REUSE))
+    say("case: decode, all index scores equal", cfg.name)
+    case = synth.make_case(cfg)
+    case.pool.idx_key[:] = 0
+    dc, src, res = run_decode(case)
+    for ell in range(cfg.L):
+        for b in range(cfg.B):
+            assert np.array_equal(res[ell]["idx"][b, 0], np.arange(cfg.K, dtype=np.int32))
+    check_against_oracle(case, res, src, range(cfg.B))
+    stagewise_topk_exact(case, dc, res)
+
+
 def test_decode_is_deterministic():
     cfg = CONFIGS[0].scaled(name="det", B=4, M=40000, K=512, P=4096,
                             modes=(FULL, REINDEX, REUSE, REINDEX))

@@ -256,6 +256,30 @@ def test_topk_candidate_slot_overflow_path():
     assert np.array_equal(g, _oracle_rows(s, K))
 
 
+@pytest.mark.parametrize("K", [512, 8192])
+def test_topk_multi_group_bin_overflow(K):
+    """Rows longer than 2^18 go to the several-work-groups-per-row select; at
+    140 rows each row has fewer candidate slots than positions, so a row whose
+    threshold bin holds (nearly) every position takes the finish step's
+    re-scan of the row.  Rows: constant; zeros with a spike every 1000
+    positions; three values; continuous."""
+    R, N = 140, 262145
+    say("case: topk multi-group overflow R=%d N=%d K=%d" % (R, N, K))
+    rng = np.random.default_rng(K)
+    s = np.full((R, N), 0.25, np.float32)
+    for r in range(R):
+        if r % 4 == 1:
+            s[r] = 0.0
+            s[r, ::1000] = 1.0
+        elif r % 4 == 2:
+            s[r] = rng.integers(0, 3, N).astype(np.float32)
+        elif r % 4 == 3:
+            s[r] = rng.random(N, dtype=np.float32)
+    g = _gpu_topk(s, K)
+    assert np.array_equal(g[0], np.arange(K, dtype=np.int32))
+    assert np.array_equal(g, _oracle_rows(s, K))
+
+
 # --------------------------------------------------------------------------- attention
 
 def test_sparse_attn_dense_and_random_selection():
