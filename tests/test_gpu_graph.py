@@ -1,0 +1,97 @@
+"""A decode step captured into a HIP graph (torch.cuda.CUDAGraph around
+csa2_decode_layers) replays to the eager call's results bit for bit.
+
+The step launches kernels only (the Top-K scratch is cleared by a fill
+kernel, not by a memset), so it can be captured.  Each replay follows eager
+work that overwrites every output and a synchronisation; after the inputs are
+changed in place, a replay must equal a new eager call on the changed inputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from fp4_kv_cache_score_amd import synth
+from fp4_kv_cache_score_amd.configs import CONFIGS, FULL, REINDEX, REUSE
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp4_kv_cache_score_amd import _lib
+    _lib.lib()
+    yield
+
+
+CASES = [
+    dict(name="graph_flat", B=8, M=20000, K=256, W=128, modes=(FULL, REINDEX, REUSE, REUSE)),
+    dict(name="graph_hier", B=4, M=40000, K=256, P=4096, W=64, modes=(FULL, REINDEX, REUSE, REINDEX)),
+]
+
+
+def _same(want, got, what):
+    for ell, (a, b) in enumerate(zip(want, got)):
+        for k in ("idx", "o", "lse"):
+            assert np.array_equal(a[k], b[k]), "%s: layer %d %s differs" % (what, ell, k)
+
+
+def _clobber(dc):
+    for d in dc.layers:
+        d["o"].fill_(12345.0)
+        d["lse"].fill_(-3.0)
+        d["idx"].fill_(-7)
+
+
+@pytest.mark.parametrize("kw", CASES, ids=[c["name"] for c in CASES])
+def test_decode_step_graph_replay(kw):
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[0].scaled(seed=90 + len(kw["name"]), **kw)
+    say("case: graph replay", cfg.name, cfg.modes)
+    case = synth.make_case(cfg)
+    dc = DeviceCase(case)
+    dc.prepare_decode()
+    dc.decode_layers()                       # eager (also loads every kernel before capture)
+    torch.cuda.synchronize()
+    want = dc.results()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dc.decode_layers()
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        _clobber(dc)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(want, dc.results(), "replay %d" % rep)
+
+    # Inputs changed in place (queries of sequence b moved to sequence B-1-b):
+    # the graph reads them at replay time.
+    for d in dc.layers:
+        for k in ("q_idx", "w_idx"):
+            if d[k] is not None:         # Reuse layers carry no indexer query
+                d[k].copy_(d[k].flip(0))
+        qv = d["q"].view(torch.int16)
+        qv.copy_(qv.flip(0))
+    torch.cuda.synchronize()
+    _clobber(dc)
+    g.replay()
+    torch.cuda.synchronize()
+    got = dc.results()
+    _clobber(dc)
+    dc.decode_layers()
+    torch.cuda.synchronize()
+    want2 = dc.results()
+    _same(want2, got, "replay on changed inputs")
+    assert not np.array_equal(want2[0]["idx"], want[0]["idx"])
