@@ -5,6 +5,8 @@ The step launches kernels only (the Top-K scratch is cleared by a fill
 kernel, not by a memset), so it can be captured.  Each replay follows eager
 work that overwrites every output and a synchronisation; after the inputs are
 changed in place, a replay must equal a new eager call on the changed inputs.
+Two steps issued from two host threads onto two streams at once must give the
+results of the same steps run one after the other.
 """
 import sys
 
@@ -95,3 +97,45 @@ def test_decode_step_graph_replay(kw):
     want2 = dc.results()
     _same(want2, got, "replay on changed inputs")
     assert not np.array_equal(want2[0]["idx"], want[0]["idx"])
+
+
+def test_decode_two_streams_two_host_threads():
+    """No global state: two decode steps with their own workspaces, issued
+    from two host threads onto two streams at once, give the results of the
+    same steps run one after the other."""
+    import threading
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    say("case: two streams, two host threads")
+    dcs, want = [], []
+    for kw in CASES:
+        cfg = CONFIGS[0].scaled(seed=70 + len(kw["name"]), **kw)
+        dc = DeviceCase(synth.make_case(cfg))
+        dc.prepare_decode()
+        dc.decode_layers()
+        torch.cuda.synchronize()
+        want.append(dc.results())
+        _clobber(dc)
+        dcs.append(dc)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in dcs]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    errors = []
+
+    def run(dc, s):
+        try:
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    dc.decode_layers()
+        except Exception as e:       # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(dc, s)) for dc, s in zip(dcs, streams)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for dc, w, kw in zip(dcs, want, CASES):
+        _same(w, dc.results(), kw["name"] + " on its own stream")
