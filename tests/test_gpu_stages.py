@@ -256,6 +256,36 @@ def test_topk_candidate_slot_overflow_path():
     assert np.array_equal(g, _oracle_rows(s, K))
 
 
+@pytest.mark.parametrize("N,K,kind", [
+    (65536, 512, "cont"), (40000, 1, "cont"), (262144, 512, "cont"), (65536, 512, "sorted"),
+    (65536, 300, "ties"), (65536, 512, "const"), (65536, 513, "cont"), (50000, 64, "mixed")])
+def test_topk_streamed_rows_sampled_bound(N, K, kind):
+    """256 rows longer than 32768 take the one-work-group select that streams
+    its row from memory (a histogram pass, then a collection pass): continuous,
+    sorted, tied and constant rows, K around 512, valid counts around 32768
+    and an unaligned tail."""
+    R = 256
+    say("case: topk streamed rows R=%d N=%d K=%d %s" % (R, N, K, kind))
+    rng = np.random.default_rng(N + K)
+    nv = None
+    if kind == "cont":
+        s = (rng.standard_normal((R, N)) ** 2).astype(np.float32)
+    elif kind == "sorted":
+        s = np.sort(rng.random((R, N), dtype=np.float32), axis=1)
+        s[1::2] = s[1::2, ::-1]
+    elif kind == "ties":
+        s = rng.integers(0, 40, size=(R, N)).astype(np.float32) * np.float32(0.25)
+    elif kind == "const":
+        s = np.full((R, N), 0.5, np.float32)
+        s[::3, ::5000] = 1.0
+    else:   # valid counts around the sampling threshold and an unaligned tail
+        s = rng.random((R, N), dtype=np.float32)
+        nv = rng.integers(30000, N + 1, size=R).astype(np.int32)
+        nv[:4] = [32767, 32768, 32769, N]
+    g = _gpu_topk(s, K, n_valid=nv)
+    assert np.array_equal(g, _oracle_rows(s, K, n_valid=nv))
+
+
 @pytest.mark.parametrize("K", [512, 8192])
 def test_topk_multi_group_bin_overflow(K):
     """Rows longer than 2^18 go to the several-work-groups-per-row select; at
