@@ -6,7 +6,8 @@ kernel, not by a memset), so it can be captured.  Each replay follows eager
 work that overwrites every output and a synchronisation; after the inputs are
 changed in place, a replay must equal a new eager call on the changed inputs.
 Two steps issued from two host threads onto two streams at once must give the
-results of the same steps run one after the other.
+results of the same steps run one after the other.  The chunked-prefill chain
+is captured and replayed the same way.
 """
 import sys
 
@@ -139,3 +140,35 @@ def test_decode_two_streams_two_host_threads():
     assert not errors, errors
     for dc, w, kw in zip(dcs, want, CASES):
         _same(w, dc.results(), kw["name"] + " on its own stream")
+
+
+@pytest.mark.parametrize("M", [4096, 40000])
+def test_prefill_chain_graph_replay(M):
+    """The chunked-prefill chain (causal scores, Top-K over the visible
+    entries, attention, window merge) captured into a graph: every replay
+    equals the eager chain (rows held in registers at M = 4096, streamed rows
+    at M = 40000)."""
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[4].scaled(name="graph_pf", seed=55, B=1, Q=256, M=M, K=128, W=128)
+    say("case: prefill chain graph replay Q=%d M=%d" % (cfg.Q, cfg.M))
+    dc = DeviceCase(synth.make_case(cfg))
+    dc.prefill()                             # eager; allocates the chain's buffers
+    torch.cuda.synchronize()
+    outs = (dc.pf_idx, dc.pf_o, dc.pf_lse)
+    want = [t.cpu().numpy() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dc.prefill()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dc.pf_idx.fill_(-7)
+        dc.pf_o.fill_(12345.0)
+        dc.pf_lse.fill_(-3.0)
+        dc.pf_scores.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, t in zip(("idx", "o", "lse"), want, outs):
+            assert np.array_equal(a, t.cpu().numpy()), "replay %d: %s differs" % (rep, name)
