@@ -618,7 +618,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "operand_formats": "E4M3 index keys and window, E2M1 + E8M0 latent, bf16 queries; "
-                           "f32 accumulation (fp16 key pairs in the attention's P.V)",
+                           "f32 accumulation (attention: bf16 matrix products of exactly "
+                           "dequantised keys, softmax weights split into bf16 hi + lo)",
         "data": "synthetic (seeded N(0,1) pool and queries, MXFP4 / E4M3 encoded)",
         "config": {"workload": cfg.name, "batch": cfg.B, "pool_entries": cfg.M, "K": cfg.K,
                    "P": cfg.P, "W": cfg.W, "heads": cfg.H, "d": cfg.D,

@@ -63,11 +63,11 @@ struct DecodeWs {
 size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t N = P > M ? P : M;
   const int64_t Kmax = P > K ? P : K;
-  const int64_t chunks = attn_chunks((int32_t)K, (int32_t)W);
+  const int32_t steps = attn_steps((int32_t)K, (int32_t)W);
   const bool big = topk_multi_wg(B, M);
   return align256(B * N * 4) + (big ? topk_ws_bytes(B, M, Kmax) : 0) +
          (big && P > 0 ? topk_ws_bytes(B, M, K) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
-         attn_ws_bytes(B, chunks > 0 ? chunks : 1);
+         attn_ws_bytes(B, steps);
 }
 
 DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
@@ -88,8 +88,7 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   }
   d.cand = (int32_t*)p;
   p += align256(B * (P > 0 ? P : 1) * 4);
-  const int32_t chunks = attn_chunks((int32_t)K, (int32_t)W);
-  const AttnWs w = attn_ws_carve(p, B, chunks > 0 ? chunks : 1);
+  const AttnWs w = attn_ws_carve(p, B, attn_steps((int32_t)K, (int32_t)W));
   d.opart = w.opart;
   d.ml = w.ml;
   return d;
@@ -172,10 +171,10 @@ size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K, 
       return topk_call_ws_bytes(B, M, K);
     case CSA2_OP_SPARSE_ATTN:
       if (K <= 0 || K > kMaxK || H != kH) return 0;
-      return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, attn_chunks(K, 0));
+      return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, attn_steps(K, 0));
     case CSA2_OP_SWA_MERGE:
       if (W < 0 || W > kMaxW || H != kH) return 0;
-      return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, W > 0 ? attn_chunks(0, W) : 1);
+      return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, attn_steps(0, W));
     case CSA2_OP_PREFILL_LAYERS:
       if (M <= 0 || K <= 0 || K > kMaxK || W < 0 || W > kMaxW || H != kH ||
           (int64_t)B * Q > kMaxRows)
@@ -234,13 +233,15 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* 
   return hip_status(launch_topk_select(scores, R, N, n_valid, N, cand, K, idx, t, false, stream));
 }
 
-// Decode attention of `rows` query rows in the workspace of a stand-alone call.
-static csa2_status attend_rows(AttnArgs& a, void* ws, int64_t rows, int32_t chunks,
+// Attention of `rows` query rows in the workspace of a stand-alone call:
+// split decode rows (Q == 1), one work-group per token for a prefill chunk.
+static csa2_status attend_rows(AttnArgs& a, void* ws, int64_t rows, int32_t steps,
                                hipStream_t stream) {
-  const AttnWs w = attn_ws_carve(ws, rows, chunks);
+  if (a.Q > 1) return hip_status(launch_attn(a, AttnPlan{1, 0}, stream));
+  const AttnWs w = attn_ws_carve(ws, rows, steps);
   a.opart = w.opart;
   a.ml = w.ml;
-  return hip_status(launch_attn_partial(a, attn_plan(rows, chunks), stream));
+  return hip_status(launch_attn(a, attn_plan(rows, steps), stream));
 }
 
 csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q, int32_t H,
@@ -253,8 +254,8 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
     return CSA2_ERR_SHAPE;
   if (!al16(q) || !al4(idx) || !al16(o) || !al4(lse)) return CSA2_ERR_ALIGN;
   const int64_t rows = (int64_t)pool->B * Q;
-  const int32_t chunks = attn_chunks(K, 0);
-  const size_t need = Q > 1 ? 256 : attn_ws_bytes(rows, chunks);
+  const int32_t steps = attn_steps(K, 0);
+  const size_t need = Q > 1 ? 256 : attn_ws_bytes(rows, steps);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
   AttnArgs a{};
@@ -275,8 +276,7 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   a.lse = lse;
   a.o_in = nullptr;
   a.lse_in = nullptr;
-  if (Q > 1) return hip_status(launch_prefill_attn(a, nullptr, nullptr, stream));
-  return attend_rows(a, ws, rows, chunks, stream);
+  return attend_rows(a, ws, rows, steps, stream);
 }
 
 csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t D,
@@ -289,8 +289,8 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   if (W > 0 && !swa) return CSA2_ERR_NULL;
   if (!al16(q) || !al16(o) || !al4(lse) || (swa && !al16(swa))) return CSA2_ERR_ALIGN;
   const int64_t rows = (int64_t)B * Q;
-  const int32_t chunks = W > 0 ? attn_chunks(0, W) : 1;
-  if (!ws || ws_bytes < (Q > 1 ? 256 : attn_ws_bytes(rows, chunks))) return CSA2_ERR_WORKSPACE;
+  const int32_t steps = attn_steps(0, W);
+  if (!ws || ws_bytes < (Q > 1 ? 256 : attn_ws_bytes(rows, steps))) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
   if (W == 0) return CSA2_OK;  // nothing to merge: (o, lse) unchanged
   AttnArgs a{};
@@ -310,8 +310,7 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   a.lse = lse;
   a.o_in = o;
   a.lse_in = lse;
-  if (Q > 1) return hip_status(launch_prefill_attn(a, o, lse, stream));
-  return attend_rows(a, ws, rows, chunks, stream);
+  return attend_rows(a, ws, rows, steps, stream);
 }
 
 csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
@@ -331,7 +330,7 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
   if (!al16(ws)) return CSA2_ERR_ALIGN;
 
   const DecodeWs d = decode_ws_carve(ws, B, M, K, P, W);
-  const AttnPlan plan = attn_plan(B, attn_chunks(K, W));
+  const AttnPlan plan = attn_plan(B, attn_steps(K, W));
   float* opart = d.opart;
   float* ml = d.ml;
 
@@ -423,7 +422,7 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     a.lse_in = nullptr;
     a.o = y.o;
     a.lse = y.lse;
-    st = hip_status(launch_attn_partial(a, plan, stream));
+    st = hip_status(launch_attn(a, plan, stream));
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;
@@ -509,7 +508,7 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
     a.lse = y.lse;
     a.o_in = nullptr;
     a.lse_in = nullptr;
-    st = hip_status(launch_prefill_attn(a, nullptr, nullptr, stream));
+    st = hip_status(launch_attn(a, AttnPlan{1, 0}, stream));
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;

@@ -1,93 +1,73 @@
-// Decode attention over the selected FP4 global entries and the FP8 window.
+// Sparse attention over the selected FP4 global entries and the FP8 window,
+// on the matrix cores, for decode (one query token per sequence) and chunked
+// prefill (many tokens).
 //
 // The global entries are FP4 E2M1 with one E8M0 scale per 32 elements and are
 // restored to real values right before use; the sliding-window rows are FP8
 // ("DeepSeek V4.1-Flash Cuts KV Cache by 437x", paragraphs on FP4 quantisation
 // and sliding window attention; "DeepSeek V4.1 Flash Architecture Breakdown",
 // section "How are cache precision and storage arranged?").  Keys and values
-// are the same 512-wide latent row (shared K/V); all 16 heads share each
-// gathered row, so each row is read from HBM once per query row.
+// are the same 512-wide latent row (shared K/V), and all 16 heads of a query
+// token attend over the same gathered rows, so one token's attention is two
+// dense contractions with the heads as rows:
+//   S^T = C . q^T   (keys x heads, over the 512 dims)
+//   O   = P . C     (heads x dims, over the keys)
+// at 16 x 512 x 2 MACs per gathered 272-byte row: matrix-core work, not a
+// memory stream.
 //
-// k_attn_partial: one work-group of 8 waves per (query row, split).  A row's
-// keys are cut into chunks of 32 (the selected global entries first, then the
-// window rows) and a split is a run of consecutive chunks.  Wave w takes the
-// 4 heads 4(w%4).. and key stream w/4: keys 16(w/4)..16(w/4)+15 of every
-// chunk, with its own online-softmax state; the two streams are merged at the
-// end.  Per chunk (double-buffered, one barrier per chunk), after computing
-// on the current buffer the next chunk is staged into the other one:
-//   stage   the chunk's codes (loaded one compute phase ahead) are
-//           restored and written to LDS twice: as bf16 rows of dim pairs
-//           with the true scale (for q . c; FP4 with gfx950's scaled
-//           FP4->bf16 convert, FP8 with the FP8->bf16 convert, both exact),
-//           and as fp16 key pairs per dim (for P x V): an FP4 value enters
-//           as E2M1 x 2^(sc - ref), ref being the largest scale code of its
-//           32-dim block among the split's entries staged so far (a running
-//           maximum, kept in LDS per staged chunk), exact while
-//           sc >= ref - 23; an FP8 value is exact;
-//   logits  q sits in registers (each lane: 4 heads x 32 dims); a lane forms
-//           4 heads x 4 keys over its 32 dims with v_dot2_f32_bf16 (exact
-//           bf16 products, fp32 sums), and the 16 lanes of a row sum their
-//           parts with 15 DPP adds: heads and keys are laid out in a
-//           lane-rotated order so that every step adds the same registers;
-//   softmax per head over the stream's 16 keys (fp32): running max, rescale
-//           factor, p = exp(z - max), running sum;
-//   P x V   each lane owns 8 dims of the 4 heads; p is rounded to fp16
-//           (relative error at most 2^-11) and every v_dot2_f32_f16 adds two
-//           keys of one dim, so the key pairs are used as staged.  The sums
-//           over global keys are in units of 2^(ref - 127) per block: they
-//           are rescaled by 2^(old - new) when a chunk raises ref, and
-//           brought to units of 1 before the first window chunk or at the
-//           end (exact powers of two).
-// With one split per row the work-group merges an incoming (o, lse) when
-// given, normalises and writes o and lse; otherwise it writes (unnormalised
-// o, max, sum) partials and k_attn_combine, launched right after it, merges
-// them (and the incoming result) by log-sum-exp weights in a fixed order, so
-// that the result equals one softmax over the union of the key sets.  All
-// arithmetic runs on the VALU with fp32 accumulation; decode keeps the matrix
-// cores for the multi-query prefill contraction.
+// k_attn: two waves per work-group; wave h owns output dims 256 h .. 256 h +
+//   255.  The row's keys (selected global entries, then its window rows) are
+//   taken 32 per step.  Each lane loads 2 blocks of 32 dims of one key (this
+//   wave's half), dequantises them exactly to bf16 (E2M1 x 2^(scale - 127) and
+//   E4M3 have at most 4 significant bits and an exponent inside bf16's range)
+//   straight into the key operand of S^T (v_mfma_f32_16x16x32_bf16, 16 keys x
+//   16 heads, the dims of the contraction taken in the order the lanes hold
+//   them, q permuted to match), and stages the same bf16 rows in LDS.  The two
+//   waves' partial S^T (one per dim half) are exchanged through LDS and added
+//   in a fixed order, so both run the same online softmax per head in fp32.
+//   S^T leaves each lane with P for 4 keys of one head, which is the A-operand
+//   layout of O += P . C (same instruction; P split into bf16 hi + lo parts so
+//   that its rounding stays below 2^-16 relative), whose B operand (8 keys of
+//   one dim per lane) comes from the staged rows with gfx950's transposing LDS
+//   read (ds_read_b64_tr_b16).  The softmax reference moves only when a logit
+//   exceeds it by more than 8 (natural log), outside the inner loop, so O stays
+//   in the matrix accumulators.  One barrier per step.
+//   Two launch shapes:
+//   - one work-group per query row over all its keys (prefill: the many rows
+//     fill the chip); rows of one XCD are consecutive tokens, whose window
+//     rows overlap in its L2;
+//   - split (decode: B rows are too few for the chip): work-group (row, s)
+//     takes a contiguous run of the row's steps and writes its unnormalised
+//     O, its softmax reference and its sum per head; k_attn_combine merges
+//     the splits of a row in a fixed order.  A work-group mostly waits on
+//     memory (its q, its entry numbers, then the gathered rows) and one
+//     compute unit serves only a few tens of GB/s, so small work-groups spread
+//     over every compute unit beat fewer, larger ones (measured: four key
+//     streams per work-group, merged in LDS, were slower for decode and for
+//     prefill).  The splits of a row land on one XCD when the row count is a
+//     multiple of 8 (they read the same q).
+// Either way the result equals one softmax over the union of the selected
+// entries and the window rows, merged with an incoming (o, lse) when given.
 #include "csa2_internal.h"
+
+#include <type_traits>
 
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 512;                   // 8 waves: 4 head groups x 2 key streams
-constexpr int KS = kKeysPerSplit;               // 32 keys per chunk, 16 per stream
-constexpr int kRowU = kD / 2;                   // staged key row: 256 u32 of dim pairs
-constexpr int kPairU = kD + 4;                  // staged key pair: 512 u32 (+ pad) of key pairs
-constexpr int kRowBufU = KS * kRowU;            // 32 KiB
-constexpr int kPairBufU = (KS / 2) * kPairU;    // 32.25 KiB
-constexpr int kMaxChunksPerSplit = 32;          // entry numbers staged per work-group: 1024
-constexpr int kGroupsPerRound = 256;            // work-groups that run at once, one per compute unit
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
 
-__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+constexpr int kWK = kAttnStepKeys;             // keys per step (two MFMA sets of 16)
+constexpr int kHalf = kD / 2;                  // output dims per wave
+constexpr int kTRow = kHalf * 2;               // staged key row of one wave: 256 bf16 (512 B)
+constexpr float kLazy = 8.f;                   // softmax reference slack (natural log units)
 
-__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
-}
-
-// fp16 pair dot product with fp32 accumulation (v_dot2_f32_f16)
-__device__ __forceinline__ float hdot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-}
-
-// Value of x in the lane named by the DPP control word (within a row of 16).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppXor7 = 0x141;       // row_half_mirror
-constexpr int kDppXor15 = 0x140;      // row_mirror
-constexpr int kDppRor4 = 0x124;       // row_ror:4 (lane i reads lane i - 4 of its row)
-constexpr int kDppRor8 = 0x128;       // row_ror:8
-constexpr int kDppRor12 = 0x12C;      // row_ror:12 (lane i reads lane i + 4 of its row)
-constexpr float kLazyMax = 8.f;       // softmax reference slack (natural log units)
-
-// Max and sum over the four rows of 16 lanes: gfx950's permlane swaps
-// exchange rows 0<->1, 2<->3 and halves 0-31<->32-63 in a VALU operation
-// (both operands the same value); each lane combines the same two values
-// in the same order, so every lane gets the same result.
+// Max and sum over the four 16-lane rows (gfx950 permlane swaps; every lane
+// combines the same two values in the same order, so all get the same result).
 __device__ __forceinline__ float rows_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -101,438 +81,381 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Staging unit of a thread: key pair kp (keys 2kp, 2kp+1 of the chunk) and a
-// 16-dim segment seg.  The bit assignment keeps both LDS layouts' stores to
-// at most two lanes per bank group.
-__device__ __forceinline__ int unit_kp(int tid) { return (tid & 1) | ((tid >> 2) & 0xE); }
-__device__ __forceinline__ int unit_seg(int tid) { return ((tid >> 1) & 3) | ((tid >> 4) & 0x1C); }
-
-struct ChunkRegs {
-  u32x4 v[2];       // per key: 16 bytes (global: 32 E2M1 codes, half of them used; window: 16 E4M3)
-  uint32_t sc[2];   // global: E8M0 scale codes
-  bool ok[2];       // key present
-};
-
-// Per-sequence bases of the inputs a work-group reads.
-struct RowBase {
-  const uint8_t* lat;     // latent of pool row 0
-  const uint8_t* sc;      // scales of pool row 0
-  const uint8_t* win;     // window row 0 of the query row
-};
-
-// One 16-byte load per key from a selected address, with no branch: an
-// absent key reads entry 0 or row 0 of the sequence and is masked by ok, so
-// that no register merge has to wait for the loads.  Every address read is
-// inside the inputs.
-__device__ __forceinline__ void load_chunk(const AttnArgs& a, const RowBase& rb, int chunk, int Cg,
-                                           const int32_t* idx_s, int key0, ChunkRegs& r) {
-  const int tid = threadIdx.x;
-  const int kp = unit_kp(tid);
-  const int seg = unit_seg(tid);
-  const bool glob = chunk < Cg;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kpos = chunk * KS + 2 * kp + i;                 // global key position
-    const int wr = (chunk - Cg) * KS + 2 * kp + i;            // window row
-    const int32_t e = idx_s[(kpos - key0) & (kMaxChunksPerSplit * KS - 1)];
-    const bool ok = glob ? (kpos < a.K && e >= 0) : (wr < a.W);
-    r.ok[i] = ok;
-    const size_t er = (size_t)(glob && ok ? e : 0);
-    const uint8_t* gsrc = rb.lat + er * kLatRow + (seg >> 1) * 16;
-    const uint8_t* wsrc = rb.win + (size_t)(!glob && ok ? wr : 0) * kD + seg * 16;
-    r.v[i] = *reinterpret_cast<const u32x4*>(glob ? gsrc : wsrc);
-    // window chunks read a byte of q instead (the pool may be absent)
-    const uint8_t* sp = glob ? rb.sc + er * kScaleRow + (seg >> 1) : reinterpret_cast<const uint8_t*>(a.q);
-    r.sc[i] = *sp;
-  }
+// Byte offset of (key row r, byte c) in a wave's staged tile: 32-byte units
+// XOR-swizzled by the row's low 3 bits, 16-byte halves swapped by its bit 3.
+// The 8 rows that half a wave's transposed read touches then fall on 8
+// different 32-byte bank groups, and the 16 rows of a staging store on 16
+// different 16-byte ones.
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * kTRow + ((((c >> 5) ^ (r & 7)) << 5) | ((c & 31) ^ (((r >> 3) & 1) << 4)));
 }
 
-// Largest of x over the 16 lanes that share lane bits 1 and 2 (the 16 key
-// pairs of one staging segment): lane bits 0, 3, 4, 5.
-__device__ __forceinline__ uint32_t kp_max(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppXor1, 0xF, 0xF, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppRor8, 0xF, 0xF, false));
-  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  x = max(a[0], a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return max(b[0], b[1]);
-}
+// kSplit: grid (rows, splits); work-group (row, s) runs steps s * cps ..
+// s * cps + cps - 1 of the row (global steps first, Cg of them, then Cw
+// window steps) and writes a partial.  Otherwise grid (rows): one work-group
+// runs every step of its row and writes o and lse.
+template <bool kPaged, bool kSplit>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_attn(AttnArgs a, int32_t Cg, int32_t Cw, int32_t cps, const float* o_in,
+            const float* lse_in) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kWK * kTRow];   // 32 KiB
+  __shared__ __attribute__((aligned(16))) float xs[2][2][64 * 8];         // partial S, by step parity
 
-// ref: this thread's block's running reference (the largest scale code of
-// the split's keys staged so far), updated here for a global chunk and
-// published in refb[block] for the compute phase.
-__device__ __forceinline__ void stage_chunk(int chunk, int Cg, const ChunkRegs& r, uint32_t* rowb,
-                                            uint32_t* pairb, int32_t* valid_s, uint32_t& ref,
-                                            uint32_t* refb) {
-  const int tid = threadIdx.x;
-  const int kp = unit_kp(tid);
-  const int seg = unit_seg(tid);
-  // Absent keys are converted like the others (their codes are finite data
-  // of entry 0 or row 0): their logits are masked and their p is 0.
-  uint32_t w[2][8];   // per key: 16 bf16 of dims seg*16 .. seg*16+15 as 8 dim pairs
-  uint32_t f[2][8];   // the same dims in fp16, in units of 2^(ref-127) for global keys
-  if (chunk < Cg) {
-    const bool hi = seg & 1;             // the 8 code bytes are the upper half of the 16 loaded
-    ref = max(ref, kp_max(max(r.ok[0] ? r.sc[0] : 0u, r.ok[1] ? r.sc[1] : 0u)));
-    if (kp == 0 && !hi) refb[seg >> 1] = ref;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t sc = r.sc[i];
-      const float scale = __uint_as_float(sc ? (sc << 23) : 0x00400000u);   // 2^(sc-127)
-      // 2^(sc-ref) <= 1 for a present key; an absent key (entry 0's codes,
-      // whose scale may exceed ref) stages zeros, so that 0 x p stays 0
-      const float rel = r.ok[i] ? __builtin_amdgcn_ldexpf(1.0f, (int)sc - (int)ref) : 0.f;
-      const uint32_t x0 = hi ? r.v[i][2] : r.v[i][0];
-      const uint32_t x1 = hi ? r.v[i][3] : r.v[i][1];
-#define CSA2_CVT_FP4(M)                                                                          \
-      w[i][M] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x0, scale, M));     \
-      w[i][4 + M] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x1, scale, M)); \
-      f[i][M] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x0, rel, M));        \
-      f[i][4 + M] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x1, rel, M));
-      CSA2_CVT_FP4(0)
-      CSA2_CVT_FP4(1)
-      CSA2_CVT_FP4(2)
-      CSA2_CVT_FP4(3)
-#undef CSA2_CVT_FP4
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        w[i][2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, false));
-        w[i][2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[i][d], 1.0f, true));
-        f[i][2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)r.v[i][d], 1.0f, false));
-        f[i][2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)r.v[i][d], 1.0f, true));
-      }
+  int row, split = 0;
+  if (kSplit) {
+    row = blockIdx.x;
+    split = blockIdx.y;
+  } else {   // rows of one XCD are consecutive tokens (their window rows overlap in L2)
+    const int bid = blockIdx.x, R = a.rows;
+    const int q8 = R >> 3, r8 = R & 7, x = bid & 7, k = bid >> 3;
+    row = x * q8 + (x < r8 ? x : r8) + k;
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    uint32_t* dst = rowb + (2 * kp + i) * kRowU + seg * 8;
-    *reinterpret_cast<u32x4*>(dst) = u32x4{w[i][0], w[i][1], w[i][2], w[i][3]};
-    *reinterpret_cast<u32x4*>(dst + 4) = u32x4{w[i][4], w[i][5], w[i][6], w[i][7]};
-  }
-  uint32_t pr[16];    // dim seg*16 + j: (key 2kp, key 2kp+1)
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    pr[2 * m] = __builtin_amdgcn_perm(f[1][m], f[0][m], 0x05040100u);
-    pr[2 * m + 1] = __builtin_amdgcn_perm(f[1][m], f[0][m], 0x07060302u);
-  }
-  uint32_t* pd = pairb + kp * kPairU + seg * 16;
-#pragma unroll
-  for (int p4 = 0; p4 < 4; ++p4)
-    *reinterpret_cast<u32x4*>(pd + 4 * p4) = u32x4{pr[4 * p4], pr[4 * p4 + 1], pr[4 * p4 + 2], pr[4 * p4 + 3]};
-  if (seg == 0) {
-    valid_s[2 * kp] = r.ok[0];
-    valid_s[2 * kp + 1] = r.ok[1];
-  }
-}
-
-// grid (splits, rows), kThreads
-__global__ __launch_bounds__(kThreads, 1)
-void k_attn_partial(AttnArgs a, int32_t Cg, int32_t C, int32_t cps) {
-  __shared__ __attribute__((aligned(16))) uint32_t rowb[2][kRowBufU];
-  __shared__ __attribute__((aligned(16))) uint32_t pairb[2][kPairBufU];
-  __shared__ __attribute__((aligned(16))) uint32_t ps[8][8][4];   // [wave][key pair][head]: fp16 p pair
-  __shared__ uint32_t refb[2][kScaleRow];   // per staged chunk and 32-dim block: the running reference
-  __shared__ int32_t idx_s[kMaxChunksPerSplit * KS];
-  __shared__ int32_t valid_s[2][KS];
-  __shared__ float mls[4][4][2];
-
-  const int row = blockIdx.y;
-  const int split = blockIdx.x;
-  const int S = gridDim.x;
   const int b = row / a.Q;
   const int t = row - b * a.Q;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hg = wave & 3;                 // heads 4hg .. 4hg+3
-  const int st = wave >> 2;                // key stream
-  const int c0 = split * cps;
-  const int c1 = (c0 + cps < C) ? c0 + cps : C;
+  const int hw = threadIdx.x >> 6;           // this wave's half of the dims
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int64_t wgap = a.pos0 >= 0 ? (int64_t)(a.W - 1) - (a.pos0 + t) : 0;
+  const int32_t wfirst = wgap > 0 ? (int32_t)wgap : 0;
 
-  // entry numbers of this split's global keys -> LDS
-  const int key0 = c0 * KS;
-  const int gend = (c1 < Cg ? c1 : Cg) * KS;
-  const int key1 = gend < a.K ? gend : a.K;
-  for (int k = key0 + tid; k < key1; k += kThreads) {   // entry -> pool row (-1 stays)
-    const int32_t e = a.idx[(size_t)row * a.K + k];
-    idx_s[k - key0] = e >= 0 ? (int32_t)pool_row(a.map, b, e, a.M) : -1;
+  // q (this half) as the B operand of S^T = C . q^T: lane (head ln, group lg)
+  // holds, for k-step s, dims 256 hw + 32 (4 (s / 4) + lg) + 8 (s % 4) .. +7,
+  // the order in which the key operand below holds them
+  bf16x8 qv[8];
+  {
+    const uint16_t* qr = a.q + ((size_t)row * kH + ln) * kD + kHalf * hw;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qv[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                             qr + 32 * (4 * (s >> 2) + lg) + 8 * (s & 3)));
+  }
+  const int32_t* irow = a.idx ? a.idx + (size_t)row * a.K : nullptr;
+  // this work-group's steps: st0 .. st_end - 1 (the loads of the step after
+  // the last are harmless re-reads)
+  int cg, ws0, st0, st_end;
+  if (kSplit) {
+    // a fixed run of steps; a step whose keys are all absent adds nothing
+    cg = Cg;
+    ws0 = 0;
+    st0 = split * cps;
+    st_end = min(st0 + cps, Cg + Cw);
+  } else {
+    // the last position holding an entry (-1 entries select nothing); the
+    // entry numbers are read 512 at a time, all loads in flight together
+    int last = -1;
+    if (Cg > 0) {
+      for (int k0 = 0; k0 < a.K; k0 += 512) {
+        int32_t e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = irow[min(k0 + 64 * u + lane, a.K - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (e[u] >= 0 && k0 + 64 * u + lane < a.K) last = max(last, k0 + 64 * u + lane);
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    cg = __builtin_amdgcn_readfirstlane(Cg > 0 ? (last + kWK) / kWK : 0);
+    ws0 = __builtin_amdgcn_readfirstlane(wfirst / kWK);   // window steps before position 0
+    st0 = 0;
+    st_end = cg + (Cw > ws0 ? Cw - ws0 : 0);
   }
 
-  // logits lane: key group kb (4 keys), dim part dp (dims 8dp + 128j .. +7, j < 4).
-  // Head slot s holds head 4hg + (s ^ hx) and key slot s key 4kb + (s ^ kx).
-  const int kb = lane >> 4;
-  const int dp = lane & 15;
-  const int hx = dp & 3;
-  const int kx = (dp >> 2) & 3;
-  u32x4 qr[4][4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint16_t* qh = a.q + ((size_t)row * kH + 4 * hg + (s ^ hx)) * kD + 8 * dp;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qr[s][j] = *reinterpret_cast<const u32x4*>(qh + 128 * j);
-  }
-  __syncthreads();
+  const uint8_t* lat_b = a.latent ? a.latent + 128 * hw : nullptr;   // indexed by pool row
+  const uint8_t* sc_b = a.scale;
+  const uint8_t* swa_b = a.swa ? a.swa + ((size_t)b * a.swa_rows + t) * kD + kHalf * hw : nullptr;
+  // a readable stand-in for loads past the last step (this row's q: 16 KiB)
+  const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.q + (size_t)row * kH * kD);
+  const int kmax = a.K > 0 ? a.K - 1 : 0;
 
-  RowBase rbase;
-  rbase.lat = a.latent;   // idx_s holds pool rows
-  rbase.sc = a.scale;
-  rbase.win = a.swa + ((size_t)b * a.swa_rows + t) * kD;
-  ChunkRegs r;
-  load_chunk(a, rbase, c0, Cg, idx_s, key0, r);
-  uint32_t sref = 0;   // running reference of the block this thread stages
-  stage_chunk(c0, Cg, r, rowb[0], pairb[0], valid_s[0], sref, refb[0]);
-  load_chunk(a, rbase, c0 + 1 < c1 ? c0 + 1 : c0, Cg, idx_s, key0, r);
-  __syncthreads();
+  // entry number for step `st` (an unconditional load at a clamped position)
+  const int32_t* irow_s = irow ? irow : reinterpret_cast<const int32_t*>(spare);
+  auto entry = [&](int st, int u) __attribute__((always_inline)) -> int32_t {
+    return irow_s[min(st * kWK + 16 * u + ln, kmax)];
+  };
+  // step `st`, set u: key 16 u + ln; lane group lg loads blocks lg and 4 + lg
+  // of this half.  Global: v0, v1 = 16 E2M1 bytes each, v2 = v3 = the entry's
+  // scale bytes.  Window: (v0, v1), (v2, v3) = 32 E4M3 bytes each.  All four
+  // loads are issued unconditionally from selected, valid addresses.
+  auto load = [&](int st, int u, int32_t e, u32x4& v0, u32x4& v1, u32x4& v2, u32x4& v3)
+      __attribute__((always_inline)) -> bool {
+    const bool g = st < cg;
+    const int kpos = st * kWK + 16 * u + ln;
+    const bool okg = kpos < a.K && e >= 0;
+    const int wr = (st - cg + ws0) * kWK + 16 * u + ln;
+    const bool okw = wr < a.W && wr >= wfirst;
+    const uint8_t *p0, *p1, *p2, *p3;
+    if (g) {
+      const int32_t ec = okg ? e : 0;                         // entry 0 exists
+      // the paged kind has its own kernel, so the contiguous loop holds no table load
+      const int64_t pr = kPaged ? pool_row(a.map, b, ec, a.M) : (int64_t)b * a.M + ec;
+      const uint8_t* gl = lat_b + (size_t)pr * kLatRow;
+      p0 = gl + 16 * lg;
+      p1 = gl + 16 * (4 + lg);
+      p2 = p3 = sc_b + (size_t)pr * kScaleRow;
+    } else {
+      const uint8_t* wp = a.W > 0 ? swa_b + (size_t)(okw ? wr : a.W - 1) * kD : spare;
+      p0 = wp + 32 * lg;
+      p1 = p0 + 16;
+      p2 = wp + 32 * (4 + lg);
+      p3 = p2 + 16;
+    }
+    v0 = *reinterpret_cast<const u32x4*>(p0);
+    v1 = *reinterpret_cast<const u32x4*>(p1);
+    v2 = *reinterpret_cast<const u32x4*>(p2);
+    v3 = *reinterpret_cast<const u32x4*>(p3);
+    return g ? okg : okw;
+  };
 
-  float acc[4][8];                         // P x V: heads 4hg.. x dims 4l..4l+3, 256+4l..
+  uint8_t* my = tile[hw];
+  // dequantise set u (k-steps 4 i + d from block 4 i + lg of this half),
+  // accumulate the partial S^T and stage the bf16 rows for P . C
+  auto score_set = [&](auto gtag, int u, const u32x4& v0, const u32x4& v1, const u32x4& v2,
+                       const u32x4& v3, f32x4& s0, f32x4& s1) __attribute__((always_inline)) {
+    constexpr bool kGlobal = decltype(gtag)::value;
+    const int r = 16 * u + ln;
 #pragma unroll
-  for (int h = 0; h < 4; ++h)
+    for (int i = 0; i < 2; ++i) {
+      const int blk = 4 * i + lg;
+      u32x4 w[4];
+      if (kGlobal) {
+        const u32x4& c = i ? v1 : v0;
+        const uint32_t sw = hw ? v2[2 + i] : v2[i];          // scale bytes of blocks 8 hw + 4 i ..
+        const uint32_t scb = (sw >> (8 * lg)) & 0xFFu;
+        const float scale = __uint_as_float(scb ? (scb << 23) : 0x00400000u);   // 2^(scb-127)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
-  float m_run = -INFINITY;                 // softmax state of head 4hg + hx in this stream
-  float l_run = 0.f;
-  uint32_t r_lo = 0, r_hi = 0;             // references of the blocks of dims 4l.. and 256+4l..
-
-  for (int c = c0; c < c1; ++c) {
-    const int cur = (c - c0) & 1;
-
-    float zs;
-    {  // logits of 4 heads x 4 keys over 32 dims, then summed over the row's 16 lanes
-      const uint32_t* rb = rowb[cur] + (16 * st + 4 * kb) * kRowU + 4 * dp;
-      float z[4][4];
+        for (int d = 0; d < 4; ++d) {
+          w[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 0));
+          w[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 1));
+          w[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 2));
+          w[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 3));
+        }
+      } else {
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) z[h][k] = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t* kr = rb + (k ^ kx) * kRowU;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 cv = *reinterpret_cast<const u32x4*>(kr + 64 * j);
-#pragma unroll
-          for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) z[h][k] = fdot2(qr[h][j][w], cv[w], z[h][k]);
+        for (int d = 0; d < 4; ++d) {
+          const u32x4& c = i ? (d < 2 ? v2 : v3) : (d < 2 ? v0 : v1);
+          const uint32_t x0 = c[2 * (d & 1)], x1 = c[2 * (d & 1) + 1];
+          w[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.0f, false));
+          w[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.0f, true));
+          w[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.0f, false));
+          w[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.0f, true));
         }
       }
-      // The partner in each step flips the lane bits that select the slot
-      // order, so the element in my slot (h, k) sits in its slot (h ^ x, k ^ y).
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) z[h][k] += dpp<kDppXor15>(z[h ^ 3][k ^ 3]);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) z[h][0] += dpp<kDppXor7>(z[h ^ 3][1]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) z[h][0] += dpp<kDppXor2>(z[h ^ 2][0]);
-      z[0][0] += dpp<kDppXor1>(z[1][0]);
-      zs = z[0][0];                        // head 4hg + hx, key 4kb + kx of the stream
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, w[d]);
+        if (d & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[4 * i + d], s1, 0, 0, 0);
+        else       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[4 * i + d], s0, 0, 0, 0);
+        *reinterpret_cast<u32x4*>(my + tile_off(r, 64 * blk + 16 * d)) = w[d];
+      }
     }
+  };
 
-    float alpha;
-    {  // online softmax of head 4hg + hx over the stream's 16 keys
-      const int kk = 4 * kb + kx;
-      const float zv = valid_s[cur][16 * st + kk] ? zs : -INFINITY;
-      float mc = fmaxf(zv, dpp<kDppRor4>(zv));
-      mc = rows_max(fmaxf(mc, dpp<kDppRor8>(mc)));
-      // The reference m_run moves only when the chunk's max passes it by
-      // more than kLazyMax, so that p <= e^kLazyMax and most chunks need no
-      // rescaling; o / l and m + log l are the same for any reference.
-      const float m_new = mc > m_run + kLazyMax ? mc : m_run;
-      float p = 0.f;
-      alpha = 1.f;
-      if (m_new != -INFINITY) {
-        p = __expf(zv - m_new);
-        alpha = __expf(m_run - m_new);
-      }
-      float ls = p + dpp<kDppRor4>(p);
-      ls = rows_sum(ls + dpp<kDppRor8>(ls));
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-      // key pairs (kk, kk + 1) for kk even: the odd key is in lane dp + 4;
-      // p in fp16 (round to nearest even, relative error below 2^-11;
-      // p <= e^kLazyMax stays far below the fp16 maximum)
-      const float po = dpp<kDppRor12>(p);
-      const uint32_t pu = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p, po}, f16x2));
-      if (!(dp & 4)) ps[wave][kk >> 1][hx] = pu;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+  // O[j][i]: head 4 lg + i, dim 256 hw + 16 j + ln
+  f32x4 O[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // softmax reference of head ln
+  float l_run = 0.f;         // this lane's share of head ln's sum
 
-    {  // P x V
-      // unit changes of the sums: a global chunk that raised a block's
-      // reference (2^(old - new)), or the first window chunk after global
-      // ones (to units of 1)
-      float glo = 1.f, ghi = 1.f;
-      if (c < Cg) {
-        const uint32_t n_lo = refb[cur][lane >> 3];
-        const uint32_t n_hi = refb[cur][8 + (lane >> 3)];
-        glo = __builtin_amdgcn_ldexpf(1.0f, (int)r_lo - (int)n_lo);
-        ghi = __builtin_amdgcn_ldexpf(1.0f, (int)r_hi - (int)n_hi);
-        r_lo = n_lo;
-        r_hi = n_hi;
-      } else if (c == Cg && c0 < Cg) {
-        glo = __builtin_amdgcn_ldexpf(1.0f, (int)r_lo - 127);
-        ghi = __builtin_amdgcn_ldexpf(1.0f, (int)r_hi - 127);
-      }
-      float al[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) al[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
-      if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f || glo != 1.f || ghi != 1.f) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[h][i] *= al[h] * glo;
-            acc[h][4 + i] *= al[h] * ghi;
-          }
-      }
-      const uint32_t* pb = pairb[cur] + (8 * st) * kPairU + 4 * lane;
-      const uint32_t* pw = &ps[wave][0][0];
-      // two register sets, each loaded one step before use; the scheduling
-      // barriers keep the compiler from sinking the loads to their uses
-      u32x4 A[3], Bx[3];
-      auto load_pair = [&](u32x4* x, int kp) {
-        x[0] = *reinterpret_cast<const u32x4*>(pw + kp * 4);
-        x[1] = *reinterpret_cast<const u32x4*>(pb + kp * kPairU);
-        x[2] = *reinterpret_cast<const u32x4*>(pb + kp * kPairU + 256);
-      };
-      auto pv_pair = [&](const u32x4* x) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[h][i] = hdot2(x[0][h], x[1][i], acc[h][i]);
-            acc[h][4 + i] = hdot2(x[0][h], x[2][i], acc[h][4 + i]);
-          }
-      };
-      load_pair(A, 0);
-#pragma unroll 1
-      for (int kp = 0; kp < 8; kp += 2) {
-        load_pair(Bx, kp + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        pv_pair(A);
-        __builtin_amdgcn_sched_barrier(0);
-        load_pair(A, (kp + 2) & 7);      // the last step reloads pair 0, unused
-        __builtin_amdgcn_sched_barrier(0);
-        pv_pair(Bx);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
+  int32_t ea = -1, eb = -1;
+  bool oka = false, okb = false;
+  if (st0 < st_end) {
+    oka = load(st0, 0, entry(st0, 0), a0, a1, a2, a3);
+    okb = load(st0, 1, entry(st0, 1), b0, b1, b2, b3);
+    ea = entry(st0 + 1, 0);
+    eb = entry(st0 + 1, 1);
+  }
+  // transposed-read rows: key 4 lg + ln / 4 (+ 16 for set 1), dims + 4 (ln % 4)
+  const int tr0 = 4 * lg + (ln >> 2), tr1 = tr0 + 16;
+
+  // one step's scores: dequantise and score both sets (the next step's loads
+  // issued as each set's registers free up), exchange the halves' partial
+  // sums; x0 / x1 = full logits of keys 4 lg + e (+16), head ln, -inf when absent
+  auto step_scores = [&](int st, f32x4& x0, f32x4& x1) __attribute__((always_inline)) -> float {
+    f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
+    const uint64_t va = __ballot(oka), vb = __ballot(okb);
+    const bool global = st < cg;
+    __asm__ volatile("" ::: "memory");       // this step's staging after the last step's reads
+    if (global) score_set(std::true_type{}, 0, a0, a1, a2, a3, sa0, sa1);
+    else        score_set(std::false_type{}, 0, a0, a1, a2, a3, sa0, sa1);
+    oka = load(st + 1, 0, ea, a0, a1, a2, a3);
+    ea = entry(st + 2, 0);
+    if (global) score_set(std::true_type{}, 1, b0, b1, b2, b3, sb0, sb1);
+    else        score_set(std::false_type{}, 1, b0, b1, b2, b3, sb0, sb1);
+    okb = load(st + 1, 1, eb, b0, b1, b2, b3);
+    eb = entry(st + 2, 1);
+    {  // the two halves' partial sums, added in a fixed order by both waves
+      float* xw = &xs[st & 1][hw][lane * 8];
+      *reinterpret_cast<f32x4*>(xw) = sa0 + sa1;
+      *reinterpret_cast<f32x4*>(xw + 4) = sb0 + sb1;
     }
-    // the next chunk's codes (loaded one compute phase ago) go to the other buffer
-    if (c + 1 < c1) stage_chunk(c + 1, Cg, r, rowb[cur ^ 1], pairb[cur ^ 1], valid_s[cur ^ 1], sref, refb[cur ^ 1]);
-    load_chunk(a, rbase, c + 2 < c1 ? c + 2 : c1 - 1, Cg, idx_s, key0, r);   // past the end: a harmless reload
     __syncthreads();
-  }
-
-  if (c1 <= Cg) {   // the split holds global keys only: to units of 1
-    const float unit_lo = __builtin_amdgcn_ldexpf(1.0f, (int)r_lo - 127);
-    const float unit_hi = __builtin_amdgcn_ldexpf(1.0f, (int)r_hi - 127);
+    const float* x0p = &xs[st & 1][0][lane * 8];
+    const float* x1p = &xs[st & 1][1][lane * 8];
+    x0 = *reinterpret_cast<const f32x4*>(x0p) + *reinterpret_cast<const f32x4*>(x1p);
+    x1 = *reinterpret_cast<const f32x4*>(x0p + 4) + *reinterpret_cast<const f32x4*>(x1p + 4);
+    float mc = -INFINITY;
+    const uint32_t ba = (uint32_t)(va >> (4 * lg)), bb = (uint32_t)(vb >> (4 * lg));   // keys 4 lg ..
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[h][i] *= unit_lo;
-        acc[h][4 + i] *= unit_hi;
-      }
-  }
-  // stream 1 hands its (o, max, sum) to stream 0 through LDS
-  float* xa = reinterpret_cast<float*>(rowb[0]) + hg * 32 * 64 + lane;
-  if (st == 1) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xa[(h * 8 + i) * 64] = acc[h][i];
-    if (lane < 4) {
-      mls[hg][lane][0] = m_run;
-      mls[hg][lane][1] = l_run;
+    for (int e = 0; e < 4; ++e) {
+      x0[e] = (ba >> e) & 1u ? x0[e] : -INFINITY;
+      x1[e] = (bb >> e) & 1u ? x1[e] : -INFINITY;
+      mc = fmaxf(mc, fmaxf(x0[e], x1[e]));
     }
-  }
-  __syncthreads();
-
-  float Mh[4], Lh[4];
-  if (st == 0) {
+    return rows_max(mc);
+  };
+  // one step's P . C on this half's dims, with the current reference
+  auto step_pv = [&](const f32x4& x0, const f32x4& x1) __attribute__((always_inline)) {
+    // absent keys are -inf: exp gives 0 (a reference of -inf only occurs while
+    // every key so far is absent, and then 0 stands in for it)
+    const float mr = m_run == -INFINITY ? 0.f : m_run;
+    float p[8];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), h));
-      const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), h));
-      const float m1 = mls[hg][h][0];
-      const float l1 = mls[hg][h][1];
-      const float M = fmaxf(m0, m1);
-      const float w0 = m0 == -INFINITY ? 0.f : __expf(m0 - M);
-      const float w1 = m1 == -INFINITY ? 0.f : __expf(m1 - M);
-      Mh[h] = M;
-      Lh[h] = l0 * w0 + l1 * w1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * w0 + xa[(h * 8 + i) * 64] * w1;
+    for (int e = 0; e < 4; ++e) {
+      p[e] = __expf(x0[e] - mr);
+      p[4 + e] = __expf(x1[e] - mr);
     }
+    // A operand: keys 4 lg + e of set 0, then of set 1 (the B reads below take
+    // the same keys); P = hi + lo in bf16
+    u32x4 ph, pl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      l_run += p[2 * e] + p[2 * e + 1];
+      const bf16x2 hv = __builtin_convertvector((f32x2){p[2 * e], p[2 * e + 1]}, bf16x2);
+      const f32x2 hf = __builtin_convertvector(hv, f32x2);
+      const bf16x2 lv = __builtin_convertvector((f32x2){p[2 * e] - hf[0], p[2 * e + 1] - hf[1]}, bf16x2);
+      ph[e] = __builtin_bit_cast(uint32_t, hv);
+      pl[e] = __builtin_bit_cast(uint32_t, lv);
+    }
+    const bf16x8 ahi = __builtin_bit_cast(bf16x8, ph);
+    const bf16x8 alo = __builtin_bit_cast(bf16x8, pl);
+    __asm__ volatile("" ::: "memory");       // staging stores before the transposed reads
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = 32 * j + 8 * (ln & 3);
+      const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(my + tile_off(tr0, c)));
+      const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(my + tile_off(tr1, c)));
+      const u32x2 c0 = __builtin_bit_cast(u32x2, r0), c1 = __builtin_bit_cast(u32x2, r1);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{c0[0], c0[1], c1[0], c1[1]});
+      O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, O[j], 0, 0, 0);
+      O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, O[j], 0, 0, 0);
+    }
+  };
+
+  // Steps run in an inner loop that touches O only with matrix instructions;
+  // a step whose logits exceed the reference by more than kLazy leaves the
+  // loop, and O is rescaled before that step's P . C.
+  int it = st0;
+  while (it < st_end) {
+    f32x4 x0, x1;
+    float mc = -INFINITY;
+    bool raise = false;
+#pragma unroll 1
+    for (; it < st_end; ++it) {
+      mc = step_scores(it, x0, x1);
+      raise = mc > m_run + kLazy;
+      if (__ballot(raise) != 0) break;
+      step_pv(x0, x1);
+    }
+    if (it >= st_end) break;
+    const float m_new = raise ? mc : m_run;
+    const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[j][i] *= al[i];
+    step_pv(x0, x1);
+    ++it;
   }
 
-  if (S == 1) {   // the whole row is here: merge an incoming result, normalise, write
-    if (st == 0) {
+  const float L = rows_sum(l_run);   // head ln's sum (relative to m_run)
+  if (kSplit) {
+    // this split's partial: O unnormalised (relative to the reference of its
+    // head), the reference and the sum per head
+    const size_t ps = (size_t)row * gridDim.y + split;
+    float* op = a.opart + ps * kH * kD + kHalf * hw;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const size_t hr = (size_t)row * kH + 4 * hg + h;
-        float M = Mh[h], L = Lh[h];
-        if (a.lse_in) {     // (o, lse) in/out may alias: each lane reads its own elements first
-          const float li = a.lse_in[hr];
-          const float M2 = fmaxf(M, li);
-          const float w1 = M == -INFINITY ? 0.f : __expf(M - M2);
-          const float w2 = li == -INFINITY ? 0.f : __expf(li - M2);
-          const float4 x0 = *reinterpret_cast<const float4*>(a.o_in + hr * kD + 4 * lane);
-          const float4 x1 = *reinterpret_cast<const float4*>(a.o_in + hr * kD + 256 + 4 * lane);
-          const float xi[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * w1 + xi[i] * w2;
-          L = L * w1 + w2;
-          M = M2;
-        }
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        float* dst = a.o + hr * kD + 4 * lane;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
-        *reinterpret_cast<float4*>(dst + 256) = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
-        if (lane == 0) a.lse[hr] = L > 0.f ? M + logf(L) : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i) op[(size_t)(4 * lg + i) * kD + 16 * j + ln] = O[j][i];
+    if (hw == 0 && lg == 0) {
+      a.ml[(ps * kH + ln) * 2] = m_run;
+      a.ml[(ps * kH + ln) * 2 + 1] = L;
     }
     return;
   }
-
-  if (st == 0) {   // this split's partial: unnormalised o, max, sum
-    float* op = a.opart + (((size_t)row * S + split) * kH + 4 * hg) * kD + 4 * lane;
+  // per head: lse, merge with an incoming result; lane (ln, lg) writes dims
+  // 256 hw + 16 j + ln of heads 4 lg + i
+  const float lse_h = L > 0.f ? m_run + logf(L) : -INFINITY;   // head ln
+  float wself[4], win[4], lse4[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      *reinterpret_cast<float4*>(op + (size_t)h * kD) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *reinterpret_cast<float4*>(op + (size_t)h * kD + 256) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+  for (int i = 0; i < 4; ++i) {
+    const float Li = __shfl(L, 4 * lg + i, 64);
+    float lse = __shfl(lse_h, 4 * lg + i, 64);
+    wself[i] = Li > 0.f ? 1.f / Li : 0.f;
+    win[i] = 0.f;
+    if (lse_in) {   // one softmax over both key sets
+      const float li = lse_in[(size_t)row * kH + 4 * lg + i];
+      const float mx = fmaxf(li, lse);
+      if (mx != -INFINITY) {
+        const float e1 = li == -INFINITY ? 0.f : __expf(li - mx);
+        const float e2 = lse == -INFINITY ? 0.f : __expf(lse - mx);
+        const float tot = e1 + e2;
+        win[i] = e1 / tot;
+        wself[i] *= e2 / tot;
+        lse = mx + logf(tot);
+      }
     }
-    if (lane < 4) {
-      const float L = lane == 0 ? Lh[0] : lane == 1 ? Lh[1] : lane == 2 ? Lh[2] : Lh[3];
-      const float M = lane == 0 ? Mh[0] : lane == 1 ? Mh[1] : lane == 2 ? Mh[2] : Mh[3];
-      float* mlp = a.ml + (((size_t)row * S + split) * kH + 4 * hg + lane) * 2;
-      mlp[0] = M;
-      mlp[1] = L;
-    }
+    lse4[i] = lse;
   }
+  // the incoming lse is read by both waves before wave 0 overwrites it
+  if (lse_in) __syncthreads();
+  float* orow = a.o + (size_t)row * kH * kD + kHalf * hw;
+  if (lse_in) {
+    // the incoming rows may be the output rows: every value this lane merges
+    // is read before any is written (one round trip, not one per value)
+    const float* inrow = o_in + (size_t)row * kH * kD + kHalf * hw;
+    f32x4 X[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[j][i] = inrow[(size_t)(4 * lg + i) * kD + 16 * j + ln];
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        orow[(size_t)(4 * lg + i) * kD + 16 * j + ln] = fmaf(win[i], X[j][i], O[j][i] * wself[i]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) orow[(size_t)(4 * lg + i) * kD + 16 * j + ln] = O[j][i] * wself[i];
+  }
+  if (hw == 0 && ln < 4)
+    a.lse[(size_t)row * kH + 4 * lg + ln] = ln == 0 ? lse4[0] : (ln == 1 ? lse4[1] : (ln == 2 ? lse4[2] : lse4[3]));
 }
 
 // One work-group (128 lanes x 4 dims) per (head, query row).  The partial
 // rows of up to kCombBatch splits are loaded together with every split's
-// (max, sum) pair, so that the merge waits on one round trip to memory; the
-// weights are formed in LDS by the first wave, and the rows are summed in
+// (reference, sum) pair, so that the merge waits on one round trip to memory;
+// the weights are formed in LDS by the first wave, and the rows are summed in
 // split order, then the incoming result.
 constexpr int kCombThreads = 128;
-constexpr int kCombMaxS = 63;            // splits per row (lane kCombMaxS holds an incoming result)
 constexpr int kCombBatch = 8;            // partial rows in flight per lane
 
 __global__ __launch_bounds__(kCombThreads)
 void k_attn_combine(const float* __restrict__ opart, const float* __restrict__ ml,
                     int32_t S, const float* o_in, const float* lse_in, float* o,
                     float* lse) {
-  __shared__ float wgt_s[kCombMaxS + 1];
+  __shared__ float wgt_s[kAttnMaxSplits + 1];
   __shared__ float L_s;
   const int h = blockIdx.x;
   const int row = blockIdx.y;
@@ -566,7 +489,7 @@ void k_attn_combine(const float* __restrict__ opart, const float* __restrict__ m
     float Lsum = w * l;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) Lsum += __shfl_xor(Lsum, off, 64);
-    if (tid <= S && tid <= kCombMaxS) wgt_s[tid] = w;
+    if (tid <= S && tid <= kAttnMaxSplits) wgt_s[tid] = w;
     if (tid == 0) L_s = Lsum > 0.f ? Lsum : 0.f;
     if (tid == 0) lse[(size_t)row * kH + h] = Lsum > 0.f ? mx + logf(Lsum) : -INFINITY;
   }
@@ -608,41 +531,73 @@ void k_attn_combine(const float* __restrict__ opart, const float* __restrict__ m
 
 }  // namespace
 
-int32_t attn_chunks(int32_t K, int32_t W) {
-  return (K > 0 ? (K + KS - 1) / KS : 0) + (W > 0 ? (W + KS - 1) / KS : 0);
+int32_t attn_steps(int32_t K, int32_t W) {
+  return (K > 0 ? (K + kWK - 1) / kWK : 0) + (W > 0 ? (W + kWK - 1) / kWK : 0);
 }
 
-AttnPlan attn_plan(int64_t rows, int32_t chunks) {
-  // Splits S per row so that the launch fills the chip without giving some
-  // compute units two work-groups while others idle (a work-group's LDS
-  // takes a compute unit): estimated time = rounds of kGroupsPerRound
-  // work-groups x (chunks per work-group + a fixed prologue), plus a merge
-  // launch when S > 1.
-  if (chunks <= 0) return AttnPlan{16, 0, 0.0};
-  AttnPlan best{16, 1, 1e30};
-  const int64_t lo = (chunks + kMaxChunksPerSplit - 1) / kMaxChunksPerSplit;
-  for (int64_t S = lo; S <= chunks && S <= kCombMaxS; ++S) {
-    const int64_t cps = (chunks + S - 1) / S;
-    if ((chunks + cps - 1) / cps != S) continue;
-    const int64_t rounds = (rows * S + kGroupsPerRound - 1) / kGroupsPerRound;
-    const double cost = (double)rounds * ((double)cps + 0.5) + (S > 1 ? 1.0 : 0.0);
-    if (cost < best.cost - 1e-9) best = AttnPlan{16, (int32_t)S, cost};
+int32_t attn_max_splits(int64_t rows, int32_t steps) {
+  // more splits than it takes to give every compute unit a few work-groups
+  // only add partial traffic
+  int64_t s = (kAttnFillGroups + rows - 1) / (rows > 0 ? rows : 1);
+  if (s > steps) s = steps;
+  if (s > kAttnMaxSplits) s = kAttnMaxSplits;
+  return (int32_t)(s > 0 ? s : 1);
+}
+
+AttnPlan attn_plan(int64_t rows, int32_t steps) {
+  // Many rows fill the chip with one work-group per row.  Fewer rows (decode)
+  // cut each row into S runs of cps steps, one work-group each, then merge
+  // the partials.  A work-group mostly waits on memory (its q, its entry
+  // numbers, then the gathered rows) and a compute unit serves only a few
+  // tens of GB/s, so the best launch spreads the rows over every compute unit
+  // with few steps per work-group, while each split adds a 32 KiB partial to
+  // write and merge.  The estimate (microseconds, fitted to measured decode
+  // launches) picks S.
+  if (steps <= 0 || rows >= kAttnSplitRows) return AttnPlan{1, 0};
+  const int32_t smax = attn_max_splits(rows, steps);
+  AttnPlan best{1, 0};
+  double best_cost = 1e30;
+  for (int32_t cps = 1; cps <= steps; ++cps) {
+    const int32_t S = (steps + cps - 1) / cps;
+    if (S > smax || (S - 1) * cps >= steps) continue;
+    const double groups = (double)(rows * S);
+    const double per_cu = groups / 256.0;          // work-groups per compute unit
+    const double rounds = per_cu <= 4.0 ? 1.0 : per_cu / 4.0;
+    const double cost = 2.0 + (per_cu > 1.0 ? per_cu : 1.0) * 0.6 + rounds * 1.8 * cps +
+                        (S > 1 ? 2.0 + groups * 0.02 : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = S > 1 ? AttnPlan{S, cps} : AttnPlan{1, 0};
+    }
   }
   return best;
 }
 
-hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
-  const int32_t Cg = a.K > 0 && a.latent ? (a.K + KS - 1) / KS : 0;
-  const int32_t C = Cg + (a.W > 0 ? (a.W + KS - 1) / KS : 0);
-  const int32_t splits = plan.splits;
-  if (C == 0 || splits <= 0) return hipSuccess;
-  const int32_t cps = (C + splits - 1) / splits;
-  if (cps > kMaxChunksPerSplit || (C + cps - 1) / cps != splits || splits > kCombMaxS)
-    return hipErrorInvalidValue;
-  k_attn_partial<<<dim3((unsigned)splits, (unsigned)a.rows), dim3(kThreads), 0, s>>>(a, Cg, C, cps);
-  if (splits == 1) return hipGetLastError();
-  k_attn_combine<<<dim3((unsigned)kH, (unsigned)a.rows), dim3(kCombThreads), 0, s>>>(
-      a.opart, a.ml, splits, a.o_in, a.lse_in, a.o, a.lse);
+hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  const int32_t Cg = a.K > 0 && a.latent ? (a.K + kWK - 1) / kWK : 0;
+  const int32_t Cw = a.W > 0 ? (a.W + kWK - 1) / kWK : 0;
+  const int32_t S = plan.splits;
+  if (S > 1) {
+    // whole steps per split
+    if (S > kAttnMaxSplits || plan.cps <= 0 || (Cg + Cw + plan.cps - 1) / plan.cps != S ||
+        !a.opart || !a.ml)
+      return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.rows, (unsigned)S);
+    if (a.map.pages)
+      k_attn<true, true><<<grid, dim3(128), 0, s>>>(a, Cg, Cw, plan.cps, nullptr, nullptr);
+    else
+      k_attn<false, true><<<grid, dim3(128), 0, s>>>(a, Cg, Cw, plan.cps, nullptr, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_attn_combine<<<dim3((unsigned)kH, (unsigned)a.rows), dim3(kCombThreads), 0, s>>>(
+        a.opart, a.ml, S, a.o_in, a.lse_in, a.o, a.lse);
+    return hipGetLastError();
+  }
+  if (a.map.pages)
+    k_attn<true, false><<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw, 0, a.o_in, a.lse_in);
+  else
+    k_attn<false, false><<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw, 0, a.o_in, a.lse_in);
   return hipGetLastError();
 }
 

@@ -32,7 +32,11 @@ inline bool topk_multi_wg(int64_t R, int64_t N) {
 constexpr int kCounterWords = 4;            // per row: [0]=above count, [1]=candidate count, [2]=bin, [3]=above the bin
 
 // Attention
-constexpr int kKeysPerSplit = 32;           // keys staged per work-group
+constexpr int kAttnStepKeys = 32;           // keys per step of the attention kernel
+constexpr int kAttnMaxSplits = 63;          // splits per row (the merge holds them and an
+                                            // incoming result in one wave)
+constexpr int kAttnFillGroups = 2048;       // decode: splits never give more work-groups than this
+constexpr int kAttnSplitRows = 512;         // query rows from which one work-group per row fills the chip
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -159,12 +163,12 @@ hipError_t launch_topk_select2(const float* scores, int32_t R, int32_t N,
                                bool zero_hist, hipStream_t s);
 
 // Attention over up to K gathered FP4 entries and up to W FP8 window rows per
-// query row.  The row's keys are cut into chunks of kKeysPerSplit (global
-// chunks first, then window chunks) and the chunks into `splits` contiguous
-// runs, one work-group each.  The result, merged with an incoming (o_in,
-// lse_in) when lse_in is given (they may alias o / lse), is written to o and
-// lse: by the work-group itself when the row has one split, otherwise by a
-// merge launch over the partials.
+// query row, on the matrix cores.  The row's keys are taken kAttnStepKeys per
+// step (global steps first, then window steps).  Prefill runs one work-group
+// per row; decode cuts a row's steps into `splits` runs of `cps` steps, one
+// work-group each, whose partials (opart, ml) a merge launch combines.  The
+// result, merged with an incoming (o_in, lse_in) when lse_in is given (they
+// may alias o / lse), is written to o and lse.
 struct AttnArgs {
   const uint8_t* latent;  // pool rows [.][kLatRow] (see PoolMap)
   const uint8_t* scale;   // pool rows [.][kScaleRow]
@@ -177,39 +181,45 @@ struct AttnArgs {
   int32_t swa_rows;       // rows per sequence in swa (Q + W - 1)
   int64_t pos0;           // prefill: position of query 0; window row t + r of query t is
                           // position pos0 + t - (W - 1) + r, rows before 0 are skipped
-                          // (< 0: every row is a token; the decode kernels ignore it)
+                          // (< 0: every row is a token; required for split launches)
   const uint16_t* q;      // [rows][kH][kD] bf16
   int32_t Q;              // query rows per sequence
   int32_t rows;           // B * Q
-  float* opart;           // [rows][splits][kH][kD]
-  float* ml;              // [rows][splits][kH][2]
+  float* opart;           // [rows][splits][kH][kD]  (split launches)
+  float* ml;              // [rows][splits][kH][2]   (split launches)
   float* o;               // [rows][kH][kD]
   float* lse;             // [rows][kH]
   const float* o_in;      // NULL or [rows][kH][kD]
   const float* lse_in;    // NULL or [rows][kH]
 };
-int32_t attn_chunks(int32_t K, int32_t W);          // chunks of one row's keys
-// Splits per row of a launch (G: heads per work-group, always kH).
+// Steps of one row's keys.
+int32_t attn_steps(int32_t K, int32_t W);
+// The most splits a decode launch of `rows` rows uses (bounds its workspace).
+int32_t attn_max_splits(int64_t rows, int32_t steps);
 struct AttnPlan {
-  int32_t G;
-  int32_t splits;
-  double cost;
+  int32_t splits;   // work-groups per row (1: one, writing o and lse itself)
+  int32_t cps;      // steps per split work-group (splits > 1)
 };
-AttnPlan attn_plan(int64_t rows, int32_t chunks);
-hipError_t launch_attn_partial(const AttnArgs& a, const AttnPlan& plan, hipStream_t s);
-// Attention workspace: per (row, split) one [kH][kD] unnormalised output and
-// kH (max, sum) pairs; `chunks` bounds the number of splits.
+// Decode: splits per row from an estimate of the launch (splits > 1 needs the
+// workspace of attn_ws_bytes).  AttnPlan{1, 0}: one work-group per row, no
+// workspace (prefill).
+AttnPlan attn_plan(int64_t rows, int32_t steps);
+hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s);
+// Decode attention workspace: per (row, split) one [kH][kD] unnormalised
+// output and kH (reference, sum) pairs, for at most attn_max_splits splits.
 struct AttnWs {
   float* opart;
   float* ml;
 };
-inline size_t attn_ws_bytes(int64_t rows, int64_t chunks) {
-  return align256(rows * chunks * kH * kD * 4) + align256(rows * chunks * kH * 2 * 4);
+inline size_t attn_ws_bytes(int64_t rows, int32_t steps) {
+  const int64_t S = attn_max_splits(rows, steps);
+  return align256(rows * S * kH * kD * 4) + align256(rows * S * kH * 2 * 4);
 }
-inline AttnWs attn_ws_carve(void* ws, int64_t rows, int64_t chunks) {
+inline AttnWs attn_ws_carve(void* ws, int64_t rows, int32_t steps) {
+  const int64_t S = attn_max_splits(rows, steps);
   AttnWs w;
   w.opart = (float*)ws;
-  w.ml = (float*)((char*)ws + align256(rows * chunks * kH * kD * 4));
+  w.ml = (float*)((char*)ws + align256(rows * S * kH * kD * 4));
   return w;
 }
 
@@ -229,12 +239,6 @@ hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_
                                 const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
                                 int32_t ratio, float* scores, int32_t* n_valid, const int32_t* len,
                                 const PoolMap& map, hipStream_t s);
-// One work-group per query row over its K selected entries and W window rows;
-// writes a.o / a.lse, merged with (o_in, lse_in) when lse_in is given (they
-// may alias a.o / a.lse).
-hipError_t launch_prefill_attn(const AttnArgs& a, const float* o_in, const float* lse_in,
-                               hipStream_t s);
-
 // Fill n 32-bit words with v.
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // Copy n int32 (Reuse layers that ask for their indices).

@@ -155,6 +155,13 @@ csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx,
                              float* scores, uint32_t* hist, hipStream_t stream);
 
 /* Top-K selection per row.
+ * The pages' Full and Reindex layers pick the Top-K entries from the indexer
+ * scores, over the whole context or, in the hierarchical case, within the
+ * candidate pool ("DeepSeek V4.1-Flash Cuts KV Cache by 437x", paragraph on
+ * the three operating modes; "DeepSeek V4.1 Flash Architecture Breakdown",
+ * section "How does the cache compress along three dimensions at once?").
+ * Readings (the pages fix neither): ties go to the lower index, and the
+ * selection is returned in ascending index order.
  * For each of R rows of N scores, select the K largest among the first
  * n_valid[r] positions (all N when n_valid is NULL).  Equal scores are broken
  * toward the LOWER position (= lower global entry, since candidate lists are
@@ -165,23 +172,36 @@ csa2_status csa2_index_score(const csa2_pool* pool, const uint8_t* q_idx,
  *   cand    NULL (output positions) or [R][N] int32 position -> entry map
  *   idx     [R][K] int32 output
  *   ws      workspace of at least csa2_workspace_bytes(CSA2_OP_TOPK, R, 1, N, K, 0, 0, 0)
- * Limits: 1 <= K <= 16384, 1 <= N < 2^31. */
+ * Limits: 1 <= K <= 16384; 1 <= N <= 2^30 (the select orders (score,
+ * position) pairs as one 62-bit key with 30 position bits); 1 <= R <= 65535
+ * (rows are a grid dimension of the launches).  Other values return
+ * CSA2_ERR_SHAPE. */
 csa2_status csa2_topk(const float* scores, int32_t R, int32_t N,
                       const int32_t* n_valid, const int32_t* cand, int32_t K,
                       int32_t* idx, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
 /* Attention over selected FP4 global entries.
+ * Every layer attends over the entries its index selects, held as FP4 (E2M1)
+ * and restored to real values for the computation ("DeepSeek V4.1-Flash Cuts
+ * KV Cache by 437x", paragraphs on the three operating modes and on FP4
+ * quantisation; "DeepSeek V4.1 Flash Architecture Breakdown", section "How are
+ * cache precision and storage arranged?").  Readings: key = value = the
+ * latent row (shared K/V), softmax scale 1 (q carries 1/sqrt(D)).
  * Per query row (b, t) and head h, the keys (= values) are the dequantised
  * latent rows c_j[i] = E2M1(code) * 2^(scale - 127) of the selected entries
  * (idx != -1); logits z_j = q[h] . c_j (scale 1); o[h] = sum softmax(z)_j c_j
  * and lse[h] = log sum exp(z).  No selected entry gives o = 0, lse = -inf.
+ * Computed on the matrix cores: the dequantised values and q enter as bf16
+ * (exact for every E2M1 value times a scale code 0..252), products and sums
+ * in fp32, and the softmax weights are split into two bf16 halves (relative
+ * rounding below 2^-16).  Decode rows (Q == 1) are cut into runs of keys on
+ * separate work-groups whose partial results (in the workspace) a merge
+ * combines; prefill rows (Q > 1) take one work-group each.
  *   q    [B][Q][H][D] bf16;  idx [B][Q][K] int32 in [-1, M)
  *   o    [B][Q][H][D] float;  lse [B][Q][H] float
  *   ws   at least csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, Q, M, K, 0, 0, H)
- * With Q > 1 (chunked prefill) each query token is one work-group on the
- * matrix cores (bf16 products, fp32 accumulation, P split into two bf16
- * halves) and the workspace is not used beyond 256 bytes. */
+ *        (256 bytes when Q > 1) */
 csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q,
                              int32_t Q, int32_t H, const int32_t* idx,
                              int32_t K, float* o, float* lse, void* ws,
@@ -204,6 +224,16 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H,
                            hipStream_t stream);
 
 /* One decode step through a static per-layer mode schedule over one pool.
+ * The pages give every layer one of three static modes over one shared pool
+ * and index: Full builds the index from scratch, Reindex re-scores with the
+ * layer's own indexer, Reuse takes the previous layer's indices with no index
+ * work; for very long contexts the indexer is hierarchical and later layers
+ * search only a candidate pool ("DeepSeek V4.1-Flash Cuts KV Cache by 437x",
+ * paragraphs on the three operating modes and on CSA2 storage; "DeepSeek V4.1
+ * Flash Architecture Breakdown", section "How does the cache compress along
+ * three dimensions at once?").  Readings: Reuse takes the most recent Full or
+ * Reindex layer; the first layer must be Full; each layer has its own query,
+ * indexer query and window.
  * Layers run in order.  Full: score all M entries, select Top-K; with P > 0
  * it also builds the candidate pool = Top-P of the same scores (ascending).
  * Reindex: with P == 0 score all M with its own indexer; with P > 0 score only

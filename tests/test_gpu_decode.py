@@ -131,6 +131,10 @@ SMALL = [
     dict(name="no_window", B=2, M=3000, K=50, W=0, modes=(FULL, REINDEX)),
     dict(name="K1_W1", B=4, M=777, K=1, W=1, modes=(FULL, REUSE)),
     dict(name="full_full", B=2, M=4096, K=256, W=128, modes=(FULL, REUSE, FULL, REINDEX)),
+    # the Full layer's Top-P and Top-K selected together by the multi-work-group
+    # select (rows over 32768 positions on few rows), on random scores
+    dict(name="hier_multiwg", B=4, M=40000, K=512, P=4096, W=128,
+         modes=(FULL, REINDEX, REUSE, REINDEX)),
 ]
 
 
@@ -194,3 +198,9 @@ def test_decode_full_size_sampled(ci, seqs):
                    for i, m in enumerate(cfg.modes)]
     rep = check_against_oracle(case, res, src, seqs)
     assert rep.rows == len(seqs) * cfg.L
+    # every row of every indexing layer, exact: the GPU's Top-K (the one-work-group
+    # select at 32768 or 65536 positions, the joint Top-P / Top-K at 262144) equals
+    # the oracle's Top-K of the GPU's own fp32 scores, with no near-tie excuse
+    stagewise_topk_exact(case, dc, res)
+    say("  exact Top-K on the GPU scores: all %d rows of %d indexing layers" % (
+        cfg.B, sum(m != REUSE for m in cfg.modes)))

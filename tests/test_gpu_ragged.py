@@ -68,6 +68,10 @@ def _check_decode(case, dc, lens, P):
     ("flat", 5, 3000, 128, 0, [3000, 1, 1777, 0, 100], (FULL, REINDEX, REUSE)),
     ("hier", 4, 4000, 64, 256, [4000, 200, 30, 0], (FULL, REINDEX, REINDEX)),
     ("multi-wg", 2, 40000, 96, 0, [40000, 12345], (FULL, REUSE, REINDEX)),
+    # hierarchical with the multi-work-group joint Top-P / Top-K: lengths full,
+    # between P and 32768, below P, below K and 0
+    ("hier-multi-wg", 5, 40000, 128, 2048, [40000, 30001, 1500, 100, 0],
+     (FULL, REINDEX, REUSE, REINDEX)),
 ])
 def test_ragged_decode(name, B, M, K, P, lens, modes):
     from fp4_kv_cache_score_amd.device import DeviceCase

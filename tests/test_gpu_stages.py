@@ -67,22 +67,23 @@ def test_fp4_dequant_bit_exact_through_single_key_attention():
     assert np.all(np.abs(lse[0, :512] - z) <= 512 * 2.0 ** -24 * mag + 1e-30)
 
 
+@pytest.mark.parametrize("gap", [23, 40, 80])
 @pytest.mark.parametrize("big", [0, 40])
-def test_sparse_attn_block_scale_spread_23_binades(big):
-    """P x V takes fp16 values E2M1 x 2^(code - ref), ref the largest code of the
-    block among the entries staged so far; they are exact down to ref - 23.
-    Entry `big` sets ref = 143 in block 0 and gets weight ~e^-4000, so the
-    output's block-0 dims come only from values 23 binades below it (fp16
-    subnormals).  With big = 40 (the second 32-key chunk) the reference rises
-    after the first chunk, whose sums are rescaled by 2^-23."""
+def test_sparse_attn_block_scale_spread(big, gap):
+    """Entry `big` has block 0 at scale code 120 + gap while every other entry
+    sits at 120, and q makes its logit hugely negative (weight ~0), so the
+    output's block-0 dims come only from values `gap` binades below the
+    largest scale in the same step (big = 0) or in the other split (big = 40,
+    the second 32-key step).  The keys enter the products as bf16 with their
+    true scale, so no spread of legal scale codes loses bits."""
     from fp4_kv_cache_score_amd.device import DeviceCase
-    say("case: sparse attention, block scales 23 binades apart, big entry %d" % big)
+    say("case: sparse attention, block scales %d binades apart, big entry %d" % (gap, big))
     cfg = CONFIGS[0].scaled(name="spread", B=1, M=64, K=64, W=0, modes=(FULL,))
     case = synth.make_case(cfg)
     rng = np.random.default_rng(23)
     case.pool.latent[:] = rng.integers(0, 256, size=case.pool.latent.shape, dtype=np.uint16)
     case.pool.scale[:] = 120
-    case.pool.scale[0, big, 0] = 143
+    case.pool.scale[0, big, 0] = 120 + gap
     cb = F.dequant_latent(case.pool.latent[0, big:big + 1], case.pool.scale[0, big:big + 1])[0, :32]
     q = case.layers[0].q                       # bf16 bits [1][1][16][512]
     q[0, 0, :, :32] = np.where(cb > 0, 0xBA80, np.where(cb < 0, 0x3A80, 0)).astype(np.uint16)
@@ -97,6 +98,48 @@ def test_sparse_attn_block_scale_spread_23_binades(big):
     say("  rel err %.3g" % err)
     assert err < ATTN_TOL
     assert np.allclose(lse[0, 0].cpu().numpy(), wl, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("gap", [40, 80])
+def test_decode_step_block_scale_spread(gap):
+    """The same spread inside a whole decode step (csa2_decode_layers: scan,
+    Top-K of 512 among 2048 entries, attention in several splits per row).
+    One entry of every sequence holds block 0 at code 125 + gap and an index
+    key equal to the indexer query (so it is selected), and q gives it a
+    hugely negative logit; every other entry has block 0 at 125 (about the
+    size of the other blocks), and the attention weight sits on them."""
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    say("case: decode step, block scales %d binades apart" % gap)
+    cfg = CONFIGS[0].scaled(name="spread_step", B=4, M=2048, K=512, W=0, modes=(FULL, REUSE))
+    case = synth.make_case(cfg)
+    p = case.pool
+    p.scale[:, :, 0] = 125
+    bigs = [37 + 100 * b for b in range(cfg.B)]
+    for b, big in enumerate(bigs):
+        p.scale[b, big, 0] = 125 + gap
+        p.idx_key[b, big] = case.layers[0].q_idx[b, 0]
+        cb = F.dequant_latent(p.latent[b, big:big + 1], p.scale[b, big:big + 1])[0, :32]
+        for L in case.layers:
+            L.q[b, 0, :, :32] = np.where(cb > 0, 0xBA80, np.where(cb < 0, 0x3A80, 0)).astype(np.uint16)
+    dc = DeviceCase(case)
+    dc.prepare_decode()
+    dc.decode_layers()
+    torch.cuda.synchronize()
+    res = dc.results()
+    worst = 0.0
+    for ell, L in enumerate(case.layers):
+        for b, big in enumerate(bigs):
+            g_idx = res[ell]["idx"][b, 0]
+            assert big in g_idx
+            keys = O.gather_keys(p.latent[b], p.scale[b], g_idx)
+            wo, wl = O.attend(L.q[b, 0], keys)
+            # block 0 carries a share well above the tolerance: losing it would fail
+            assert np.abs(wo[:, :32]).max() > 5 * ATTN_TOL * np.abs(wo).max()
+            err = attn_rel_err(res[ell]["o"][b, 0], wo)
+            worst = max(worst, err)
+            assert err < ATTN_TOL, "layer %d seq %d err %g" % (ell, b, err)
+            assert np.allclose(res[ell]["lse"][b, 0], wl, rtol=1e-5, atol=1e-5)
+    say("  worst rel err %.3g" % worst)
 
 
 def test_fp8_window_rows_bit_exact_and_merge():
