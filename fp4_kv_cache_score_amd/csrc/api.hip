@@ -38,9 +38,42 @@ csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E
 constexpr int32_t kMaxW = 4096;
 constexpr int32_t kMaxRows = 65535;  // grid.y limit for row-indexed launches
 
-// Top-K workspace: nothing for rows the one-work-group select handles.
+// Top-K workspace: the sliced select's winners when it takes the shape,
+// otherwise the multi-work-group scratch (nothing for the one-work-group
+// row select).
 size_t topk_call_ws_bytes(int64_t R, int64_t N, int64_t K) {
+  if (topk_slicing(R, N, K).taken) {
+    const size_t b = topk_slice_ws_bytes(R, N, K);
+    return b > 256 ? b : 256;
+  }
   return topk_multi_wg(R, N) ? topk_ws_bytes(R, N, K) : 256;
+}
+
+// Sliced-select winners for any row length up to Nmax (prefill chunks see a
+// growing prefix of the pool).
+size_t topk_slice_ws_max(int64_t R, int64_t Nmax, int64_t K) {
+  // the keepers of a taken shape fit kFinalMaxN per row
+  size_t b = topk_slice_ws_bytes(R, Nmax, K);
+  if (Nmax > kFinalMaxN) {
+    const size_t cap = align256((size_t)(R * kFinalMaxN * 4)) * 2;
+    b = b > cap ? b : cap;
+  }
+  return b;
+}
+
+// How a decode step selects: the sliced select for the Top-K (and for the
+// Top-P of a hierarchical Full layer) when it takes the shape, otherwise
+// the one-work-group row select or the multi-work-group select (`big`),
+// whose histogram and counters live in the workspace.
+struct DecodeSelect {
+  bool sliced_k, sliced_p, big;
+};
+DecodeSelect decode_select(int64_t B, int64_t M, int64_t K, int64_t P) {
+  DecodeSelect d;
+  d.sliced_k = topk_slicing(B, M, K).taken;
+  d.sliced_p = P > 0 && topk_slicing(B, M, P).taken;
+  d.big = topk_multi_wg(B, M) && (!d.sliced_k || (P > 0 && !d.sliced_p));
+  return d;
 }
 
 // decode_layers workspace: scores [B][N] | multi-work-group Top-K scratch
@@ -52,7 +85,9 @@ size_t topk_call_ws_bytes(int64_t R, int64_t N, int64_t K) {
 // the row it holds; the multi-work-group select gets one histogram pass).
 struct DecodeWs {
   float* scores;
+  DecodeSelect sel;
   bool big;
+  void* slice;     // sliced-select winners
   TopkWs t;
   TopkWs t2;   // the Top-K's lists when the Top-P is selected beside it
   int32_t* cand;
@@ -60,14 +95,23 @@ struct DecodeWs {
   float* ml;
 };
 
+size_t decode_slice_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P) {
+  const DecodeSelect sel = decode_select(B, M, K, P);
+  size_t b = sel.sliced_k ? topk_slice_ws_bytes(B, M, K) : 0;
+  if (sel.sliced_p && topk_slice_ws_bytes(B, M, P) > b) b = topk_slice_ws_bytes(B, M, P);
+  // a hierarchical Reindex layer selects K among its P candidates
+  if (P > 0 && topk_slicing(B, P, K).S > 0 && topk_slice_ws_bytes(B, P, K) > b) b = topk_slice_ws_bytes(B, P, K);
+  return b;
+}
+
 size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t N = P > M ? P : M;
   const int64_t Kmax = P > K ? P : K;
   const int32_t steps = attn_steps((int32_t)K, (int32_t)W);
-  const bool big = topk_multi_wg(B, M);
+  const bool big = decode_select(B, M, K, P).big;
   return align256(B * N * 4) + (big ? topk_ws_bytes(B, M, Kmax) : 0) +
          (big && P > 0 ? topk_ws_bytes(B, M, K) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
-         attn_ws_bytes(B, steps);
+         decode_slice_ws_bytes(B, M, K, P) + attn_ws_bytes(B, steps);
 }
 
 DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
@@ -77,7 +121,8 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   char* p = (char*)ws;
   d.scores = (float*)p;
   p += align256(B * N * 4);
-  d.big = topk_multi_wg(B, M);
+  d.sel = decode_select(B, M, K, P);
+  d.big = d.sel.big;
   if (d.big) {
     d.t = topk_ws_carve(p, B, M, Kmax);
     p += topk_ws_bytes(B, M, Kmax);
@@ -88,6 +133,8 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
   }
   d.cand = (int32_t*)p;
   p += align256(B * (P > 0 ? P : 1) * 4);
+  d.slice = p;
+  p += decode_slice_ws_bytes(B, M, K, P);
   const AttnWs w = attn_ws_carve(p, B, attn_steps((int32_t)K, (int32_t)W));
   d.opart = w.opart;
   d.ml = w.ml;
@@ -131,7 +178,8 @@ csa2_status check_layers(const csa2_layer* layers, int32_t L, int32_t W) {
 // few and long.
 size_t prefill_ws_bytes(int64_t B, int64_t Q, int64_t M, int64_t K) {
   const int64_t R = B * Q;
-  return align256(R * M * 4) + align256(R * 4) + (topk_multi_wg(R, M) ? topk_ws_bytes(R, M, K) : 0);
+  return align256(R * M * 4) + align256(R * 4) + (topk_multi_wg(R, M) ? topk_ws_bytes(R, M, K) : 0) +
+         topk_slice_ws_max(R, M, K);
 }
 
 // Entries that some query of a chunk can see, rounded up to a multiple of 4
@@ -222,6 +270,8 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* 
     return CSA2_ERR_ALIGN;
   if (!ws || ws_bytes < topk_call_ws_bytes(R, N, K)) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
+  if (topk_slicing(R, N, K).taken)
+    return hip_status(launch_topk_sliced(scores, R, N, n_valid, N, cand, K, idx, ws, stream));
   if (!topk_multi_wg(R, N))
     return hip_status(launch_topk_rows(scores, R, N, n_valid, N, K, nullptr, false, cand, idx,
                                        stream));
@@ -355,7 +405,17 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
                                          nullptr, (int32_t)M, d.scores, nullptr, pool->len,
                                          pool_map(pool), stream));
       if (st != CSA2_OK) return st;
-      if (!d.big) {
+      const bool want_p = y.mode == CSA2_FULL && P > 0;
+      if (d.sel.sliced_k && (!want_p || d.sel.sliced_p)) {
+        if (want_p) {
+          st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, (int32_t)M, pool->len,
+                                             (int32_t)M, nullptr, P, d.cand, d.slice, stream));
+          if (st != CSA2_OK) return st;
+        }
+        st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
+                                           nullptr, K, y.idx_out, d.slice, stream));
+        if (st != CSA2_OK) return st;
+      } else if (!d.big) {
         if (y.mode == CSA2_FULL && P > 0) {
           st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
                                            P, nullptr, false, nullptr, d.cand, stream));
@@ -388,9 +448,13 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
                                          d.cand, P, d.scores, nullptr, pool->len,
                                          pool_map(pool), stream));
       if (st != CSA2_OK) return st;
-      // a ragged sequence has min(P, len) candidates (the row kernel clamps len to P)
-      st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, pool->len, n_cand, K, nullptr, false,
-                                       d.cand, y.idx_out, stream));
+      // a ragged sequence has min(P, len) candidates (the selects clamp len to P)
+      if (topk_slicing(B, P, K).taken)
+        st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, P, pool->len, n_cand, d.cand, K,
+                                           y.idx_out, d.slice, stream));
+      else
+        st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, pool->len, n_cand, K, nullptr,
+                                         false, d.cand, y.idx_out, stream));
       if (st != CSA2_OK) return st;
       cur = y.idx_out;
       cur_layer = l;
@@ -452,8 +516,10 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
   p += align256(R * M * 4);
   int32_t* n_valid = (int32_t*)p;
   p += align256(R * 4);
-  const bool big = N > 0 && topk_multi_wg(R, N);
+  const bool sliced = N > 0 && topk_slicing(R, N, K).taken;
+  const bool big = N > 0 && !sliced && topk_multi_wg(R, N);
   const TopkWs t = big ? topk_ws_carve(p, R, N, K) : TopkWs{};
+  void* slice_ws = p + (topk_multi_wg(R, M) ? topk_ws_bytes(R, M, K) : 0);
 
   const int32_t* cur = nullptr;
   int32_t cur_layer = -1;
@@ -467,7 +533,10 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
                                              y.w_idx, Q, pos0, pos0 >= 0 ? ratio : 1, scores,
                                              n_valid, pool->len, pool_map(pool), stream));
         if (st != CSA2_OK) return st;
-        if (!big) {
+        if (sliced) {
+          st = hip_status(launch_topk_sliced(scores, (int32_t)R, (int32_t)N, n_valid, (int32_t)N,
+                                             nullptr, K, y.idx_out, slice_ws, stream));
+        } else if (!big) {
           st = hip_status(launch_topk_rows(scores, (int32_t)R, (int32_t)N, n_valid, (int32_t)N, K,
                                            nullptr, false, nullptr, y.idx_out, stream));
         } else {

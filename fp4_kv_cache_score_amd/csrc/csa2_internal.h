@@ -31,6 +31,48 @@ inline bool topk_multi_wg(int64_t R, int64_t N) {
 }
 constexpr int kCounterWords = 4;            // per row: [0]=above count, [1]=candidate count, [2]=bin, [3]=above the bin
 
+// Sliced select: rows of at most kFinalMaxN positions take one work-group;
+// longer rows (on fewer than kRowSplitR rows) are cut into S slices of
+// 1024 * pt positions, each slice's keepers (a superset of its Top-K, at most
+// `slots`) found by one work-group, then the row's Top-K from all keepers,
+// which must fit one work-group (S * slots <= kFinalMaxN).
+constexpr int kFinalMaxN = 16384;
+struct TopkSlicing {
+  bool taken;      // the sliced select takes this shape
+  int32_t S;       // slices (0: the row itself goes to the final select)
+  int32_t pt;      // positions per thread of a slice (slice = 1024 pt)
+  int32_t slots;   // keepers per slice
+};
+inline int32_t topk_slot_count(int64_t K) {
+  // room for the threshold digit's group beyond K; a multiple of 64 (the
+  // final select reads the keepers 16 bytes at a time)
+  const int64_t extra = K / 4 > 64 ? K / 4 : 64;
+  return (int32_t)((K + extra + 63) / 64 * 64);
+}
+inline TopkSlicing topk_slicing(int64_t R, int64_t N, int64_t K) {
+  TopkSlicing t{false, 0, 0, 0};
+  if (N <= kFinalMaxN) {   // the row itself goes to one work-group
+    t.taken = true;
+    return t;
+  }
+  if (R >= kRowSplitR) return t;   // many long rows: the one-work-group row select
+  const int64_t slots = topk_slot_count(K);
+  // the smallest slice that gives at most one round of work-groups (a slice
+  // must hold several times K to filter anything, and all keepers must fit
+  // the final select), else the largest slice that fits
+  for (int pt = 4; pt <= 16; pt *= 2) {
+    const int64_t len = 1024 * pt;
+    const int64_t S = (N + len - 1) / len;
+    if (len < 4 * K || S * slots > kFinalMaxN) continue;
+    t.taken = true;
+    t.S = (int32_t)S;
+    t.pt = pt;
+    t.slots = (int32_t)slots;
+    if (R * S <= 256) break;
+  }
+  return t;
+}
+
 // Attention
 constexpr int kAttnStepKeys = 32;           // keys per step of the attention kernel
 constexpr int kAttnMaxSplits = 63;          // splits per row (the merge holds them and an
@@ -99,6 +141,12 @@ inline int32_t topk_cap(int64_t R, int64_t N) {
   return (int32_t)(c > 0 ? c : 1);
 }
 
+// Slice keepers of the sliced select: keys and positions [R][S][slots].
+inline size_t topk_slice_ws_bytes(int64_t R, int64_t N, int64_t K) {
+  const TopkSlicing s = topk_slicing(R, N, K);
+  return s.S > 0 ? align256((size_t)(R * s.S * s.slots * 4)) * 2 : 0;
+}
+
 inline size_t topk_ws_bytes(int64_t R, int64_t N, int64_t K) {
   int64_t cap = topk_cap(R, N);
   return align256(R * kHistBins * 4) + align256(R * kCounterWords * 4) +
@@ -142,6 +190,10 @@ hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
                             const int32_t* n_valid, int32_t n_all, int32_t K,
                             uint32_t* hist, bool zero_hist, const int32_t* cand,
                             int32_t* out, hipStream_t s);
+// Sliced select (topk_slicing(R, N, K).taken): ws holds topk_slice_ws_bytes.
+hipError_t launch_topk_sliced(const float* scores, int32_t R, int32_t N,
+                              const int32_t* n_valid, int32_t n_all, const int32_t* cand,
+                              int32_t K, int32_t* out, void* ws, hipStream_t s);
 hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
                             const int32_t* n_valid, int32_t n_all,
                             uint32_t* hist, hipStream_t s);

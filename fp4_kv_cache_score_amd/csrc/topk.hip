@@ -880,6 +880,444 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
   for (uint32_t i = tot + tid; i < (uint32_t)K; i += kRowThreads) orow[i] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Sliced select: a row is cut into slices of kFinalThreads * PT positions;
+// one work-group per slice keeps a superset of the slice's Top-K
+// (k_topk_slice) and one work-group per row selects the row's Top-K from the
+// slices' keepers (k_topk_final).  A slice's Top-K under the (key, lower
+// position) order holds every element of the row's Top-K that lies in the
+// slice (an element the slice drops has K better ones in the slice alone), so
+// the union of the slices' keepers holds the row's Top-K.  A slice keeps
+// everything at or above the radix digit that holds its K-th key, as long as
+// that fits its topk_slot_count(K) slots (one radix pass, usually), otherwise
+// it refines as the exact select does.  Rows of at most kFinalMaxN positions
+// go to k_topk_final directly.
+//
+// Both levels run one block select.  Elements are loaded with coalesced
+// 16-byte loads: thread t holds G = PT / 4 groups of 4, group u covering the
+// block's positions 4096 u + 4 t .. 4096 u + 4 t + 3, so the block's
+// position order is (group, thread, element); the kept elements leave in
+// that order through one block scan of per-group counts (packed two to a
+// word).  Work-groups are 1024 threads: with one wave per SIMD every
+// dependent step of these short phases waits its full latency (measured: an
+// LDS clear and barrier take 437 ns on 256 threads, 120 ns on 1024).  Every
+// phase ends in one barrier: the histogram is double-buffered (a pass clears
+// the other buffer) and the scans and digit searches rotate their LDS slots.
+// ---------------------------------------------------------------------------
+
+constexpr int kFinalThreads = 1024;
+constexpr int kSelNW = kFinalThreads / 64;
+constexpr int kGroupSpan = 4 * kFinalThreads;   // positions per element group
+
+struct BlockSelLds {
+  uint32_t hist[2][kHistBins];        // double-buffered histogram; output staging afterwards
+  uint32_t scan[4][2 * kSelNW];       // rotating scan slots
+  uint32_t res[4][4];                 // rotating digit-search results
+  uint32_t red[3][kSelNW];            // count, min, max per wave
+};
+
+__device__ __forceinline__ uint32_t key_hi(uint32_t k, int sh) { return sh >= 32 ? 0u : k >> sh; }
+
+// Sum, minimum and maximum over the 64 lanes of a wave, in lane 63: DPP row
+// shifts within each row of 16, then the row results added with readlane.
+struct Wred {
+  uint32_t sum, mn, mx;
+};
+template <int CTRL>
+__device__ __forceinline__ void wred_step(uint32_t& s, uint32_t& mn, uint32_t& mx) {
+  // a lane with no source in its row reads the identity (0 for the sum and
+  // the maximum, all ones for the minimum)
+  s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, CTRL, 0xF, 0xF, true);
+  mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFFu, (int)mn, CTRL, 0xF, 0xF, false));
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ Wred wave_reduce3(uint32_t s, uint32_t mn, uint32_t mx) {
+  wred_step<0x111>(s, mn, mx);   // row_shr:1
+  wred_step<0x112>(s, mn, mx);   // row_shr:2
+  wred_step<0x114>(s, mn, mx);   // row_shr:4
+  wred_step<0x118>(s, mn, mx);   // row_shr:8
+  Wred r;
+  r.sum = (uint32_t)__builtin_amdgcn_readlane((int)s, 15) + (uint32_t)__builtin_amdgcn_readlane((int)s, 31) +
+          (uint32_t)__builtin_amdgcn_readlane((int)s, 47) + (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
+  r.mn = min(min((uint32_t)__builtin_amdgcn_readlane((int)mn, 15), (uint32_t)__builtin_amdgcn_readlane((int)mn, 31)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)mn, 47), (uint32_t)__builtin_amdgcn_readlane((int)mn, 63)));
+  r.mx = max(max((uint32_t)__builtin_amdgcn_readlane((int)mx, 15), (uint32_t)__builtin_amdgcn_readlane((int)mx, 31)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)mx, 47), (uint32_t)__builtin_amdgcn_readlane((int)mx, 63)));
+  return r;
+}
+
+// Exclusive prefix (in position order) and total of G per-group counts
+// (each < 2^16) over the block: fields of 16 bits, two groups to a word,
+// scanned together; one barrier.  `slot` must not have been used by the
+// previous three calls.
+template <int G>
+__device__ void scan_groups(const uint32_t (&c)[G], uint32_t* slot, uint32_t (&pre)[G],
+                            uint32_t (&tot)[G]) {
+  constexpr int W = (G + 1) / 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t v[W], x[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    v[w] = c[2 * w] | (2 * w + 1 < G ? c[2 * w + 1] << 16 : 0u);
+    x[w] = wave_incl_scan(v[w]);
+    if (lane == 63) slot[wave * W + w] = x[w];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < kSelNW; ++k) {
+      const uint32_t s = slot[k * W + w];
+      before += k < wave ? s : 0u;
+      all += s;
+    }
+    const uint32_t ex = before + x[w] - v[w];
+    pre[2 * w] = ex & 0xFFFFu;
+    tot[2 * w] = all & 0xFFFFu;
+    if (2 * w + 1 < G) {
+      pre[2 * w + 1] = ex >> 16;
+      tot[2 * w + 1] = all >> 16;
+    }
+  }
+}
+
+// Digit holding the need-th largest of the 2^w bins (counted from the top):
+// the digit, the count above it and its own count (block-uniform); two
+// barriers, `slot` / `rs` as in scan_groups.
+__device__ void find_digit(const uint32_t* h, int w, uint32_t need, uint32_t* slot, uint32_t* rs,
+                           uint32_t* digit, uint32_t* above, uint32_t* count) {
+  constexpr int kPer = kHistBins / kFinalThreads;     // 4 bins per thread at most
+  const int nb = 1 << w;
+  const int per = (nb + kFinalThreads - 1) / kFinalThreads;
+  const int top = nb - 1 - (int)threadIdx.x * per;    // thread 0 owns the highest bins
+  uint32_t c[kPer];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    c[i] = (i < per && top - i >= 0) ? h[top - i] : 0u;
+    s += c[i];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(s);
+  if (lane == 63) slot[wave] = x;
+  __syncthreads();
+  uint32_t ex = x - s;
+#pragma unroll
+  for (int k = 0; k < kSelNW; ++k) ex += k < wave ? slot[k] : 0u;
+  if (ex < need && need <= ex + s) {
+    uint32_t acc = ex;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (acc < need && need <= acc + c[i]) {
+        rs[0] = (uint32_t)(top - i);
+        rs[1] = acc;
+        rs[2] = c[i];
+      }
+      acc += c[i];
+    }
+  }
+  __syncthreads();
+  *digit = rs[0];
+  *above = rs[1];
+  *count = rs[2];
+}
+
+// The K largest of the block's elements (key 0: absent; no score maps to it),
+// equal keys going to the earlier element in position order, or a superset
+// of them: at most `budget` (>= K) elements, all those at or above the radix
+// digit that holds the K-th key once that group fits the budget.  sel[i] is
+// set for the kept elements of this thread; returns how many are kept
+// (min(K, present) when budget == K).  `round` counts the rotating slots used.
+template <int PT>
+__device__ uint32_t block_select(const uint32_t (&key)[PT], uint32_t K, uint32_t budget,
+                                 BlockSelLds& L, bool (&sel)[PT], int& round) {
+  constexpr int G = PT / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t cnt = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    if (key[i]) {
+      ++cnt;
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+  }
+  const Wred wr = wave_reduce3(cnt, kmin, kmax);
+  if (lane == 0) {
+    L.red[0][wave] = wr.sum;
+    L.red[1][wave] = wr.mn;
+    L.red[2][wave] = wr.mx;
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) L.hist[0][i] = 0u;
+  __syncthreads();
+  uint32_t tot = 0;
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int k = 0; k < kSelNW; ++k) {
+    tot += L.red[0][k];
+    kmin = min(kmin, L.red[1][k]);
+    kmax = max(kmax, L.red[2][k]);
+  }
+  if (tot <= budget) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) sel[i] = key[i] != 0u;
+    return tot;
+  }
+  // bits at and above `shift` are fixed in `prefix`; every present key shares
+  // the bits above the highest one where kmin and kmax differ
+  const uint32_t diff = kmin ^ kmax;
+  int shift = diff ? 32 - __builtin_clz(diff) : 0;
+  uint32_t prefix = key_hi(kmax, shift);
+  uint32_t need = K;
+  uint32_t group = tot;   // elements matching the prefix
+  bool all = false;       // every element matching the prefix is kept
+  int buf = 0;
+  while (shift > 0) {
+    const int w = shift < kHistBits ? shift : kHistBits;
+    const int sh = shift - w;
+    const uint32_t mask = (1u << w) - 1u;
+    uint32_t* h = L.hist[buf];
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+      if (key[i] && key_hi(key[i], shift) == prefix) atomicAdd(&h[(key[i] >> sh) & mask], 1u);
+    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) L.hist[buf ^ 1][i] = 0u;
+    __syncthreads();
+    uint32_t d, ab, c;
+    find_digit(h, w, need, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
+    ++round;
+    buf ^= 1;
+    prefix = (prefix << w) | d;
+    need -= ab;
+    group = c;
+    shift = sh;
+    if (K - need + c <= budget) {   // (budget == K: exactly when the group is needed whole)
+      all = true;
+      break;
+    }
+  }
+  // above the prefix: kept; equal to it: kept when the group fits, otherwise
+  // (equal keys) the earliest `need` of them in position order
+  bool eq[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const uint32_t hk = key_hi(key[i], shift);
+    eq[i] = key[i] && hk == prefix;
+    sel[i] = key[i] && hk > prefix;
+  }
+  if (all) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) sel[i] = sel[i] || eq[i];
+    return K - need + group;
+  }
+  uint32_t tc[G], pre[G], gt[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    tc[u] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tc[u] += eq[4 * u + j] ? 1u : 0u;
+  }
+  scan_groups<G>(tc, L.scan[round & 3], pre, gt);
+  ++round;
+  uint32_t before = 0;
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    uint32_t rank = before + pre[u];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (eq[4 * u + j]) {
+        sel[4 * u + j] = rank < need;
+        ++rank;
+      }
+    }
+    before += gt[u];
+  }
+  return K;
+}
+
+// Output index (in position order) of each kept element of this thread: one
+// scan of the per-group kept counts.
+template <int PT>
+__device__ void kept_order(const bool (&sel)[PT], BlockSelLds& L, int& round, uint32_t (&oidx)[PT]) {
+  constexpr int G = PT / 4;
+  uint32_t kc[G], pre[G], gt[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    kc[u] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kc[u] += sel[4 * u + j] ? 1u : 0u;
+  }
+  scan_groups<G>(kc, L.scan[round & 3], pre, gt);
+  ++round;
+  uint32_t before = 0;
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    uint32_t o = before + pre[u];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      oidx[4 * u + j] = o;
+      o += sel[4 * u + j] ? 1u : 0u;
+    }
+    before += gt[u];
+  }
+}
+
+// Slice s of row r (positions s * 1024 PT ..): a superset of its K largest
+// keys (at most `slots`), keys and positions in ascending position order, then
+// key 0 up to `slots` (slots [r][s][0 .. slots)).
+template <int PT>
+__global__ __launch_bounds__(kFinalThreads)
+void k_topk_slice(const float* __restrict__ scores, int32_t N, const int32_t* __restrict__ n_valid,
+                  int32_t n_all, int32_t K, int32_t slots, uint32_t* __restrict__ ckey,
+                  int32_t* __restrict__ cpos) {
+  constexpr int G = PT / 4;
+  __shared__ BlockSelLds L;
+  const int row = blockIdx.y, s = blockIdx.x;
+  const int32_t n = row_count(n_valid, n_all, row, N);
+  const int32_t b0 = s * (kFinalThreads * PT) + 4 * (int32_t)threadIdx.x;   // group 0's first position
+  const float* sr = scores + (size_t)row * N;
+  uint32_t key[PT];
+  const bool vec = (N & 3) == 0 && ((uintptr_t)scores & 15u) == 0;
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    const int32_t p = b0 + kGroupSpan * u;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (vec) {
+      if (p < n) v = *reinterpret_cast<const float4*>(sr + p);   // p + 3 < N: N is a multiple of 4
+    } else {
+      v.x = p < n ? sr[p] : 0.f;
+      v.y = p + 1 < n ? sr[p + 1] : 0.f;
+      v.z = p + 2 < n ? sr[p + 2] : 0.f;
+      v.w = p + 3 < n ? sr[p + 3] : 0.f;
+    }
+    key[4 * u + 0] = p + 0 < n ? score_key(v.x) : 0u;
+    key[4 * u + 1] = p + 1 < n ? score_key(v.y) : 0u;
+    key[4 * u + 2] = p + 2 < n ? score_key(v.z) : 0u;
+    key[4 * u + 3] = p + 3 < n ? score_key(v.w) : 0u;
+  }
+  bool sel[PT];
+  int round = 0;
+  const uint32_t kept = block_select<PT>(key, (uint32_t)K, (uint32_t)slots, L, sel, round);
+  uint32_t oidx[PT];
+  kept_order<PT>(sel, L, round, oidx);
+  const size_t base = ((size_t)row * gridDim.x + s) * slots;
+  // the keepers go out through LDS (coalesced stores) when they fit the
+  // histogram buffers, which the select no longer needs
+  const bool staged = 2 * kept <= 2 * kHistBins;
+  uint32_t* sk = &L.hist[0][0];
+  int32_t* sp = reinterpret_cast<int32_t*>(sk + kept);
+#pragma unroll
+  for (int u = 0; u < G; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * u + j;
+      if (sel[i]) {
+        if (staged) {
+          sk[oidx[i]] = key[i];
+          sp[oidx[i]] = b0 + kGroupSpan * u + j;
+        } else {
+          ckey[base + oidx[i]] = key[i];
+          cpos[base + oidx[i]] = b0 + kGroupSpan * u + j;
+        }
+      }
+    }
+  if (staged) {
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < kept; i += kFinalThreads) {
+      ckey[base + i] = sk[i];
+      cpos[base + i] = sp[i];
+    }
+  }
+  for (uint32_t i = kept + threadIdx.x; i < (uint32_t)slots; i += kFinalThreads) ckey[base + i] = 0u;
+}
+
+// Row r's Top-K as ascending entries (through cand when given), -1 padded.
+// Elements: `total` slots of keepers (ckey / cpos from k_topk_slice, in
+// position order, total a multiple of 4) or, with total == 0, the row's own
+// scores (N <= kFinalThreads * PT).
+template <int PT>
+__global__ __launch_bounds__(kFinalThreads)
+void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __restrict__ n_valid,
+                  int32_t n_all, int32_t total, const uint32_t* __restrict__ ckey,
+                  const int32_t* __restrict__ cpos, int32_t K, const int32_t* __restrict__ cand_map,
+                  int32_t* __restrict__ out) {
+  constexpr int G = PT / 4;
+  __shared__ BlockSelLds L;
+  const int row = blockIdx.x;
+  const int32_t b0 = 4 * (int32_t)threadIdx.x;
+  uint32_t key[PT];
+  int32_t pos[PT];
+  if (total == 0) {
+    const int32_t n = row_count(n_valid, n_all, row, N);
+    const float* sr = scores + (size_t)row * N;
+    const bool vec = (N & 3) == 0 && ((uintptr_t)scores & 15u) == 0;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int32_t p = b0 + kGroupSpan * u;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (vec) {
+        if (p < n) v = *reinterpret_cast<const float4*>(sr + p);
+      } else {
+        v.x = p < n ? sr[p] : 0.f;
+        v.y = p + 1 < n ? sr[p + 1] : 0.f;
+        v.z = p + 2 < n ? sr[p + 2] : 0.f;
+        v.w = p + 3 < n ? sr[p + 3] : 0.f;
+      }
+      key[4 * u + 0] = p + 0 < n ? score_key(v.x) : 0u;
+      key[4 * u + 1] = p + 1 < n ? score_key(v.y) : 0u;
+      key[4 * u + 2] = p + 2 < n ? score_key(v.z) : 0u;
+      key[4 * u + 3] = p + 3 < n ? score_key(v.w) : 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pos[4 * u + j] = p + j;
+    }
+  } else {
+    const uint32_t* kr = ckey + (size_t)row * total;
+    const int32_t* pr = cpos + (size_t)row * total;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int32_t e = b0 + kGroupSpan * u;
+      u32x4 kv = {0u, 0u, 0u, 0u};
+      u32x4 pv = {0u, 0u, 0u, 0u};
+      if (e < total) {   // total is a multiple of 4
+        kv = *reinterpret_cast<const u32x4*>(kr + e);
+        pv = *reinterpret_cast<const u32x4*>(pr + e);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        key[4 * u + j] = kv[j];
+        pos[4 * u + j] = (int32_t)pv[j];
+      }
+    }
+  }
+  bool sel[PT];
+  int round = 0;
+  const uint32_t chosen = block_select<PT>(key, (uint32_t)K, (uint32_t)K, L, sel, round);
+  uint32_t oidx[PT];
+  kept_order<PT>(sel, L, round, oidx);
+  int32_t* orow = out + (size_t)row * K;
+  const int32_t* mrow = cand_map ? cand_map + (size_t)row * N : nullptr;
+  // positions go out through LDS (coalesced stores, and the map lookups of a
+  // candidate list one per thread) when they fit the histogram buffers
+  const bool staged = chosen <= 2 * kHistBins;
+  int32_t* sp = reinterpret_cast<int32_t*>(&L.hist[0][0]);
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    if (sel[i]) {
+      if (staged) sp[oidx[i]] = pos[i];
+      else orow[oidx[i]] = mrow ? mrow[pos[i]] : pos[i];
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < chosen; i += kFinalThreads) {
+      const int32_t p = sp[i];
+      orow[i] = mrow ? mrow[p] : p;
+    }
+  }
+  for (uint32_t i = chosen + threadIdx.x; i < (uint32_t)K; i += kFinalThreads) orow[i] = -1;
+}
+
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -931,6 +1369,41 @@ hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
     else
       k_topk_row<false, false><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, nullptr, 0, cand, out);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_sliced(const float* scores, int32_t R, int32_t N,
+                              const int32_t* n_valid, int32_t n_all, const int32_t* cand,
+                              int32_t K, int32_t* out, void* ws, hipStream_t s) {
+  const TopkSlicing sl = topk_slicing(R, N, K);
+  if (!sl.taken || R <= 0 || K <= 0) return hipErrorInvalidValue;
+  uint32_t* ckey = nullptr;
+  int32_t* cpos = nullptr;
+  int64_t elems = N;
+  int32_t total = 0;
+  if (sl.S > 0) {
+    if (!ws) return hipErrorInvalidValue;
+    ckey = (uint32_t*)ws;
+    cpos = (int32_t*)((char*)ws + align256((size_t)R * sl.S * sl.slots * 4));
+    const dim3 grid((unsigned)sl.S, (unsigned)R), block(kFinalThreads);
+    if (sl.pt == 4)
+      k_topk_slice<4><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
+    else if (sl.pt == 8)
+      k_topk_slice<8><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
+    else
+      k_topk_slice<16><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    total = sl.S * sl.slots;
+    elems = total;
+  }
+  const dim3 grid((unsigned)R), block(kFinalThreads);
+  if (elems <= kFinalThreads * 4)
+    k_topk_final<4><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
+  else if (elems <= kFinalThreads * 8)
+    k_topk_final<8><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
+  else
+    k_topk_final<16><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
   return hipGetLastError();
 }
 
