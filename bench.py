@@ -2,19 +2,25 @@
 """CSA2 decode benchmark on one MI355X: query-tokens/s and achieved HBM bandwidth.
 
 A step is one decode token for every sequence of the batch through the whole
-layer schedule (csa2_decode_layers: indexer scan, Top-K, FP4 gather +
-attention, FP8 window merge per layer) with all inputs resident in HBM.
-The default workload is the 128K-context decode (batch 32, pool M = 32768,
-K = 512, W = 128, layers Full / Reindex / Reuse / Reuse); the 1M-context
-hierarchical decode (batch 8, M = 262144, P = 8192, Full + 3 Reindex) is
-measured too and reported under "extra".
+layer schedule (indexer scan, Top-K, FP4 gather + attention, FP8 window merge
+per layer) with all inputs resident in HBM.  The headline is the MALL-cold
+step: before every layer a 512 MiB read-write sweep evicts the 256 MB
+last-level cache (outside the timed region), the layer alone
+(csa2_decode_layer) is timed between HIP events on the stream it runs on, and
+a step's time is the sum of its layers' times; the median over the timed
+steps is reported.  (In a model the weights read between two layers evict
+that cache.)  Back-to-back whole steps (csa2_decode_layers, warm) are reported
+beside it.  The default workload is the 128K-context decode (batch 32, pool
+M = 32768, K = 512, W = 128, layers Full / Reindex / Reuse / Reuse); the
+1M-context hierarchical decode (batch 8, M = 262144, P = 8192, Full + 3
+Reindex) and the 20-layer schedule are measured the same way under "extra".
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the indexer
 scan): algorithmic bytes per launch / its mean duration, timed with HIP
 events on the stream it runs on; `traffic` is the counter-measured HBM bytes
 per launch recorded under profiles/ for the same kernel source (null when the
-kernel changed since).  `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload on one host core.
+kernel changed since).  `cpu_baseline` times the CPU oracle on bounded samples
+of the 128K, 1M and prefill workloads on one host core.
 """
 import argparse
 import hashlib
@@ -109,36 +115,40 @@ def time_structs(dc, structs, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
-def per_layer_ms(dc, steps: int):
-    """Per-layer ms (warm): the step over the schedule's first l layers, differenced.
+def cold_layers_ms(dc, steps: int, sweep_mib: int = 512, write: bool = False):
+    """MALL-cold steps: before every layer a sweep of sweep_mib MiB (outside the
+    timed region), then the layer alone (csa2_decode_layer) between HIP events.
+    Returns (median step ms, per-layer median ms, all step ms), a step's time
+    being the sum of its layers' times.
 
-    Every prefix of a valid schedule is valid (it starts with a Full layer)."""
-    structs = dc.layer_structs(idx_for_reuse=False)
-    out, prev = [], 0.0
-    for n in range(1, len(structs) + 1):
-        t = time_structs(dc, structs[:n], steps, 2)
-        out.append(t - prev)
-        prev = t
-    return out
-
-
-def cold_step_ms(dc, steps: int) -> float:
-    """Median ms of a step that starts with the MALL evicted: a 512 MiB read-write
-    sweep runs before each timed step, outside its events."""
+    The sweep reads (write=False), as the weights a model streams between two
+    layers are read: it evicts the cache and leaves it clean.  A written sweep
+    (write=True) leaves up to the cache's size in dirty lines, whose write-back
+    to HBM then lands inside the next layer's timed region."""
     import torch
     stream = torch.cuda.current_stream()
-    sweep = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    sweep = torch.zeros(sweep_mib << 20, dtype=torch.uint8, device="cuda")
+    sweep_f = sweep.view(torch.float32)
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    L = dc.cfg.L
+    dc.prepare_decode(idx_for_reuse=False)
     dc.decode_layers()
-    for a, b in evs:
-        sweep.add_(1)
-        a.record(stream)
-        dc.decode_layers()
-        b.record(stream)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(L)] for _ in range(steps)]
+    for row in evs:
+        for ell, (a, b) in enumerate(row):
+            if write:
+                sweep.add_(1)
+            else:
+                torch.sum(sweep_f, out=sink)
+            a.record(stream)
+            dc.decode_layer(ell)
+            b.record(stream)
     torch.cuda.synchronize()
-    del sweep
-    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+    del sweep, sweep_f, sink
+    per = np.array([[a.elapsed_time(b) for a, b in row] for row in evs])   # [steps][L]
+    T = per.sum(axis=1)
+    return float(np.median(T)), np.median(per, axis=0).tolist(), T.tolist()
 
 
 def all_full_ms(dc, steps: int, warmup: int) -> float:
@@ -224,7 +234,8 @@ def measure_prefill(ci: int, steps: int, warmup: int, context: bool = True):
     stage_ms = [_time_calls(lambda st=st: dc.prefill_stage(st), steps, warmup) for st in range(4)]
     attn_ms = ms - stage_ms[0] - stage_ms[1]          # the fused attention pass, by difference
     idx_flop, attn_flop = _prefill_flops(cfg, cfg.pos0)
-    res = dict(workload=cfg.name, query_tokens_per_s=cfg.B * cfg.Q / (ms * 1e-3), ms_per_step=ms,
+    res = dict(workload=cfg.name, case=case,
+               query_tokens_per_s=cfg.B * cfg.Q / (ms * 1e-3), ms_per_step=ms,
                path="csa2_prefill_layers (score, Top-K, one attention pass over K + W keys)",
                stage_ms={"index_score_mfma": stage_ms[0], "topk": stage_ms[1],
                          "attention_fused_mfma": attn_ms},
@@ -281,8 +292,29 @@ def measure_prefill(ci: int, steps: int, warmup: int, context: bool = True):
     return res
 
 
-def cpu_baseline(case, budget_s: float = 15.0):
-    """The CPU oracle, single-threaded, on whole sequences until the budget is used."""
+def host_info() -> dict:
+    """The host the CPU baseline runs on: logical CPUs, CPU model, BLAS threads."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = {i.get("internal_api", i.get("prefix", "?")): i.get("num_threads")
+                for i in threadpool_info()}
+    except Exception:
+        pass
+    return dict(host_cpu_count=os.cpu_count(), cpu_model=model, blas_threads_default=blas)
+
+
+def cpu_decode(case, budget_s: float) -> dict:
+    """The CPU oracle, single-threaded, on whole sequences of a decode workload
+    (all layers) until the budget is used."""
     from threadpoolctl import threadpool_limits
     from oracle import csa2 as O
     cfg = case.cfg
@@ -305,6 +337,30 @@ def cpu_baseline(case, budget_s: float = 15.0):
                        "BLAS limited to 1 thread)" % (done, cfg.B, cfg.name, cfg.L, el))
 
 
+def cpu_prefill(case, budget_s: float) -> dict:
+    """The CPU oracle, single-threaded, on query tokens of a prefill chunk
+    (Full layer: score the visible entries, Top-K, attention with the window)
+    until the budget is used."""
+    from threadpoolctl import threadpool_limits
+    from oracle import csa2 as O
+    cfg = case.cfg
+    p = case.pool
+    L = case.layers[0]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for t in range(cfg.Q - 1, -1, -1):
+            O.prefill_query(p.latent[0], p.scale[0], p.idx_key[0], L.q_idx[0, t], L.w_idx[0, t],
+                            L.q[0, t], L.swa[0], t, cfg.pos0, cfg.ratio, cfg.K, cfg.W)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    el = time.perf_counter() - t0
+    return dict(value=done / el, unit="query-tokens/s", cores=1, kind="oracle",
+                sample="%d of %d query tokens of %s (the newest first; %.1f s, NumPy fp64, "
+                       "BLAS limited to 1 thread)" % (done, cfg.Q, cfg.name, el))
+
+
 def measure(ci: int, steps: int, warmup: int, score_launches: int, detail: bool = False):
     import torch
     from fp4_kv_cache_score_amd import synth
@@ -316,20 +372,31 @@ def measure(ci: int, steps: int, warmup: int, score_launches: int, detail: bool 
     log("generated %s in %.1f s" % (cfg.name, time.perf_counter() - t0))
     dc = DeviceCase(case)
     torch.cuda.synchronize()
-    ms, wall = time_decode(dc, steps, warmup)
-    log("%s: %.3f ms/step (wall %.3f s for %d steps)" % (cfg.name, ms, wall, steps))
+    dc.prepare_decode(idx_for_reuse=False)
+    for _ in range(warmup):
+        dc.decode_layers()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms, per_layer, all_steps = cold_layers_ms(dc, steps)
+    wall = time.perf_counter() - t0
+    log("%s: MALL-cold step %.3f ms (median of %d; layers %s ms; wall %.2f s with the sweeps)" % (
+        cfg.name, ms, steps, ["%.4f" % x for x in per_layer], wall))
+    warm_ms, _ = time_decode(dc, steps, 2)
+    log("%s: warm back-to-back step %.3f ms" % (cfg.name, warm_ms))
     ab = algorithmic_bytes(cfg)
     k_ms, k_min = time_score_kernel(dc, score_launches)
     per_launch = cfg.B * cfg.M * cfg.HI * cfg.DI + cfg.B * (cfg.HI * cfg.DI + cfg.HI * 4)
     log("%s: scan kernel mean %.3f ms (min %.3f) per launch" % (cfg.name, k_ms, k_min))
-    res = dict(cfg=cfg, case=case, ms=ms, wall=wall, bytes=ab, k_ms=k_ms, per_launch=per_launch)
+    res = dict(cfg=cfg, case=case, ms=ms, per_layer_ms=per_layer, step_ms_all=all_steps,
+               warm_ms=warm_ms, wall=wall, bytes=ab, k_ms=k_ms, per_launch=per_launch)
     if detail:
+        rw_ms, rw_layers, _ = cold_layers_ms(dc, max(10, steps // 2), write=True)
+        res["rw_sweep_ms"], res["rw_sweep_layers_ms"] = rw_ms, rw_layers
+        log("%s: step after read-write sweeps %.3f ms (layers %s)" % (
+            cfg.name, rw_ms, ["%.4f" % x for x in rw_layers]))
         dc.prepare_decode(idx_for_reuse=False)
-        res["per_layer_ms"] = per_layer_ms(dc, max(5, steps // 2))
-        res["cold_ms"] = cold_step_ms(dc, max(10, steps // 2))
         res["all_full_ms"] = all_full_ms(dc, max(5, steps // 2), 2)
-        log("%s: per layer %s ms; MALL-cold step %.3f ms; all-Full schedule %.3f ms" % (
-            cfg.name, ["%.4f" % x for x in res["per_layer_ms"]], res["cold_ms"], res["all_full_ms"]))
+        log("%s: all-Full schedule %.3f ms (warm)" % (cfg.name, res["all_full_ms"]))
     del dc
     torch.cuda.empty_cache()
     return res
@@ -490,14 +557,20 @@ def measure_host_tier(ci: int, reps: int = 5):
 
 
 def step_detail(r) -> dict:
-    """Per-layer, MALL-cold and all-Full figures of a decode workload."""
-    if "per_layer_ms" not in r:
-        return {}
+    """Cold per-layer, warm and all-Full figures of a decode workload."""
     B = r["cfg"].B
-    return dict(per_layer_ms=r["per_layer_ms"],
-                cold_ms_per_step=r["cold_ms"], cold_query_tokens_per_s=B / (r["cold_ms"] * 1e-3),
-                all_full_ms_per_step=r["all_full_ms"],
-                all_full_query_tokens_per_s=B / (r["all_full_ms"] * 1e-3))
+    d = dict(mall_cold_ms_per_step=r["ms"], mall_cold_query_tokens_per_s=B / (r["ms"] * 1e-3),
+             mall_cold_per_layer_ms=r["per_layer_ms"],
+             mall_cold_step_ms_min_max=[min(r["step_ms_all"]), max(r["step_ms_all"])],
+             warm_ms_per_step=r["warm_ms"], warm_query_tokens_per_s=B / (r["warm_ms"] * 1e-3),
+             warm_step_frac_of_peak=r["bytes"]["total"] / (r["warm_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    if "rw_sweep_ms" in r:
+        d.update(read_write_sweep_ms_per_step=r["rw_sweep_ms"],
+                 read_write_sweep_per_layer_ms=r["rw_sweep_layers_ms"])
+    if "all_full_ms" in r:
+        d.update(all_full_ms_per_step=r["all_full_ms"],
+                 all_full_query_tokens_per_s=B / (r["all_full_ms"] * 1e-3))
+    return d
 
 
 def main():
@@ -511,7 +584,8 @@ def main():
     ap.add_argument("--prefill", type=int, nargs="*", default=[4],
                     help="chunked-prefill configs measured into 'extra'")
     ap.add_argument("--score-launches", type=int, default=20)
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of CPU oracle work per baseline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the chunked-prefill measurement of --prefill configs, without "
@@ -545,6 +619,7 @@ def main():
     if args.prefill_only:   # a counter pass over prefill chunks alone
         for ci in args.prefill:
             r = measure_prefill(ci, args.steps, args.warmup, context=False)
+            r.pop("case")
             print(json.dumps({"workload": r.pop("workload"), **r}), flush=True)
         return
 
@@ -560,7 +635,8 @@ def main():
 
     head = measure(args.config, args.steps, args.warmup, args.score_launches, detail=True)
     cfg = head["cfg"]
-    value = cfg.B / (head["ms"] * 1e-3)
+    value = cfg.B / (head["ms"] * 1e-3)      # the MALL-cold step (sum of per-layer times)
+    cpu_cases = {cfg.name: head["case"]}
     achieved = head["per_launch"] / (head["k_ms"] * 1e-3) / 1e9
     traffic = recorded_traffic(cfg.name)
     step_gbs = head["bytes"]["total"] / (head["ms"] * 1e-3) / 1e9
@@ -570,6 +646,8 @@ def main():
             continue
         r = measure(ci, args.steps, args.warmup, args.score_launches, detail=ci in (1, 2))
         c = r["cfg"]
+        if ci == 2:
+            cpu_cases[c.name] = r["case"]
         extra[c.name] = dict(
             query_tokens_per_s=c.B / (r["ms"] * 1e-3), ms_per_step=r["ms"],
             step_hbm_gbs=r["bytes"]["total"] / (r["ms"] * 1e-3) / 1e9,
@@ -581,6 +659,7 @@ def main():
         del r
     for ci in args.prefill:
         r = measure_prefill(ci, max(3, args.steps // 5), 2)
+        cpu_cases[r["workload"]] = r.pop("case")
         extra[r.pop("workload")] = r
         log("prefill: %.3f ms/step %s" % (r["ms_per_step"], r["stage_ms"]))
     extra[cfg.name] = step_detail(head)
@@ -592,8 +671,8 @@ def main():
         rg["lengths_mean"], cfg.M, rg["ms_per_step"], rg["step_hbm_gbs"]))
     pg = measure_paged(args.config, args.steps, args.warmup)
     extra["paged_" + cfg.name] = pg
-    log("paged pool (pages of %d entries): %.3f ms/step against %.3f contiguous" % (
-        pg["page_entries"], pg["ms_per_step"], head["ms"]))
+    log("paged pool (pages of %d entries): %.3f ms/step against %.3f contiguous (warm)" % (
+        pg["page_entries"], pg["ms_per_step"], head["warm_ms"]))
     ht = measure_host_tier(args.config)
     extra["host_tier_" + cfg.name] = ht
     log("host tier: restore %.1f GB/s, offload %.1f GB/s; decode %.3f ms alone, %.3f ms beside "
@@ -603,7 +682,14 @@ def main():
         ap_res["bulk_gbs"], ap_res["one_entry_per_sequence_us"]))
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(head["case"], args.cpu_budget)
+        per = {}
+        for name, case in cpu_cases.items():
+            per[name] = (cpu_prefill(case, args.cpu_budget) if case.cfg.Q > 1
+                         else cpu_decode(case, args.cpu_budget))
+            log("cpu oracle %s: %.3g query-tokens/s" % (name, per[name]["value"]))
+        cpu = dict(per[cfg.name])
+        cpu.update(host_info())
+        cpu["per_workload"] = per
 
     out = {
         "metric": "CSA2 decode query-tokens/s at 128K ctx (achieved HBM GB/s vs peak)",
@@ -624,6 +710,10 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.B, "pool_entries": cfg.M, "K": cfg.K,
                    "P": cfg.P, "W": cfg.W, "heads": cfg.H, "d": cfg.D,
                    "layers": "/".join({0: "Full", 1: "Reindex", 2: "Reuse"}[m] for m in cfg.modes)},
+        "timing": "MALL-cold: a 512 MiB read sweep before every layer (outside the timed "
+                  "region), each layer alone between HIP events, a step = the sum of its "
+                  "layers, median of the timed steps; warm back-to-back steps and steps after "
+                  "read-write sweeps in extra",
         "step_hbm_gbs": step_gbs,
         "step_frac_of_peak": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": head["bytes"]["total"],

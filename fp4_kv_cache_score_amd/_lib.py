@@ -26,7 +26,8 @@ CSA2_OP_PREFILL_LAYERS = 4
 EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
            "csa2_pool_append", "csa2_swa_append", "csa2_pool_restore", "csa2_pool_offload",
            "csa2_swa_restore", "csa2_swa_offload",
-           "csa2_decode_layers", "csa2_prefill_layers", "csa2_workspace_bytes",
+           "csa2_decode_layers", "csa2_decode_layer", "csa2_prefill_layers",
+           "csa2_workspace_bytes",
            "csa2_status_string",
            "csa2_version")
 
@@ -72,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.csa2_decode_layers.argtypes = [POINTER(csa2_pool), POINTER(csa2_layer), c_int32,
                                          c_int32, c_int32, c_int32, c_int32, POINTER(c_int32),
                                          c_void_p, c_size_t, c_void_p]
+        L.csa2_decode_layer.argtypes = [POINTER(csa2_pool), POINTER(csa2_layer), c_int32, c_int32,
+                                        c_int32, c_int32, c_int32, c_int32, POINTER(c_int32),
+                                        c_void_p, c_size_t, c_void_p]
         L.csa2_prefill_layers.argtypes = [POINTER(csa2_pool), POINTER(csa2_layer), c_int32,
                                           c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
                                           POINTER(c_int32), c_void_p, c_size_t, c_void_p]
@@ -92,7 +96,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_version.argtypes = []
         L.csa2_version.restype = c_char_p
         for fn in ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
-                   "csa2_decode_layers", "csa2_prefill_layers", "csa2_pool_append",
+                   "csa2_decode_layers", "csa2_decode_layer", "csa2_prefill_layers",
+                   "csa2_pool_append",
                    "csa2_swa_append", "csa2_pool_restore", "csa2_pool_offload",
                    "csa2_swa_restore", "csa2_swa_offload"):
             getattr(L, fn).restype = c_int
@@ -196,6 +201,19 @@ def csa2_decode_layers(pool: csa2_pool, layers, H: int, K: int, P: int, W: int, 
                                   ws_bytes, _s(stream))
     _check("csa2_decode_layers", st, raise_on_error)
     return st, list(src)
+
+
+def csa2_decode_layer(pool: csa2_pool, layers, l: int, H: int, K: int, P: int, W: int, ws,
+                      ws_bytes: int, stream=None, raise_on_error=True):
+    """Layer l of the schedule `layers` (a sequence of csa2_layer, or a ctypes
+    array of them).  Returns (status, source layer of l)."""
+    if not isinstance(layers, ctypes.Array):
+        layers = (csa2_layer * len(layers))(*layers)
+    src = c_int32(-1)
+    st = lib().csa2_decode_layer(ctypes.byref(pool), layers, len(layers), l, H, K, P, W,
+                                 ctypes.byref(src), _p(ws), ws_bytes, _s(stream))
+    _check("csa2_decode_layer", st, raise_on_error)
+    return st, src.value
 
 
 def csa2_prefill_layers(pool: csa2_pool, layers, Q: int, pos0: int, ratio: int, H: int, K: int,

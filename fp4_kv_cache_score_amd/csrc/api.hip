@@ -38,6 +38,13 @@ csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E
 constexpr int32_t kMaxW = 4096;
 constexpr int32_t kMaxRows = 65535;  // grid.y limit for row-indexed launches
 
+// Workspace of a stand-alone decode attention call (at least 256 bytes, as
+// every call that takes a workspace asks for some).
+size_t attn_call_ws_bytes(int64_t rows, int32_t steps) {
+  const size_t b = attn_ws_bytes(rows, steps);
+  return b > 256 ? b : 256;
+}
+
 // Top-K workspace: the sliced select's winners when it takes the shape,
 // otherwise the multi-work-group scratch (nothing for the one-work-group
 // row select).
@@ -219,10 +226,10 @@ size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K, 
       return topk_call_ws_bytes(B, M, K);
     case CSA2_OP_SPARSE_ATTN:
       if (K <= 0 || K > kMaxK || H != kH) return 0;
-      return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, attn_steps(K, 0));
+      return Q > 1 ? 256 : attn_call_ws_bytes((int64_t)B * Q, attn_steps(K, 0));
     case CSA2_OP_SWA_MERGE:
       if (W < 0 || W > kMaxW || H != kH) return 0;
-      return Q > 1 ? 256 : attn_ws_bytes((int64_t)B * Q, attn_steps(0, W));
+      return Q > 1 ? 256 : attn_call_ws_bytes((int64_t)B * Q, attn_steps(0, W));
     case CSA2_OP_PREFILL_LAYERS:
       if (M <= 0 || K <= 0 || K > kMaxK || W < 0 || W > kMaxW || H != kH ||
           (int64_t)B * Q > kMaxRows)
@@ -305,7 +312,7 @@ csa2_status csa2_sparse_attn(const csa2_pool* pool, const uint16_t* q, int32_t Q
   if (!al16(q) || !al4(idx) || !al16(o) || !al4(lse)) return CSA2_ERR_ALIGN;
   const int64_t rows = (int64_t)pool->B * Q;
   const int32_t steps = attn_steps(K, 0);
-  const size_t need = Q > 1 ? 256 : attn_ws_bytes(rows, steps);
+  const size_t need = Q > 1 ? 256 : attn_call_ws_bytes(rows, steps);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
   AttnArgs a{};
@@ -340,7 +347,7 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   if (!al16(q) || !al16(o) || !al4(lse) || (swa && !al16(swa))) return CSA2_ERR_ALIGN;
   const int64_t rows = (int64_t)B * Q;
   const int32_t steps = attn_steps(0, W);
-  if (!ws || ws_bytes < (Q > 1 ? 256 : attn_ws_bytes(rows, steps))) return CSA2_ERR_WORKSPACE;
+  if (!ws || ws_bytes < (Q > 1 ? 256 : attn_call_ws_bytes(rows, steps))) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
   if (W == 0) return CSA2_OK;  // nothing to merge: (o, lse) unchanged
   AttnArgs a{};
@@ -363,9 +370,13 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
   return attend_rows(a, ws, rows, steps, stream);
 }
 
-csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
-                               int32_t H, int32_t K, int32_t P, int32_t W, int32_t* src_layer,
-                               void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the decode entry points.
+csa2_status check_decode(const csa2_pool* pool, const csa2_layer* layers, int32_t L, int32_t H,
+                         int32_t K, int32_t P, int32_t W, void* ws, size_t ws_bytes) {
   csa2_status st = check_pool(pool);
   if (st != CSA2_OK) return st;
   if (!layers) return CSA2_ERR_NULL;
@@ -374,122 +385,160 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     return CSA2_ERR_SHAPE;
   st = check_layers(layers, L, W);
   if (st != CSA2_OK) return st;
-  const int64_t B = pool->B, M = pool->M;
-  const size_t need = decode_ws_bytes(B, M, K, P, W);
-  if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+  if (!ws || ws_bytes < decode_ws_bytes(pool->B, pool->M, K, P, W)) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
 
-  const DecodeWs d = decode_ws_carve(ws, B, M, K, P, W);
-  const AttnPlan plan = attn_plan(B, attn_steps(K, W));
-  float* opart = d.opart;
-  float* ml = d.ml;
+// The layer whose indices layer l uses: itself (Full / Reindex) or the most
+// recent Full or Reindex layer before it (layer 0 is Full).
+int32_t source_layer(const csa2_layer* layers, int32_t l) {
+  int32_t s = l;
+  while (s > 0 && layers[s].mode == CSA2_REUSE) --s;
+  return s;
+}
 
-  // The multi-work-group select's histogram and counters start zeroed; every
-  // select leaves them zeroed again.
-  if (d.big) {
-    st = zero_hist_counters(d.t, B, stream);
+// Layer l of a decode step: its index work (Full / Reindex), the copy a
+// Reuse layer asks for, and its attention.  The multi-work-group select's
+// histogram and counters are zero on entry and left zero.
+csa2_status decode_one(const csa2_pool* pool, const csa2_layer* layers, int32_t l, int32_t K,
+                       int32_t P, int32_t W, const DecodeWs& d, const AttnPlan& plan,
+                       hipStream_t stream) {
+  const int64_t B = pool->B, M = pool->M;
+  const int32_t n_cand = (int32_t)(P < M ? P : M);
+  const csa2_layer& y = layers[l];
+  csa2_status st = CSA2_OK;
+  if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
+    st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
+                                       nullptr, (int32_t)M, d.scores, nullptr, pool->len,
+                                       pool_map(pool), stream));
     if (st != CSA2_OK) return st;
-    if (P > 0) {
-      st = zero_hist_counters(d.t2, B, stream);
+    const bool want_p = y.mode == CSA2_FULL && P > 0;
+    if (d.sel.sliced_k && (!want_p || d.sel.sliced_p)) {
+      if (want_p) {
+        st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
+                                           nullptr, P, d.cand, d.slice, stream));
+        if (st != CSA2_OK) return st;
+      }
+      st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
+                                         nullptr, K, y.idx_out, d.slice, stream));
+    } else if (!d.big) {
+      if (want_p) {
+        st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, P,
+                                         nullptr, false, nullptr, d.cand, stream));
+        if (st != CSA2_OK) return st;
+      }
+      st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, K,
+                                       nullptr, false, nullptr, y.idx_out, stream));
+    } else {
+      st = hip_status(launch_topk_hist(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
+                                       d.t.hist, stream));
       if (st != CSA2_OK) return st;
+      if (want_p) {
+        // Top-P and the layer's Top-K from one histogram, one collect pass
+        // over the scores and one finish launch (the two selects of a row
+        // run on two work-groups side by side)
+        st = hip_status(launch_topk_select2(d.scores, (int32_t)B, (int32_t)M, pool->len,
+                                            (int32_t)M, P, d.cand, d.t, K, y.idx_out, d.t2, true,
+                                            stream));
+      } else {
+        st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, nullptr, K,
+                             y.idx_out, d.t, true, stream);
+      }
     }
+    if (st != CSA2_OK) return st;
+  } else if (y.mode == CSA2_REINDEX) {  // hierarchical: score inside the candidate pool
+    st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
+                                       d.cand, P, d.scores, nullptr, pool->len, pool_map(pool),
+                                       stream));
+    if (st != CSA2_OK) return st;
+    // a ragged sequence has min(P, len) candidates (the selects clamp len to P)
+    if (topk_slicing(B, P, K).taken)
+      st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, P, pool->len, n_cand, d.cand, K,
+                                         y.idx_out, d.slice, stream));
+    else
+      st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, pool->len, n_cand, K, nullptr,
+                                       false, d.cand, y.idx_out, stream));
+    if (st != CSA2_OK) return st;
+  }
+  const int32_t* cur = layers[source_layer(layers, l)].idx_out;
+  if (y.mode == CSA2_REUSE && y.idx_out && y.idx_out != cur) {
+    st = hip_status(launch_copy_i32(y.idx_out, cur, B * K, stream));
+    if (st != CSA2_OK) return st;
   }
 
-  const int32_t* cur = nullptr;
-  int32_t cur_layer = -1;
-  const int32_t n_cand = (int32_t)(P < M ? P : M);
-  for (int32_t l = 0; l < L; ++l) {
-    const csa2_layer& y = layers[l];
-    if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
-      st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         nullptr, (int32_t)M, d.scores, nullptr, pool->len,
-                                         pool_map(pool), stream));
-      if (st != CSA2_OK) return st;
-      const bool want_p = y.mode == CSA2_FULL && P > 0;
-      if (d.sel.sliced_k && (!want_p || d.sel.sliced_p)) {
-        if (want_p) {
-          st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, (int32_t)M, pool->len,
-                                             (int32_t)M, nullptr, P, d.cand, d.slice, stream));
-          if (st != CSA2_OK) return st;
-        }
-        st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
-                                           nullptr, K, y.idx_out, d.slice, stream));
-        if (st != CSA2_OK) return st;
-      } else if (!d.big) {
-        if (y.mode == CSA2_FULL && P > 0) {
-          st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
-                                           P, nullptr, false, nullptr, d.cand, stream));
-          if (st != CSA2_OK) return st;
-        }
-        st = hip_status(launch_topk_rows(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, K,
-                                         nullptr, false, nullptr, y.idx_out, stream));
-        if (st != CSA2_OK) return st;
-      } else {
-        st = hip_status(launch_topk_hist(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
-                                         d.t.hist, stream));
-        if (st != CSA2_OK) return st;
-        if (y.mode == CSA2_FULL && P > 0) {
-          // Top-P and the layer's Top-K from one histogram, one collect pass
-          // over the scores and one finish launch (the two selects of a row
-          // run on two work-groups side by side)
-          st = hip_status(launch_topk_select2(d.scores, (int32_t)B, (int32_t)M, pool->len,
-                                              (int32_t)M, P, d.cand, d.t, K, y.idx_out, d.t2,
-                                              true, stream));
-        } else {
-          st = select_rows_big(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M, nullptr, K,
-                               y.idx_out, d.t, true, stream);
-        }
-        if (st != CSA2_OK) return st;
-      }
-      cur = y.idx_out;
-      cur_layer = l;
-    } else if (y.mode == CSA2_REINDEX) {  // hierarchical: score inside the candidate pool
-      st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
-                                         d.cand, P, d.scores, nullptr, pool->len,
-                                         pool_map(pool), stream));
-      if (st != CSA2_OK) return st;
-      // a ragged sequence has min(P, len) candidates (the selects clamp len to P)
-      if (topk_slicing(B, P, K).taken)
-        st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, P, pool->len, n_cand, d.cand, K,
-                                           y.idx_out, d.slice, stream));
-      else
-        st = hip_status(launch_topk_rows(d.scores, (int32_t)B, P, pool->len, n_cand, K, nullptr,
-                                         false, d.cand, y.idx_out, stream));
-      if (st != CSA2_OK) return st;
-      cur = y.idx_out;
-      cur_layer = l;
-    } else {  // Reuse
-      if (y.idx_out && y.idx_out != cur) {
-        st = hip_status(launch_copy_i32(y.idx_out, cur, B * K, stream));
-        if (st != CSA2_OK) return st;
-      }
-    }
-    if (src_layer) src_layer[l] = cur_layer;
+  AttnArgs a{};
+  a.latent = pool->latent;
+  a.scale = pool->scale;
+  a.M = M;
+  a.map = pool_map(pool);
+  a.idx = cur;
+  a.K = K;
+  a.swa = y.swa;
+  a.W = W;
+  a.swa_rows = W;
+  a.pos0 = -1;
+  a.q = y.q;
+  a.Q = 1;
+  a.rows = (int32_t)B;
+  a.opart = d.opart;
+  a.ml = d.ml;
+  a.o_in = nullptr;
+  a.lse_in = nullptr;
+  a.o = y.o;
+  a.lse = y.lse;
+  return hip_status(launch_attn(a, plan, stream));
+}
 
-    AttnArgs a{};
-    a.latent = pool->latent;
-    a.scale = pool->scale;
-    a.M = M;
-    a.map = pool_map(pool);
-    a.idx = cur;
-    a.K = K;
-    a.swa = y.swa;
-    a.W = W;
-    a.swa_rows = W;
-    a.pos0 = -1;
-    a.q = y.q;
-    a.Q = 1;
-    a.rows = (int32_t)B;
-    a.opart = opart;
-    a.ml = ml;
-    a.o_in = nullptr;
-    a.lse_in = nullptr;
-    a.o = y.o;
-    a.lse = y.lse;
-    st = hip_status(launch_attn(a, plan, stream));
+// Zero the multi-work-group select's histograms and counters (the selects
+// leave them zeroed again).
+csa2_status zero_big(const DecodeWs& d, int64_t B, int32_t P, hipStream_t stream) {
+  csa2_status st = zero_hist_counters(d.t, B, stream);
+  if (st == CSA2_OK && P > 0) st = zero_hist_counters(d.t2, B, stream);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
+                               int32_t H, int32_t K, int32_t P, int32_t W, int32_t* src_layer,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  csa2_status st = check_decode(pool, layers, L, H, K, P, W, ws, ws_bytes);
+  if (st != CSA2_OK) return st;
+  const int64_t B = pool->B;
+  const DecodeWs d = decode_ws_carve(ws, B, pool->M, K, P, W);
+  const AttnPlan plan = attn_plan(B, attn_steps(K, W));
+  if (d.big) {
+    st = zero_big(d, B, P, stream);
     if (st != CSA2_OK) return st;
+  }
+  for (int32_t l = 0; l < L; ++l) {
+    st = decode_one(pool, layers, l, K, P, W, d, plan, stream);
+    if (st != CSA2_OK) return st;
+    if (src_layer) src_layer[l] = source_layer(layers, l);
   }
   return CSA2_OK;
+}
+
+csa2_status csa2_decode_layer(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
+                              int32_t l, int32_t H, int32_t K, int32_t P, int32_t W,
+                              int32_t* src_layer, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (l < 0 || l >= L) return CSA2_ERR_SHAPE;
+  csa2_status st = check_decode(pool, layers, L, H, K, P, W, ws, ws_bytes);
+  if (st != CSA2_OK) return st;
+  const int64_t B = pool->B;
+  const DecodeWs d = decode_ws_carve(ws, B, pool->M, K, P, W);
+  const AttnPlan plan = attn_plan(B, attn_steps(K, W));
+  const csa2_layer& y = layers[l];
+  if (d.big && (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0))) {
+    st = zero_big(d, B, P, stream);
+    if (st != CSA2_OK) return st;
+  }
+  st = decode_one(pool, layers, l, K, P, W, d, plan, stream);
+  if (st == CSA2_OK && src_layer) *src_layer = source_layer(layers, l);
+  return st;
 }
 
 csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,

@@ -258,17 +258,22 @@ struct AttnPlan {
 AttnPlan attn_plan(int64_t rows, int32_t steps);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s);
 // Decode attention workspace: per (row, split) one [kH][kD] unnormalised
-// output and kH (reference, sum) pairs, for at most attn_max_splits splits.
+// output and kH (reference, sum) pairs, for the splits attn_plan gives the
+// shape (nothing when it takes one work-group per row).
 struct AttnWs {
   float* opart;
   float* ml;
 };
+inline int64_t attn_ws_splits(int64_t rows, int32_t steps) {
+  const AttnPlan p = attn_plan(rows, steps);
+  return p.splits > 1 ? p.splits : 0;
+}
 inline size_t attn_ws_bytes(int64_t rows, int32_t steps) {
-  const int64_t S = attn_max_splits(rows, steps);
+  const int64_t S = attn_ws_splits(rows, steps);
   return align256(rows * S * kH * kD * 4) + align256(rows * S * kH * 2 * 4);
 }
 inline AttnWs attn_ws_carve(void* ws, int64_t rows, int32_t steps) {
-  const int64_t S = attn_max_splits(rows, steps);
+  const int64_t S = attn_ws_splits(rows, steps);
   AttnWs w;
   w.opart = (float*)ws;
   w.ml = (float*)((char*)ws + align256(rows * S * kH * kD * 4));

@@ -120,6 +120,18 @@ class DeviceCase:
         self.src_layer = src
         return src
 
+    def decode_layer(self, l: int, stream=None) -> int:
+        """Layer l alone (csa2_decode_layer); layers before it must have run."""
+        if getattr(self, "_structs", None) is None:
+            self.prepare_decode()
+        cfg = self.cfg
+        if getattr(self, "_struct_arr", None) is None or self._struct_arr_src is not self._structs:
+            self._struct_arr = (C.csa2_layer * len(self._structs))(*self._structs)
+            self._struct_arr_src = self._structs
+        _, src = C.csa2_decode_layer(self.pool, self._struct_arr, l, cfg.H, cfg.K, cfg.P, cfg.W,
+                                     self.ws, self.ws_bytes, stream)
+        return src
+
     # -- single-stage calls ----------------------------------------------------
     def index_scores(self, ell: int, cand=None, P: int = 0, hist=None, stream=None):
         cfg = self.cfg

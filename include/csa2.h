@@ -251,6 +251,21 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers,
                                int32_t W, int32_t* src_layer, void* ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/* Layer l alone of the decode step csa2_decode_layers describes: the shape
+ * of a model that runs each layer's attention between its other work.  The
+ * schedule (layers, L) is checked whole.  Layers 0 .. l-1 must have run (by
+ * this call or by csa2_decode_layers) on the same pool, layer array and
+ * workspace: a Reuse layer reads its source layer's idx_out, and a Reindex
+ * layer of a hierarchical step (P > 0) scores the candidate pool that the
+ * Full layer left in the workspace.  Results equal those of
+ * csa2_decode_layers, bit for bit.
+ *   l          0 <= l < L (else CSA2_ERR_SHAPE)
+ *   src_layer  NULL or host int32 output: the layer whose indices l uses
+ *   other arguments as in csa2_decode_layers (same workspace size) */
+csa2_status csa2_decode_layer(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
+                              int32_t l, int32_t H, int32_t K, int32_t P, int32_t W,
+                              int32_t* src_layer, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* One chunk of Q tokens per sequence (chunked prefill) through the same
  * static per-layer mode schedule as csa2_decode_layers.  The pages name
  * prefill as the cost that CSA2's index reuse cuts and give every layer its

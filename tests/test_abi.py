@@ -48,9 +48,14 @@ def test_workspace_bytes():
     assert ws(C.CSA2_OP_TOPK, 4, 1, 300001, 512, 0, 0, 0) > 4 * 4096 * 4
     assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 0, 0, 0, 0) == 0
     assert ws(C.CSA2_OP_TOPK, 32, 1, 32768, 16385, 0, 0, 0) == 0
-    assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 16) >= 32 * 16 * 16 * 512 * 4
+    # decode rows are split: at least two partials of [16][512] floats per row
+    part = 16 * 512 * 4
+    assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 16) >= 32 * 2 * part
     assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 8) == 0
-    assert ws(C.CSA2_OP_SWA_MERGE, 32, 1, 0, 0, 0, 128, 16) >= 32 * 4 * 16 * 512 * 4
+    assert ws(C.CSA2_OP_SWA_MERGE, 32, 1, 0, 0, 0, 128, 16) >= 32 * 2 * part
+    assert ws(C.CSA2_OP_SPARSE_ATTN, 1, 2048, 65536, 512, 0, 0, 16) == 256   # prefill: none
+    # sized by the splits the launch uses, not by one split per step
+    assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 16) < 32 * 16 * part
     d = ws(C.CSA2_OP_DECODE_LAYERS, 8, 1, 262144, 512, 8192, 128, 16)
     assert d >= 8 * 262144 * 4
     assert ws(C.CSA2_OP_DECODE_LAYERS, 8, 1, 262144, 512, 256, 128, 16) == 0  # P < K
@@ -188,6 +193,26 @@ def test_decode_layers_schedule_and_argument_errors():
     assert run([_layer(F), _layer(RU, idx_out=None)]) == C.CSA2_ERR_WORKSPACE
     assert run([_layer(F)], ws=None, nb=need) == C.CSA2_ERR_WORKSPACE
     assert run([_layer(F)], pool=_pool(scale=None)) == C.CSA2_ERR_NULL
+
+
+def test_decode_layer_argument_errors():
+    """The per-layer call checks the whole schedule and the layer number."""
+    pool = _pool()
+    need = C.csa2_workspace_bytes(C.CSA2_OP_DECODE_LAYERS, 2, 1, 1024, 64, 0, 128, 16)
+    F, RI, RU = C.CSA2_FULL, C.CSA2_REINDEX, C.CSA2_REUSE
+
+    def run(layers, l, nb=need - 1, **kw):
+        st, _ = C.csa2_decode_layer(pool, layers, l, 16, kw.get("K", 64), 0, 128, A, nb, 0,
+                                    raise_on_error=False)
+        return st
+
+    good = [_layer(F), _layer(RI), _layer(RU)]
+    assert run(good, -1) == C.CSA2_ERR_SHAPE
+    assert run(good, 3) == C.CSA2_ERR_SHAPE
+    assert run(good, 0, K=0) == C.CSA2_ERR_SHAPE
+    assert run([_layer(RU), _layer(F)], 1) == C.CSA2_ERR_SCHEDULE     # layer 0 not Full
+    assert run([_layer(F), _layer(RI, q_idx=None)], 0) == C.CSA2_ERR_NULL
+    assert run(good, 2) == C.CSA2_ERR_WORKSPACE
 
 
 def test_prefill_layers_schedule_and_argument_errors():

@@ -188,6 +188,31 @@ def test_decode_is_deterministic():
             assert np.array_equal(a[k], b[k])
 
 
+@pytest.mark.parametrize("kw", [
+    dict(name="pl_flat", B=3, M=5000, K=64, W=128, modes=(FULL, REINDEX, REUSE, REINDEX, REUSE)),
+    dict(name="pl_hier", B=4, M=40000, K=512, P=4096, W=128, modes=(FULL, REINDEX, REUSE, REINDEX)),
+    dict(name="pl_big", B=2, M=300000, K=128, P=0, W=64, modes=(FULL, REUSE, REINDEX)),
+], ids=["flat", "hier", "big"])
+def test_decode_layer_by_layer_equals_whole_step(kw):
+    """csa2_decode_layer for l = 0 .. L-1 gives the indices, outputs and lse of
+    csa2_decode_layers bit for bit (the hierarchical Reindex layers read the
+    candidate pool the Full layer's call left in the workspace)."""
+    cfg = CONFIGS[0].scaled(seed=300 + len(kw["name"]), **kw)
+    say("case: layer by layer", cfg.name, cfg.modes)
+    case = synth.make_case(cfg)
+    dc, src, whole = run_decode(case)
+    for d in dc.layers:   # scramble the outputs first
+        d["o"].fill_(7.0)
+        d["lse"].fill_(7.0)
+        d["idx"].fill_(-7)
+    srcs = [dc.decode_layer(l) for l in range(cfg.L)]
+    torch.cuda.synchronize()
+    assert srcs == src
+    for a, b in zip(whole, dc.results()):
+        for k in ("idx", "o", "lse"):
+            assert np.array_equal(a[k], b[k]), k
+
+
 @pytest.mark.parametrize("ci,seqs", [(1, (0, 17, 31)), (2, (0, 5)), (3, (0, 63))])
 def test_decode_full_size_sampled(ci, seqs):
     cfg = CONFIGS[ci]
