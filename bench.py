@@ -140,7 +140,7 @@ def cold_layers_ms(dc, steps: int, sweep_mib: int = 512, write: bool = False):
             if write:
                 sweep.add_(1)
             else:
-                torch.sum(sweep_f, out=sink)
+                torch.sum(sweep_f, dim=0, out=sink)
             a.record(stream)
             dc.decode_layer(ell)
             b.record(stream)
