@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("CSA2_LIB", os.path.join(_HERE, "libcsa2.so"))
 
 CSA2_OK, CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_ALIGN = 0, 1, 2, 3
-CSA2_ERR_SCHEDULE, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 4, 5, 6
+CSA2_ERR_SCHEDULE, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP, CSA2_ERR_SCRATCH = 4, 5, 6, 7
+CSA2_NOALLOC_SCRATCH_BYTES = 64 << 20
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
 CSA2_OP_TOPK, CSA2_OP_SPARSE_ATTN, CSA2_OP_SWA_MERGE, CSA2_OP_DECODE_LAYERS = 0, 1, 2, 3
 CSA2_OP_PREFILL_LAYERS = 4
@@ -26,8 +27,8 @@ CSA2_OP_PREFILL_LAYERS = 4
 EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
            "csa2_pool_append", "csa2_swa_append", "csa2_pool_restore", "csa2_pool_offload",
            "csa2_swa_restore", "csa2_swa_offload",
-           "csa2_decode_layers", "csa2_decode_layer", "csa2_prefill_layers",
-           "csa2_workspace_bytes",
+           "csa2_decode_layers", "csa2_decode_layer", "csa2_decode_layers_noalloc",
+           "csa2_prefill_layers", "csa2_workspace_bytes",
            "csa2_status_string",
            "csa2_version")
 
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.csa2_decode_layer.argtypes = [POINTER(csa2_pool), POINTER(csa2_layer), c_int32, c_int32,
                                         c_int32, c_int32, c_int32, c_int32, POINTER(c_int32),
                                         c_void_p, c_size_t, c_void_p]
+        L.csa2_decode_layers_noalloc.argtypes = [POINTER(csa2_pool), POINTER(csa2_layer),
+                                                 c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                 POINTER(c_int32), c_void_p]
         L.csa2_prefill_layers.argtypes = [POINTER(csa2_pool), POINTER(csa2_layer), c_int32,
                                           c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
                                           POINTER(c_int32), c_void_p, c_size_t, c_void_p]
@@ -96,8 +100,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_version.argtypes = []
         L.csa2_version.restype = c_char_p
         for fn in ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
-                   "csa2_decode_layers", "csa2_decode_layer", "csa2_prefill_layers",
-                   "csa2_pool_append",
+                   "csa2_decode_layers", "csa2_decode_layer", "csa2_decode_layers_noalloc",
+                   "csa2_prefill_layers", "csa2_pool_append",
                    "csa2_swa_append", "csa2_pool_restore", "csa2_pool_offload",
                    "csa2_swa_restore", "csa2_swa_offload"):
             getattr(L, fn).restype = c_int
@@ -200,6 +204,19 @@ def csa2_decode_layers(pool: csa2_pool, layers, H: int, K: int, P: int, W: int, 
     st = lib().csa2_decode_layers(ctypes.byref(pool), arr, L, H, K, P, W, src, _p(ws),
                                   ws_bytes, _s(stream))
     _check("csa2_decode_layers", st, raise_on_error)
+    return st, list(src)
+
+
+def csa2_decode_layers_noalloc(pool: csa2_pool, layers, H: int, K: int, P: int, W: int,
+                               stream=None, raise_on_error=True):
+    """csa2_decode_layers in the library's static scratch (no workspace
+    argument, no device allocation).  Returns (status, src_layer list)."""
+    L = len(layers)
+    arr = (csa2_layer * L)(*layers)
+    src = (c_int32 * L)()
+    st = lib().csa2_decode_layers_noalloc(ctypes.byref(pool), arr, L, H, K, P, W, src,
+                                          _s(stream))
+    _check("csa2_decode_layers_noalloc", st, raise_on_error)
     return st, list(src)
 
 

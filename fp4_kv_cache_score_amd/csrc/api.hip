@@ -4,6 +4,8 @@
 #include "csa2.h"
 #include "csa2_internal.h"
 
+#include <mutex>
+
 using namespace csa2;
 
 namespace {
@@ -211,6 +213,7 @@ const char* csa2_status_string(csa2_status s) {
     case CSA2_ERR_SCHEDULE: return "invalid layer mode schedule";
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_HIP: return "HIP launch or runtime error";
+    case CSA2_ERR_SCRATCH: return "step needs more than the library's static scratch";
   }
   return "unknown status";
 }
@@ -374,16 +377,23 @@ csa2_status csa2_swa_merge(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
 
 namespace {
 
-// Argument checks shared by the decode entry points.
-csa2_status check_decode(const csa2_pool* pool, const csa2_layer* layers, int32_t L, int32_t H,
-                         int32_t K, int32_t P, int32_t W, void* ws, size_t ws_bytes) {
+// Argument checks shared by the decode entry points: the pool, the sizes and
+// the schedule.
+csa2_status check_decode_args(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
+                              int32_t H, int32_t K, int32_t P, int32_t W) {
   csa2_status st = check_pool(pool);
   if (st != CSA2_OK) return st;
   if (!layers) return CSA2_ERR_NULL;
   if (L <= 0 || H != kH || K <= 0 || K > kMaxK || P < 0 || P > kMaxK || (P > 0 && P < K) ||
       W < 0 || W > kMaxW || pool->B > kMaxRows)
     return CSA2_ERR_SHAPE;
-  st = check_layers(layers, L, W);
+  return check_layers(layers, L, W);
+}
+
+// ... and the caller's workspace.
+csa2_status check_decode(const csa2_pool* pool, const csa2_layer* layers, int32_t L, int32_t H,
+                         int32_t K, int32_t P, int32_t W, void* ws, size_t ws_bytes) {
+  const csa2_status st = check_decode_args(pool, layers, L, H, K, P, W);
   if (st != CSA2_OK) return st;
   if (!ws || ws_bytes < decode_ws_bytes(pool->B, pool->M, K, P, W)) return CSA2_ERR_WORKSPACE;
   if (!al16(ws)) return CSA2_ERR_ALIGN;
@@ -498,18 +508,16 @@ csa2_status zero_big(const DecodeWs& d, int64_t B, int32_t P, hipStream_t stream
   return st;
 }
 
-}  // namespace
-
-extern "C" {
-
-csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
-                               int32_t H, int32_t K, int32_t P, int32_t W, int32_t* src_layer,
-                               void* ws, size_t ws_bytes, hipStream_t stream) {
-  csa2_status st = check_decode(pool, layers, L, H, K, P, W, ws, ws_bytes);
-  if (st != CSA2_OK) return st;
+// Every layer of a decode step on a checked, large enough workspace.  What
+// must start at zero (the multi-work-group select's histograms and counters)
+// is cleared here by a fill kernel; everything else in the workspace is
+// written before it is read.
+csa2_status decode_step(const csa2_pool* pool, const csa2_layer* layers, int32_t L, int32_t K,
+                        int32_t P, int32_t W, int32_t* src_layer, void* ws, hipStream_t stream) {
   const int64_t B = pool->B;
   const DecodeWs d = decode_ws_carve(ws, B, pool->M, K, P, W);
   const AttnPlan plan = attn_plan(B, attn_steps(K, W));
+  csa2_status st = CSA2_OK;
   if (d.big) {
     st = zero_big(d, B, P, stream);
     if (st != CSA2_OK) return st;
@@ -520,6 +528,53 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, 
     if (src_layer) src_layer[l] = source_layer(layers, l);
   }
   return CSA2_OK;
+}
+
+}  // namespace
+
+// Workspace of csa2_decode_layers_noalloc: one array per GPU in the
+// library's own device memory, held from the library's load on that GPU to
+// the end of the process.  Host code never hands the array's name to a
+// kernel or a copy (on the host it names a stand-in, not device memory): it
+// asks HIP for the array's address on each device once and uses that.
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchBytes = CSA2_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The array's address on the current device (looked up on the first call
+// made with that device current), or a HIP error.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
+                               int32_t H, int32_t K, int32_t P, int32_t W, int32_t* src_layer,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  const csa2_status st = check_decode(pool, layers, L, H, K, P, W, ws, ws_bytes);
+  if (st != CSA2_OK) return st;
+  return decode_step(pool, layers, L, K, P, W, src_layer, ws, stream);
 }
 
 csa2_status csa2_decode_layer(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
@@ -539,6 +594,18 @@ csa2_status csa2_decode_layer(const csa2_pool* pool, const csa2_layer* layers, i
   st = decode_one(pool, layers, l, K, P, W, d, plan, stream);
   if (st == CSA2_OK && src_layer) *src_layer = source_layer(layers, l);
   return st;
+}
+
+csa2_status csa2_decode_layers_noalloc(const csa2_pool* pool, const csa2_layer* layers,
+                                       int32_t L, int32_t H, int32_t K, int32_t P, int32_t W,
+                                       int32_t* src_layer, hipStream_t stream) {
+  const csa2_status st = check_decode_args(pool, layers, L, H, K, P, W);
+  if (st != CSA2_OK) return st;
+  if (decode_ws_bytes(pool->B, pool->M, K, P, W) > kScratchBytes) return CSA2_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return CSA2_ERR_HIP;
+  return decode_step(pool, layers, L, K, P, W, src_layer, ws, stream);
 }
 
 csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers, int32_t L,

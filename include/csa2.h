@@ -54,8 +54,13 @@ typedef enum csa2_status {
   CSA2_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned */
   CSA2_ERR_SCHEDULE = 4,   /* invalid per-layer mode schedule */
   CSA2_ERR_WORKSPACE = 5,  /* workspace missing or too small */
-  CSA2_ERR_HIP = 6         /* a HIP launch or runtime call failed */
+  CSA2_ERR_HIP = 6,        /* a HIP launch or runtime call failed */
+  CSA2_ERR_SCRATCH = 7     /* the call needs more than the static scratch */
 } csa2_status;
+
+/* Size of the device array that csa2_decode_layers_noalloc works in (one
+ * per GPU, in the library's own device memory until the process ends). */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 };
 
@@ -265,6 +270,30 @@ csa2_status csa2_decode_layers(const csa2_pool* pool, const csa2_layer* layers,
 csa2_status csa2_decode_layer(const csa2_pool* pool, const csa2_layer* layers, int32_t L,
                               int32_t l, int32_t H, int32_t K, int32_t P, int32_t W,
                               int32_t* src_layer, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* csa2_decode_layers for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The caller still passes the pool, the layers' inputs and their
+ * outputs; the workspace is a fixed array of CSA2_NOALLOC_SCRATCH_BYTES per
+ * GPU inside the library.  No device memory is allocated or freed by the
+ * call (the array's address on the current device is looked up once, on the
+ * first call made with that device current).  The stream must belong to the
+ * current device.
+ *   Limit: a step whose csa2_workspace_bytes(CSA2_OP_DECODE_LAYERS, B, 1, M,
+ *   K, P, W, H) exceeds CSA2_NOALLOC_SCRATCH_BYTES returns CSA2_ERR_SCRATCH
+ *   before any HIP call (64 MiB holds, e.g., B = 64 at M = 65536 or B = 8 at
+ *   M = 262144 with P = 8192, K = 512, W = 128).
+ *   Races: every call on one GPU shares that GPU's array and leaves its
+ *   contents behind; calls whose work overlaps on the device (calls on
+ *   different streams, or from several host threads, without an ordering
+ *   between them) race and their results are undefined.  Calls in order on
+ *   one stream are safe; the call clears what must start at zero itself.
+ *   Other arguments, results and errors as in csa2_decode_layers (results
+ *   equal, bit for bit); CSA2_ERR_HIP when the array's address cannot be
+ *   obtained. */
+csa2_status csa2_decode_layers_noalloc(const csa2_pool* pool, const csa2_layer* layers,
+                                       int32_t L, int32_t H, int32_t K, int32_t P, int32_t W,
+                                       int32_t* src_layer, hipStream_t stream);
 
 /* One chunk of Q tokens per sequence (chunked prefill) through the same
  * static per-layer mode schedule as csa2_decode_layers.  The pages name

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert C.csa2_status_string(s)
     assert C.csa2_status_string(0) == "ok"
     assert "unknown" in C.csa2_status_string(99)
@@ -213,6 +213,32 @@ def test_decode_layer_argument_errors():
     assert run([_layer(RU), _layer(F)], 1) == C.CSA2_ERR_SCHEDULE     # layer 0 not Full
     assert run([_layer(F), _layer(RI, q_idx=None)], 0) == C.CSA2_ERR_NULL
     assert run(good, 2) == C.CSA2_ERR_WORKSPACE
+
+
+def test_decode_layers_noalloc_argument_errors():
+    """The static-scratch decode checks its arguments as csa2_decode_layers does
+    and refuses a step larger than its scratch, all before any HIP call."""
+    F, RI, RU = C.CSA2_FULL, C.CSA2_REINDEX, C.CSA2_REUSE
+
+    def run(layers, pool=None, K=64, P=0, W=128, H=16):
+        st, _ = C.csa2_decode_layers_noalloc(pool or _pool(), layers, H, K, P, W, 0,
+                                             raise_on_error=False)
+        return st
+
+    assert run([_layer(RU), _layer(F)]) == C.CSA2_ERR_SCHEDULE
+    assert run([_layer(F)], K=0) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F)], H=8) == C.CSA2_ERR_SHAPE
+    assert run([_layer(F)], P=32) == C.CSA2_ERR_SHAPE          # P < K
+    assert run([_layer(F, lse=None)]) == C.CSA2_ERR_NULL
+    assert run([_layer(F)], pool=_pool(idx_key=None)) == C.CSA2_ERR_NULL
+    ws = C.csa2_workspace_bytes
+    lim = C.CSA2_NOALLOC_SCRATCH_BYTES
+    assert ws(C.CSA2_OP_DECODE_LAYERS, 64, 1, 262144, 512, 0, 128, 16) > lim
+    assert run([_layer(F)], pool=_pool(B=64, M=262144), K=512) == C.CSA2_ERR_SCRATCH
+    # the workloads it is meant for fit
+    assert ws(C.CSA2_OP_DECODE_LAYERS, 64, 1, 65536, 512, 0, 128, 16) <= lim
+    assert ws(C.CSA2_OP_DECODE_LAYERS, 8, 1, 262144, 512, 8192, 128, 16) <= lim
+    assert ws(C.CSA2_OP_DECODE_LAYERS, 32, 1, 32768, 512, 0, 128, 16) <= lim
 
 
 def test_prefill_layers_schedule_and_argument_errors():
