@@ -62,8 +62,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
 
 constexpr int kWK = kAttnStepKeys;             // keys per step (two MFMA sets of 16)
-constexpr int kHalf = kD / 2;                  // output dims per wave
-constexpr int kTRow = kHalf * 2;               // staged key row of one wave: 256 bf16 (512 B)
+constexpr int kHalf = kD / 2;                  // output dims per wave of k_attn
+constexpr int kQuarter = kD / 4;               // output dims per wave of k_attn_dec
 constexpr float kLazy = 8.f;                   // softmax reference slack (natural log units)
 
 // Max and sum over the four 16-lane rows (gfx950 permlane swaps; every lane
@@ -81,35 +81,267 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Byte offset of (key row r, byte c) in a wave's staged tile: 32-byte units
-// XOR-swizzled by the row's low 3 bits, 16-byte halves swapped by its bit 3.
-// The 8 rows that half a wave's transposed read touches then fall on 8
-// different 32-byte bank groups, and the 16 rows of a staging store on 16
-// different 16-byte ones.
+// A wave owns kDims consecutive output dims (part p: dims kDims p ..); each
+// lane dequantises NB = kDims / 128 blocks of 32 dims of one key per set.
+// Byte offset of (key row r, byte c) in a wave's staged tile of kDims bf16
+// per row: 32-byte units XOR-swizzled by the row's low 3 bits, 16-byte halves
+// swapped by its bit 3.  The 8 rows that half a wave's transposed read
+// touches then fall on 8 different 32-byte bank groups, and the 16 rows of a
+// staging store on 16 different 16-byte ones (rows are a multiple of 256
+// bytes long, so the bank of a byte depends only on its place in the row).
+template <int kDims>
 __device__ __forceinline__ int tile_off(int r, int c) {
-  return r * kTRow + ((((c >> 5) ^ (r & 7)) << 5) | ((c & 31) ^ (((r >> 3) & 1) << 4)));
+  return r * (2 * kDims) + ((((c >> 5) ^ (r & 7)) << 5) | ((c & 31) ^ (((r >> 3) & 1) << 4)));
 }
 
-// kSplit: grid (rows, splits); work-group (row, s) runs steps s * cps ..
-// s * cps + cps - 1 of the row (global steps first, Cg of them, then Cw
-// window steps) and writes a partial.  Otherwise grid (rows): one work-group
-// runs every step of its row and writes o and lse.
-template <bool kPaged, bool kSplit>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_attn(AttnArgs a, int32_t Cg, int32_t Cw, int32_t cps, const float* o_in,
-            const float* lse_in) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kWK * kTRow];   // 32 KiB
-  __shared__ __attribute__((aligned(16))) float xs[2][2][64 * 8];         // partial S, by step parity
+// q (this wave's part) as the B operand of S^T = C . q^T: lane (head ln,
+// group lg) holds, for k-step s, dims kDims p + 32 (4 (s / 4) + lg) + 8 (s % 4)
+// .. +7, the order in which score_set holds the keys' dims.
+template <int kDims>
+__device__ __forceinline__ void load_q(const uint16_t* q, int row, int p, int ln, int lg,
+                                       bf16x8 (&qv)[kDims / 32]) {
+  const uint16_t* qr = q + ((size_t)row * kH + ln) * kD + kDims * p;
+#pragma unroll
+  for (int s = 0; s < kDims / 32; ++s)
+    qv[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                           qr + 32 * (4 * (s >> 2) + lg) + 8 * (s & 3)));
+}
 
-  int row, split = 0;
-  if (kSplit) {
-    row = blockIdx.x;
-    split = blockIdx.y;
-  } else {   // rows of one XCD are consecutive tokens (their window rows overlap in L2)
-    const int bid = blockIdx.x, R = a.rows;
-    const int q8 = R >> 3, r8 = R & 7, x = bid & 7, k = bid >> 3;
-    row = x * q8 + (x < r8 ? x : r8) + k;
+// Set u of a step (keys 16 u .. 16 u + 15; this lane: key 16 u + ln, blocks
+// 4 i + lg, i < NB, of this wave's part): dequantise exactly to bf16, add the
+// partial S^T (s0: k-steps of even d, s1: odd d) and stage the bf16 rows in
+// this wave's tile for P . C.  Global keys: c0 (, c1) = the 16 E2M1 bytes of
+// the block(s), c2 = the key's 16 scale bytes (words NB p .. NB p + NB - 1:
+// this part's).  Window rows: (c0, c1) (, (c2, c3)) = the 32 E4M3 bytes of
+// the block(s).
+template <bool kGlobal, int kDims>
+__device__ __forceinline__ void score_set(uint8_t* my, const bf16x8 (&qv)[kDims / 32], int p,
+                                          int ln, int lg, int u, const u32x4& c0,
+                                          const u32x4& c1, const u32x4& c2, const u32x4& c3,
+                                          f32x4& s0, f32x4& s1) {
+  constexpr int NB = kDims / 128;
+  const int r = 16 * u + ln;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int blk = 4 * i + lg;
+    u32x4 w[4];
+    if (kGlobal) {
+      const u32x4& c = i ? c1 : c0;
+      const uint32_t sw = c2[NB * p + i];                    // scale bytes of blocks 4 (NB p + i) ..
+      const uint32_t scb = (sw >> (8 * lg)) & 0xFFu;
+      const float scale = __uint_as_float(scb ? (scb << 23) : 0x00400000u);   // 2^(scb-127)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        w[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 0));
+        w[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 1));
+        w[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 2));
+        w[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 3));
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const u32x4& c = i ? (d < 2 ? c2 : c3) : (d < 2 ? c0 : c1);
+        const uint32_t x0 = c[2 * (d & 1)], x1 = c[2 * (d & 1) + 1];
+        w[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.0f, false));
+        w[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.0f, true));
+        w[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.0f, false));
+        w[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.0f, true));
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, w[d]);
+      if (d & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[4 * i + d], s1, 0, 0, 0);
+      else       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[4 * i + d], s0, 0, 0, 0);
+      *reinterpret_cast<u32x4*>(my + tile_off<kDims>(r, 64 * blk + 16 * d)) = w[d];
+    }
   }
+}
+
+// The NW parts' partial S^T (sa: set 0, sb: set 1) added in a fixed order by
+// every wave through xsb (this step's parity buffer; one barrier).  x0 / x1 =
+// logits of keys 4 lg + e (+16), head ln, -inf where the ballots va / vb (bit
+// = key) say absent; returns the step's largest logit of head ln.
+template <int NW>
+__device__ __forceinline__ float exchange_logits(float (*xsb)[64 * 8], int p, int lane, int lg,
+                                                 const f32x4& sa, const f32x4& sb, uint64_t va,
+                                                 uint64_t vb, f32x4& x0, f32x4& x1) {
+  float* xw = &xsb[p][lane * 8];
+  *reinterpret_cast<f32x4*>(xw) = sa;
+  *reinterpret_cast<f32x4*>(xw + 4) = sb;
+  __syncthreads();
+  x0 = *reinterpret_cast<const f32x4*>(&xsb[0][lane * 8]);
+  x1 = *reinterpret_cast<const f32x4*>(&xsb[0][lane * 8 + 4]);
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    x0 += *reinterpret_cast<const f32x4*>(&xsb[w][lane * 8]);
+    x1 += *reinterpret_cast<const f32x4*>(&xsb[w][lane * 8 + 4]);
+  }
+  float mc = -INFINITY;
+  const uint32_t ba = (uint32_t)(va >> (4 * lg)), bb = (uint32_t)(vb >> (4 * lg));   // keys 4 lg ..
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x0[e] = (ba >> e) & 1u ? x0[e] : -INFINITY;
+    x1[e] = (bb >> e) & 1u ? x1[e] : -INFINITY;
+    mc = fmaxf(mc, fmaxf(x0[e], x1[e]));
+  }
+  return rows_max(mc);
+}
+
+// One step's P . C on this wave's part of the dims, with the current
+// reference (absent keys are -inf: exp gives 0; a reference of -inf only
+// occurs while every key so far is absent, and then 0 stands in for it).
+// O[j][i]: head 4 lg + i, dim kDims p + 16 j + ln.
+template <int kDims>
+__device__ __forceinline__ void pv_step(const uint8_t* my, int tr0, int tr1, int ln,
+                                        const f32x4& x0, const f32x4& x1, float m_run,
+                                        float& l_run, f32x4 (&O)[kDims / 16]) {
+  const float mr = m_run == -INFINITY ? 0.f : m_run;
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    p[e] = __expf(x0[e] - mr);
+    p[4 + e] = __expf(x1[e] - mr);
+  }
+  // A operand: keys 4 lg + e of set 0, then of set 1 (the B reads below take
+  // the same keys); P = hi + lo in bf16
+  u32x4 ph, pl;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    l_run += p[2 * e] + p[2 * e + 1];
+    const bf16x2 hv = __builtin_convertvector((f32x2){p[2 * e], p[2 * e + 1]}, bf16x2);
+    const f32x2 hf = __builtin_convertvector(hv, f32x2);
+    const bf16x2 lv = __builtin_convertvector((f32x2){p[2 * e] - hf[0], p[2 * e + 1] - hf[1]}, bf16x2);
+    ph[e] = __builtin_bit_cast(uint32_t, hv);
+    pl[e] = __builtin_bit_cast(uint32_t, lv);
+  }
+  const bf16x8 ahi = __builtin_bit_cast(bf16x8, ph);
+  const bf16x8 alo = __builtin_bit_cast(bf16x8, pl);
+  __asm__ volatile("" ::: "memory");       // staging stores before the transposed reads
+#pragma unroll
+  for (int j = 0; j < kDims / 16; ++j) {
+    const int c = 32 * j + 8 * (ln & 3);
+    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(my + tile_off<kDims>(tr0, c)));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(my + tile_off<kDims>(tr1, c)));
+    const u32x2 c0 = __builtin_bit_cast(u32x2, r0), c1 = __builtin_bit_cast(u32x2, r1);
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{c0[0], c0[1], c1[0], c1[1]});
+    O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, O[j], 0, 0, 0);
+    O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, O[j], 0, 0, 0);
+  }
+}
+
+// Move head ln's softmax reference to the step's largest logit mc (when
+// `raise`) and rescale O and this lane's sum to it.  The kernels run their
+// steps in an inner loop that touches O only with matrix instructions; a
+// step whose logits exceed the reference by more than kLazy leaves that loop
+// and comes here before its P . C.
+template <int NJ>
+__device__ __forceinline__ void raise_reference(bool raise, float mc, int lg, f32x4 (&O)[NJ],
+                                                float& m_run, float& l_run) {
+  const float m_new = raise ? mc : m_run;
+  const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+  l_run *= alpha;
+  m_run = m_new;
+  float al[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) O[j][i] *= al[i];
+}
+
+// A split's partial of a row: O unnormalised (relative to the reference of
+// its head), the reference and the sum per head.
+template <int kDims>
+__device__ __forceinline__ void store_partial(const AttnArgs& a, int row, int split, int splits,
+                                              int p, int ln, int lg,
+                                              const f32x4 (&O)[kDims / 16], float m_run,
+                                              float L) {
+  const size_t ps = (size_t)row * splits + split;
+  float* op = a.opart + ps * kH * kD + kDims * p;
+#pragma unroll
+  for (int j = 0; j < kDims / 16; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[(size_t)(4 * lg + i) * kD + 16 * j + ln] = O[j][i];
+  if (p == 0 && lg == 0) {
+    a.ml[(ps * kH + ln) * 2] = m_run;
+    a.ml[(ps * kH + ln) * 2 + 1] = L;
+  }
+}
+
+// A row's result: o normalised and lse per head, merged with an incoming
+// (o_in, lse_in) into one softmax over both key sets when given (o_in may be
+// a.o itself).  Called by every thread of the work-group.
+template <int kDims>
+__device__ __forceinline__ void store_final(const AttnArgs& a, int row, int p, int ln, int lg,
+                                            const f32x4 (&O)[kDims / 16], float m_run, float L,
+                                            const float* o_in, const float* lse_in) {
+  // per head: lse, merge with an incoming result; lane (ln, lg) writes dims
+  // kDims p + 16 j + ln of heads 4 lg + i
+  const float lse_h = L > 0.f ? m_run + logf(L) : -INFINITY;   // head ln
+  float wself[4], win[4], lse4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float Li = __shfl(L, 4 * lg + i, 64);
+    float lse = __shfl(lse_h, 4 * lg + i, 64);
+    wself[i] = Li > 0.f ? 1.f / Li : 0.f;
+    win[i] = 0.f;
+    if (lse_in) {   // one softmax over both key sets
+      const float li = lse_in[(size_t)row * kH + 4 * lg + i];
+      const float mx = fmaxf(li, lse);
+      if (mx != -INFINITY) {
+        const float e1 = li == -INFINITY ? 0.f : __expf(li - mx);
+        const float e2 = lse == -INFINITY ? 0.f : __expf(lse - mx);
+        const float tot = e1 + e2;
+        win[i] = e1 / tot;
+        wself[i] *= e2 / tot;
+        lse = mx + logf(tot);
+      }
+    }
+    lse4[i] = lse;
+  }
+  // the incoming lse is read by every wave before wave 0 overwrites it
+  if (lse_in) __syncthreads();
+  float* orow = a.o + (size_t)row * kH * kD + kDims * p;
+  if (lse_in) {
+    // the incoming rows may be the output rows: every value this lane merges
+    // is read before any is written (one round trip, not one per value)
+    const float* inrow = o_in + (size_t)row * kH * kD + kDims * p;
+    f32x4 X[kDims / 16];
+#pragma unroll
+    for (int j = 0; j < kDims / 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[j][i] = inrow[(size_t)(4 * lg + i) * kD + 16 * j + ln];
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < kDims / 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        orow[(size_t)(4 * lg + i) * kD + 16 * j + ln] = fmaf(win[i], X[j][i], O[j][i] * wself[i]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kDims / 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) orow[(size_t)(4 * lg + i) * kD + 16 * j + ln] = O[j][i] * wself[i];
+  }
+  if (p == 0 && ln < 4)
+    a.lse[(size_t)row * kH + 4 * lg + ln] = ln == 0 ? lse4[0] : (ln == 1 ? lse4[1] : (ln == 2 ? lse4[2] : lse4[3]));
+}
+
+// One work-group per query row over all its keys (many rows: prefill, or a
+// decode batch large enough to fill the chip).  Each step's rows are loaded
+// into registers one step ahead.
+template <bool kPaged>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_attn(AttnArgs a, int32_t Cg, int32_t Cw) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kWK * 2 * kHalf];   // 32 KiB
+  __shared__ __attribute__((aligned(16))) float xs[2][2][64 * 8];             // partial S, by step parity
+
+  // rows of one XCD are consecutive tokens (their window rows overlap in L2)
+  const int R = a.rows;
+  const int q8 = R >> 3, r8 = R & 7, xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
+  const int row = xcd * q8 + (xcd < r8 ? xcd : r8) + kk;
   const int b = row / a.Q;
   const int t = row - b * a.Q;
   const int hw = threadIdx.x >> 6;           // this wave's half of the dims
@@ -119,47 +351,26 @@ void k_attn(AttnArgs a, int32_t Cg, int32_t Cw, int32_t cps, const float* o_in,
   const int64_t wgap = a.pos0 >= 0 ? (int64_t)(a.W - 1) - (a.pos0 + t) : 0;
   const int32_t wfirst = wgap > 0 ? (int32_t)wgap : 0;
 
-  // q (this half) as the B operand of S^T = C . q^T: lane (head ln, group lg)
-  // holds, for k-step s, dims 256 hw + 32 (4 (s / 4) + lg) + 8 (s % 4) .. +7,
-  // the order in which the key operand below holds them
   bf16x8 qv[8];
-  {
-    const uint16_t* qr = a.q + ((size_t)row * kH + ln) * kD + kHalf * hw;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qv[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                             qr + 32 * (4 * (s >> 2) + lg) + 8 * (s & 3)));
-  }
+  load_q<kHalf>(a.q, row, hw, ln, lg, qv);
   const int32_t* irow = a.idx ? a.idx + (size_t)row * a.K : nullptr;
-  // this work-group's steps: st0 .. st_end - 1 (the loads of the step after
-  // the last are harmless re-reads)
-  int cg, ws0, st0, st_end;
-  if (kSplit) {
-    // a fixed run of steps; a step whose keys are all absent adds nothing
-    cg = Cg;
-    ws0 = 0;
-    st0 = split * cps;
-    st_end = min(st0 + cps, Cg + Cw);
-  } else {
-    // the last position holding an entry (-1 entries select nothing); the
-    // entry numbers are read 512 at a time, all loads in flight together
-    int last = -1;
-    if (Cg > 0) {
-      for (int k0 = 0; k0 < a.K; k0 += 512) {
-        int32_t e[8];
+  // the last position holding an entry (-1 entries select nothing); the
+  // entry numbers are read 512 at a time, all loads in flight together
+  int last = -1;
+  if (Cg > 0) {
+    for (int k0 = 0; k0 < a.K; k0 += 512) {
+      int32_t e[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) e[u] = irow[min(k0 + 64 * u + lane, a.K - 1)];
+      for (int u = 0; u < 8; ++u) e[u] = irow[min(k0 + 64 * u + lane, a.K - 1)];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (e[u] >= 0 && k0 + 64 * u + lane < a.K) last = max(last, k0 + 64 * u + lane);
-      }
+      for (int u = 0; u < 8; ++u)
+        if (e[u] >= 0 && k0 + 64 * u + lane < a.K) last = max(last, k0 + 64 * u + lane);
     }
-    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
-    cg = __builtin_amdgcn_readfirstlane(Cg > 0 ? (last + kWK) / kWK : 0);
-    ws0 = __builtin_amdgcn_readfirstlane(wfirst / kWK);   // window steps before position 0
-    st0 = 0;
-    st_end = cg + (Cw > ws0 ? Cw - ws0 : 0);
   }
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  const int cg = __builtin_amdgcn_readfirstlane(Cg > 0 ? (last + kWK) / kWK : 0);
+  const int ws0 = __builtin_amdgcn_readfirstlane(wfirst / kWK);   // window steps before position 0
+  const int st_end = cg + (Cw > ws0 ? Cw - ws0 : 0);
 
   const uint8_t* lat_b = a.latent ? a.latent + 128 * hw : nullptr;   // indexed by pool row
   const uint8_t* sc_b = a.scale;
@@ -208,50 +419,6 @@ void k_attn(AttnArgs a, int32_t Cg, int32_t Cw, int32_t cps, const float* o_in,
   };
 
   uint8_t* my = tile[hw];
-  // dequantise set u (k-steps 4 i + d from block 4 i + lg of this half),
-  // accumulate the partial S^T and stage the bf16 rows for P . C
-  auto score_set = [&](auto gtag, int u, const u32x4& v0, const u32x4& v1, const u32x4& v2,
-                       const u32x4& v3, f32x4& s0, f32x4& s1) __attribute__((always_inline)) {
-    constexpr bool kGlobal = decltype(gtag)::value;
-    const int r = 16 * u + ln;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = 4 * i + lg;
-      u32x4 w[4];
-      if (kGlobal) {
-        const u32x4& c = i ? v1 : v0;
-        const uint32_t sw = hw ? v2[2 + i] : v2[i];          // scale bytes of blocks 8 hw + 4 i ..
-        const uint32_t scb = (sw >> (8 * lg)) & 0xFFu;
-        const float scale = __uint_as_float(scb ? (scb << 23) : 0x00400000u);   // 2^(scb-127)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          w[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 0));
-          w[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 1));
-          w[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 2));
-          w[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], scale, 3));
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const u32x4& c = i ? (d < 2 ? v2 : v3) : (d < 2 ? v0 : v1);
-          const uint32_t x0 = c[2 * (d & 1)], x1 = c[2 * (d & 1) + 1];
-          w[d][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.0f, false));
-          w[d][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.0f, true));
-          w[d][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.0f, false));
-          w[d][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.0f, true));
-        }
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, w[d]);
-        if (d & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[4 * i + d], s1, 0, 0, 0);
-        else       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[4 * i + d], s0, 0, 0, 0);
-        *reinterpret_cast<u32x4*>(my + tile_off(r, 64 * blk + 16 * d)) = w[d];
-      }
-    }
-  };
-
-  // O[j][i]: head 4 lg + i, dim 256 hw + 16 j + ln
   f32x4 O[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -261,94 +428,32 @@ void k_attn(AttnArgs a, int32_t Cg, int32_t Cw, int32_t cps, const float* o_in,
   u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
   int32_t ea = -1, eb = -1;
   bool oka = false, okb = false;
-  if (st0 < st_end) {
-    oka = load(st0, 0, entry(st0, 0), a0, a1, a2, a3);
-    okb = load(st0, 1, entry(st0, 1), b0, b1, b2, b3);
-    ea = entry(st0 + 1, 0);
-    eb = entry(st0 + 1, 1);
+  if (st_end > 0) {
+    oka = load(0, 0, entry(0, 0), a0, a1, a2, a3);
+    okb = load(0, 1, entry(0, 1), b0, b1, b2, b3);
+    ea = entry(1, 0);
+    eb = entry(1, 1);
   }
-  // transposed-read rows: key 4 lg + ln / 4 (+ 16 for set 1), dims + 4 (ln % 4)
-  const int tr0 = 4 * lg + (ln >> 2), tr1 = tr0 + 16;
-
-  // one step's scores: dequantise and score both sets (the next step's loads
-  // issued as each set's registers free up), exchange the halves' partial
-  // sums; x0 / x1 = full logits of keys 4 lg + e (+16), head ln, -inf when absent
+  // one step's logits: dequantise and score both sets (the next step's loads
+  // issued as each set's registers free up), then exchange the halves' sums
   auto step_scores = [&](int st, f32x4& x0, f32x4& x1) __attribute__((always_inline)) -> float {
     f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
     const uint64_t va = __ballot(oka), vb = __ballot(okb);
     const bool global = st < cg;
     __asm__ volatile("" ::: "memory");       // this step's staging after the last step's reads
-    if (global) score_set(std::true_type{}, 0, a0, a1, a2, a3, sa0, sa1);
-    else        score_set(std::false_type{}, 0, a0, a1, a2, a3, sa0, sa1);
+    if (global) score_set<true, kHalf>(my, qv, hw, ln, lg, 0, a0, a1, a2, a3, sa0, sa1);
+    else        score_set<false, kHalf>(my, qv, hw, ln, lg, 0, a0, a1, a2, a3, sa0, sa1);
     oka = load(st + 1, 0, ea, a0, a1, a2, a3);
     ea = entry(st + 2, 0);
-    if (global) score_set(std::true_type{}, 1, b0, b1, b2, b3, sb0, sb1);
-    else        score_set(std::false_type{}, 1, b0, b1, b2, b3, sb0, sb1);
+    if (global) score_set<true, kHalf>(my, qv, hw, ln, lg, 1, b0, b1, b2, b3, sb0, sb1);
+    else        score_set<false, kHalf>(my, qv, hw, ln, lg, 1, b0, b1, b2, b3, sb0, sb1);
     okb = load(st + 1, 1, eb, b0, b1, b2, b3);
     eb = entry(st + 2, 1);
-    {  // the two halves' partial sums, added in a fixed order by both waves
-      float* xw = &xs[st & 1][hw][lane * 8];
-      *reinterpret_cast<f32x4*>(xw) = sa0 + sa1;
-      *reinterpret_cast<f32x4*>(xw + 4) = sb0 + sb1;
-    }
-    __syncthreads();
-    const float* x0p = &xs[st & 1][0][lane * 8];
-    const float* x1p = &xs[st & 1][1][lane * 8];
-    x0 = *reinterpret_cast<const f32x4*>(x0p) + *reinterpret_cast<const f32x4*>(x1p);
-    x1 = *reinterpret_cast<const f32x4*>(x0p + 4) + *reinterpret_cast<const f32x4*>(x1p + 4);
-    float mc = -INFINITY;
-    const uint32_t ba = (uint32_t)(va >> (4 * lg)), bb = (uint32_t)(vb >> (4 * lg));   // keys 4 lg ..
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x0[e] = (ba >> e) & 1u ? x0[e] : -INFINITY;
-      x1[e] = (bb >> e) & 1u ? x1[e] : -INFINITY;
-      mc = fmaxf(mc, fmaxf(x0[e], x1[e]));
-    }
-    return rows_max(mc);
+    return exchange_logits<2>(xs[st & 1], hw, lane, lg, sa0 + sa1, sb0 + sb1, va, vb, x0, x1);
   };
-  // one step's P . C on this half's dims, with the current reference
-  auto step_pv = [&](const f32x4& x0, const f32x4& x1) __attribute__((always_inline)) {
-    // absent keys are -inf: exp gives 0 (a reference of -inf only occurs while
-    // every key so far is absent, and then 0 stands in for it)
-    const float mr = m_run == -INFINITY ? 0.f : m_run;
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[e] = __expf(x0[e] - mr);
-      p[4 + e] = __expf(x1[e] - mr);
-    }
-    // A operand: keys 4 lg + e of set 0, then of set 1 (the B reads below take
-    // the same keys); P = hi + lo in bf16
-    u32x4 ph, pl;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      l_run += p[2 * e] + p[2 * e + 1];
-      const bf16x2 hv = __builtin_convertvector((f32x2){p[2 * e], p[2 * e + 1]}, bf16x2);
-      const f32x2 hf = __builtin_convertvector(hv, f32x2);
-      const bf16x2 lv = __builtin_convertvector((f32x2){p[2 * e] - hf[0], p[2 * e + 1] - hf[1]}, bf16x2);
-      ph[e] = __builtin_bit_cast(uint32_t, hv);
-      pl[e] = __builtin_bit_cast(uint32_t, lv);
-    }
-    const bf16x8 ahi = __builtin_bit_cast(bf16x8, ph);
-    const bf16x8 alo = __builtin_bit_cast(bf16x8, pl);
-    __asm__ volatile("" ::: "memory");       // staging stores before the transposed reads
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int c = 32 * j + 8 * (ln & 3);
-      const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(my + tile_off(tr0, c)));
-      const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(my + tile_off(tr1, c)));
-      const u32x2 c0 = __builtin_bit_cast(u32x2, r0), c1 = __builtin_bit_cast(u32x2, r1);
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{c0[0], c0[1], c1[0], c1[1]});
-      O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, O[j], 0, 0, 0);
-      O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, O[j], 0, 0, 0);
-    }
-  };
-
-  // Steps run in an inner loop that touches O only with matrix instructions;
-  // a step whose logits exceed the reference by more than kLazy leaves the
-  // loop, and O is rescaled before that step's P . C.
-  int it = st0;
-  while (it < st_end) {
+  // transposed-read rows: key 4 lg + ln / 4 (+ 16 for set 1), dims + 4 (ln % 4)
+  const int tr0 = 4 * lg + (ln >> 2), tr1 = tr0 + 16;
+  for (int it = 0; it < st_end;) {
     f32x4 x0, x1;
     float mc = -INFINITY;
     bool raise = false;
@@ -357,90 +462,187 @@ void k_attn(AttnArgs a, int32_t Cg, int32_t Cw, int32_t cps, const float* o_in,
       mc = step_scores(it, x0, x1);
       raise = mc > m_run + kLazy;
       if (__ballot(raise) != 0) break;
-      step_pv(x0, x1);
+      pv_step<kHalf>(my, tr0, tr1, ln, x0, x1, m_run, l_run, O);
     }
     if (it >= st_end) break;
-    const float m_new = raise ? mc : m_run;
-    const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
-    l_run *= alpha;
-    m_run = m_new;
-    float al[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O[j][i] *= al[i];
-    step_pv(x0, x1);
+    raise_reference<16>(raise, mc, lg, O, m_run, l_run);
+    pv_step<kHalf>(my, tr0, tr1, ln, x0, x1, m_run, l_run, O);
     ++it;
+  }
+  store_final<kHalf>(a, row, hw, ln, lg, O, m_run, rows_sum(l_run), a.o_in, a.lse_in);
+}
+
+// Decode (one query row per sequence, B rows too few for the chip): grid
+// (rows, splits); work-group (row, s) runs steps s * cps .. s * cps + cps - 1
+// of its row (global steps first, Cg of them, then Cw window steps).  A
+// decode launch has fewer work-groups than the chip has compute units, so a
+// work-group's steps run back to back on one compute unit: four waves, one
+// per SIMD, each owning a quarter of the dims (its own dequantisation, S^T
+// partial and P . C; the partial logits summed through LDS), which halves
+// the serial chain of matrix instructions and LDS round trips per step
+// against two waves on halves.  Each wave first issues the transfers of up
+// to kDecDepth steps at once, direct global-to-LDS, into a ring of per-step
+// slots (its own quarter of every row), so a work-group waits on memory once
+// per kDecDepth steps (entry numbers, then rows) rather than once per step.
+// Slot layout, 16-byte chunks XOR-swizzled so that the 16 rows a set reads
+// fall on different banks: global step, chunk c of key k (the quarter's 64
+// E2M1 bytes) at 64 k + 16 (c ^ (k / 4 % 4)) and the key's 16 scale bytes at
+// kScaleOff + 16 k; window step, chunk c of row r (the quarter's 128 E4M3
+// bytes) at 128 r + 16 (c ^ (r % 8)).  kSplit: a partial per work-group,
+// merged by k_attn_combine; otherwise one work-group per row writes o and
+// lse.
+constexpr int kDecWaves = kD / kQuarter;       // 4
+constexpr int kDecDepth = 5;                   // steps in flight per wave
+constexpr int kSlot = kWK * kQuarter;          // 4 KiB: a window step of one wave
+constexpr int kScaleOff = kWK * kQuarter / 2;  // a global step's scales (after 32 x 64 bytes)
+
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_dst) {
+  // 16 bytes per lane; lane l's bytes land at lds_dst + 16 l (lds_dst uniform)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+template <bool kPaged, bool kSplit>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_attn_dec(AttnArgs a, int32_t Cg, int32_t Cw, int32_t cps) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kDecWaves][kDecDepth][kSlot];   // 80 KiB
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kDecWaves][kWK * 2 * kQuarter]; // 32 KiB
+  __shared__ __attribute__((aligned(16))) float xs[2][kDecWaves][64 * 8];             // 16 KiB
+  __shared__ int32_t ents[kDecWaves][kDecDepth * kWK];
+
+  const int row = blockIdx.x, split = blockIdx.y;
+  const int b = row;                         // one query row per sequence
+  const int p = threadIdx.x >> 6;            // this wave's quarter of the dims
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int st0 = split * cps;
+  const int st_end = min(st0 + cps, Cg + Cw);
+
+  bf16x8 qv[kQuarter / 32];
+  load_q<kQuarter>(a.q, row, p, ln, lg, qv);
+  const int32_t* irow = a.idx ? a.idx + (size_t)row * a.K : nullptr;
+  const uint8_t* lat_b = a.latent ? a.latent + (kQuarter / 2) * p : nullptr;
+  const uint8_t* swa_b = a.swa ? a.swa + (size_t)b * a.swa_rows * kD + kQuarter * p : nullptr;
+  uint8_t* my = tile[p];
+  uint8_t (*rg)[kSlot] = ring[p];
+  int32_t* en = ents[p];
+
+  f32x4 O[kQuarter / 16];
+#pragma unroll
+  for (int j = 0; j < kQuarter / 16; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  // transposed-read rows: key 4 lg + ln / 4 (+ 16 for set 1), dims + 4 (ln % 4)
+  const int tr0 = 4 * lg + (ln >> 2), tr1 = tr0 + 16;
+
+  for (int bs = st0; bs < st_end; bs += kDecDepth) {
+    const int nb = min(kDecDepth, st_end - bs);
+    const int ng = max(0, min(bs + nb, Cg) - bs);   // global steps of the batch
+    // the batch's entry numbers (-1 past K), this wave's copy
+    int32_t ev[(kDecDepth * kWK + 63) / 64];
+#pragma unroll
+    for (int m = 0; m < (kDecDepth * kWK + 63) / 64; ++m) {
+      const int t = lane + 64 * m;
+      const int kpos = bs * kWK + t;
+      ev[m] = t < ng * kWK && kpos < a.K ? irow[kpos] : -1;
+    }
+#pragma unroll
+    for (int m = 0; m < (kDecDepth * kWK + 63) / 64; ++m)
+      if (lane + 64 * m < kDecDepth * kWK) en[lane + 64 * m] = ev[m];
+    for (int s = 0; s < ng; ++s) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int k = 16 * j + (lane >> 2);
+        const int c = (lane & 3) ^ ((k >> 2) & 3);
+        const int32_t e = en[s * kWK + k];
+        const int32_t ec = e >= 0 ? e : 0;                     // entry 0 exists
+        const int64_t pr = kPaged ? pool_row(a.map, b, ec, a.M) : (int64_t)b * a.M + ec;
+        dma16(lat_b + (size_t)pr * kLatRow + 16 * c, &rg[s][1024 * j]);
+      }
+      const int k = lane & 31;
+      const int32_t e = en[s * kWK + k];
+      const int32_t ec = e >= 0 ? e : 0;
+      const int64_t pr = kPaged ? pool_row(a.map, b, ec, a.M) : (int64_t)b * a.M + ec;
+      dma16(a.scale + (size_t)pr * kScaleRow, &rg[s][kScaleOff]);
+    }
+    // the window rows (issued after the entry numbers were waited for: a
+    // wait for a load counts every transfer issued before it)
+    for (int s = ng; s < nb; ++s) {
+      const int wr0 = (bs + s - Cg) * kWK;
+#pragma unroll
+      for (int j = 0; j < kSlot / 1024; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const int wr = min(wr0 + r, a.W - 1);
+        dma16(swa_b + (size_t)wr * kD + 16 * c, &rg[s][1024 * j]);
+      }
+    }
+    // every transfer of the batch (and q) has landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+    auto step_scores = [&](int it, f32x4& x0, f32x4& x1) __attribute__((always_inline)) -> float {
+      const uint8_t* sl = rg[it - bs];
+      f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
+      bool oka, okb;
+      __asm__ volatile("" ::: "memory");     // this step's staging after the last step's reads
+      if (it < Cg) {
+        const int s = it - bs;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int k = 16 * u + ln;
+          const u32x4 c0 = *reinterpret_cast<const u32x4*>(sl + 64 * k + ((lg ^ ((k >> 2) & 3)) << 4));
+          const u32x4 sc = *reinterpret_cast<const u32x4*>(sl + kScaleOff + 16 * k);
+          const bool ok = en[s * kWK + k] >= 0;
+          if (u == 0) {
+            oka = ok;
+            score_set<true, kQuarter>(my, qv, p, ln, lg, 0, c0, c0, sc, sc, sa0, sa1);
+          } else {
+            okb = ok;
+            score_set<true, kQuarter>(my, qv, p, ln, lg, 1, c0, c0, sc, sc, sb0, sb1);
+          }
+        }
+      } else {
+        const int wr0 = (it - Cg) * kWK;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 16 * u + ln, x = r & 7;
+          const uint8_t* rp = sl + 128 * r;
+          const u32x4 c0 = *reinterpret_cast<const u32x4*>(rp + (((2 * lg) ^ x) << 4));
+          const u32x4 c1 = *reinterpret_cast<const u32x4*>(rp + (((2 * lg + 1) ^ x) << 4));
+          const bool ok = wr0 + r < a.W;
+          if (u == 0) {
+            oka = ok;
+            score_set<false, kQuarter>(my, qv, p, ln, lg, 0, c0, c1, c0, c1, sa0, sa1);
+          } else {
+            okb = ok;
+            score_set<false, kQuarter>(my, qv, p, ln, lg, 1, c0, c1, c0, c1, sb0, sb1);
+          }
+        }
+      }
+      return exchange_logits<kDecWaves>(xs[it & 1], p, lane, lg, sa0 + sa1, sb0 + sb1,
+                                        __ballot(oka), __ballot(okb), x0, x1);
+    };
+    for (int it = bs; it < bs + nb;) {
+      f32x4 x0, x1;
+      float mc = -INFINITY;
+      bool raise = false;
+#pragma unroll 1
+      for (; it < bs + nb; ++it) {
+        mc = step_scores(it, x0, x1);
+        raise = mc > m_run + kLazy;
+        if (__ballot(raise) != 0) break;
+        pv_step<kQuarter>(my, tr0, tr1, ln, x0, x1, m_run, l_run, O);
+      }
+      if (it >= bs + nb) break;
+      raise_reference<kQuarter / 16>(raise, mc, lg, O, m_run, l_run);
+      pv_step<kQuarter>(my, tr0, tr1, ln, x0, x1, m_run, l_run, O);
+      ++it;
+    }
   }
 
   const float L = rows_sum(l_run);   // head ln's sum (relative to m_run)
-  if (kSplit) {
-    // this split's partial: O unnormalised (relative to the reference of its
-    // head), the reference and the sum per head
-    const size_t ps = (size_t)row * gridDim.y + split;
-    float* op = a.opart + ps * kH * kD + kHalf * hw;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) op[(size_t)(4 * lg + i) * kD + 16 * j + ln] = O[j][i];
-    if (hw == 0 && lg == 0) {
-      a.ml[(ps * kH + ln) * 2] = m_run;
-      a.ml[(ps * kH + ln) * 2 + 1] = L;
-    }
-    return;
-  }
-  // per head: lse, merge with an incoming result; lane (ln, lg) writes dims
-  // 256 hw + 16 j + ln of heads 4 lg + i
-  const float lse_h = L > 0.f ? m_run + logf(L) : -INFINITY;   // head ln
-  float wself[4], win[4], lse4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float Li = __shfl(L, 4 * lg + i, 64);
-    float lse = __shfl(lse_h, 4 * lg + i, 64);
-    wself[i] = Li > 0.f ? 1.f / Li : 0.f;
-    win[i] = 0.f;
-    if (lse_in) {   // one softmax over both key sets
-      const float li = lse_in[(size_t)row * kH + 4 * lg + i];
-      const float mx = fmaxf(li, lse);
-      if (mx != -INFINITY) {
-        const float e1 = li == -INFINITY ? 0.f : __expf(li - mx);
-        const float e2 = lse == -INFINITY ? 0.f : __expf(lse - mx);
-        const float tot = e1 + e2;
-        win[i] = e1 / tot;
-        wself[i] *= e2 / tot;
-        lse = mx + logf(tot);
-      }
-    }
-    lse4[i] = lse;
-  }
-  // the incoming lse is read by both waves before wave 0 overwrites it
-  if (lse_in) __syncthreads();
-  float* orow = a.o + (size_t)row * kH * kD + kHalf * hw;
-  if (lse_in) {
-    // the incoming rows may be the output rows: every value this lane merges
-    // is read before any is written (one round trip, not one per value)
-    const float* inrow = o_in + (size_t)row * kH * kD + kHalf * hw;
-    f32x4 X[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) X[j][i] = inrow[(size_t)(4 * lg + i) * kD + 16 * j + ln];
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        orow[(size_t)(4 * lg + i) * kD + 16 * j + ln] = fmaf(win[i], X[j][i], O[j][i] * wself[i]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) orow[(size_t)(4 * lg + i) * kD + 16 * j + ln] = O[j][i] * wself[i];
-  }
-  if (hw == 0 && ln < 4)
-    a.lse[(size_t)row * kH + 4 * lg + ln] = ln == 0 ? lse4[0] : (ln == 1 ? lse4[1] : (ln == 2 ? lse4[2] : lse4[3]));
+  if (kSplit) store_partial<kQuarter>(a, row, split, gridDim.y, p, ln, lg, O, m_run, L);
+  else        store_final<kQuarter>(a, row, p, ln, lg, O, m_run, L, a.o_in, a.lse_in);
 }
 
 // One work-group (128 lanes x 4 dims) per (head, query row).  The partial
@@ -545,29 +747,29 @@ int32_t attn_max_splits(int64_t rows, int32_t steps) {
 }
 
 AttnPlan attn_plan(int64_t rows, int32_t steps) {
-  // Many rows fill the chip with one work-group per row.  Fewer rows (decode)
-  // cut each row into S runs of cps steps, one work-group each, then merge
-  // the partials.  A work-group mostly waits on memory (its q, its entry
-  // numbers, then the gathered rows) and a compute unit serves only a few
-  // tens of GB/s, so the best launch spreads the rows over every compute unit
-  // with few steps per work-group, while each split adds a 32 KiB partial to
-  // write and merge.  The estimate (microseconds, fitted to measured decode
-  // launches) picks S.
+  // Many rows fill the chip with one work-group per row (k_attn).  Fewer rows
+  // (decode) cut each row into S runs of cps steps, one k_attn_dec
+  // work-group each (one per compute unit: its LDS), then merge the partials.
+  // A work-group waits for its entry numbers, then for its gathered rows
+  // (once per kDecDepth steps), then computes its steps (about 1.3 us each,
+  // a chain of LDS round trips, matrix instructions and a barrier); each
+  // split adds a 32 KiB partial to write and merge.  The estimate
+  // (microseconds, fitted to timestamps taken inside decode launches) picks S.
   if (steps <= 0 || rows >= kAttnSplitRows) return AttnPlan{1, 0};
   const int32_t smax = attn_max_splits(rows, steps);
-  AttnPlan best{1, 0};
+  AttnPlan best{1, steps};
   double best_cost = 1e30;
-  for (int32_t cps = 1; cps <= steps; ++cps) {
-    const int32_t S = (steps + cps - 1) / cps;
-    if (S > smax || (S - 1) * cps >= steps) continue;
+  for (int32_t S = 1; S <= smax; ++S) {
+    const int32_t cps = (steps + S - 1) / S;
+    if ((S - 1) * cps >= steps) continue;          // every split holds a step
     const double groups = (double)(rows * S);
-    const double per_cu = groups / 256.0;          // work-groups per compute unit
-    const double rounds = per_cu <= 4.0 ? 1.0 : per_cu / 4.0;
-    const double cost = 2.0 + (per_cu > 1.0 ? per_cu : 1.0) * 0.6 + rounds * 1.8 * cps +
-                        (S > 1 ? 2.0 + groups * 0.02 : 0.0);
+    const double rounds = (double)(((int64_t)groups + 255) / 256);
+    const double batches = (double)((cps + kDecDepth - 1) / kDecDepth);
+    const double cost = rounds * (2.0 + 0.8 * batches + 1.35 * cps) +
+                        (S > 1 ? 3.0 + groups * 0.004 : 0.0);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
-      best = S > 1 ? AttnPlan{S, cps} : AttnPlan{1, 0};
+      best = AttnPlan{S, cps};
     }
   }
   return best;
@@ -578,26 +780,31 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
   const int32_t Cg = a.K > 0 && a.latent ? (a.K + kWK - 1) / kWK : 0;
   const int32_t Cw = a.W > 0 ? (a.W + kWK - 1) / kWK : 0;
   const int32_t S = plan.splits;
-  if (S > 1) {
-    // whole steps per split
-    if (S > kAttnMaxSplits || plan.cps <= 0 || (Cg + Cw + plan.cps - 1) / plan.cps != S ||
-        !a.opart || !a.ml)
+  if (plan.cps > 0) {
+    // decode: whole steps per split, one query row per sequence
+    if (S < 1 || S > kAttnMaxSplits || (Cg + Cw + plan.cps - 1) / plan.cps != S ||
+        (S - 1) * plan.cps >= Cg + Cw || a.Q != 1 || a.pos0 >= 0 ||
+        (S > 1 && (!a.opart || !a.ml)))
       return hipErrorInvalidValue;
     const dim3 grid((unsigned)a.rows, (unsigned)S);
-    if (a.map.pages)
-      k_attn<true, true><<<grid, dim3(128), 0, s>>>(a, Cg, Cw, plan.cps, nullptr, nullptr);
-    else
-      k_attn<false, true><<<grid, dim3(128), 0, s>>>(a, Cg, Cw, plan.cps, nullptr, nullptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    k_attn_combine<<<dim3((unsigned)kH, (unsigned)a.rows), dim3(kCombThreads), 0, s>>>(
-        a.opart, a.ml, S, a.o_in, a.lse_in, a.o, a.lse);
+    if (S > 1) {
+      if (a.map.pages) k_attn_dec<true, true><<<grid, dim3(64 * kDecWaves), 0, s>>>(a, Cg, Cw, plan.cps);
+      else             k_attn_dec<false, true><<<grid, dim3(64 * kDecWaves), 0, s>>>(a, Cg, Cw, plan.cps);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      k_attn_combine<<<dim3((unsigned)kH, (unsigned)a.rows), dim3(kCombThreads), 0, s>>>(
+          a.opart, a.ml, S, a.o_in, a.lse_in, a.o, a.lse);
+    } else {
+      if (a.map.pages) k_attn_dec<true, false><<<grid, dim3(64 * kDecWaves), 0, s>>>(a, Cg, Cw, plan.cps);
+      else             k_attn_dec<false, false><<<grid, dim3(64 * kDecWaves), 0, s>>>(a, Cg, Cw, plan.cps);
+    }
     return hipGetLastError();
   }
+  if (S != 1) return hipErrorInvalidValue;
   if (a.map.pages)
-    k_attn<true, false><<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw, 0, a.o_in, a.lse_in);
+    k_attn<true><<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw);
   else
-    k_attn<false, false><<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw, 0, a.o_in, a.lse_in);
+    k_attn<false><<<dim3((unsigned)a.rows), dim3(128), 0, s>>>(a, Cg, Cw);
   return hipGetLastError();
 }
 

@@ -250,7 +250,7 @@ int32_t attn_steps(int32_t K, int32_t W);
 int32_t attn_max_splits(int64_t rows, int32_t steps);
 struct AttnPlan {
   int32_t splits;   // work-groups per row (1: one, writing o and lse itself)
-  int32_t cps;      // steps per split work-group (splits > 1)
+  int32_t cps;      // decode: steps per work-group (0: the one-work-group-per-row kernel)
 };
 // Decode: splits per row from an estimate of the launch (splits > 1 needs the
 // workspace of attn_ws_bytes).  AttnPlan{1, 0}: one work-group per row, no
