@@ -52,8 +52,8 @@ def test_workspace_bytes():
     part = 16 * 512 * 4
     assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 16) >= 32 * 2 * part
     assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 8) == 0
-    # four window steps per row: one work-group per row, no partials
-    assert ws(C.CSA2_OP_SWA_MERGE, 32, 1, 0, 0, 0, 128, 16) == 256
+    # at most one partial per step (four window steps per row)
+    assert 256 <= ws(C.CSA2_OP_SWA_MERGE, 32, 1, 0, 0, 0, 128, 16) <= 32 * 4 * (part + 128) + 512
     assert ws(C.CSA2_OP_SPARSE_ATTN, 1, 2048, 65536, 512, 0, 0, 16) == 256   # prefill: none
     # sized by the splits the launch uses, not by one split per step
     assert ws(C.CSA2_OP_SPARSE_ATTN, 32, 1, 32768, 512, 0, 0, 16) < 32 * 16 * part
