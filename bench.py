@@ -490,6 +490,37 @@ def measure_paged(ci: int, steps: int, warmup: int, page_log2: int = 8):
                 step_hbm_gbs=algorithmic_bytes(cfg)["total"] / (ms * 1e-3) / 1e9)
 
 
+def measure_fused_select(ci: int, steps: int, warmup: int):
+    """The Full layer's index work at a decode workload's shape, two ways: the
+    scan writing the scores then the Top-K select (what csa2_decode_layers
+    runs), and the fused single pass of csa2_score_topk (no score round trip)."""
+    import torch
+    from fp4_kv_cache_score_amd import _lib as C
+    from fp4_kv_cache_score_amd import synth
+    from fp4_kv_cache_score_amd.configs import CONFIGS
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[ci]
+    if C.csa2_workspace_bytes(C.CSA2_OP_SCORE_TOPK, cfg.B, 1, cfg.M, cfg.K, 0, 0, 0) == 0:
+        return None
+    dc = DeviceCase(synth.make_case(cfg))
+    d = dc.layers[0]
+    scores = torch.empty((cfg.B, cfg.M), dtype=torch.float32, device="cuda")
+    nb = C.csa2_workspace_bytes(C.CSA2_OP_TOPK, cfg.B, 1, cfg.M, cfg.K, 0, 0, 0)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((cfg.B, cfg.K), dtype=torch.int32, device="cuda")
+
+    def two_pass():
+        C.csa2_index_score(dc.pool, d["q_idx"], d["w_idx"], 1, -1, 1, None, 0, scores, None)
+        C.csa2_topk(scores, cfg.B, cfg.M, None, None, cfg.K, idx, ws, nb)
+
+    two = _time_calls(two_pass, steps, warmup)
+    fused = _time_calls(lambda: dc.score_topk(0), steps, warmup)
+    del dc
+    torch.cuda.empty_cache()
+    return dict(two_pass_ms=two, fused_ms=fused,
+                note="csa2_decode_layers runs the two-pass form (the faster one here)")
+
+
 def measure_host_tier(ci: int, reps: int = 5):
     """Host tier at a decode workload's pool shape: one sequence's whole pool
     (M entries x 784 B) restored from / offloaded to page-locked host memory,
@@ -673,6 +704,11 @@ def main():
     extra["paged_" + cfg.name] = pg
     log("paged pool (pages of %d entries): %.3f ms/step against %.3f contiguous (warm)" % (
         pg["page_entries"], pg["ms_per_step"], head["warm_ms"]))
+    fz = measure_fused_select(args.config, args.steps, args.warmup)
+    if fz:
+        extra["fused_score_topk_" + cfg.name] = fz
+        log("Full-layer index work: scan + select %.3f ms, fused single pass %.3f ms" % (
+            fz["two_pass_ms"], fz["fused_ms"]))
     ht = measure_host_tier(args.config)
     extra["host_tier_" + cfg.name] = ht
     log("host tier: restore %.1f GB/s, offload %.1f GB/s; decode %.3f ms alone, %.3f ms beside "

@@ -22,9 +22,10 @@ CSA2_ERR_SCHEDULE, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP, CSA2_ERR_SCRATCH = 4, 5, 6,
 CSA2_NOALLOC_SCRATCH_BYTES = 64 << 20
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
 CSA2_OP_TOPK, CSA2_OP_SPARSE_ATTN, CSA2_OP_SWA_MERGE, CSA2_OP_DECODE_LAYERS = 0, 1, 2, 3
-CSA2_OP_PREFILL_LAYERS = 4
+CSA2_OP_PREFILL_LAYERS, CSA2_OP_SCORE_TOPK = 4, 5
 
-EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
+EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_score_topk", "csa2_sparse_attn",
+           "csa2_swa_merge",
            "csa2_pool_append", "csa2_swa_append", "csa2_pool_restore", "csa2_pool_offload",
            "csa2_swa_restore", "csa2_swa_offload",
            "csa2_decode_layers", "csa2_decode_layer", "csa2_decode_layers_noalloc",
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
                                        c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.csa2_swa_merge.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                      c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.csa2_score_topk.argtypes = [POINTER(csa2_pool), c_void_p, c_void_p, c_int32, c_void_p,
+                                      c_void_p, c_size_t, c_void_p]
         L.csa2_decode_layers.argtypes = [POINTER(csa2_pool), POINTER(csa2_layer), c_int32,
                                          c_int32, c_int32, c_int32, c_int32, POINTER(c_int32),
                                          c_void_p, c_size_t, c_void_p]
@@ -99,7 +102,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_status_string.restype = c_char_p
         L.csa2_version.argtypes = []
         L.csa2_version.restype = c_char_p
-        for fn in ("csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_swa_merge",
+        for fn in ("csa2_index_score", "csa2_topk", "csa2_score_topk", "csa2_sparse_attn",
+                   "csa2_swa_merge",
                    "csa2_decode_layers", "csa2_decode_layer", "csa2_decode_layers_noalloc",
                    "csa2_prefill_layers", "csa2_pool_append",
                    "csa2_swa_append", "csa2_pool_restore", "csa2_pool_offload",
@@ -193,6 +197,13 @@ def csa2_swa_merge(q, B: int, Q: int, H: int, D: int, swa, W: int, o, lse, ws,
     st = lib().csa2_swa_merge(_p(q), B, Q, H, D, _p(swa), W, _p(o), _p(lse), _p(ws),
                               ws_bytes, _s(stream))
     return _check("csa2_swa_merge", st, raise_on_error)
+
+
+def csa2_score_topk(pool: csa2_pool, q_idx, w_idx, K: int, idx, ws, ws_bytes: int, stream=None,
+                    raise_on_error=True) -> int:
+    st = lib().csa2_score_topk(ctypes.byref(pool), _p(q_idx), _p(w_idx), K, _p(idx), _p(ws),
+                               ws_bytes, _s(stream))
+    return _check("csa2_score_topk", st, raise_on_error)
 
 
 def csa2_decode_layers(pool: csa2_pool, layers, H: int, K: int, P: int, W: int, ws,

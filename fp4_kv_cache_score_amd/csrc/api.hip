@@ -73,7 +73,10 @@ size_t topk_slice_ws_max(int64_t R, int64_t Nmax, int64_t K) {
 // How a decode step selects: the sliced select for the Top-K (and for the
 // Top-P of a hierarchical Full layer) when it takes the shape, otherwise
 // the one-work-group row select or the multi-work-group select (`big`),
-// whose histogram and counters live in the workspace.
+// whose histogram and counters live in the workspace.  (The fused score ->
+// Top-K of csa2_score_topk is not used here: on the decode shapes its one
+// 1024-thread work-group per compute unit streams the keys slower than the
+// scan kernel's many small ones, more than the slice launch it saves.)
 struct DecodeSelect {
   bool sliced_k, sliced_p, big;
 };
@@ -243,6 +246,9 @@ size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t M, int32_t K, 
           W < 0 || W > kMaxW || H != kH)
         return 0;
       return decode_ws_bytes(B, M, K, P, W);
+    case CSA2_OP_SCORE_TOPK:
+      if (K <= 0 || K > kMaxK || M > kMaxTopkN || !score_topk_slicing(B, M, K).taken) return 0;
+      return score_topk_ws_bytes(B, M, K);
   }
   return 0;
 }
@@ -291,6 +297,22 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N, const int32_t* 
   st = hip_status(launch_topk_hist(scores, R, N, n_valid, N, t.hist, stream));
   if (st != CSA2_OK) return st;
   return hip_status(launch_topk_select(scores, R, N, n_valid, N, cand, K, idx, t, false, stream));
+}
+
+csa2_status csa2_score_topk(const csa2_pool* pool, const uint8_t* q_idx, const float* w_idx,
+                            int32_t K, int32_t* idx, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  csa2_status st = check_pool(pool);
+  if (st != CSA2_OK) return st;
+  if (!q_idx || !w_idx || !idx) return CSA2_ERR_NULL;
+  if (pool->B > kMaxRows || pool->M > kMaxTopkN || K <= 0 || K > kMaxK ||
+      !score_topk_slicing(pool->B, pool->M, K).taken)
+    return CSA2_ERR_SHAPE;
+  if (!al16(q_idx) || !al4(w_idx) || !al4(idx)) return CSA2_ERR_ALIGN;
+  if (!ws || ws_bytes < score_topk_ws_bytes(pool->B, pool->M, K)) return CSA2_ERR_WORKSPACE;
+  if (!al16(ws)) return CSA2_ERR_ALIGN;
+  return hip_status(launch_score_topk(pool->idx_key, pool->B, pool->M, q_idx, w_idx, pool->len,
+                                      pool_map(pool), K, idx, ws, stream));
 }
 
 // Attention of `rows` query rows in the workspace of a stand-alone call:

@@ -147,6 +147,26 @@ inline size_t topk_slice_ws_bytes(int64_t R, int64_t N, int64_t K) {
   return s.S > 0 ? align256((size_t)(R * s.S * s.slots * 4)) * 2 : 0;
 }
 
+// Fused score -> Top-K of flat rows (one query row per sequence): slices of
+// kScoreSlice entries scored and filtered in LDS, then the final select,
+// which must hold every slice's keepers.
+constexpr int kScoreSlice = 4096;
+inline TopkSlicing score_topk_slicing(int64_t R, int64_t N, int64_t K) {
+  TopkSlicing t{false, 0, 4, 0};
+  if (R <= 0 || N <= 0 || K <= 0) return t;
+  const int64_t S = (N + kScoreSlice - 1) / kScoreSlice;
+  const int64_t slots = topk_slot_count(K);
+  if (S * slots > kFinalMaxN) return t;
+  t.taken = true;
+  t.S = (int32_t)S;
+  t.slots = (int32_t)slots;
+  return t;
+}
+inline size_t score_topk_ws_bytes(int64_t R, int64_t N, int64_t K) {
+  const TopkSlicing s = score_topk_slicing(R, N, K);
+  return s.taken ? align256((size_t)(R * s.S * s.slots * 4)) * 2 : 0;
+}
+
 inline size_t topk_ws_bytes(int64_t R, int64_t N, int64_t K) {
   int64_t cap = topk_cap(R, N);
   return align256(R * kHistBins * 4) + align256(R * kCounterWords * 4) +
@@ -194,6 +214,12 @@ hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
 hipError_t launch_topk_sliced(const float* scores, int32_t R, int32_t N,
                               const int32_t* n_valid, int32_t n_all, const int32_t* cand,
                               int32_t K, int32_t* out, void* ws, hipStream_t s);
+// Fused score -> Top-K of B flat rows (score_topk_slicing(B, M, K).taken):
+// the indexer score of every visible entry and the row's Top-K, without
+// writing the scores; ws holds score_topk_ws_bytes.
+hipError_t launch_score_topk(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
+                             const float* w_idx, const int32_t* len, const PoolMap& map,
+                             int32_t K, int32_t* out, void* ws, hipStream_t s);
 hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
                             const int32_t* n_valid, int32_t n_all,
                             uint32_t* hist, hipStream_t s);

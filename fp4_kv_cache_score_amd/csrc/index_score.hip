@@ -5,30 +5,23 @@
 // 437x", paragraph on the three operating modes):
 //   s_j = sum_h w_h * ReLU(sum_i qI[h][i] * kI[j][h][i]),  8 heads x 64 E4M3.
 //
-// Work split: a pool entry's 512-byte key row is read by 32 lanes with one
-// 16-byte load each (two entries per wave64 load), so every wave load is a
-// fully coalesced 1 KiB; each lane issues them in batches of 4, the next
-// batch in flight while the current one is computed.  Lane
-// (sub = lane & 31) owns bytes [16*sub, 16*sub+16) of the row, i.e. indexer
-// head sub/4 and 16 of its 64 dims.  The FP8 x FP8
-// products are exact in fp32; each lane accumulates its 16 products with
-// fmaf, a 4-lane butterfly completes the head dot, then ReLU, the head weight
-// and an 8-head butterfly give the score.  Every lane holds the full query
-// slice it needs in registers, so HBM sees each key byte exactly once.
+// Work split (the arithmetic is in index_math.h): a pool entry's 512-byte
+// key row is read by 32 lanes with one 16-byte load each (two entries per
+// wave64 load), so every wave load is a fully coalesced 1 KiB; each lane
+// issues them in batches of 4, the next batch in flight while the current one
+// is computed.  Every lane holds the full query slice it needs in registers,
+// so HBM sees each key byte exactly once.
 // Optionally the kernel adds the scores' top-12-bit order keys into a
 // per-row histogram (the first radix digit of the Top-K select), built in
 // LDS per work-group and flushed with one atomic per non-empty bin.
 #include "csa2_internal.h"
+#include "index_math.h"
 
 namespace csa2 {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;                        // 16-byte loads per lane and batch (two batches in flight)
-
-__device__ __forceinline__ float bfly_add(float v, int m) {
-  return v + __shfl_xor(v, m, 64);
-}
 
 // EPW pool entries per wave, 4 waves per work-group.  With a candidate list
 // the work-group first copies its EPW * 4 entry numbers to LDS (one round
@@ -74,18 +67,7 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
   }
   float qf[16];
   const uint8_t* qsrc = q_idx + (size_t)row * kKeyRow + sub * 16;
-  {
-    const u32x4 qv = *reinterpret_cast<const u32x4*>(qsrc);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)qv[d], false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)qv[d], true);
-      qf[4 * d + 0] = lo.x;
-      qf[4 * d + 1] = lo.y;
-      qf[4 * d + 2] = hi.x;
-      qf[4 * d + 3] = hi.y;
-    }
-  }
+  load_q_slice(qsrc, qf);
   const float wh = w_idx[(size_t)row * kHI + head];
 
   if (kHist)
@@ -132,22 +114,7 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
     __builtin_amdgcn_sched_barrier(0);     // the next batch issues before this one is used
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      float acc = 0.f;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[cb][u][d], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[cb][u][d], true);
-        acc = fmaf(lo.x, qf[4 * d + 0], acc);
-        acc = fmaf(lo.y, qf[4 * d + 1], acc);
-        acc = fmaf(hi.x, qf[4 * d + 2], acc);
-        acc = fmaf(hi.y, qf[4 * d + 3], acc);
-      }
-      acc = bfly_add(acc, 1);
-      acc = bfly_add(acc, 2);
-      float r = acc > 0.f ? acc * wh : 0.f;
-      r = bfly_add(r, 4);
-      r = bfly_add(r, 8);
-      r = bfly_add(r, 16);
+      const float r = entry_score(v[cb][u], qf, wh);
       const int64_t p = g0 + wofs + it * (2 * kUnroll) + 2 * u + half;
       if (sub == 0 && p < N) {
         srow[p] = ok[cb][u] ? r : -INFINITY;

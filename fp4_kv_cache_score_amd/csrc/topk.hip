@@ -33,6 +33,7 @@
 // Ties, -0 vs +0, rows with fewer than K valid positions are handled exactly;
 // the result is deterministic.
 #include "csa2_internal.h"
+#include "index_math.h"
 
 namespace csa2 {
 namespace {
@@ -1232,6 +1233,102 @@ void k_topk_slice(const float* __restrict__ scores, int32_t N, const int32_t* __
   for (uint32_t i = kept + threadIdx.x; i < (uint32_t)slots; i += kFinalThreads) ckey[base + i] = 0u;
 }
 
+// Fused score -> Top-K (flat rows): work-group (s, r) scores slice s of row
+// r (entries 4096 s .. 4096 s + 4095, one query row per sequence) straight
+// into LDS and keeps that slice's superset of its K largest, as k_topk_slice
+// does from scores in memory; k_topk_final then selects the row's Top-K from
+// the keepers.  The scores never go to memory, and the slice select's launch
+// and its read of them go away.  16 waves of 256 entries each, streamed as
+// the scan kernel streams them (same lanes, same arithmetic: the same float
+// for every entry), with batches of kFusedUnroll loads per lane, the next
+// batch in flight while one is scored.
+constexpr int kFusedSlice = kScoreSlice;                  // entries per work-group
+static_assert(kFusedSlice == 4 * kFinalThreads, "a fused slice is one element group");
+constexpr int kFusedEPW = kFusedSlice / (kFinalThreads / 64);   // 256 per wave
+constexpr int kFusedUnroll = 8;
+
+__global__ __launch_bounds__(kFinalThreads)
+void k_score_slice(const uint8_t* __restrict__ key, int64_t M, const uint8_t* __restrict__ q_idx,
+                   const float* __restrict__ w_idx, const int32_t* __restrict__ len, PoolMap map,
+                   int32_t K, int32_t slots, uint32_t* __restrict__ ckey,
+                   int32_t* __restrict__ cpos) {
+  __shared__ BlockSelLds L;
+  __shared__ __attribute__((aligned(16))) uint32_t sk[kFusedSlice];   // order keys, 0: absent
+  const int row = blockIdx.y, s = blockIdx.x;
+  const int b = row;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, sub = lane & 31, head = sub >> 2;
+  const int64_t vis = len ? (int64_t)len[b] : M;
+  const int64_t g0 = (int64_t)s * kFusedSlice;
+  const int wofs = wave * kFusedEPW;
+
+  float qf[16];
+  const uint8_t* qsrc = q_idx + (size_t)row * kKeyRow + sub * 16;
+  load_q_slice(qsrc, qf);
+  const float wh = w_idx[(size_t)row * kHI + head];
+  const uint8_t* kb = key + sub * 16;
+
+  constexpr int kBatch = 2 * kFusedUnroll;                  // entries per batch of a wave
+  constexpr int kIters = kFusedEPW / kBatch;
+  u32x4 v[2][kFusedUnroll];
+  bool ok[2][kFusedUnroll];
+  auto issue = [&](int it, int bi) __attribute__((always_inline)) {
+    const int64_t p0 = g0 + wofs + it * kBatch;
+    // a batch's 16 entries lie in one page (pages hold >= 64 entries)
+    const int64_t roff = map.pages ? (p0 < vis ? pool_row(map, b, p0, M) : 0) - p0
+                                   : (int64_t)b * M;
+#pragma unroll
+    for (int u = 0; u < kFusedUnroll; ++u) {
+      const int64_t p = p0 + 2 * u + half;
+      const bool valid = p < vis;
+      ok[bi][u] = valid;
+      // absent entries read the query row (their key is 0 whatever they hold)
+      const uint8_t* src = valid ? kb + (roff + p) * kKeyRow : qsrc;
+      v[bi][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+    }
+  };
+  issue(0, 0);
+#pragma unroll 2
+  for (int it = 0; it < kIters; ++it) {
+    const int cb = it & 1;
+    if (it + 1 < kIters) issue(it + 1, cb ^ 1);
+    __builtin_amdgcn_sched_barrier(0);     // the next batch issues before this one is used
+#pragma unroll
+    for (int u = 0; u < kFusedUnroll; ++u) {
+      const float r = entry_score(v[cb][u], qf, wh);
+      if (sub == 0) sk[wofs + it * kBatch + 2 * u + half] = ok[cb][u] ? score_key(r) : 0u;
+    }
+  }
+  __syncthreads();
+
+  // thread t: slice positions 4 t .. 4 t + 3 (group 0 of k_topk_slice<4>)
+  const u32x4 kv = *reinterpret_cast<const u32x4*>(&sk[4 * threadIdx.x]);
+  uint32_t keyv[4] = {kv[0], kv[1], kv[2], kv[3]};
+  bool sel[4];
+  int round = 0;
+  const uint32_t kept = block_select<4>(keyv, (uint32_t)K, (uint32_t)slots, L, sel, round);
+  uint32_t oidx[4];
+  kept_order<4>(sel, L, round, oidx);
+  const size_t base = ((size_t)row * gridDim.x + s) * slots;
+  const int32_t b0 = s * kFusedSlice + 4 * (int32_t)threadIdx.x;
+  // the keepers go out through LDS (coalesced stores): the slice's own keys
+  // are no longer needed
+  __syncthreads();
+  int32_t* sp = reinterpret_cast<int32_t*>(&L.hist[0][0]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (sel[j]) {
+      sk[oidx[j]] = keyv[j];
+      sp[oidx[j]] = b0 + j;
+    }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < kept; i += kFinalThreads) {
+    ckey[base + i] = sk[i];
+    cpos[base + i] = sp[i];
+  }
+  for (uint32_t i = kept + threadIdx.x; i < (uint32_t)slots; i += kFinalThreads) ckey[base + i] = 0u;
+}
+
 // Row r's Top-K as ascending entries (through cand when given), -1 padded.
 // Elements: `total` slots of keepers (ckey / cpos from k_topk_slice, in
 // position order, total a multiple of 4) or, with total == 0, the row's own
@@ -1404,6 +1501,28 @@ hipError_t launch_topk_sliced(const float* scores, int32_t R, int32_t N,
     k_topk_final<8><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
   else
     k_topk_final<16><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_topk(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
+                             const float* w_idx, const int32_t* len, const PoolMap& map,
+                             int32_t K, int32_t* out, void* ws, hipStream_t s) {
+  const TopkSlicing sl = score_topk_slicing(B, M, K);
+  if (!sl.taken || !ws) return hipErrorInvalidValue;
+  uint32_t* ckey = (uint32_t*)ws;
+  int32_t* cpos = (int32_t*)((char*)ws + align256((size_t)B * sl.S * sl.slots * 4));
+  k_score_slice<<<dim3((unsigned)sl.S, (unsigned)B), dim3(kFinalThreads), 0, s>>>(
+      key, M, q_idx, w_idx, len, map, K, sl.slots, ckey, cpos);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int32_t total = sl.S * sl.slots;
+  const dim3 grid((unsigned)B), block(kFinalThreads);
+  if (total <= kFinalThreads * 4)
+    k_topk_final<4><<<grid, block, 0, s>>>(nullptr, (int32_t)M, len, (int32_t)M, total, ckey, cpos, K, nullptr, out);
+  else if (total <= kFinalThreads * 8)
+    k_topk_final<8><<<grid, block, 0, s>>>(nullptr, (int32_t)M, len, (int32_t)M, total, ckey, cpos, K, nullptr, out);
+  else
+    k_topk_final<16><<<grid, block, 0, s>>>(nullptr, (int32_t)M, len, (int32_t)M, total, ckey, cpos, K, nullptr, out);
   return hipGetLastError();
 }
 

@@ -142,6 +142,18 @@ class DeviceCase:
                            P, scores, hist, stream)
         return scores
 
+    def score_topk(self, ell: int, K: int = None, stream=None):
+        """Layer ell's indexer score and Top-K in one pass (csa2_score_topk)."""
+        cfg = self.cfg
+        K = cfg.K if K is None else K
+        d = self.layers[ell]
+        nb = C.csa2_workspace_bytes(C.CSA2_OP_SCORE_TOPK, cfg.B, 1, cfg.M, K, 0, 0, 0)
+        assert nb > 0, "shape not taken by the fused select"
+        ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        idx = torch.empty((cfg.B, K), dtype=torch.int32, device=self.device)
+        C.csa2_score_topk(self.pool, d["q_idx"], d["w_idx"], K, idx, ws, nb, stream)
+        return idx
+
     def topk(self, scores: torch.Tensor, K: int, n_valid=None, cand=None, stream=None):
         R = scores.numel() // scores.shape[-1]
         N = scores.shape[-1]

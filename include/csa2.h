@@ -70,7 +70,8 @@ enum {
   CSA2_OP_SPARSE_ATTN = 1,
   CSA2_OP_SWA_MERGE = 2,
   CSA2_OP_DECODE_LAYERS = 3,
-  CSA2_OP_PREFILL_LAYERS = 4
+  CSA2_OP_PREFILL_LAYERS = 4,
+  CSA2_OP_SCORE_TOPK = 5
 };
 
 /* The shared global KV pool: B sequences of up to M compressed entries each,
@@ -185,6 +186,28 @@ csa2_status csa2_topk(const float* scores, int32_t R, int32_t N,
                       const int32_t* n_valid, const int32_t* cand, int32_t K,
                       int32_t* idx, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* Indexer score and Top-K of a flat decode row in one pass: the result of
+ * csa2_index_score (Q = 1, no candidate list, every entry of the sequence's
+ * length visible) followed by csa2_topk with n_valid = the pool's lengths,
+ * bit for bit, without writing the scores.  The Full layer scores the
+ * context and selects its Top-K entries ("DeepSeek V4.1-Flash Cuts KV Cache
+ * by 437x", paragraph on the three operating modes); the single pass is this
+ * library's fusion of those two steps.  Each work-group scores 4096 entries
+ * of one row into LDS and keeps a superset of their Top-K (every member of
+ * the row's Top-K that lies among them); one work-group per row then selects
+ * the Top-K from all keepers.
+ *   pool    the pool (B, M, len, pages used)
+ *   q_idx   [B][HI][DI] E4M3;  w_idx [B][HI] float
+ *   idx     [B][K] int32 output: ascending entry numbers, -1 padded
+ *   ws      at least csa2_workspace_bytes(CSA2_OP_SCORE_TOPK, B, 1, M, K, 0, 0, 0)
+ * Limits: 1 <= K <= 16384 and ceil(M / 4096) * (K + max(K / 4, 64), rounded
+ * up to a multiple of 64) <= 16384 (every keeper fits the final select; M
+ * up to 114688 at K = 512), 1 <= B <= 65535.  Other shapes return
+ * CSA2_ERR_SHAPE (csa2_workspace_bytes returns 0 for them). */
+csa2_status csa2_score_topk(const csa2_pool* pool, const uint8_t* q_idx, const float* w_idx,
+                            int32_t K, int32_t* idx, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* Attention over selected FP4 global entries.
  * Every layer attends over the entries its index selects, held as FP4 (E2M1)

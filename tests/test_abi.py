@@ -242,6 +242,26 @@ def test_decode_layers_noalloc_argument_errors():
     assert ws(C.CSA2_OP_DECODE_LAYERS, 32, 1, 32768, 512, 0, 128, 16) <= lim
 
 
+def test_score_topk_argument_errors():
+    ws = C.csa2_workspace_bytes
+    need = ws(C.CSA2_OP_SCORE_TOPK, 2, 1, 1024, 64, 0, 0, 0)
+    assert need >= 2 * 2 * 64 * 4                      # keys and positions of the keepers
+    assert ws(C.CSA2_OP_SCORE_TOPK, 32, 1, 32768, 512, 0, 0, 0) > 0
+    assert ws(C.CSA2_OP_SCORE_TOPK, 8, 1, 262144, 512, 0, 0, 0) == 0   # keepers overflow
+    assert ws(C.CSA2_OP_SCORE_TOPK, 2, 1, 1024, 0, 0, 0, 0) == 0
+
+    def run(pool=None, q=A, w=A, K=64, idx=A2, w_=A, nb=need):
+        return C.csa2_score_topk(pool or _pool(), q, w, K, idx, w_, nb, 0, raise_on_error=False)
+
+    assert run(q=None) == C.CSA2_ERR_NULL
+    assert run(idx=None) == C.CSA2_ERR_NULL
+    assert run(K=0) == C.CSA2_ERR_SHAPE
+    assert run(pool=_pool(B=8, M=262144), K=512) == C.CSA2_ERR_SHAPE
+    assert run(q=A + 4) == C.CSA2_ERR_ALIGN
+    assert run(nb=need - 1) == C.CSA2_ERR_WORKSPACE
+    assert run(w_=None) == C.CSA2_ERR_WORKSPACE
+
+
 def test_prefill_layers_schedule_and_argument_errors():
     pool = _pool()
     need = C.csa2_workspace_bytes(C.CSA2_OP_PREFILL_LAYERS, 2, 64, 1024, 64, 0, 128, 16)
