@@ -37,7 +37,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-SCORE_SRC = os.path.join(ROOT, "fp4_kv_cache_score_amd", "csrc", "index_score.hip")
+SCORE_SRC = [os.path.join(ROOT, "fp4_kv_cache_score_amd", "csrc", f)
+             for f in ("index_score.hip", "index_math.h")]
 
 
 def log(*a):
@@ -45,7 +46,11 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the scan kernel's sources (its body and its arithmetic)."""
+    h = hashlib.sha256()
+    for f in SCORE_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 # The scan as the decode step launches it: 64 entries per wave, flat, no histogram.
