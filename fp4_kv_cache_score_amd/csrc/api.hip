@@ -77,14 +77,18 @@ size_t topk_slice_ws_max(int64_t R, int64_t Nmax, int64_t K) {
 // Top-K of csa2_score_topk is not used here: on the decode shapes its one
 // 1024-thread work-group per compute unit streams the keys slower than the
 // scan kernel's many small ones, more than the slice launch it saves.)
+// A hierarchical Full layer whose Top-P the sliced select cannot take selects
+// its Top-P and Top-K together with the threshold-bin select (`bin`) when the
+// rows allow it.
 struct DecodeSelect {
-  bool sliced_k, sliced_p, big;
+  bool sliced_k, sliced_p, bin, big;
 };
 DecodeSelect decode_select(int64_t B, int64_t M, int64_t K, int64_t P) {
   DecodeSelect d;
   d.sliced_k = topk_slicing(B, M, K).taken;
   d.sliced_p = P > 0 && topk_slicing(B, M, P).taken;
-  d.big = topk_multi_wg(B, M) && (!d.sliced_k || (P > 0 && !d.sliced_p));
+  d.bin = P > 0 && !d.sliced_p && topk_multi_wg(B, M) && topk_bin_taken(M);
+  d.big = topk_multi_wg(B, M) && (!d.sliced_k || (P > 0 && !d.sliced_p && !d.bin));
   return d;
 }
 
@@ -99,6 +103,8 @@ struct DecodeWs {
   float* scores;
   DecodeSelect sel;
   bool big;
+  uint32_t* hist;  // threshold-bin select: the Full layer's histograms (topk_bin_hist_words)
+  void* bin;       // threshold-bin select: kept elements per chunk
   void* slice;     // sliced-select winners
   TopkWs t;
   TopkWs t2;   // the Top-K's lists when the Top-P is selected beside it
@@ -120,10 +126,13 @@ size_t decode_ws_bytes(int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
   const int64_t N = P > M ? P : M;
   const int64_t Kmax = P > K ? P : K;
   const int32_t steps = attn_steps((int32_t)K, (int32_t)W);
-  const bool big = decode_select(B, M, K, P).big;
+  const DecodeSelect sel = decode_select(B, M, K, P);
+  const bool big = sel.big;
   return align256(B * N * 4) + (big ? topk_ws_bytes(B, M, Kmax) : 0) +
-         (big && P > 0 ? topk_ws_bytes(B, M, K) : 0) + align256(B * (P > 0 ? P : 1) * 4) +
-         decode_slice_ws_bytes(B, M, K, P) + attn_ws_bytes(B, steps);
+         (big && P > 0 ? topk_ws_bytes(B, M, K) : 0) +
+         (sel.bin ? align256(topk_bin_hist_words(B) * 4) + topk_bin_ws_bytes(B, M) : 0) +
+         align256(B * (P > 0 ? P : 1) * 4) + decode_slice_ws_bytes(B, M, K, P) +
+         attn_ws_bytes(B, steps);
 }
 
 DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, int64_t W) {
@@ -142,6 +151,12 @@ DecodeWs decode_ws_carve(void* ws, int64_t B, int64_t M, int64_t K, int64_t P, i
       d.t2 = topk_ws_carve(p, B, M, K);
       p += topk_ws_bytes(B, M, K);
     }
+  }
+  if (d.sel.bin) {
+    d.hist = (uint32_t*)p;
+    p += align256(topk_bin_hist_words(B) * 4);
+    d.bin = p;
+    p += topk_bin_ws_bytes(B, M);
   }
   d.cand = (int32_t*)p;
   p += align256(B * (P > 0 ? P : 1) * 4);
@@ -446,7 +461,15 @@ csa2_status decode_one(const csa2_pool* pool, const csa2_layer* layers, int32_t 
                                        pool_map(pool), stream));
     if (st != CSA2_OK) return st;
     const bool want_p = y.mode == CSA2_FULL && P > 0;
-    if (d.sel.sliced_k && (!want_p || d.sel.sliced_p)) {
+    if (want_p && d.sel.bin) {
+      // Top-P and the layer's Top-K from one histogram and one collect pass
+      st = hip_status(launch_topk_hist(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
+                                       d.hist, stream));
+      if (st != CSA2_OK) return st;
+      st = hip_status(launch_topk_bin_select(d.scores, (int32_t)B, (int32_t)M, pool->len,
+                                             (int32_t)M, d.hist, P, d.cand, K, y.idx_out, d.bin,
+                                             stream));
+    } else if (d.sel.sliced_k && (!want_p || d.sel.sliced_p)) {
       if (want_p) {
         st = hip_status(launch_topk_sliced(d.scores, (int32_t)B, (int32_t)M, pool->len, (int32_t)M,
                                            nullptr, P, d.cand, d.slice, stream));
@@ -530,6 +553,17 @@ csa2_status zero_big(const DecodeWs& d, int64_t B, int32_t P, hipStream_t stream
   return st;
 }
 
+// Zero what the Full layer's selects need zeroed on entry (they leave it
+// zeroed again): the multi-work-group select's histograms and counters, the
+// threshold-bin select's histogram.
+csa2_status zero_full_layer(const DecodeWs& d, int64_t B, int32_t P, hipStream_t stream) {
+  csa2_status st = CSA2_OK;
+  if (d.big) st = zero_big(d, B, P, stream);
+  if (st == CSA2_OK && d.sel.bin)
+    st = hip_status(launch_fill_zero(d.hist, topk_bin_hist_words(B), stream));
+  return st;
+}
+
 // Every layer of a decode step on a checked, large enough workspace.  What
 // must start at zero (the multi-work-group select's histograms and counters)
 // is cleared here by a fill kernel; everything else in the workspace is
@@ -539,11 +573,8 @@ csa2_status decode_step(const csa2_pool* pool, const csa2_layer* layers, int32_t
   const int64_t B = pool->B;
   const DecodeWs d = decode_ws_carve(ws, B, pool->M, K, P, W);
   const AttnPlan plan = attn_plan(B, attn_steps(K, W));
-  csa2_status st = CSA2_OK;
-  if (d.big) {
-    st = zero_big(d, B, P, stream);
-    if (st != CSA2_OK) return st;
-  }
+  csa2_status st = zero_full_layer(d, B, P, stream);
+  if (st != CSA2_OK) return st;
   for (int32_t l = 0; l < L; ++l) {
     st = decode_one(pool, layers, l, K, P, W, d, plan, stream);
     if (st != CSA2_OK) return st;
@@ -609,8 +640,8 @@ csa2_status csa2_decode_layer(const csa2_pool* pool, const csa2_layer* layers, i
   const DecodeWs d = decode_ws_carve(ws, B, pool->M, K, P, W);
   const AttnPlan plan = attn_plan(B, attn_steps(K, W));
   const csa2_layer& y = layers[l];
-  if (d.big && (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0))) {
-    st = zero_big(d, B, P, stream);
+  if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
+    st = zero_full_layer(d, B, P, stream);
     if (st != CSA2_OK) return st;
   }
   st = decode_one(pool, layers, l, K, P, W, d, plan, stream);

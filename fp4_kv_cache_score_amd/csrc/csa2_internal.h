@@ -167,6 +167,21 @@ inline size_t score_topk_ws_bytes(int64_t R, int64_t N, int64_t K) {
   return s.taken ? align256((size_t)(R * s.S * s.slots * 4)) * 2 : 0;
 }
 
+// Threshold-bin select (a few long rows, a large K, up to two selects from
+// one histogram): every position at or above the threshold bin, per
+// 4096-position chunk, keys and positions [R][chunks][4096] and counts
+// [R][chunks].
+// Its histograms (row [R][4096], then the threshold bins' next digit
+// [R][2][4096], topk_bin_hist_words) start zeroed and are left zeroed.
+constexpr int kBinChunk = 4096;
+constexpr int kBinMaxChunks = 256;   // rows up to 2^20 positions
+inline bool topk_bin_taken(int64_t N) { return N > 0 && N <= (int64_t)kBinChunk * kBinMaxChunks; }
+inline int64_t topk_bin_hist_words(int64_t R) { return R * kHistBins * 3; }
+inline size_t topk_bin_ws_bytes(int64_t R, int64_t N) {
+  const int64_t nch = (N + kBinChunk - 1) / kBinChunk;
+  return 2 * align256((size_t)(R * nch * kBinChunk * 4)) + align256((size_t)(R * nch * 4));
+}
+
 inline size_t topk_ws_bytes(int64_t R, int64_t N, int64_t K) {
   int64_t cap = topk_cap(R, N);
   return align256(R * kHistBins * 4) + align256(R * kCounterWords * 4) +
@@ -223,6 +238,14 @@ hipError_t launch_score_topk(const uint8_t* key, int32_t B, int64_t M, const uin
 hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
                             const int32_t* n_valid, int32_t n_all,
                             uint32_t* hist, hipStream_t s);
+// Threshold-bin select on scores whose histogram is in hist (topk_bin_taken(N);
+// hist holds topk_bin_hist_words words, zeroed on entry, zeroed on return):
+// the K0 largest of each row to out0 and the K1 largest (K1 <= K0; 0: none)
+// to out1, both ascending; ws holds topk_bin_ws_bytes; hist is left zeroed.
+hipError_t launch_topk_bin_select(const float* scores, int32_t R, int32_t N,
+                                  const int32_t* n_valid, int32_t n_all, uint32_t* hist,
+                                  int32_t K0, int32_t* out0, int32_t K1, int32_t* out1, void* ws,
+                                  hipStream_t s);
 // Multi-work-group select on scores whose histogram is in ws.hist and whose
 // counters are zero; leaves the counters (and, with zero_hist, the
 // histogram) zeroed.

@@ -68,6 +68,26 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
 }
 
+// The calling wave's exclusive prefix over the block's per-wave totals
+// slot[k * stride] (k < NW <= 16) and their sum: lane k reads total k, a DPP
+// scan runs within the first row of 16 lanes, and two single-lane reads give
+// the results (a few instructions per wave instead of NW reads and adds).
+template <int NW>
+__device__ __forceinline__ void wave_prefix(const uint32_t* slot, int stride, uint32_t* before,
+                                            uint32_t* all) {
+  static_assert(NW >= 1 && NW <= 16, "one DPP row of totals");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t r = slot[(lane < NW ? lane : 0) * stride];
+  uint32_t t = lane < NW ? r : 0u;
+  t += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x111, 0xF, 0xF, true);   // row_shr:1
+  t += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x112, 0xF, 0xF, true);   // row_shr:2
+  t += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x114, 0xF, 0xF, true);   // row_shr:4
+  t += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x118, 0xF, 0xF, true);   // row_shr:8
+  *all = (uint32_t)__builtin_amdgcn_readlane((int)t, NW - 1);
+  const uint32_t prev = (uint32_t)__builtin_amdgcn_readlane((int)t, wave > 0 ? wave - 1 : 0);
+  *before = wave > 0 ? prev : 0u;
+}
+
 // Exclusive prefix sum over the NT threads of a block; *total receives the sum.
 // lds must hold NT/64 words and is free again on return.  Each wave scans
 // with DPP, publishes its total, and every wave then adds the totals of the
@@ -78,15 +98,10 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t* total) 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
-  if (lane == 63) lds[wave] = x;
+  lds[wave] = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);   // every lane: no branch
   __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t c = lds[w];
-    before += w < wave ? c : 0u;
-    all += c;
-  }
+  uint32_t before, all;
+  wave_prefix<NW>(lds, 1, &before, &all);
   *total = all;
   __syncthreads();
   return before + x - v;
@@ -97,12 +112,11 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t* total) 
 // above[s] = number of keys in bins above bin[s]; above < K <= above + h[bin].
 // bin[s] is -1 if the histogram holds fewer than K_s keys (K1 = 0: unused).
 // lds: NT/64 + 5 words.  h is 16-byte aligned.
-template <int NT>
-__device__ void threshold_bins(const uint32_t* h, uint32_t K0, uint32_t K1, uint32_t* lds,
-                               int* bin, uint32_t* above) {
-  constexpr int PER = kHistBins / NT;          // a multiple of 4
-  const int lo = kHistBins - (int)(threadIdx.x + 1) * PER;   // thread 0 owns the highest bins
-  uint32_t c[PER];                             // c[i] = h[lo + PER - 1 - i], highest first
+// This thread's PER bins of a 4096-bin histogram, highest first: thread 0
+// owns the highest bins, c[i] = h[4096 - PER tid - 1 - i].  h 16-byte aligned.
+template <int PER>
+__device__ __forceinline__ void hist_slice(const uint32_t* h, uint32_t (&c)[PER]) {
+  const int lo = kHistBins - (int)(threadIdx.x + 1) * PER;
 #pragma unroll
   for (int j = 0; j < PER / 4; ++j) {
     const uint4 v = *reinterpret_cast<const uint4*>(h + lo + 4 * j);
@@ -111,15 +125,34 @@ __device__ void threshold_bins(const uint32_t* h, uint32_t K0, uint32_t K1, uint
     c[PER - 3 - 4 * j] = v.z;
     c[PER - 4 - 4 * j] = v.w;
   }
+}
+
+template <int NT>
+__device__ void threshold_bins_c(const uint32_t (&c)[kHistBins / NT], uint32_t K0, uint32_t K1,
+                                 uint32_t* lds, int* bin, uint32_t* above);
+
+template <int NT>
+__device__ void threshold_bins(const uint32_t* h, uint32_t K0, uint32_t K1, uint32_t* lds,
+                               int* bin, uint32_t* above) {
+  uint32_t c[kHistBins / NT];
+  hist_slice(h, c);
+  threshold_bins_c<NT>(c, K0, K1, lds, bin, above);
+}
+
+// threshold_bins on counts already in registers (hist_slice's layout)
+template <int NT>
+__device__ void threshold_bins_c(const uint32_t (&c)[kHistBins / NT], uint32_t K0, uint32_t K1,
+                                 uint32_t* lds, int* bin, uint32_t* above) {
+  constexpr int PER = kHistBins / NT;          // a multiple of 4
   uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) s += c[i];
-  if (threadIdx.x == 0) {
-    lds[NT / 64 + 1] = 0xFFFFFFFFu;
-    lds[NT / 64 + 2] = 0u;
-    lds[NT / 64 + 3] = 0xFFFFFFFFu;
-    lds[NT / 64 + 4] = 0u;
-  }
+  // every thread stores the same defaults (a store behind a branch costs far
+  // more than the redundant writes in these once-per-block phases)
+  lds[NT / 64 + 1] = 0xFFFFFFFFu;
+  lds[NT / 64 + 2] = 0u;
+  lds[NT / 64 + 3] = 0xFFFFFFFFu;
+  lds[NT / 64 + 4] = 0u;
   uint32_t tot;
   const uint32_t ex = block_excl_scan<NT>(s, lds, &tot);
   const int top = kHistBins - 1 - (int)threadIdx.x * PER;
@@ -127,17 +160,20 @@ __device__ void threshold_bins(const uint32_t* h, uint32_t K0, uint32_t K1, uint
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const uint32_t K = Ks[t];
-    if (K > 0 && ex < K && K <= ex + s) {
-      uint32_t acc = ex;
+    // the bin where the running count first reaches K (selects, no branch)
+    uint32_t acc = ex, fb = 0u, fa = 0u;
+    bool hit = false;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (acc + c[i] >= K) {
-          lds[NT / 64 + 1 + 2 * t] = (uint32_t)(top - i);
-          lds[NT / 64 + 2 + 2 * t] = acc;
-          break;
-        }
-        acc += c[i];
-      }
+    for (int i = 0; i < PER; ++i) {
+      const bool hi = K > 0 && acc < K && K <= acc + c[i];
+      fb = hi ? (uint32_t)(top - i) : fb;
+      fa = hi ? acc : fa;
+      hit = hit || hi;
+      acc += c[i];
+    }
+    if (hit) {
+      lds[NT / 64 + 1 + 2 * t] = fb;
+      lds[NT / 64 + 2 + 2 * t] = fa;
     }
   }
   __syncthreads();
@@ -911,13 +947,19 @@ constexpr int kSelNW = kFinalThreads / 64;
 constexpr int kGroupSpan = 4 * kFinalThreads;   // positions per element group
 
 struct BlockSelLds {
-  uint32_t hist[2][kHistBins];        // double-buffered histogram; output staging afterwards
+  alignas(16) uint32_t hist[2][kHistBins];   // double-buffered histogram; output staging afterwards
   uint32_t scan[4][2 * kSelNW];       // rotating scan slots
   uint32_t res[4][4];                 // rotating digit-search results
   uint32_t red[3][kSelNW];            // count, min, max per wave
 };
 
 __device__ __forceinline__ uint32_t key_hi(uint32_t k, int sh) { return sh >= 32 ? 0u : k >> sh; }
+
+// Zero a 4096-bin LDS histogram (16-byte aligned): one 16-byte store per thread.
+__device__ __forceinline__ void zero_hist(uint32_t* h) {
+  static_assert(kHistBins == 4 * kFinalThreads, "one 16-byte store per thread");
+  reinterpret_cast<uint4*>(h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+}
 
 // Sum, minimum and maximum over the 64 lanes of a wave, in lane 63: DPP row
 // shifts within each row of 16, then the row results added with readlane.
@@ -961,18 +1003,13 @@ __device__ void scan_groups(const uint32_t (&c)[G], uint32_t* slot, uint32_t (&p
   for (int w = 0; w < W; ++w) {
     v[w] = c[2 * w] | (2 * w + 1 < G ? c[2 * w + 1] << 16 : 0u);
     x[w] = wave_incl_scan(v[w]);
-    if (lane == 63) slot[wave * W + w] = x[w];
+    slot[wave * W + w] = (uint32_t)__builtin_amdgcn_readlane((int)x[w], 63);   // every lane
   }
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < W; ++w) {
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int k = 0; k < kSelNW; ++k) {
-      const uint32_t s = slot[k * W + w];
-      before += k < wave ? s : 0u;
-      all += s;
-    }
+    uint32_t before, all;
+    wave_prefix<kSelNW>(slot + w, W, &before, &all);
     const uint32_t ex = before + x[w] - v[w];
     pre[2 * w] = ex & 0xFFFFu;
     tot[2 * w] = all & 0xFFFFu;
@@ -986,6 +1023,10 @@ __device__ void scan_groups(const uint32_t (&c)[G], uint32_t* slot, uint32_t (&p
 // Digit holding the need-th largest of the 2^w bins (counted from the top):
 // the digit, the count above it and its own count (block-uniform); two
 // barriers, `slot` / `rs` as in scan_groups.
+__device__ void find_digit_c(const uint32_t (&c)[kHistBins / kFinalThreads], int top, uint32_t need,
+                             uint32_t* slot, uint32_t* rs, uint32_t* digit, uint32_t* above,
+                             uint32_t* count);
+
 __device__ void find_digit(const uint32_t* h, int w, uint32_t need, uint32_t* slot, uint32_t* rs,
                            uint32_t* digit, uint32_t* above, uint32_t* count) {
   constexpr int kPer = kHistBins / kFinalThreads;     // 4 bins per thread at most
@@ -993,30 +1034,43 @@ __device__ void find_digit(const uint32_t* h, int w, uint32_t need, uint32_t* sl
   const int per = (nb + kFinalThreads - 1) / kFinalThreads;
   const int top = nb - 1 - (int)threadIdx.x * per;    // thread 0 owns the highest bins
   uint32_t c[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) c[i] = (i < per && top - i >= 0) ? h[top - i] : 0u;
+  find_digit_c(c, top, need, slot, rs, digit, above, count);
+}
+
+// find_digit on this thread's bins in registers: c[i] is bin top - i (0 past
+// the thread's share or below bin 0).
+__device__ void find_digit_c(const uint32_t (&c)[kHistBins / kFinalThreads], int top, uint32_t need,
+                             uint32_t* slot, uint32_t* rs, uint32_t* digit, uint32_t* above,
+                             uint32_t* count) {
+  constexpr int kPer = kHistBins / kFinalThreads;
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    c[i] = (i < per && top - i >= 0) ? h[top - i] : 0u;
-    s += c[i];
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = 0; i < kPer; ++i) s += c[i];
+  const int wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(s);
-  if (lane == 63) slot[wave] = x;
+  slot[wave] = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);   // every lane: no branch
   __syncthreads();
-  uint32_t ex = x - s;
+  uint32_t before, all;
+  wave_prefix<kSelNW>(slot, 1, &before, &all);
+  const uint32_t ex = before + x - s;
+  // the bin holding the need-th count (selects; one lane stores)
+  uint32_t acc = ex, fd = 0u, fa = 0u, fc = 0u;
+  bool hit = false;
 #pragma unroll
-  for (int k = 0; k < kSelNW; ++k) ex += k < wave ? slot[k] : 0u;
-  if (ex < need && need <= ex + s) {
-    uint32_t acc = ex;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (acc < need && need <= acc + c[i]) {
-        rs[0] = (uint32_t)(top - i);
-        rs[1] = acc;
-        rs[2] = c[i];
-      }
-      acc += c[i];
-    }
+  for (int i = 0; i < kPer; ++i) {
+    const bool hi = acc < need && need <= acc + c[i];
+    fd = hi ? (uint32_t)(top - i) : fd;
+    fa = hi ? acc : fa;
+    fc = hi ? c[i] : fc;
+    hit = hit || hi;
+    acc += c[i];
+  }
+  if (hit) {
+    rs[0] = fd;
+    rs[1] = fa;
+    rs[2] = fc;
   }
   __syncthreads();
   *digit = rs[0];
@@ -1045,21 +1099,25 @@ __device__ uint32_t block_select(const uint32_t (&key)[PT], uint32_t K, uint32_t
     }
   }
   const Wred wr = wave_reduce3(cnt, kmin, kmax);
-  if (lane == 0) {
-    L.red[0][wave] = wr.sum;
-    L.red[1][wave] = wr.mn;
-    L.red[2][wave] = wr.mx;
-  }
-  for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) L.hist[0][i] = 0u;
+  L.red[0][wave] = wr.sum;   // wave-uniform values, every lane stores
+  L.red[1][wave] = wr.mn;
+  L.red[2][wave] = wr.mx;
+  zero_hist(L.hist[0]);
   __syncthreads();
-  uint32_t tot = 0;
-  kmin = 0xFFFFFFFFu;
-  kmax = 0u;
-#pragma unroll
-  for (int k = 0; k < kSelNW; ++k) {
-    tot += L.red[0][k];
-    kmin = min(kmin, L.red[1][k]);
-    kmax = max(kmax, L.red[2][k]);
+  // the block's count, minimum and maximum: lane k takes wave k's values
+  uint32_t tot, rs = 0u, rn = 0xFFFFFFFFu, rx = 0u;
+  {
+    const int k = lane < kSelNW ? lane : 0;
+    rs = lane < kSelNW ? L.red[0][k] : 0u;
+    rn = lane < kSelNW ? L.red[1][k] : 0xFFFFFFFFu;
+    rx = lane < kSelNW ? L.red[2][k] : 0u;
+    wred_step<0x111>(rs, rn, rx);
+    wred_step<0x112>(rs, rn, rx);
+    wred_step<0x114>(rs, rn, rx);
+    wred_step<0x118>(rs, rn, rx);
+    tot = (uint32_t)__builtin_amdgcn_readlane((int)rs, kSelNW - 1);
+    kmin = (uint32_t)__builtin_amdgcn_readlane((int)rn, kSelNW - 1);
+    kmax = (uint32_t)__builtin_amdgcn_readlane((int)rx, kSelNW - 1);
   }
   if (tot <= budget) {
 #pragma unroll
@@ -1083,7 +1141,7 @@ __device__ uint32_t block_select(const uint32_t (&key)[PT], uint32_t K, uint32_t
 #pragma unroll
     for (int i = 0; i < PT; ++i)
       if (key[i] && key_hi(key[i], shift) == prefix) atomicAdd(&h[(key[i] >> sh) & mask], 1u);
-    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) L.hist[buf ^ 1][i] = 0u;
+    zero_hist(L.hist[buf ^ 1]);
     __syncthreads();
     uint32_t d, ab, c;
     find_digit(h, w, need, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
@@ -1415,6 +1473,330 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
   for (uint32_t i = chosen + threadIdx.x; i < (uint32_t)K; i += kFinalThreads) orow[i] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Threshold-bin select for a few long rows and a large K (the hierarchical
+// Full layer's Top-P with its Top-K): after the histogram pass over the row's
+// top 12 key bits, k_topk_bin_collect keeps every position whose top digit
+// is at or above the digit holding the K0-th largest key, a superset of the
+// row's Top-K0 (which holds its Top-K1, K1 <= K0), each 4096-position chunk
+// into a region of its own in position order (one block scan, no atomics),
+// and counts the members of the K0-th and the K1-th key's bins by their next
+// 12 bits (fine histograms).  k_topk_bin_final then selects, per row, the K0
+// and the K1 largest of the kept elements exactly under the (key, lower
+// position) order: the first 24 bits of each threshold come from the two
+// histograms; when the kept list exceeds one register tile (16384) but the
+// elements at or above the K0 threshold's 24 bits fit, those are compacted
+// in list order into the row's scratch list; one more radix pass over the
+// last 8 bits (an LDS histogram) finishes each threshold; ties go to the
+// earlier element, both lists are written ascending.  Kept lists that do not
+// fit are streamed from the regions.  The final clears the row's histograms
+// for the next use.
+// ---------------------------------------------------------------------------
+constexpr int kBinThreads = 256;
+constexpr int kBinPer = kBinChunk / kBinThreads;     // 16 consecutive positions per thread
+
+__global__ __launch_bounds__(kBinThreads)
+void k_topk_bin_collect(const float* __restrict__ scores, int32_t N, const int32_t* __restrict__ n_valid,
+                        int32_t n_all, const uint32_t* __restrict__ hist, int32_t K0, int32_t K1,
+                        uint32_t* __restrict__ fine, uint32_t* __restrict__ rkey,
+                        int32_t* __restrict__ rpos, uint32_t* __restrict__ rcnt) {
+  __shared__ uint32_t lds[kBinThreads / 64 + 5];
+  __shared__ uint32_t lf[2][kHistBins];     // next 12 bits of each threshold bin's members
+  const int row = blockIdx.y, c = blockIdx.x, nch = gridDim.x;
+  const int32_t n = row_count(n_valid, n_all, row, N);
+  const int32_t c0 = c * kBinChunk;
+  const int32_t p0 = c0 + kBinPer * (int32_t)threadIdx.x;
+  const float* sr = scores + (size_t)row * N;
+  uint32_t key[kBinPer];
+  const bool vec = (N & 3) == 0 && ((uintptr_t)scores & 15u) == 0;
+#pragma unroll
+  for (int u = 0; u < kBinPer / 4; ++u) {
+    const int32_t p = p0 + 4 * u;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (vec) {
+      if (p < n) v = *reinterpret_cast<const float4*>(sr + p);   // p + 3 < N: N is a multiple of 4
+    } else {
+      v.x = p < n ? sr[p] : 0.f;
+      v.y = p + 1 < n ? sr[p + 1] : 0.f;
+      v.z = p + 2 < n ? sr[p + 2] : 0.f;
+      v.w = p + 3 < n ? sr[p + 3] : 0.f;
+    }
+    key[4 * u + 0] = p + 0 < n ? score_key(v.x) : 0u;
+    key[4 * u + 1] = p + 1 < n ? score_key(v.y) : 0u;
+    key[4 * u + 2] = p + 2 < n ? score_key(v.z) : 0u;
+    key[4 * u + 3] = p + 3 < n ? score_key(v.w) : 0u;
+  }
+  for (int i = threadIdx.x; i < 2 * kHistBins; i += kBinThreads) lf[i / kHistBins][i % kHistBins] = 0u;
+  int bin[2];
+  uint32_t above[2];
+  threshold_bins<kBinThreads>(hist + (size_t)row * kHistBins, (uint32_t)K0, (uint32_t)K1, lds, bin,
+                              above);
+  const int b0 = n > K0 ? bin[0] : -1;      // every present position when the row has no more than K0
+  const int b1 = K1 > 0 && n > K1 ? bin[1] : -1;
+  // the threshold bins' members by their next 12 bits (the final select's
+  // second digit), one atomic per non-empty bin and work-group
+#pragma unroll
+  for (int i = 0; i < kBinPer; ++i) {
+    const int d = (int)(key[i] >> (32 - kHistBits));
+    const uint32_t f = (key[i] >> (32 - 2 * kHistBits)) & (kHistBins - 1);
+    if (key[i] && b0 >= 0 && d == b0) atomicAdd(&lf[0][f], 1u);
+    if (key[i] && b1 >= 0 && d == b1) atomicAdd(&lf[1][f], 1u);
+  }
+  __syncthreads();
+  uint32_t* fr = fine + (size_t)row * 2 * kHistBins;
+  for (int i = threadIdx.x; i < 2 * kHistBins; i += kBinThreads) {
+    const uint32_t v = lf[i / kHistBins][i % kHistBins];
+    if (v) atomicAdd(&fr[i], v);
+  }
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kBinPer; ++i) cnt += key[i] && (int)(key[i] >> (32 - kHistBits)) >= b0 ? 1u : 0u;
+  uint32_t tot;
+  uint32_t o = block_excl_scan<kBinThreads>(cnt, lds, &tot);
+  const size_t base = ((size_t)row * nch + c) * kBinChunk;
+#pragma unroll
+  for (int i = 0; i < kBinPer; ++i) {
+    if (key[i] && (int)(key[i] >> (32 - kHistBits)) >= b0) {
+      rkey[base + o] = key[i];
+      rpos[base + o] = p0 + i;
+      ++o;
+    }
+  }
+  if (threadIdx.x == 0) rcnt[(size_t)row * nch + c] = tot;
+}
+
+// Direct global -> LDS transfer of 4 bytes per lane: lane l's word lands at
+// lds_dst + 4 l (lds_dst wave-uniform); lanes outside EXEC transfer nothing.
+__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
+}
+
+// One select's threshold over the kept list: elements whose key bits at and
+// above `shift` exceed `prefix` are chosen, and of those equal to it the
+// first `take` in list order.
+struct BinThr {
+  int shift;
+  uint32_t prefix;
+  uint32_t take;
+};
+
+constexpr int kBinList = kFinalThreads * 16;   // kept elements per LDS tile
+
+struct BinLds {
+  uint32_t key[kBinList + 64];       // a tile of the kept list, list order (+ one transfer of slack)
+  int32_t pos[kBinList + 64];
+  uint32_t h[2][256];                // low-byte histograms of the two 24-bit threshold groups
+  uint32_t pre[kBinMaxChunks + 1];   // chunk offsets in the kept list
+  uint32_t scan[4][8 * kSelNW];      // rotating scan slots (up to 16 fields)
+  uint32_t res[4][4];
+};
+
+__global__ __launch_bounds__(kFinalThreads)
+void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_all,
+                      uint32_t* __restrict__ hist, uint32_t* __restrict__ fine, int32_t nch,
+                      const uint32_t* __restrict__ rkey, const int32_t* __restrict__ rpos,
+                      const uint32_t* __restrict__ rcnt, int32_t K0, int32_t* __restrict__ out0,
+                      int32_t K1, int32_t* __restrict__ out1) {
+  constexpr int kPer = kHistBins / kFinalThreads;   // 4 bins of each histogram per thread
+  static_assert(kPer == 4, "one 16-byte slice of each histogram per thread");
+  __shared__ __attribute__((aligned(16))) BinLds L;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t n = row_count(n_valid, n_all, row, N);
+  uint32_t* hrow = hist + (size_t)row * kHistBins;
+  uint32_t* frow = fine + (size_t)row * 2 * kHistBins;
+  // one round trip for the chunk counts and this thread's share of the row
+  // histogram and of both fine histograms
+  const uint32_t v = tid < nch ? rcnt[(size_t)row * nch + tid] : 0u;
+  uint32_t hc[kPer], f0c[kPer], f1c[kPer];
+  hist_slice(hrow, hc);
+  hist_slice(frow, f0c);
+  hist_slice(frow + kHistBins, f1c);
+  int round = 0;
+  {
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kFinalThreads>(v, L.scan[0], &tot);
+    if (tid < nch) L.pre[tid] = ex;
+    L.pre[nch] = tot;      // every thread, the same value
+  }
+  __syncthreads();
+  const uint32_t T = L.pre[nch];
+  const int ntiles = (int)((T + kBinList - 1) / kBinList);
+
+  // list tile t into LDS: each wave transfers its chunks' share, 64 at a time;
+  // wait_tile() before reading it
+  auto issue_tile = [&](int t) {
+    const uint32_t lo = (uint32_t)t * kBinList;
+    const uint32_t hi = T - lo < (uint32_t)kBinList ? T : lo + kBinList;
+    for (int c = wave; c < nch; c += kSelNW) {
+      const uint32_t pc = L.pre[c];
+      const uint32_t a = pc > lo ? pc : lo;
+      const uint32_t b = L.pre[c + 1] < hi ? L.pre[c + 1] : hi;
+      const uint32_t* ks = rkey + ((size_t)row * nch + c) * kBinChunk;
+      const int32_t* ps = rpos + ((size_t)row * nch + c) * kBinChunk;
+      for (uint32_t e = a; e < b; e += 64) {
+        if (e + lane < b) {
+          dma4(ks + (e + lane - pc), &L.key[e - lo]);
+          dma4(ps + (e + lane - pc), &L.pos[e - lo]);
+        }
+      }
+    }
+  };
+  auto wait_tile = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's transfers have landed
+    __syncthreads();
+  };
+  auto tile_count = [&](int t) -> uint32_t {
+    const uint32_t lo = (uint32_t)t * kBinList;
+    return T - lo < (uint32_t)kBinList ? T - lo : (uint32_t)kBinList;
+  };
+  // keys of group u for this thread (0: absent or past the tile's cnt elements)
+  auto group_keys = [&](int u, uint32_t cnt, uint32_t (&k4)[4]) {
+    const uint32_t e = 4096u * u + 4u * tid;
+    const uint4 kv = *reinterpret_cast<const uint4*>(&L.key[e]);
+    k4[0] = e + 0 < cnt ? kv.x : 0u;
+    k4[1] = e + 1 < cnt ? kv.y : 0u;
+    k4[2] = e + 2 < cnt ? kv.z : 0u;
+    k4[3] = e + 3 < cnt ? kv.w : 0u;
+  };
+  if (ntiles > 0) issue_tile(0);   // in flight while the thresholds are found
+
+  // Thresholds.  A row with at most K present positions keeps all of them.
+  // Otherwise the first 24 bits come from the row histogram and the
+  // threshold bin's fine histogram; unless that whole 24-bit group is
+  // chosen, one pass over the list's low bytes gives the last 8.
+  const bool g0 = n > K0, g1 = K1 > 0 && n > K1;
+  BinThr th0{32, 0u, T}, th1{32, 0u, T};
+  bool pass0 = false, pass1 = false;
+  {
+    int bin[2];
+    uint32_t above[2];
+    threshold_bins_c<kFinalThreads>(hc, g0 ? (uint32_t)K0 : 0u, g1 ? (uint32_t)K1 : 0u,
+                                    L.scan[round & 3], bin, above);
+    ++round;
+    const int top = kHistBins - 1 - kPer * tid;
+    auto first24 = [&](const uint32_t (&fc)[kPer], uint32_t K, int b, uint32_t ab0, BinThr& th,
+                       bool& pass) {
+      uint32_t d, ab, c;
+      find_digit_c(fc, top, K - ab0, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
+      ++round;
+      th = BinThr{32 - 2 * kHistBits, ((uint32_t)b << kHistBits) | d, K - ab0 - ab};
+      pass = c != th.take;
+    };
+    if (g0) first24(f0c, (uint32_t)K0, bin[0], above[0], th0, pass0);
+    if (g1) first24(f1c, (uint32_t)K1, bin[1], above[1], th1, pass1);
+  }
+  if (ntiles > 0) wait_tile();
+  if (pass0 || pass1) {
+    for (int i = tid; i < 2 * 256; i += kFinalThreads) L.h[i >> 8][i & 255] = 0u;
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      if (t > 0) {
+        __syncthreads();   // every thread is done with the previous tile
+        issue_tile(t);
+        wait_tile();
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint32_t k4[4];
+        group_keys(u, tile_count(t), k4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (pass0 && k4[j] && (k4[j] >> 8) == th0.prefix) atomicAdd(&L.h[0][k4[j] & 255u], 1u);
+          if (pass1 && k4[j] && (k4[j] >> 8) == th1.prefix) atomicAdd(&L.h[1][k4[j] & 255u], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    auto last8 = [&](const uint32_t* h, BinThr& th) {
+      uint32_t d, ab, c;
+      find_digit(h, 8, th.take, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
+      ++round;
+      th = BinThr{0, (th.prefix << 8) | d, th.take - ab};
+    };
+    if (pass0) last8(L.h[0], th0);
+    if (pass1) last8(L.h[1], th1);
+    if (ntiles > 1) {
+      __syncthreads();
+      issue_tile(0);
+      wait_tile();
+    }
+  }
+
+  // Output: an element's index in a select's list is the number chosen
+  // before it in list order, (greater before) + min(equal before, take).
+  // Select 1 (short) stores directly; select 0 stages its tile's share in
+  // the key array (dead once its counts are scanned), then stores it
+  // coalesced.
+  uint32_t gb0 = 0, eb0 = 0, gb1 = 0, eb1 = 0;
+  auto emit = [&](uint32_t cnt, const BinThr& th, uint32_t& gb, uint32_t& eb, int32_t K, int32_t* out,
+                  bool stage) {
+    uint32_t mg = 0u, me = 0u;   // bit 4 u + j: element greater than / equal to the threshold prefix
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t k4[4];
+      group_keys(u, cnt, k4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t hk = key_hi(k4[j], th.shift);
+        mg |= k4[j] && hk > th.prefix ? 1u << (4 * u + j) : 0u;
+        me |= k4[j] && hk == th.prefix ? 1u << (4 * u + j) : 0u;
+      }
+    }
+    uint32_t f[8], pf[8], tt[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f[2 * u] = __builtin_popcount((mg >> (4 * u)) & 15u);
+      f[2 * u + 1] = __builtin_popcount((me >> (4 * u)) & 15u);
+    }
+    scan_groups<8>(f, L.scan[round & 3], pf, tt);   // its barrier: every key of the tile read
+    ++round;
+    const uint32_t ob = gb + (eb < th.take ? eb : th.take);   // chosen before this tile
+    int32_t* dst = stage ? reinterpret_cast<int32_t*>(L.key) : out + (size_t)row * K + ob;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t g = gb + pf[2 * u], e = eb + pf[2 * u + 1];
+      const int4 pv = *reinterpret_cast<const int4*>(&L.pos[4096 * u + 4 * tid]);
+      const int32_t ps[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool gt = (mg >> (4 * u + j)) & 1u, eq = (me >> (4 * u + j)) & 1u;
+        const uint32_t o = g + (e < th.take ? e : th.take);
+        if ((gt || (eq && e < th.take)) && o < (uint32_t)K) dst[o - ob] = ps[j];
+        g += gt ? 1u : 0u;
+        e += eq ? 1u : 0u;
+      }
+      gb += tt[2 * u];
+      eb += tt[2 * u + 1];
+    }
+    if (stage) {
+      const uint32_t oe = gb + (eb < th.take ? eb : th.take);
+      const uint32_t m = (oe < (uint32_t)K ? oe : (uint32_t)K) - (ob < (uint32_t)K ? ob : (uint32_t)K);
+      __syncthreads();
+      int32_t* og = out + (size_t)row * K + ob;
+      for (uint32_t i = tid; i < m; i += kFinalThreads) og[i] = dst[i];
+    }
+  };
+  for (int t = 0; t < ntiles; ++t) {
+    if (t > 0) {
+      __syncthreads();   // the staged share of the last tile has been stored
+      issue_tile(t);
+      wait_tile();
+    }
+    if (K1 > 0) emit(tile_count(t), th1, gb1, eb1, K1, out1, false);
+    emit(tile_count(t), th0, gb0, eb0, K0, out0, true);
+  }
+  const uint32_t c0 = gb0 + (eb0 < th0.take ? eb0 : th0.take);
+  const uint32_t c1 = gb1 + (eb1 < th1.take ? eb1 : th1.take);
+  for (uint32_t i = c0 + tid; i < (uint32_t)K0; i += kFinalThreads) out0[(size_t)row * K0 + i] = -1;
+  for (uint32_t i = c1 + tid; i < (uint32_t)K1; i += kFinalThreads) out1[(size_t)row * K1 + i] = -1;
+  // leave the row's histograms zeroed for the next select
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4*>(hrow)[tid] = z;
+  reinterpret_cast<uint4*>(frow)[tid] = z;
+  reinterpret_cast<uint4*>(frow)[tid + kFinalThreads] = z;
+}
+
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -1523,6 +1905,27 @@ hipError_t launch_score_topk(const uint8_t* key, int32_t B, int64_t M, const uin
     k_topk_final<8><<<grid, block, 0, s>>>(nullptr, (int32_t)M, len, (int32_t)M, total, ckey, cpos, K, nullptr, out);
   else
     k_topk_final<16><<<grid, block, 0, s>>>(nullptr, (int32_t)M, len, (int32_t)M, total, ckey, cpos, K, nullptr, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_bin_select(const float* scores, int32_t R, int32_t N,
+                                  const int32_t* n_valid, int32_t n_all, uint32_t* hist,
+                                  int32_t K0, int32_t* out0, int32_t K1, int32_t* out1, void* ws,
+                                  hipStream_t s) {
+  const int32_t nch = (N + kBinChunk - 1) / kBinChunk;
+  if (!ws || nch > kBinMaxChunks || K0 <= 0 || K1 < 0 || K1 > K0) return hipErrorInvalidValue;
+  const size_t reg = align256((size_t)R * nch * kBinChunk * 4);
+  char* p = (char*)ws;
+  uint32_t* rkey = (uint32_t*)p;  p += reg;
+  int32_t* rpos = (int32_t*)p;    p += reg;
+  uint32_t* rcnt = (uint32_t*)p;
+  uint32_t* fine = hist + (size_t)R * kHistBins;   // [R][2][4096] after the row histograms
+  k_topk_bin_collect<<<dim3((unsigned)nch, (unsigned)R), dim3(kBinThreads), 0, s>>>(
+      scores, N, n_valid, n_all, hist, K0, K1, fine, rkey, rpos, rcnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_topk_bin_final<<<dim3((unsigned)R), dim3(kFinalThreads), 0, s>>>(
+      N, n_valid, n_all, hist, fine, nch, rkey, rpos, rcnt, K0, out0, K1, out1);
   return hipGetLastError();
 }
 

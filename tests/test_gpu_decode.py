@@ -135,6 +135,14 @@ SMALL = [
     # select (rows over 32768 positions on few rows), on random scores
     dict(name="hier_multiwg", B=4, M=40000, K=512, P=4096, W=128,
          modes=(FULL, REINDEX, REUSE, REINDEX)),
+    # a Top-P too large for the sliced select on long rows: the threshold-bin
+    # select takes the Full layer's Top-P and Top-K together
+    dict(name="hier_bin", B=2, M=70000, K=512, P=8192, W=64, modes=(FULL, REINDEX, REUSE)),
+    # more kept elements than one register tile (the threshold bin is wide)
+    # while those at or above the Top-P's 24-bit prefix fit: compacted first
+    dict(name="hier_bin_compact", B=2, M=100000, K=512, P=12288, W=64, modes=(FULL, REINDEX, REUSE)),
+    # a Top-P of 16384: the kept list is streamed from its chunk regions
+    dict(name="hier_bin_stream", B=2, M=70000, K=256, P=16384, W=64, modes=(FULL, REINDEX)),
 ]
 
 
@@ -171,6 +179,22 @@ def test_decode_hierarchical_all_scores_equal():
         for b in range(cfg.B):
             assert np.array_equal(res[ell]["idx"][b, 0], np.arange(cfg.K, dtype=np.int32))
     check_against_oracle(case, res, src, range(cfg.B))
+    stagewise_topk_exact(case, dc, res)
+
+
+def test_decode_bin_select_all_scores_equal():
+    """All scores 0 on the threshold-bin path: the threshold bin holds the whole
+    row (70000 kept elements, more than one register tile), so the exact select
+    streams them; the Top-P and the Top-K must be the lowest positions."""
+    cfg = CONFIGS[0].scaled(name="bin_ties", seed=8, B=2, M=70000, K=512, P=8192, W=32,
+                            modes=(FULL, REINDEX, REUSE))
+    say("case: decode, threshold-bin select, all index scores equal", cfg.name)
+    case = synth.make_case(cfg)
+    case.pool.idx_key[:] = 0
+    dc, src, res = run_decode(case)
+    for ell in range(cfg.L):
+        for b in range(cfg.B):
+            assert np.array_equal(res[ell]["idx"][b, 0], np.arange(cfg.K, dtype=np.int32))
     stagewise_topk_exact(case, dc, res)
 
 

@@ -72,6 +72,9 @@ def _check_decode(case, dc, lens, P):
     # between P and 32768, below P, below K and 0
     ("hier-multi-wg", 5, 40000, 128, 2048, [40000, 30001, 1500, 100, 0],
      (FULL, REINDEX, REUSE, REINDEX)),
+    # the threshold-bin joint select: lengths full, between P and M, below P,
+    # below K and 0
+    ("hier-bin", 5, 70000, 256, 8192, [70000, 40001, 5000, 100, 0], (FULL, REINDEX, REUSE)),
 ])
 def test_ragged_decode(name, B, M, K, P, lens, modes):
     from fp4_kv_cache_score_amd.device import DeviceCase
