@@ -944,21 +944,29 @@ void k_topk_row(const float* __restrict__ scores, int32_t N,
 
 constexpr int kFinalThreads = 1024;
 constexpr int kSelNW = kFinalThreads / 64;
-constexpr int kGroupSpan = 4 * kFinalThreads;   // positions per element group
 
-struct BlockSelLds {
+// LDS of the block select on NT threads.  A scan slot holds every wave's
+// packed group counts: NT / 64 waves x (PT / 8) words, at most 32 words for
+// the NT x PT <= 16384 elements a block selects from.
+template <int NT>
+struct BlockSelLdsT {
   alignas(16) uint32_t hist[2][kHistBins];   // double-buffered histogram; output staging afterwards
-  uint32_t scan[4][2 * kSelNW];       // rotating scan slots
-  uint32_t res[4][4];                 // rotating digit-search results
-  uint32_t red[3][kSelNW];            // count, min, max per wave
+  uint32_t scan[4][32];                      // rotating scan slots
+  uint32_t res[4][4];                        // rotating digit-search results
+  uint32_t red[3][NT / 64];                  // count, min, max per wave
 };
+using BlockSelLds = BlockSelLdsT<kFinalThreads>;
 
 __device__ __forceinline__ uint32_t key_hi(uint32_t k, int sh) { return sh >= 32 ? 0u : k >> sh; }
 
-// Zero a 4096-bin LDS histogram (16-byte aligned): one 16-byte store per thread.
-__device__ __forceinline__ void zero_hist(uint32_t* h) {
-  static_assert(kHistBins == 4 * kFinalThreads, "one 16-byte store per thread");
-  reinterpret_cast<uint4*>(h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+// Zero a 4096-bin LDS histogram (16-byte aligned) with NT threads, 16 bytes
+// per store.
+template <int NT>
+__device__ __forceinline__ void clear_hist(uint32_t* h) {
+  static_assert(kHistBins % (4 * NT) == 0, "whole 16-byte stores per thread");
+#pragma unroll
+  for (int i = 0; i < kHistBins / (4 * NT); ++i)
+    reinterpret_cast<uint4*>(h)[threadIdx.x + NT * i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Sum, minimum and maximum over the 64 lanes of a wave, in lane 63: DPP row
@@ -993,10 +1001,11 @@ __device__ __forceinline__ Wred wave_reduce3(uint32_t s, uint32_t mn, uint32_t m
 // (each < 2^16) over the block: fields of 16 bits, two groups to a word,
 // scanned together; one barrier.  `slot` must not have been used by the
 // previous three calls.
-template <int G>
+template <int NT, int G>
 __device__ void scan_groups(const uint32_t (&c)[G], uint32_t* slot, uint32_t (&pre)[G],
                             uint32_t (&tot)[G]) {
   constexpr int W = (G + 1) / 2;
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t v[W], x[W];
 #pragma unroll
@@ -1009,7 +1018,7 @@ __device__ void scan_groups(const uint32_t (&c)[G], uint32_t* slot, uint32_t (&p
 #pragma unroll
   for (int w = 0; w < W; ++w) {
     uint32_t before, all;
-    wave_prefix<kSelNW>(slot + w, W, &before, &all);
+    wave_prefix<NW>(slot + w, W, &before, &all);
     const uint32_t ex = before + x[w] - v[w];
     pre[2 * w] = ex & 0xFFFFu;
     tot[2 * w] = all & 0xFFFFu;
@@ -1023,28 +1032,31 @@ __device__ void scan_groups(const uint32_t (&c)[G], uint32_t* slot, uint32_t (&p
 // Digit holding the need-th largest of the 2^w bins (counted from the top):
 // the digit, the count above it and its own count (block-uniform); two
 // barriers, `slot` / `rs` as in scan_groups.
-__device__ void find_digit_c(const uint32_t (&c)[kHistBins / kFinalThreads], int top, uint32_t need,
+template <int NT>
+__device__ void find_digit_c(const uint32_t (&c)[kHistBins / NT], int top, uint32_t need,
                              uint32_t* slot, uint32_t* rs, uint32_t* digit, uint32_t* above,
                              uint32_t* count);
 
+template <int NT>
 __device__ void find_digit(const uint32_t* h, int w, uint32_t need, uint32_t* slot, uint32_t* rs,
                            uint32_t* digit, uint32_t* above, uint32_t* count) {
-  constexpr int kPer = kHistBins / kFinalThreads;     // 4 bins per thread at most
+  constexpr int kPer = kHistBins / NT;                // bins per thread at most
   const int nb = 1 << w;
-  const int per = (nb + kFinalThreads - 1) / kFinalThreads;
+  const int per = (nb + NT - 1) / NT;
   const int top = nb - 1 - (int)threadIdx.x * per;    // thread 0 owns the highest bins
   uint32_t c[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) c[i] = (i < per && top - i >= 0) ? h[top - i] : 0u;
-  find_digit_c(c, top, need, slot, rs, digit, above, count);
+  find_digit_c<NT>(c, top, need, slot, rs, digit, above, count);
 }
 
 // find_digit on this thread's bins in registers: c[i] is bin top - i (0 past
 // the thread's share or below bin 0).
-__device__ void find_digit_c(const uint32_t (&c)[kHistBins / kFinalThreads], int top, uint32_t need,
+template <int NT>
+__device__ void find_digit_c(const uint32_t (&c)[kHistBins / NT], int top, uint32_t need,
                              uint32_t* slot, uint32_t* rs, uint32_t* digit, uint32_t* above,
                              uint32_t* count) {
-  constexpr int kPer = kHistBins / kFinalThreads;
+  constexpr int kPer = kHistBins / NT;
   uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) s += c[i];
@@ -1053,7 +1065,7 @@ __device__ void find_digit_c(const uint32_t (&c)[kHistBins / kFinalThreads], int
   slot[wave] = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);   // every lane: no branch
   __syncthreads();
   uint32_t before, all;
-  wave_prefix<kSelNW>(slot, 1, &before, &all);
+  wave_prefix<NT / 64>(slot, 1, &before, &all);
   const uint32_t ex = before + x - s;
   // the bin holding the need-th count (selects; one lane stores)
   uint32_t acc = ex, fd = 0u, fa = 0u, fc = 0u;
@@ -1084,10 +1096,12 @@ __device__ void find_digit_c(const uint32_t (&c)[kHistBins / kFinalThreads], int
 // digit that holds the K-th key once that group fits the budget.  sel[i] is
 // set for the kept elements of this thread; returns how many are kept
 // (min(K, present) when budget == K).  `round` counts the rotating slots used.
-template <int PT>
+template <int NT, int PT>
 __device__ uint32_t block_select(const uint32_t (&key)[PT], uint32_t K, uint32_t budget,
-                                 BlockSelLds& L, bool (&sel)[PT], int& round) {
+                                 BlockSelLdsT<NT>& L, bool (&sel)[PT], int& round) {
   constexpr int G = PT / 4;
+  constexpr int NW = NT / 64;
+  static_assert(NW * ((G + 1) / 2) <= 32, "the group scan fits a 32-word slot");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t cnt = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
@@ -1102,22 +1116,22 @@ __device__ uint32_t block_select(const uint32_t (&key)[PT], uint32_t K, uint32_t
   L.red[0][wave] = wr.sum;   // wave-uniform values, every lane stores
   L.red[1][wave] = wr.mn;
   L.red[2][wave] = wr.mx;
-  zero_hist(L.hist[0]);
+  clear_hist<NT>(L.hist[0]);
   __syncthreads();
   // the block's count, minimum and maximum: lane k takes wave k's values
   uint32_t tot, rs = 0u, rn = 0xFFFFFFFFu, rx = 0u;
   {
-    const int k = lane < kSelNW ? lane : 0;
-    rs = lane < kSelNW ? L.red[0][k] : 0u;
-    rn = lane < kSelNW ? L.red[1][k] : 0xFFFFFFFFu;
-    rx = lane < kSelNW ? L.red[2][k] : 0u;
+    const int k = lane < NW ? lane : 0;
+    rs = lane < NW ? L.red[0][k] : 0u;
+    rn = lane < NW ? L.red[1][k] : 0xFFFFFFFFu;
+    rx = lane < NW ? L.red[2][k] : 0u;
     wred_step<0x111>(rs, rn, rx);
     wred_step<0x112>(rs, rn, rx);
     wred_step<0x114>(rs, rn, rx);
     wred_step<0x118>(rs, rn, rx);
-    tot = (uint32_t)__builtin_amdgcn_readlane((int)rs, kSelNW - 1);
-    kmin = (uint32_t)__builtin_amdgcn_readlane((int)rn, kSelNW - 1);
-    kmax = (uint32_t)__builtin_amdgcn_readlane((int)rx, kSelNW - 1);
+    tot = (uint32_t)__builtin_amdgcn_readlane((int)rs, NW - 1);
+    kmin = (uint32_t)__builtin_amdgcn_readlane((int)rn, NW - 1);
+    kmax = (uint32_t)__builtin_amdgcn_readlane((int)rx, NW - 1);
   }
   if (tot <= budget) {
 #pragma unroll
@@ -1141,10 +1155,10 @@ __device__ uint32_t block_select(const uint32_t (&key)[PT], uint32_t K, uint32_t
 #pragma unroll
     for (int i = 0; i < PT; ++i)
       if (key[i] && key_hi(key[i], shift) == prefix) atomicAdd(&h[(key[i] >> sh) & mask], 1u);
-    zero_hist(L.hist[buf ^ 1]);
+    clear_hist<NT>(L.hist[buf ^ 1]);
     __syncthreads();
     uint32_t d, ab, c;
-    find_digit(h, w, need, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
+    find_digit<NT>(h, w, need, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
     ++round;
     buf ^= 1;
     prefix = (prefix << w) | d;
@@ -1177,7 +1191,7 @@ __device__ uint32_t block_select(const uint32_t (&key)[PT], uint32_t K, uint32_t
 #pragma unroll
     for (int j = 0; j < 4; ++j) tc[u] += eq[4 * u + j] ? 1u : 0u;
   }
-  scan_groups<G>(tc, L.scan[round & 3], pre, gt);
+  scan_groups<NT, G>(tc, L.scan[round & 3], pre, gt);
   ++round;
   uint32_t before = 0;
 #pragma unroll
@@ -1197,8 +1211,8 @@ __device__ uint32_t block_select(const uint32_t (&key)[PT], uint32_t K, uint32_t
 
 // Output index (in position order) of each kept element of this thread: one
 // scan of the per-group kept counts.
-template <int PT>
-__device__ void kept_order(const bool (&sel)[PT], BlockSelLds& L, int& round, uint32_t (&oidx)[PT]) {
+template <int NT, int PT>
+__device__ void kept_order(const bool (&sel)[PT], BlockSelLdsT<NT>& L, int& round, uint32_t (&oidx)[PT]) {
   constexpr int G = PT / 4;
   uint32_t kc[G], pre[G], gt[G];
 #pragma unroll
@@ -1207,7 +1221,7 @@ __device__ void kept_order(const bool (&sel)[PT], BlockSelLds& L, int& round, ui
 #pragma unroll
     for (int j = 0; j < 4; ++j) kc[u] += sel[4 * u + j] ? 1u : 0u;
   }
-  scan_groups<G>(kc, L.scan[round & 3], pre, gt);
+  scan_groups<NT, G>(kc, L.scan[round & 3], pre, gt);
   ++round;
   uint32_t before = 0;
 #pragma unroll
@@ -1225,22 +1239,23 @@ __device__ void kept_order(const bool (&sel)[PT], BlockSelLds& L, int& round, ui
 // Slice s of row r (positions s * 1024 PT ..): a superset of its K largest
 // keys (at most `slots`), keys and positions in ascending position order, then
 // key 0 up to `slots` (slots [r][s][0 .. slots)).
-template <int PT>
-__global__ __launch_bounds__(kFinalThreads)
+template <int NT, int PT>
+__global__ __launch_bounds__(NT)
 void k_topk_slice(const float* __restrict__ scores, int32_t N, const int32_t* __restrict__ n_valid,
                   int32_t n_all, int32_t K, int32_t slots, uint32_t* __restrict__ ckey,
                   int32_t* __restrict__ cpos) {
   constexpr int G = PT / 4;
-  __shared__ BlockSelLds L;
+  constexpr int GS = 4 * NT;   // positions per element group
+  __shared__ BlockSelLdsT<NT> L;
   const int row = blockIdx.y, s = blockIdx.x;
   const int32_t n = row_count(n_valid, n_all, row, N);
-  const int32_t b0 = s * (kFinalThreads * PT) + 4 * (int32_t)threadIdx.x;   // group 0's first position
+  const int32_t b0 = s * (NT * PT) + 4 * (int32_t)threadIdx.x;   // group 0's first position
   const float* sr = scores + (size_t)row * N;
   uint32_t key[PT];
   const bool vec = (N & 3) == 0 && ((uintptr_t)scores & 15u) == 0;
 #pragma unroll
   for (int u = 0; u < G; ++u) {
-    const int32_t p = b0 + kGroupSpan * u;
+    const int32_t p = b0 + GS * u;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (vec) {
       if (p < n) v = *reinterpret_cast<const float4*>(sr + p);   // p + 3 < N: N is a multiple of 4
@@ -1257,9 +1272,9 @@ void k_topk_slice(const float* __restrict__ scores, int32_t N, const int32_t* __
   }
   bool sel[PT];
   int round = 0;
-  const uint32_t kept = block_select<PT>(key, (uint32_t)K, (uint32_t)slots, L, sel, round);
+  const uint32_t kept = block_select<NT, PT>(key, (uint32_t)K, (uint32_t)slots, L, sel, round);
   uint32_t oidx[PT];
-  kept_order<PT>(sel, L, round, oidx);
+  kept_order<NT, PT>(sel, L, round, oidx);
   const size_t base = ((size_t)row * gridDim.x + s) * slots;
   // the keepers go out through LDS (coalesced stores) when they fit the
   // histogram buffers, which the select no longer needs
@@ -1274,21 +1289,21 @@ void k_topk_slice(const float* __restrict__ scores, int32_t N, const int32_t* __
       if (sel[i]) {
         if (staged) {
           sk[oidx[i]] = key[i];
-          sp[oidx[i]] = b0 + kGroupSpan * u + j;
+          sp[oidx[i]] = b0 + GS * u + j;
         } else {
           ckey[base + oidx[i]] = key[i];
-          cpos[base + oidx[i]] = b0 + kGroupSpan * u + j;
+          cpos[base + oidx[i]] = b0 + GS * u + j;
         }
       }
     }
   if (staged) {
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < kept; i += kFinalThreads) {
+    for (uint32_t i = threadIdx.x; i < kept; i += NT) {
       ckey[base + i] = sk[i];
       cpos[base + i] = sp[i];
     }
   }
-  for (uint32_t i = kept + threadIdx.x; i < (uint32_t)slots; i += kFinalThreads) ckey[base + i] = 0u;
+  for (uint32_t i = kept + threadIdx.x; i < (uint32_t)slots; i += NT) ckey[base + i] = 0u;
 }
 
 // Fused score -> Top-K (flat rows): work-group (s, r) scores slice s of row
@@ -1364,9 +1379,9 @@ void k_score_slice(const uint8_t* __restrict__ key, int64_t M, const uint8_t* __
   uint32_t keyv[4] = {kv[0], kv[1], kv[2], kv[3]};
   bool sel[4];
   int round = 0;
-  const uint32_t kept = block_select<4>(keyv, (uint32_t)K, (uint32_t)slots, L, sel, round);
+  const uint32_t kept = block_select<kFinalThreads, 4>(keyv, (uint32_t)K, (uint32_t)slots, L, sel, round);
   uint32_t oidx[4];
-  kept_order<4>(sel, L, round, oidx);
+  kept_order<kFinalThreads, 4>(sel, L, round, oidx);
   const size_t base = ((size_t)row * gridDim.x + s) * slots;
   const int32_t b0 = s * kFusedSlice + 4 * (int32_t)threadIdx.x;
   // the keepers go out through LDS (coalesced stores): the slice's own keys
@@ -1390,15 +1405,16 @@ void k_score_slice(const uint8_t* __restrict__ key, int64_t M, const uint8_t* __
 // Row r's Top-K as ascending entries (through cand when given), -1 padded.
 // Elements: `total` slots of keepers (ckey / cpos from k_topk_slice, in
 // position order, total a multiple of 4) or, with total == 0, the row's own
-// scores (N <= kFinalThreads * PT).
-template <int PT>
-__global__ __launch_bounds__(kFinalThreads)
+// scores (N <= NT * PT).
+template <int NT, int PT>
+__global__ __launch_bounds__(NT)
 void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __restrict__ n_valid,
                   int32_t n_all, int32_t total, const uint32_t* __restrict__ ckey,
                   const int32_t* __restrict__ cpos, int32_t K, const int32_t* __restrict__ cand_map,
                   int32_t* __restrict__ out) {
   constexpr int G = PT / 4;
-  __shared__ BlockSelLds L;
+  constexpr int GS = 4 * NT;   // positions per element group
+  __shared__ BlockSelLdsT<NT> L;
   const int row = blockIdx.x;
   const int32_t b0 = 4 * (int32_t)threadIdx.x;
   uint32_t key[PT];
@@ -1409,7 +1425,7 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
     const bool vec = (N & 3) == 0 && ((uintptr_t)scores & 15u) == 0;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int32_t p = b0 + kGroupSpan * u;
+      const int32_t p = b0 + GS * u;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (vec) {
         if (p < n) v = *reinterpret_cast<const float4*>(sr + p);
@@ -1431,7 +1447,7 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
     const int32_t* pr = cpos + (size_t)row * total;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int32_t e = b0 + kGroupSpan * u;
+      const int32_t e = b0 + GS * u;
       u32x4 kv = {0u, 0u, 0u, 0u};
       u32x4 pv = {0u, 0u, 0u, 0u};
       if (e < total) {   // total is a multiple of 4
@@ -1447,9 +1463,9 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
   }
   bool sel[PT];
   int round = 0;
-  const uint32_t chosen = block_select<PT>(key, (uint32_t)K, (uint32_t)K, L, sel, round);
+  const uint32_t chosen = block_select<NT, PT>(key, (uint32_t)K, (uint32_t)K, L, sel, round);
   uint32_t oidx[PT];
-  kept_order<PT>(sel, L, round, oidx);
+  kept_order<NT, PT>(sel, L, round, oidx);
   int32_t* orow = out + (size_t)row * K;
   const int32_t* mrow = cand_map ? cand_map + (size_t)row * N : nullptr;
   // positions go out through LDS (coalesced stores, and the map lookups of a
@@ -1465,12 +1481,12 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
   }
   if (staged) {
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < chosen; i += kFinalThreads) {
+    for (uint32_t i = threadIdx.x; i < chosen; i += NT) {
       const int32_t p = sp[i];
       orow[i] = mrow ? mrow[p] : p;
     }
   }
-  for (uint32_t i = chosen + threadIdx.x; i < (uint32_t)K; i += kFinalThreads) orow[i] = -1;
+  for (uint32_t i = chosen + threadIdx.x; i < (uint32_t)K; i += NT) orow[i] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1501,7 +1517,6 @@ void k_topk_bin_collect(const float* __restrict__ scores, int32_t N, const int32
                         uint32_t* __restrict__ fine, uint32_t* __restrict__ rkey,
                         int32_t* __restrict__ rpos, uint32_t* __restrict__ rcnt) {
   __shared__ uint32_t lds[kBinThreads / 64 + 5];
-  __shared__ uint32_t lf[2][kHistBins];     // next 12 bits of each threshold bin's members
   const int row = blockIdx.y, c = blockIdx.x, nch = gridDim.x;
   const int32_t n = row_count(n_valid, n_all, row, N);
   const int32_t c0 = c * kBinChunk;
@@ -1526,7 +1541,6 @@ void k_topk_bin_collect(const float* __restrict__ scores, int32_t N, const int32
     key[4 * u + 2] = p + 2 < n ? score_key(v.z) : 0u;
     key[4 * u + 3] = p + 3 < n ? score_key(v.w) : 0u;
   }
-  for (int i = threadIdx.x; i < 2 * kHistBins; i += kBinThreads) lf[i / kHistBins][i % kHistBins] = 0u;
   int bin[2];
   uint32_t above[2];
   threshold_bins<kBinThreads>(hist + (size_t)row * kHistBins, (uint32_t)K0, (uint32_t)K1, lds, bin,
@@ -1534,19 +1548,15 @@ void k_topk_bin_collect(const float* __restrict__ scores, int32_t N, const int32
   const int b0 = n > K0 ? bin[0] : -1;      // every present position when the row has no more than K0
   const int b1 = K1 > 0 && n > K1 ? bin[1] : -1;
   // the threshold bins' members by their next 12 bits (the final select's
-  // second digit), one atomic per non-empty bin and work-group
+  // second digit): a few hundred per chunk, added straight to the row's fine
+  // histograms
+  uint32_t* fr = fine + (size_t)row * 2 * kHistBins;
 #pragma unroll
   for (int i = 0; i < kBinPer; ++i) {
     const int d = (int)(key[i] >> (32 - kHistBits));
     const uint32_t f = (key[i] >> (32 - 2 * kHistBits)) & (kHistBins - 1);
-    if (key[i] && b0 >= 0 && d == b0) atomicAdd(&lf[0][f], 1u);
-    if (key[i] && b1 >= 0 && d == b1) atomicAdd(&lf[1][f], 1u);
-  }
-  __syncthreads();
-  uint32_t* fr = fine + (size_t)row * 2 * kHistBins;
-  for (int i = threadIdx.x; i < 2 * kHistBins; i += kBinThreads) {
-    const uint32_t v = lf[i / kHistBins][i % kHistBins];
-    if (v) atomicAdd(&fr[i], v);
+    if (key[i] && b0 >= 0 && d == b0) atomicAdd(&fr[f], 1u);
+    if (key[i] && b1 >= 0 && d == b1) atomicAdd(&fr[kHistBins + f], 1u);
   }
   uint32_t cnt = 0;
 #pragma unroll
@@ -1678,7 +1688,7 @@ void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_
     auto first24 = [&](const uint32_t (&fc)[kPer], uint32_t K, int b, uint32_t ab0, BinThr& th,
                        bool& pass) {
       uint32_t d, ab, c;
-      find_digit_c(fc, top, K - ab0, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
+      find_digit_c<kFinalThreads>(fc, top, K - ab0, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
       ++round;
       th = BinThr{32 - 2 * kHistBits, ((uint32_t)b << kHistBits) | d, K - ab0 - ab};
       pass = c != th.take;
@@ -1710,7 +1720,7 @@ void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_
     __syncthreads();
     auto last8 = [&](const uint32_t* h, BinThr& th) {
       uint32_t d, ab, c;
-      find_digit(h, 8, th.take, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
+      find_digit<kFinalThreads>(h, 8, th.take, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
       ++round;
       th = BinThr{0, (th.prefix << 8) | d, th.take - ab};
     };
@@ -1749,7 +1759,7 @@ void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_
       f[2 * u] = __builtin_popcount((mg >> (4 * u)) & 15u);
       f[2 * u + 1] = __builtin_popcount((me >> (4 * u)) & 15u);
     }
-    scan_groups<8>(f, L.scan[round & 3], pf, tt);   // its barrier: every key of the tile read
+    scan_groups<kFinalThreads, 8>(f, L.scan[round & 3], pf, tt);   // its barrier: every key of the tile read
     ++round;
     const uint32_t ob = gb + (eb < th.take ? eb : th.take);   // chosen before this tile
     int32_t* dst = stage ? reinterpret_cast<int32_t*>(L.key) : out + (size_t)row * K + ob;
@@ -1851,6 +1861,35 @@ hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
   return hipGetLastError();
 }
 
+// The slice and final selects run on 1024 threads (16 waves on a CU).
+// Measured at 128K decode: slice 5.8 / 6.4 / 8.8 us and final 6.7 / 8.2 /
+// 12.8 us on 1024 / 512 / 256 threads (the same slices, 4 / 8 / 16
+// positions a thread): the per-wave steps cost fewer issue cycles on fewer
+// waves, but their dependent latencies are no longer hidden.
+template <int NT>
+hipError_t launch_final_nt(dim3 grid, hipStream_t s, int64_t elems, const float* scores, int32_t N,
+                           const int32_t* n_valid, int32_t n_all, int32_t total,
+                           const uint32_t* ckey, const int32_t* cpos, int32_t K,
+                           const int32_t* cand, int32_t* out) {
+  const dim3 block(NT);
+  if (elems <= NT * 4)
+    k_topk_final<NT, 4><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
+  else if (elems <= NT * 8)
+    k_topk_final<NT, 8><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
+  else
+    k_topk_final<NT, 16><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
+  return hipGetLastError();
+}
+
+// k_topk_final over `elems` elements per row (at most kFinalMaxN).
+hipError_t launch_final(dim3 grid, hipStream_t s, int64_t elems, const float* scores, int32_t N,
+                        const int32_t* n_valid, int32_t n_all, int32_t total, const uint32_t* ckey,
+                        const int32_t* cpos, int32_t K, const int32_t* cand, int32_t* out) {
+  static_assert(kFinalThreads * 16 >= kFinalMaxN, "one work-group holds the largest final select");
+  return launch_final_nt<kFinalThreads>(grid, s, elems, scores, N, n_valid, n_all, total, ckey, cpos, K,
+                                        cand, out);
+}
+
 hipError_t launch_topk_sliced(const float* scores, int32_t R, int32_t N,
                               const int32_t* n_valid, int32_t n_all, const int32_t* cand,
                               int32_t K, int32_t* out, void* ws, hipStream_t s) {
@@ -1864,26 +1903,21 @@ hipError_t launch_topk_sliced(const float* scores, int32_t R, int32_t N,
     if (!ws) return hipErrorInvalidValue;
     ckey = (uint32_t*)ws;
     cpos = (int32_t*)((char*)ws + align256((size_t)R * sl.S * sl.slots * 4));
+    // a slice of 1024 pt positions
     const dim3 grid((unsigned)sl.S, (unsigned)R), block(kFinalThreads);
     if (sl.pt == 4)
-      k_topk_slice<4><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
+      k_topk_slice<kFinalThreads, 4><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
     else if (sl.pt == 8)
-      k_topk_slice<8><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
+      k_topk_slice<kFinalThreads, 8><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
     else
-      k_topk_slice<16><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
+      k_topk_slice<kFinalThreads, 16><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, K, sl.slots, ckey, cpos);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     total = sl.S * sl.slots;
     elems = total;
   }
-  const dim3 grid((unsigned)R), block(kFinalThreads);
-  if (elems <= kFinalThreads * 4)
-    k_topk_final<4><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
-  else if (elems <= kFinalThreads * 8)
-    k_topk_final<8><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
-  else
-    k_topk_final<16><<<grid, block, 0, s>>>(scores, N, n_valid, n_all, total, ckey, cpos, K, cand, out);
-  return hipGetLastError();
+  return launch_final(dim3((unsigned)R), s, elems, scores, N, n_valid, n_all, total, ckey, cpos, K,
+                      cand, out);
 }
 
 hipError_t launch_score_topk(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
@@ -1898,14 +1932,8 @@ hipError_t launch_score_topk(const uint8_t* key, int32_t B, int64_t M, const uin
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int32_t total = sl.S * sl.slots;
-  const dim3 grid((unsigned)B), block(kFinalThreads);
-  if (total <= kFinalThreads * 4)
-    k_topk_final<4><<<grid, block, 0, s>>>(nullptr, (int32_t)M, len, (int32_t)M, total, ckey, cpos, K, nullptr, out);
-  else if (total <= kFinalThreads * 8)
-    k_topk_final<8><<<grid, block, 0, s>>>(nullptr, (int32_t)M, len, (int32_t)M, total, ckey, cpos, K, nullptr, out);
-  else
-    k_topk_final<16><<<grid, block, 0, s>>>(nullptr, (int32_t)M, len, (int32_t)M, total, ckey, cpos, K, nullptr, out);
-  return hipGetLastError();
+  return launch_final(dim3((unsigned)B), s, total, nullptr, (int32_t)M, len, (int32_t)M, total, ckey,
+                      cpos, K, nullptr, out);
 }
 
 hipError_t launch_topk_bin_select(const float* scores, int32_t R, int32_t N,

@@ -138,10 +138,10 @@ SMALL = [
     # a Top-P too large for the sliced select on long rows: the threshold-bin
     # select takes the Full layer's Top-P and Top-K together
     dict(name="hier_bin", B=2, M=70000, K=512, P=8192, W=64, modes=(FULL, REINDEX, REUSE)),
-    # more kept elements than one register tile (the threshold bin is wide)
-    # while those at or above the Top-P's 24-bit prefix fit: compacted first
+    # more kept elements than one LDS tile of the exact select (the threshold
+    # bin is wide): the final takes the kept list in two tiles
     dict(name="hier_bin_compact", B=2, M=100000, K=512, P=12288, W=64, modes=(FULL, REINDEX, REUSE)),
-    # a Top-P of 16384: the kept list is streamed from its chunk regions
+    # a Top-P of 16384: kept lists over one tile, both thresholds refined
     dict(name="hier_bin_stream", B=2, M=70000, K=256, P=16384, W=64, modes=(FULL, REINDEX)),
 ]
 
