@@ -1,7 +1,7 @@
 """GPU parity of the chunked-prefill path (Q query tokens per sequence) against the oracle.
 
-The Q > 1 calls run the matrix-core kernels: the FP8 indexer contraction
-(csa2_index_score), and the bf16 attention over each token's selected FP4
+The Q > 1 calls run the matrix-core kernels: the indexer contraction of E4M3
+keys and queries widened exactly to bf16 (csa2_index_score), and the bf16 attention over each token's selected FP4
 entries and its own window rows (csa2_sparse_attn, csa2_swa_merge).  Checked:
 * scores of every (token, entry) within the fp32 bound, -inf where the entry
   is not yet visible to the token (ragged query / entry tiles, causal and not);
