@@ -198,6 +198,22 @@ def test_decode_bin_select_all_scores_equal():
     stagewise_topk_exact(case, dc, res)
 
 
+def test_decode_hier_rows_over_2_20():
+    """Rows of more than 2^20 positions: the Full layer's Top-P and Top-K go to
+    the multi-work-group select with the two finishes side by side (the
+    threshold-bin select holds rows up to 2^20).  Checked stage by stage: the
+    layer's indices equal the oracle's Top-K of the GPU's own scores, and the
+    Reindex layer's equal it within the exact Top-P (the whole oracle step on
+    a million entries would not fit this test's time)."""
+    cfg = CONFIGS[0].scaled(name="hier_over_2_20", seed=21, B=2, M=(1 << 20) + 4096, K=512, P=8192,
+                            W=32, modes=(FULL, REINDEX))
+    say("case: decode, rows over 2^20 positions, joint multi-work-group select", cfg.name)
+    case = synth.make_case(cfg)
+    dc, src, res = run_decode(case)
+    assert list(src) == [0, 1]
+    stagewise_topk_exact(case, dc, res)
+
+
 def test_decode_is_deterministic():
     cfg = CONFIGS[0].scaled(name="det", B=4, M=40000, K=512, P=4096,
                             modes=(FULL, REINDEX, REUSE, REINDEX))
