@@ -450,7 +450,7 @@ int32_t source_layer(const csa2_layer* layers, int32_t l) {
 // histogram and counters are zero on entry and left zero.
 csa2_status decode_one(const csa2_pool* pool, const csa2_layer* layers, int32_t l, int32_t K,
                        int32_t P, int32_t W, const DecodeWs& d, const AttnPlan& plan,
-                       hipStream_t stream) {
+                       const ZeroSpans* zero, hipStream_t stream) {
   const int64_t B = pool->B, M = pool->M;
   const int32_t n_cand = (int32_t)(P < M ? P : M);
   const csa2_layer& y = layers[l];
@@ -458,7 +458,7 @@ csa2_status decode_one(const csa2_pool* pool, const csa2_layer* layers, int32_t 
   if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
     st = hip_status(launch_index_score(pool->idx_key, (int32_t)B, M, y.q_idx, y.w_idx, 1, -1, 1,
                                        nullptr, (int32_t)M, d.scores, nullptr, pool->len,
-                                       pool_map(pool), stream));
+                                       pool_map(pool), stream, zero));
     if (st != CSA2_OK) return st;
     const bool want_p = y.mode == CSA2_FULL && P > 0;
     if (want_p && d.sel.bin) {
@@ -545,38 +545,45 @@ csa2_status decode_one(const csa2_pool* pool, const csa2_layer* layers, int32_t 
   return hip_status(launch_attn(a, plan, stream));
 }
 
-// Zero the multi-work-group select's histograms and counters (the selects
-// leave them zeroed again).
-csa2_status zero_big(const DecodeWs& d, int64_t B, int32_t P, hipStream_t stream) {
-  csa2_status st = zero_hist_counters(d.t, B, stream);
-  if (st == CSA2_OK && P > 0) st = zero_hist_counters(d.t2, B, stream);
-  return st;
-}
-
-// Zero what the Full layer's selects need zeroed on entry (they leave it
-// zeroed again): the multi-work-group select's histograms and counters, the
-// threshold-bin select's histogram.
-csa2_status zero_full_layer(const DecodeWs& d, int64_t B, int32_t P, hipStream_t stream) {
-  csa2_status st = CSA2_OK;
-  if (d.big) st = zero_big(d, B, P, stream);
-  if (st == CSA2_OK && d.sel.bin)
-    st = hip_status(launch_fill_zero(d.hist, topk_bin_hist_words(B), stream));
-  return st;
+// What a Full layer's selects need zeroed on entry (they leave it zeroed
+// again): the multi-work-group select's histograms and counters, the
+// threshold-bin select's histograms.  The layer's scan clears them on the
+// side; nullptr when nothing is needed.
+const ZeroSpans* full_layer_zero(const DecodeWs& d, int64_t B, int32_t P, ZeroSpans* z) {
+  *z = ZeroSpans{{nullptr, nullptr, nullptr}, {0, 0, 0}};
+  int k = 0;
+  auto add = [&](uint32_t* p, int64_t n) {
+    z->p[k] = p;
+    z->n[k] = n;
+    ++k;
+  };
+  auto hist_counters = [&](const TopkWs& t) {
+    return (int64_t)((char*)t.counters - (char*)t.hist) / 4 + B * kCounterWords;
+  };
+  if (d.big) {
+    add(d.t.hist, hist_counters(d.t));
+    if (P > 0) add(d.t2.hist, hist_counters(d.t2));
+  }
+  if (d.sel.bin) add(d.hist, topk_bin_hist_words(B));
+  return k > 0 ? z : nullptr;
 }
 
 // Every layer of a decode step on a checked, large enough workspace.  What
-// must start at zero (the multi-work-group select's histograms and counters)
-// is cleared here by a fill kernel; everything else in the workspace is
-// written before it is read.
+// must start at zero (the selects' histograms and counters) is cleared by
+// layer 0's scan on the side, a kernel like every other step of the call
+// (so the call can be captured in a graph); the selects leave it zeroed for
+// the later Full layers, and everything else in the workspace is written
+// before it is read.
 csa2_status decode_step(const csa2_pool* pool, const csa2_layer* layers, int32_t L, int32_t K,
                         int32_t P, int32_t W, int32_t* src_layer, void* ws, hipStream_t stream) {
   const int64_t B = pool->B;
   const DecodeWs d = decode_ws_carve(ws, B, pool->M, K, P, W);
   const AttnPlan plan = attn_plan(B, attn_steps(K, W));
-  csa2_status st = zero_full_layer(d, B, P, stream);
-  if (st != CSA2_OK) return st;
+  ZeroSpans zs;
+  const ZeroSpans* zero = full_layer_zero(d, B, P, &zs);   // layer 0 is Full: its scan clears them
+  csa2_status st = CSA2_OK;
   for (int32_t l = 0; l < L; ++l) {
-    st = decode_one(pool, layers, l, K, P, W, d, plan, stream);
+    st = decode_one(pool, layers, l, K, P, W, d, plan, l == 0 ? zero : nullptr, stream);
     if (st != CSA2_OK) return st;
     if (src_layer) src_layer[l] = source_layer(layers, l);
   }
@@ -640,11 +647,10 @@ csa2_status csa2_decode_layer(const csa2_pool* pool, const csa2_layer* layers, i
   const DecodeWs d = decode_ws_carve(ws, B, pool->M, K, P, W);
   const AttnPlan plan = attn_plan(B, attn_steps(K, W));
   const csa2_layer& y = layers[l];
-  if (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0)) {
-    st = zero_full_layer(d, B, P, stream);
-    if (st != CSA2_OK) return st;
-  }
-  st = decode_one(pool, layers, l, K, P, W, d, plan, stream);
+  ZeroSpans zs;
+  const ZeroSpans* zero = (y.mode == CSA2_FULL || (y.mode == CSA2_REINDEX && P == 0))
+                              ? full_layer_zero(d, B, P, &zs) : nullptr;
+  st = decode_one(pool, layers, l, K, P, W, d, plan, zero, stream);
   if (st == CSA2_OK && src_layer) *src_layer = source_layer(layers, l);
   return st;
 }

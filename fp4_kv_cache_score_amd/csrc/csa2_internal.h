@@ -208,14 +208,24 @@ inline TopkWs topk_ws_carve(void* ws, int64_t R, int64_t N, int64_t K) {
 // Zero n 32-bit words (a kernel, so that it is safe inside captured graphs).
 hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t s);
 
+// Up to three spans of 32-bit words that a launch zeroes on the side, for the
+// launches after it on the stream (16-byte aligned, n a multiple of 4;
+// n = 0: unused).
+struct ZeroSpans {
+  uint32_t* p[3];
+  int64_t n[3];
+};
+
 // Indexer scores; see csa2_index_score.  len (optional, [B]): sequence b has
 // len[b] <= M entries (a ragged batch); entries at or past it score -inf.
+// zero (optional): spans the scan's first work-groups clear as well (one
+// fill launch fewer ahead of a select that needs zeroed counters).
 hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
                               const uint8_t* q_idx, const float* w_idx,
                               int32_t Q, int64_t pos0, int32_t ratio,
                               const int32_t* cand, int32_t N, float* scores,
                               uint32_t* hist, const int32_t* len, const PoolMap& map,
-                              hipStream_t s);
+                              hipStream_t s, const ZeroSpans* zero = nullptr);
 
 // Top-K pieces.  n_valid: device [R] or NULL (then n_all applies to every row).
 // launch_topk_rows: one work-group per row, N <= kRowMaxN.  hist: NULL (the

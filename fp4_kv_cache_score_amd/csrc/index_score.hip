@@ -33,8 +33,16 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
                    const float* __restrict__ w_idx, int32_t Q, int64_t pos0,
                    int32_t ratio, const int32_t* __restrict__ cand, int32_t N,
                    float* __restrict__ scores, uint32_t* __restrict__ hist,
-                   const int32_t* __restrict__ len, PoolMap map) {
+                   const int32_t* __restrict__ len, PoolMap map, ZeroSpans zs) {
   constexpr int kEntriesPerWG = EPW * (kThreads / 64);
+  {  // the spans to clear on the side: 16 bytes per thread of the first work-groups
+    const int64_t t = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t q0 = zs.n[0] / 4, q1 = q0 + zs.n[1] / 4, q2 = q1 + zs.n[2] / 4;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    if (t < q0) reinterpret_cast<uint4*>(zs.p[0])[t] = z;
+    else if (t < q1) reinterpret_cast<uint4*>(zs.p[1])[t - q0] = z;
+    else if (t < q2) reinterpret_cast<uint4*>(zs.p[2])[t - q1] = z;
+  }
   constexpr int kIters = EPW / (2 * kUnroll);
   static_assert(EPW % (2 * kUnroll) == 0, "EPW must be a multiple of 16");
   __shared__ uint32_t lh[kHist ? kHistBins : 1];
@@ -134,23 +142,37 @@ void k_index_score(const uint8_t* __restrict__ key, int64_t M,
 }
 
 template <int EPW>
-void launch_epw(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
-                const float* w_idx, int32_t Q, int64_t pos0, int32_t ratio, const int32_t* cand,
-                int32_t N, float* scores, uint32_t* hist, const int32_t* len, const PoolMap& map,
-                hipStream_t s) {
+hipError_t launch_epw(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,
+                      const float* w_idx, int32_t Q, int64_t pos0, int32_t ratio,
+                      const int32_t* cand, int32_t N, float* scores, uint32_t* hist,
+                      const int32_t* len, const PoolMap& map, hipStream_t s,
+                      const ZeroSpans* zero) {
   const dim3 grid((unsigned)((N + EPW * 4 - 1) / (EPW * 4)), (unsigned)(B * Q));
   const dim3 block(kThreads);
+  ZeroSpans zs{{nullptr, nullptr, nullptr}, {0, 0, 0}};
+  if (zero) {
+    const int64_t threads = (int64_t)grid.x * grid.y * kThreads;
+    int64_t words = 0;
+    for (int i = 0; i < 3; ++i) {
+      if (zero->n[i] < 0 || (zero->n[i] & 3) || (zero->n[i] && ((uintptr_t)zero->p[i] & 15)))
+        return hipErrorInvalidValue;
+      words += zero->n[i];
+    }
+    if (words / 4 > threads) return hipErrorInvalidValue;
+    zs = *zero;
+  }
   if (cand) {
     if (hist)
-      k_index_score<EPW, true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map);
+      k_index_score<EPW, true, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, zs);
     else
-      k_index_score<EPW, true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map);
+      k_index_score<EPW, true, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, zs);
   } else {
     if (hist)
-      k_index_score<EPW, false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map);
+      k_index_score<EPW, false, true><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, zs);
     else
-      k_index_score<EPW, false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map);
+      k_index_score<EPW, false, false><<<grid, block, 0, s>>>(key, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, zs);
   }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -160,16 +182,16 @@ hipError_t launch_index_score(const uint8_t* key, int32_t B, int64_t M,
                               int32_t Q, int64_t pos0, int32_t ratio,
                               const int32_t* cand, int32_t N, float* scores,
                               uint32_t* hist, const int32_t* len, const PoolMap& map,
-                              hipStream_t s) {
+                              hipStream_t s, const ZeroSpans* zero) {
   // 64 entries per wave (256 per work-group) keep enough loads in flight on
   // long rows; short rows (candidate pools) take 32 so that the launch still
   // has >= 1024 work-groups.
   const int64_t rows = (int64_t)B * Q;
   if (rows * ((N + 255) / 256) >= 1024)
-    launch_epw<64>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, s);
-  else
-    launch_epw<32>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, s);
-  return hipGetLastError();
+    return launch_epw<64>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, s,
+                          zero);
+  return launch_epw<32>(key, B, M, q_idx, w_idx, Q, pos0, ratio, cand, N, scores, hist, len, map, s,
+                        zero);
 }
 
 }  // namespace csa2

@@ -1497,16 +1497,13 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
 // row's Top-K0 (which holds its Top-K1, K1 <= K0), each 4096-position chunk
 // into a region of its own in position order (one block scan, no atomics),
 // and counts the members of the K0-th and the K1-th key's bins by their next
-// 12 bits (fine histograms).  k_topk_bin_final then selects, per row, the K0
-// and the K1 largest of the kept elements exactly under the (key, lower
-// position) order: the first 24 bits of each threshold come from the two
-// histograms; when the kept list exceeds one register tile (16384) but the
-// elements at or above the K0 threshold's 24 bits fit, those are compacted
-// in list order into the row's scratch list; one more radix pass over the
-// last 8 bits (an LDS histogram) finishes each threshold; ties go to the
-// earlier element, both lists are written ascending.  Kept lists that do not
-// fit are streamed from the regions.  The final clears the row's histograms
-// for the next use.
+// 12 bits (fine histograms, device-scope atomics).  k_topk_bin_final then
+// selects, per row, the K0 and the K1 largest of the kept elements exactly
+// under the (key, lower position) order: the kept list goes to LDS (direct
+// global-to-LDS transfers, 16384 elements a tile); the first 24 bits of each
+// threshold come from the two histograms and one pass over the list's low
+// bytes gives the last 8; ties go to the earlier element and both lists are
+// written ascending.  The final clears the row's histograms for the next use.
 // ---------------------------------------------------------------------------
 constexpr int kBinThreads = 256;
 constexpr int kBinPer = kBinChunk / kBinThreads;     // 16 consecutive positions per thread
