@@ -1420,27 +1420,43 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
   uint32_t key[PT];
   int32_t pos[PT];
   if (total == 0) {
+    // the row's own scores; with a candidate list, each element's entry
+    // number comes in with its score (no lookup after the select)
     const int32_t n = row_count(n_valid, n_all, row, N);
     const float* sr = scores + (size_t)row * N;
-    const bool vec = (N & 3) == 0 && ((uintptr_t)scores & 15u) == 0;
+    const int32_t* mr = cand_map ? cand_map + (size_t)row * N : nullptr;
+    const bool vec = (N & 3) == 0 && ((uintptr_t)scores & 15u) == 0 &&
+                     ((uintptr_t)cand_map & 15u) == 0;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int32_t p = b0 + GS * u;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      int4 m = make_int4(p, p + 1, p + 2, p + 3);
       if (vec) {
-        if (p < n) v = *reinterpret_cast<const float4*>(sr + p);
+        if (p < n) {
+          v = *reinterpret_cast<const float4*>(sr + p);
+          if (mr) m = *reinterpret_cast<const int4*>(mr + p);
+        }
       } else {
         v.x = p < n ? sr[p] : 0.f;
         v.y = p + 1 < n ? sr[p + 1] : 0.f;
         v.z = p + 2 < n ? sr[p + 2] : 0.f;
         v.w = p + 3 < n ? sr[p + 3] : 0.f;
+        if (mr) {
+          m.x = p < n ? mr[p] : 0;
+          m.y = p + 1 < n ? mr[p + 1] : 0;
+          m.z = p + 2 < n ? mr[p + 2] : 0;
+          m.w = p + 3 < n ? mr[p + 3] : 0;
+        }
       }
       key[4 * u + 0] = p + 0 < n ? score_key(v.x) : 0u;
       key[4 * u + 1] = p + 1 < n ? score_key(v.y) : 0u;
       key[4 * u + 2] = p + 2 < n ? score_key(v.z) : 0u;
       key[4 * u + 3] = p + 3 < n ? score_key(v.w) : 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pos[4 * u + j] = p + j;
+      pos[4 * u + 0] = m.x;
+      pos[4 * u + 1] = m.y;
+      pos[4 * u + 2] = m.z;
+      pos[4 * u + 3] = m.w;
     }
   } else {
     const uint32_t* kr = ckey + (size_t)row * total;
@@ -1467,7 +1483,9 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
   uint32_t oidx[PT];
   kept_order<NT, PT>(sel, L, round, oidx);
   int32_t* orow = out + (size_t)row * K;
-  const int32_t* mrow = cand_map ? cand_map + (size_t)row * N : nullptr;
+  // keepers' positions still go through the candidate list (the row's own
+  // elements carry their entry numbers already)
+  const int32_t* mrow = cand_map && total > 0 ? cand_map + (size_t)row * N : nullptr;
   // positions go out through LDS (coalesced stores, and the map lookups of a
   // candidate list one per thread) when they fit the histogram buffers
   const bool staged = chosen <= 2 * kHistBins;
