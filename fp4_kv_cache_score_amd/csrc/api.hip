@@ -446,8 +446,8 @@ int32_t source_layer(const csa2_layer* layers, int32_t l) {
 }
 
 // Layer l of a decode step: its index work (Full / Reindex), the copy a
-// Reuse layer asks for, and its attention.  The multi-work-group select's
-// histogram and counters are zero on entry and left zero.
+// Reuse layer asks for, and its attention.  zero: what a Full (or flat
+// Reindex) layer's scan clears on the side for its selects.
 csa2_status decode_one(const csa2_pool* pool, const csa2_layer* layers, int32_t l, int32_t K,
                        int32_t P, int32_t W, const DecodeWs& d, const AttnPlan& plan,
                        const ZeroSpans* zero, hipStream_t stream) {
@@ -545,10 +545,10 @@ csa2_status decode_one(const csa2_pool* pool, const csa2_layer* layers, int32_t 
   return hip_status(launch_attn(a, plan, stream));
 }
 
-// What a Full layer's selects need zeroed on entry (they leave it zeroed
-// again): the multi-work-group select's histograms and counters, the
-// threshold-bin select's histograms.  The layer's scan clears them on the
-// side; nullptr when nothing is needed.
+// What a Full layer's selects need zeroed on entry: the multi-work-group
+// select's histograms and counters (which it leaves zeroed again) and the
+// threshold-bin select's histograms (which it leaves filled).  The layer's
+// scan clears them on the side; nullptr when nothing is needed.
 const ZeroSpans* full_layer_zero(const DecodeWs& d, int64_t B, int32_t P, ZeroSpans* z) {
   *z = ZeroSpans{{nullptr, nullptr, nullptr}, {0, 0, 0}};
   int k = 0;
@@ -570,20 +570,19 @@ const ZeroSpans* full_layer_zero(const DecodeWs& d, int64_t B, int32_t P, ZeroSp
 
 // Every layer of a decode step on a checked, large enough workspace.  What
 // must start at zero (the selects' histograms and counters) is cleared by
-// layer 0's scan on the side, a kernel like every other step of the call
-// (so the call can be captured in a graph); the selects leave it zeroed for
-// the later Full layers, and everything else in the workspace is written
-// before it is read.
+// each Full layer's scan on the side, a kernel like every other step of the
+// call (so the call can be captured in a graph); everything else in the
+// workspace is written before it is read.
 csa2_status decode_step(const csa2_pool* pool, const csa2_layer* layers, int32_t L, int32_t K,
                         int32_t P, int32_t W, int32_t* src_layer, void* ws, hipStream_t stream) {
   const int64_t B = pool->B;
   const DecodeWs d = decode_ws_carve(ws, B, pool->M, K, P, W);
   const AttnPlan plan = attn_plan(B, attn_steps(K, W));
   ZeroSpans zs;
-  const ZeroSpans* zero = full_layer_zero(d, B, P, &zs);   // layer 0 is Full: its scan clears them
+  const ZeroSpans* zero = full_layer_zero(d, B, P, &zs);
   csa2_status st = CSA2_OK;
   for (int32_t l = 0; l < L; ++l) {
-    st = decode_one(pool, layers, l, K, P, W, d, plan, l == 0 ? zero : nullptr, stream);
+    st = decode_one(pool, layers, l, K, P, W, d, plan, zero, stream);
     if (st != CSA2_OK) return st;
     if (src_layer) src_layer[l] = source_layer(layers, l);
   }

@@ -172,7 +172,8 @@ inline size_t score_topk_ws_bytes(int64_t R, int64_t N, int64_t K) {
 // 4096-position chunk, keys and positions [R][chunks][4096] and counts
 // [R][chunks].
 // Its histograms (row [R][4096], then the threshold bins' next digit
-// [R][2][4096], topk_bin_hist_words) start zeroed and are left zeroed.
+// [R][2][4096], topk_bin_hist_words) must be zeroed before each select; the
+// select leaves them filled.
 constexpr int kBinChunk = 4096;
 constexpr int kBinMaxChunks = 256;   // rows up to 2^20 positions
 inline bool topk_bin_taken(int64_t N) { return N > 0 && N <= (int64_t)kBinChunk * kBinMaxChunks; }
@@ -209,8 +210,9 @@ inline TopkWs topk_ws_carve(void* ws, int64_t R, int64_t N, int64_t K) {
 hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t s);
 
 // Up to three spans of 32-bit words that a launch zeroes on the side, for the
-// launches after it on the stream (16-byte aligned, n a multiple of 4;
-// n = 0: unused).
+// launches after it on the stream (n = 0: unused).  The scan takes them when
+// they are 16-byte aligned multiples of 4 words that its grid covers, 16
+// bytes per thread; otherwise fill launches ahead of it clear them.
 struct ZeroSpans {
   uint32_t* p[3];
   int64_t n[3];
@@ -249,7 +251,7 @@ hipError_t launch_topk_hist(const float* scores, int32_t R, int32_t N,
                             const int32_t* n_valid, int32_t n_all,
                             uint32_t* hist, hipStream_t s);
 // Threshold-bin select on scores whose histogram is in hist (topk_bin_taken(N);
-// hist holds topk_bin_hist_words words, zeroed on entry, zeroed on return):
+// hist holds topk_bin_hist_words words, zeroed on entry, filled on return):
 // the K0 largest of each row to out0 and the K1 largest (K1 <= K0; 0: none)
 // to out1, both ascending; ws holds topk_bin_ws_bytes; hist is left zeroed.
 hipError_t launch_topk_bin_select(const float* scores, int32_t R, int32_t N,

@@ -151,15 +151,24 @@ hipError_t launch_epw(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q
   const dim3 block(kThreads);
   ZeroSpans zs{{nullptr, nullptr, nullptr}, {0, 0, 0}};
   if (zero) {
+    // spans the grid cannot take 16 bytes per thread go to fill launches
     const int64_t threads = (int64_t)grid.x * grid.y * kThreads;
     int64_t words = 0;
+    bool side = true;
     for (int i = 0; i < 3; ++i) {
-      if (zero->n[i] < 0 || (zero->n[i] & 3) || (zero->n[i] && ((uintptr_t)zero->p[i] & 15)))
-        return hipErrorInvalidValue;
+      if (zero->n[i] < 0) return hipErrorInvalidValue;
+      side = side && !(zero->n[i] & 3) && !(zero->n[i] && ((uintptr_t)zero->p[i] & 15));
       words += zero->n[i];
     }
-    if (words / 4 > threads) return hipErrorInvalidValue;
-    zs = *zero;
+    if (side && words / 4 <= threads) {
+      zs = *zero;
+    } else {
+      for (int i = 0; i < 3; ++i) {
+        if (!zero->n[i]) continue;
+        const hipError_t e = launch_fill_zero(zero->p[i], zero->n[i], s);
+        if (e != hipSuccess) return e;
+      }
+    }
   }
   if (cand) {
     if (hist)

@@ -1521,7 +1521,9 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
 // global-to-LDS transfers, 16384 elements a tile); the first 24 bits of each
 // threshold come from the two histograms and one pass over the list's low
 // bytes gives the last 8; ties go to the earlier element and both lists are
-// written ascending.  The final clears the row's histograms for the next use.
+// written ascending, the two selects of a row in work-groups of their own.
+// The histograms must be zeroed before the histogram pass (the decode step's
+// scan clears them on the side); nothing here clears them.
 // ---------------------------------------------------------------------------
 constexpr int kBinThreads = 256;
 constexpr int kBinPer = kBinChunk / kBinThreads;     // 16 consecutive positions per thread
@@ -1616,27 +1618,29 @@ struct BinLds {
   uint32_t res[4][4];
 };
 
+// One select of a row per work-group: blockIdx.y = 0 takes the K0 largest
+// into out0, 1 the K1 largest into out1 (the two run side by side; they
+// share only the kept list and the histograms, which neither writes).
 __global__ __launch_bounds__(kFinalThreads)
 void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_all,
-                      uint32_t* __restrict__ hist, uint32_t* __restrict__ fine, int32_t nch,
-                      const uint32_t* __restrict__ rkey, const int32_t* __restrict__ rpos,
+                      const uint32_t* __restrict__ hist, const uint32_t* __restrict__ fine,
+                      int32_t nch, const uint32_t* __restrict__ rkey, const int32_t* __restrict__ rpos,
                       const uint32_t* __restrict__ rcnt, int32_t K0, int32_t* __restrict__ out0,
                       int32_t K1, int32_t* __restrict__ out1) {
   constexpr int kPer = kHistBins / kFinalThreads;   // 4 bins of each histogram per thread
   static_assert(kPer == 4, "one 16-byte slice of each histogram per thread");
   __shared__ __attribute__((aligned(16))) BinLds L;
-  const int row = blockIdx.x;
+  const int row = blockIdx.x, which = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n = row_count(n_valid, n_all, row, N);
-  uint32_t* hrow = hist + (size_t)row * kHistBins;
-  uint32_t* frow = fine + (size_t)row * 2 * kHistBins;
+  const int32_t K = which == 0 ? K0 : K1;
+  int32_t* orow = (which == 0 ? out0 : out1) + (size_t)row * K;
   // one round trip for the chunk counts and this thread's share of the row
-  // histogram and of both fine histograms
+  // histogram and of this select's fine histogram
   const uint32_t v = tid < nch ? rcnt[(size_t)row * nch + tid] : 0u;
-  uint32_t hc[kPer], f0c[kPer], f1c[kPer];
-  hist_slice(hrow, hc);
-  hist_slice(frow, f0c);
-  hist_slice(frow + kHistBins, f1c);
+  uint32_t hc[kPer], fc[kPer];
+  hist_slice(hist + (size_t)row * kHistBins, hc);
+  hist_slice(fine + ((size_t)row * 2 + which) * kHistBins, fc);
   int round = 0;
   {
     uint32_t tot;
@@ -1684,36 +1688,29 @@ void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_
     k4[2] = e + 2 < cnt ? kv.z : 0u;
     k4[3] = e + 3 < cnt ? kv.w : 0u;
   };
-  if (ntiles > 0) issue_tile(0);   // in flight while the thresholds are found
+  if (ntiles > 0) issue_tile(0);   // in flight while the threshold is found
 
-  // Thresholds.  A row with at most K present positions keeps all of them.
-  // Otherwise the first 24 bits come from the row histogram and the
+  // The threshold.  A row with at most K present positions keeps all of
+  // them.  Otherwise the first 24 bits come from the row histogram and the
   // threshold bin's fine histogram; unless that whole 24-bit group is
   // chosen, one pass over the list's low bytes gives the last 8.
-  const bool g0 = n > K0, g1 = K1 > 0 && n > K1;
-  BinThr th0{32, 0u, T}, th1{32, 0u, T};
-  bool pass0 = false, pass1 = false;
-  {
+  BinThr th{32, 0u, T};
+  bool pass = false;
+  if (n > K) {
     int bin[2];
     uint32_t above[2];
-    threshold_bins_c<kFinalThreads>(hc, g0 ? (uint32_t)K0 : 0u, g1 ? (uint32_t)K1 : 0u,
-                                    L.scan[round & 3], bin, above);
+    threshold_bins_c<kFinalThreads>(hc, (uint32_t)K, 0u, L.scan[round & 3], bin, above);
     ++round;
-    const int top = kHistBins - 1 - kPer * tid;
-    auto first24 = [&](const uint32_t (&fc)[kPer], uint32_t K, int b, uint32_t ab0, BinThr& th,
-                       bool& pass) {
-      uint32_t d, ab, c;
-      find_digit_c<kFinalThreads>(fc, top, K - ab0, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
-      ++round;
-      th = BinThr{32 - 2 * kHistBits, ((uint32_t)b << kHistBits) | d, K - ab0 - ab};
-      pass = c != th.take;
-    };
-    if (g0) first24(f0c, (uint32_t)K0, bin[0], above[0], th0, pass0);
-    if (g1) first24(f1c, (uint32_t)K1, bin[1], above[1], th1, pass1);
+    uint32_t d, ab, c;
+    find_digit_c<kFinalThreads>(fc, kHistBins - 1 - kPer * tid, (uint32_t)K - above[0],
+                                L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
+    ++round;
+    th = BinThr{32 - 2 * kHistBits, ((uint32_t)bin[0] << kHistBits) | d, (uint32_t)K - above[0] - ab};
+    pass = c != th.take;
   }
   if (ntiles > 0) wait_tile();
-  if (pass0 || pass1) {
-    for (int i = tid; i < 2 * 256; i += kFinalThreads) L.h[i >> 8][i & 255] = 0u;
+  if (pass) {
+    for (int i = tid; i < 256; i += kFinalThreads) L.h[0][i] = 0u;
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       if (t > 0) {
@@ -1726,21 +1723,15 @@ void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_
         uint32_t k4[4];
         group_keys(u, tile_count(t), k4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (pass0 && k4[j] && (k4[j] >> 8) == th0.prefix) atomicAdd(&L.h[0][k4[j] & 255u], 1u);
-          if (pass1 && k4[j] && (k4[j] >> 8) == th1.prefix) atomicAdd(&L.h[1][k4[j] & 255u], 1u);
-        }
+        for (int j = 0; j < 4; ++j)
+          if (k4[j] && (k4[j] >> 8) == th.prefix) atomicAdd(&L.h[0][k4[j] & 255u], 1u);
       }
     }
     __syncthreads();
-    auto last8 = [&](const uint32_t* h, BinThr& th) {
-      uint32_t d, ab, c;
-      find_digit<kFinalThreads>(h, 8, th.take, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
-      ++round;
-      th = BinThr{0, (th.prefix << 8) | d, th.take - ab};
-    };
-    if (pass0) last8(L.h[0], th0);
-    if (pass1) last8(L.h[1], th1);
+    uint32_t d, ab, c;
+    find_digit<kFinalThreads>(L.h[0], 8, th.take, L.scan[round & 3], L.res[round & 3], &d, &ab, &c);
+    ++round;
+    th = BinThr{0, (th.prefix << 8) | d, th.take - ab};
     if (ntiles > 1) {
       __syncthreads();
       issue_tile(0);
@@ -1748,14 +1739,18 @@ void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_
     }
   }
 
-  // Output: an element's index in a select's list is the number chosen
-  // before it in list order, (greater before) + min(equal before, take).
-  // Select 1 (short) stores directly; select 0 stages its tile's share in
-  // the key array (dead once its counts are scanned), then stores it
-  // coalesced.
-  uint32_t gb0 = 0, eb0 = 0, gb1 = 0, eb1 = 0;
-  auto emit = [&](uint32_t cnt, const BinThr& th, uint32_t& gb, uint32_t& eb, int32_t K, int32_t* out,
-                  bool stage) {
+  // Output: an element's index in the list is the number chosen before it
+  // in list order, (greater before) + min(equal before, take).  A tile's
+  // share is staged in the key array (dead once its counts are scanned) and
+  // stored coalesced.
+  uint32_t gb = 0, eb = 0;
+  for (int t = 0; t < ntiles; ++t) {
+    if (t > 0) {
+      __syncthreads();   // the staged share of the last tile has been stored
+      issue_tile(t);
+      wait_tile();
+    }
+    const uint32_t cnt = tile_count(t);
     uint32_t mg = 0u, me = 0u;   // bit 4 u + j: element greater than / equal to the threshold prefix
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1774,10 +1769,10 @@ void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_
       f[2 * u] = __builtin_popcount((mg >> (4 * u)) & 15u);
       f[2 * u + 1] = __builtin_popcount((me >> (4 * u)) & 15u);
     }
-    scan_groups<kFinalThreads, 8>(f, L.scan[round & 3], pf, tt);   // its barrier: every key of the tile read
+    scan_groups<kFinalThreads, 8>(f, L.scan[round & 3], pf, tt);   // its barrier: every key read
     ++round;
     const uint32_t ob = gb + (eb < th.take ? eb : th.take);   // chosen before this tile
-    int32_t* dst = stage ? reinterpret_cast<int32_t*>(L.key) : out + (size_t)row * K + ob;
+    int32_t* stage = reinterpret_cast<int32_t*>(L.key);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       uint32_t g = gb + pf[2 * u], e = eb + pf[2 * u + 1];
@@ -1787,39 +1782,20 @@ void k_topk_bin_final(int32_t N, const int32_t* __restrict__ n_valid, int32_t n_
       for (int j = 0; j < 4; ++j) {
         const bool gt = (mg >> (4 * u + j)) & 1u, eq = (me >> (4 * u + j)) & 1u;
         const uint32_t o = g + (e < th.take ? e : th.take);
-        if ((gt || (eq && e < th.take)) && o < (uint32_t)K) dst[o - ob] = ps[j];
+        if ((gt || (eq && e < th.take)) && o < (uint32_t)K) stage[o - ob] = ps[j];
         g += gt ? 1u : 0u;
         e += eq ? 1u : 0u;
       }
       gb += tt[2 * u];
       eb += tt[2 * u + 1];
     }
-    if (stage) {
-      const uint32_t oe = gb + (eb < th.take ? eb : th.take);
-      const uint32_t m = (oe < (uint32_t)K ? oe : (uint32_t)K) - (ob < (uint32_t)K ? ob : (uint32_t)K);
-      __syncthreads();
-      int32_t* og = out + (size_t)row * K + ob;
-      for (uint32_t i = tid; i < m; i += kFinalThreads) og[i] = dst[i];
-    }
-  };
-  for (int t = 0; t < ntiles; ++t) {
-    if (t > 0) {
-      __syncthreads();   // the staged share of the last tile has been stored
-      issue_tile(t);
-      wait_tile();
-    }
-    if (K1 > 0) emit(tile_count(t), th1, gb1, eb1, K1, out1, false);
-    emit(tile_count(t), th0, gb0, eb0, K0, out0, true);
+    const uint32_t oe = gb + (eb < th.take ? eb : th.take);
+    const uint32_t m = (oe < (uint32_t)K ? oe : (uint32_t)K) - (ob < (uint32_t)K ? ob : (uint32_t)K);
+    __syncthreads();
+    for (uint32_t i = tid; i < m; i += kFinalThreads) orow[ob + i] = stage[i];
   }
-  const uint32_t c0 = gb0 + (eb0 < th0.take ? eb0 : th0.take);
-  const uint32_t c1 = gb1 + (eb1 < th1.take ? eb1 : th1.take);
-  for (uint32_t i = c0 + tid; i < (uint32_t)K0; i += kFinalThreads) out0[(size_t)row * K0 + i] = -1;
-  for (uint32_t i = c1 + tid; i < (uint32_t)K1; i += kFinalThreads) out1[(size_t)row * K1 + i] = -1;
-  // leave the row's histograms zeroed for the next select
-  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-  reinterpret_cast<uint4*>(hrow)[tid] = z;
-  reinterpret_cast<uint4*>(frow)[tid] = z;
-  reinterpret_cast<uint4*>(frow)[tid + kFinalThreads] = z;
+  const uint32_t chosen = gb + (eb < th.take ? eb : th.take);
+  for (uint32_t i = chosen + tid; i < (uint32_t)K; i += kFinalThreads) orow[i] = -1;
 }
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
@@ -1967,7 +1943,7 @@ hipError_t launch_topk_bin_select(const float* scores, int32_t R, int32_t N,
       scores, N, n_valid, n_all, hist, K0, K1, fine, rkey, rpos, rcnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_topk_bin_final<<<dim3((unsigned)R), dim3(kFinalThreads), 0, s>>>(
+  k_topk_bin_final<<<dim3((unsigned)R, K1 > 0 ? 2u : 1u), dim3(kFinalThreads), 0, s>>>(
       N, n_valid, n_all, hist, fine, nch, rkey, rpos, rcnt, K0, out0, K1, out1);
   return hipGetLastError();
 }
