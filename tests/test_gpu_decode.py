@@ -140,9 +140,9 @@ SMALL = [
     dict(name="hier_bin", B=2, M=70000, K=512, P=8192, W=64, modes=(FULL, REINDEX, REUSE)),
     # more kept elements than one LDS tile of the exact select (the threshold
     # bin is wide): the final takes the kept list in two tiles
-    dict(name="hier_bin_compact", B=2, M=100000, K=512, P=12288, W=64, modes=(FULL, REINDEX, REUSE)),
+    dict(name="hier_bin_two_tiles", B=2, M=100000, K=512, P=12288, W=64, modes=(FULL, REINDEX, REUSE)),
     # a Top-P of 16384: kept lists over one tile, both thresholds refined
-    dict(name="hier_bin_stream", B=2, M=70000, K=256, P=16384, W=64, modes=(FULL, REINDEX)),
+    dict(name="hier_bin_p16384", B=2, M=70000, K=256, P=16384, W=64, modes=(FULL, REINDEX)),
 ]
 
 
