@@ -61,7 +61,9 @@ size_t topk_call_ws_bytes(int64_t R, int64_t N, int64_t K) {
 // Sliced-select winners for any row length up to Nmax (prefill chunks see a
 // growing prefix of the pool).
 size_t topk_slice_ws_max(int64_t R, int64_t Nmax, int64_t K) {
-  // the keepers of a taken shape fit kFinalMaxN per row
+  // the keepers of a taken shape fit kFinalMaxN per row; many rows are never
+  // sliced
+  if (R >= kRowSplitR) return 0;
   size_t b = topk_slice_ws_bytes(R, Nmax, K);
   if (Nmax > kFinalMaxN) {
     const size_t cap = align256((size_t)(R * kFinalMaxN * 4)) * 2;
@@ -200,13 +202,21 @@ csa2_status check_layers(const csa2_layer* layers, int32_t L, int32_t W) {
   return CSA2_OK;
 }
 
+// Whether a prefill chunk of R rows of N positions takes the group select.
+inline bool prefill_group(int64_t R, int64_t N, int64_t K) {
+  return R >= kRowSplitR && topk_group_taken(N, K);
+}
+
 // prefill_layers workspace: scores [B*Q][M] (a chunk uses a row length N <= M)
 // | visible counts [B*Q] | multi-work-group Top-K scratch when the rows are
-// few and long.
+// few and long | sliced-select keepers | run maxima [B*Q][runs] of the group
+// select.
 size_t prefill_ws_bytes(int64_t B, int64_t Q, int64_t M, int64_t K) {
   const int64_t R = B * Q;
+  const bool grp = R >= kRowSplitR && M > kFinalMaxN && K > 0 && K <= 512;   // some N <= M takes it
   return align256(R * M * 4) + align256(R * 4) + (topk_multi_wg(R, M) ? topk_ws_bytes(R, M, K) : 0) +
-         topk_slice_ws_max(R, M, K);
+         topk_slice_ws_max(R, M, K) +
+         (grp ? align256((size_t)R * topk_group_runs(M < 16 * 8192 ? M : 16 * 8192) * 4) : 0);
 }
 
 // Entries that some query of a chunk can see, rounded up to a multiple of 4
@@ -690,10 +700,12 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
   p += align256(R * M * 4);
   int32_t* n_valid = (int32_t*)p;
   p += align256(R * 4);
-  const bool sliced = N > 0 && topk_slicing(R, N, K).taken;
-  const bool big = N > 0 && !sliced && topk_multi_wg(R, N);
+  const bool grp = N > 0 && prefill_group(R, N, K);
+  const bool sliced = N > 0 && !grp && topk_slicing(R, N, K).taken;
+  const bool big = N > 0 && !grp && !sliced && topk_multi_wg(R, N);
   const TopkWs t = big ? topk_ws_carve(p, R, N, K) : TopkWs{};
   void* slice_ws = p + (topk_multi_wg(R, M) ? topk_ws_bytes(R, M, K) : 0);
+  float* gmax = grp ? (float*)((char*)slice_ws + topk_slice_ws_max(R, M, K)) : nullptr;
 
   const int32_t* cur = nullptr;
   int32_t cur_layer = -1;
@@ -705,9 +717,12 @@ csa2_status csa2_prefill_layers(const csa2_pool* pool, const csa2_layer* layers,
       } else {
         st = hip_status(launch_prefill_score(pool->idx_key, (int32_t)B, M, (int32_t)N, y.q_idx,
                                              y.w_idx, Q, pos0, pos0 >= 0 ? ratio : 1, scores,
-                                             n_valid, pool->len, pool_map(pool), stream));
+                                             n_valid, pool->len, pool_map(pool), stream, gmax));
         if (st != CSA2_OK) return st;
-        if (sliced) {
+        if (grp) {
+          st = hip_status(launch_topk_group(scores, gmax, (int32_t)R, (int32_t)N, n_valid,
+                                            (int32_t)N, K, y.idx_out, stream));
+        } else if (sliced) {
           st = hip_status(launch_topk_sliced(scores, (int32_t)R, (int32_t)N, n_valid, (int32_t)N,
                                              nullptr, K, y.idx_out, slice_ws, stream));
         } else if (!big) {

@@ -237,6 +237,18 @@ hipError_t launch_topk_rows(const float* scores, int32_t R, int32_t N,
                             const int32_t* n_valid, int32_t n_all, int32_t K,
                             uint32_t* hist, bool zero_hist, const int32_t* cand,
                             int32_t* out, hipStream_t s);
+// Group select (rows longer than kFinalMaxN whose scores come with the
+// maximum of every run of 16 positions, gmax [ceil(N / 128)][R][8] as the
+// prefill score kernel writes it; N a multiple of 4; 16-byte aligned): the
+// Top-K of each row from the K best runs, K <= 512.
+inline bool topk_group_taken(int64_t N, int64_t K) {
+  return N > kFinalMaxN && N <= (int64_t)16 * 8192 && K > 0 && K <= 512;
+}
+// run maxima per row, with the padding of the last 128-entry tile
+inline int64_t topk_group_runs(int64_t N) { return 8 * ((N + 127) / 128); }
+hipError_t launch_topk_group(const float* scores, const float* gmax, int32_t R, int32_t N,
+                             const int32_t* n_valid, int32_t n_all, int32_t K, int32_t* out,
+                             hipStream_t s);
 // Sliced select (topk_slicing(R, N, K).taken): ws holds topk_slice_ws_bytes.
 hipError_t launch_topk_sliced(const float* scores, int32_t R, int32_t N,
                               const int32_t* n_valid, int32_t n_all, const int32_t* cand,
@@ -352,11 +364,14 @@ hipError_t launch_window_append(uint8_t* swa, int32_t B, int32_t W, const float*
 // Chunked prefill (Q > 1 query tokens per sequence), matrix-core kernels.
 // Scores [B][Q][N] of pool entries 0 .. N-1 (N <= M) for every query (no
 // candidate list, no histogram); invisible entries get -inf.  n_valid
-// (optional, [B][Q]) receives each query's count of visible entries.
+// (optional, [B][Q]) receives each query's count of visible entries.  gmax
+// (optional, [ceil(N / 128)][B Q][8]) receives the largest visible score of
+// every run of 16 entries (-inf for a run the query cannot see), at
+// [e / 128][b Q + q][e % 128 / 16] for the run starting at entry e.
 hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_t N,
                                 const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
                                 int32_t ratio, float* scores, int32_t* n_valid, const int32_t* len,
-                                const PoolMap& map, hipStream_t s);
+                                const PoolMap& map, hipStream_t s, float* gmax = nullptr);
 // Fill n 32-bit words with v.
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // Copy n int32 (Reuse layers that ask for their indices).

@@ -17,6 +17,9 @@
 //   computes a 64 x 64 block with v_mfma_f32_32x32x16_bf16 (the products are
 //   exact in fp32), and the fp32 head result is folded into the score as
 //   w_h * ReLU(.).  Entries a query cannot see yet are written as -inf.
+//   When asked, the kernel also writes the largest visible score of every
+//   run of 16 entries of each query: a run is one 16-lane row of the
+//   product's layout, reduced with four DPP rotations.
 //   The FP8 matrix instruction is not used: measured on gfx950, its
 //   accumulation error reaches ~450 x 2^-24 of the sum of |products| (about
 //   2^-15 relative), against ~0.4 x 2^-24 for the bf16 instruction and for
@@ -51,13 +54,53 @@ __device__ __forceinline__ int64_t visible(int64_t pos0, int32_t t, int32_t rati
   return v < M ? v : M;
 }
 
+// Signed-integer image of a float that orders as the floats do (-0 just
+// below +0); the map is its own inverse.
+__device__ __forceinline__ int32_t ord_i32(int32_t u) { return u ^ ((u >> 31) & 0x7FFFFFFF); }
+
+// Sixteen values per lane, the maximum of each over the 16 lanes of a DPP row
+// (lanes 16 j .. 16 j + 15); lane i of the row receives value i's.  A
+// reduce-scatter: at each of four exchanges a lane keeps half of its values
+// and takes the partner's copies of them, the partners being the lanes across
+// bit 3 (rotation by 8), across bits 0-2 (mirror in each half-row), across
+// bit 1 and across bit 0 (quad swaps); the kept half follows the lane's own
+// bit 3, 2, 1, 0, and the four partner sets together span the row.  15
+// exchanges in place of 64.
+__device__ __forceinline__ int32_t row16_max_scatter(const int32_t (&m)[16]) {
+  const int l = threadIdx.x & 15;
+  const bool b3 = l & 8, b2 = l & 4, b1 = l & 2, b0 = l & 1;
+  int32_t y[8], z[4], w[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int32_t send = b3 ? m[k] : m[k + 8], keep = b3 ? m[k + 8] : m[k];
+    y[k] = max(keep, __builtin_amdgcn_mov_dpp(send, 0x128, 0xF, 0xF, true));   // row_ror:8
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int32_t send = b2 ? y[k] : y[k + 4], keep = b2 ? y[k + 4] : y[k];
+    z[k] = max(keep, __builtin_amdgcn_mov_dpp(send, 0x141, 0xF, 0xF, true));   // row_half_mirror
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int32_t send = b1 ? z[k] : z[k + 2], keep = b1 ? z[k + 2] : z[k];
+    w[k] = max(keep, __builtin_amdgcn_mov_dpp(send, 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
+  }
+  const int32_t send = b0 ? w[0] : w[1], keep = b0 ? w[1] : w[0];
+  return max(keep, __builtin_amdgcn_mov_dpp(send, 0xB1, 0xF, 0xF, true));      // quad_perm [1,0,3,2]
+}
+
 // Scores of entries 0 .. N-1 (N <= M; also the score row length) for every
 // query; n_valid (optional, [B][Q]) receives each query's visible count.
+// gmax (optional, [ceil(N / 128)][B * Q][8]): at [t][b Q + q][j] the largest
+// visible score of entries 128 t + 16 j .. + 15 of query q of sequence b
+// (-inf when it sees none); each work-group writes its tile's runs as whole
+// 128-byte lines.
 __global__ __launch_bounds__(kSThreads, 2)
 void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
                      const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
                      int32_t Q, int64_t pos0, int32_t ratio, float* __restrict__ scores,
-                     int32_t* __restrict__ n_valid, const int32_t* __restrict__ len, PoolMap map) {
+                     int32_t* __restrict__ n_valid, const int32_t* __restrict__ len, PoolMap map,
+                     float* __restrict__ gmax) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[2][kSQ * kSRow];
   __shared__ __attribute__((aligned(16))) uint8_t ks[2][kSE * kSRow];
   __shared__ __attribute__((aligned(16))) float ws[kHI][kSQ];   // head weights, rows contiguous
@@ -83,6 +126,12 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
       const int r = i / kSE, c = i - r * kSE;
       if (q0 + r < Q && e0 + c < N) sb[(size_t)(q0 + r) * N + e0 + c] = -INFINITY;
     }
+    if (gmax)
+      for (int i = tid; i < kSQ * (kSE / 16); i += kSThreads) {
+        const int r = i / (kSE / 16), j = i - r * (kSE / 16);
+        if (q0 + r < Q)
+          gmax[(((size_t)(e0 >> 7) * gridDim.z + b) * Q + q0 + r) * (kSE / 16) + j] = -INFINITY;
+      }
     return;
   }
 
@@ -211,11 +260,11 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   // write: value v of block (r, c) is query row 8*(v/4) + 4*g + v%4, entry lr
   const int32_t ea = (int32_t)e0 + 64 * we + lr;     // entries of blocks c = 0, 1
   const int32_t eb = ea + 32;
+  const bool full = q0 + kSQ <= Q && e0 + kSE <= N && e0 + kSE <= (int64_t)vis_s[0];
   // A tile inside the chunk and the scanned entries, all of whose entries its
   // first (least-seeing) query sees: every value is stored, no test per value;
   // 32-bit offsets from the sequence's score base.
-  if (q0 + kSQ <= Q && e0 + kSE <= N && e0 + kSE <= (int64_t)vis_s[0] &&
-      (uint64_t)Q * (uint64_t)N < (1ull << 31)) {
+  if (full && (uint64_t)Q * (uint64_t)N < (1ull << 31)) {
     const uint32_t o0 = (uint32_t)(q0 + 64 * wq + 4 * g) * (uint32_t)N + (uint32_t)ea;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
@@ -225,20 +274,63 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
         sb[off] = acc[r][0][v];
         sb[off + 32] = acc[r][1][v];
       }
-    return;
+  } else {
+    const bool oka = ea < N, okb = eb < N;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (q0 + tr >= Q) continue;
+        const int32_t vis = vis_s[tr];
+        float* srow = sb + (size_t)(q0 + tr) * N;
+        if (oka) srow[ea] = ea < vis ? acc[r][0][v] : -INFINITY;
+        if (okb) srow[eb] = eb < vis ? acc[r][1][v] : -INFINITY;
+      }
   }
-  const bool oka = ea < N, okb = eb < N;
+  // the run maxima after the score stores are issued (their traffic drains
+  // meanwhile)
+  if (gmax) {
+    // the head weights are no longer read: their LDS holds the tile's run
+    // maxima, [query][run] (128 x 8)
+    float* gm_s = &ws[0][0];
+    static_assert(kHI * kSQ == kSQ * (kSE / 16), "the run maxima fit the head weights' LDS");
+    static_assert(kSThreads == 2 * kSQ, "two threads write a query's runs");
+    // run maxima: block (r, c) holds 32 entries (one per lane of a half-wave)
+    // for 16 query rows; each 16-lane row of the wave is one run of one row
+    // per value, and after the reduction lane i of a row writes value i
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (q0 + tr >= Q) continue;
-      const int32_t vis = vis_s[tr];
-      float* srow = sb + (size_t)(q0 + tr) * N;
-      if (oka) srow[ea] = ea < vis ? acc[r][0][v] : -INFINITY;
-      if (okb) srow[eb] = eb < vis ? acc[r][1][v] : -INFINITY;
-    }
+      for (int c = 0; c < 2; ++c) {
+        const int32_t e = c ? eb : ea;
+        int32_t m[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = acc[r][c][v];
+          if (!full) {
+            const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
+            x = e < N && e < vis_s[tr] ? x : -INFINITY;
+          }
+          m[v] = ord_i32(__float_as_int(x));
+        }
+        const int32_t o = row16_max_scatter(m);
+        const int i = lane & 15;
+        const int ql = 64 * wq + 32 * r + 8 * (i >> 2) + 4 * g + (i & 3);
+        const int rl = 4 * we + 2 * c + ((lane >> 4) & 1);   // run of the tile (0 .. 7)
+        gm_s[ql * (kSE / 16) + rl] = __int_as_float(ord_i32(o));
+      }
+    // a barrier ordering LDS only: the score stores stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    // a query's 8 runs of the tile go out as two 16-byte pieces, the tile's
+    // queries contiguous (runs past N hold -inf)
+    const int ql = tid >> 1, h = tid & 1;
+    if (q0 + ql < Q)
+      *reinterpret_cast<float4*>(gmax + (((size_t)(e0 >> 7) * gridDim.z + b) * Q + q0 + ql) * (kSE / 16) + 4 * h) =
+          *reinterpret_cast<const float4*>(&gm_s[ql * (kSE / 16) + 4 * h]);
+  }
 }
 
 }  // namespace
@@ -246,11 +338,11 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
 hipError_t launch_prefill_score(const uint8_t* key, int32_t B, int64_t M, int32_t N,
                                 const uint8_t* q_idx, const float* w_idx, int32_t Q, int64_t pos0,
                                 int32_t ratio, float* scores, int32_t* n_valid, const int32_t* len,
-                                const PoolMap& map, hipStream_t s) {
+                                const PoolMap& map, hipStream_t s, float* gmax) {
   if (N <= 0 || N > M || Q <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + kSE - 1) / kSE), (unsigned)((Q + kSQ - 1) / kSQ), (unsigned)B);
   k_prefill_score<<<grid, dim3(kSThreads), 0, s>>>(key, M, N, q_idx, w_idx, Q, pos0, ratio, scores,
-                                                   n_valid, len, map);
+                                                   n_valid, len, map, gmax);
   return hipGetLastError();
 }
 

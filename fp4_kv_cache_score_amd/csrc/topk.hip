@@ -95,7 +95,6 @@ __device__ __forceinline__ void wave_prefix(const uint32_t* slot, int stride, ui
 template <int NT>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
   lds[wave] = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);   // every lane: no branch
@@ -1006,7 +1005,7 @@ __device__ void scan_groups(const uint32_t (&c)[G], uint32_t* slot, uint32_t (&p
                             uint32_t (&tot)[G]) {
   constexpr int W = (G + 1) / 2;
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
   uint32_t v[W], x[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) {
@@ -1406,8 +1405,10 @@ void k_score_slice(const uint8_t* __restrict__ key, int64_t M, const uint8_t* __
 // Elements: `total` slots of keepers (ckey / cpos from k_topk_slice, in
 // position order, total a multiple of 4) or, with total == 0, the row's own
 // scores (N <= NT * PT).
+// (8 waves per SIMD: with more than about 100 SGPRs a SIMD holds 7 waves and
+// a compute unit only one 1024-thread work-group)
 template <int NT, int PT>
-__global__ __launch_bounds__(NT)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __restrict__ n_valid,
                   int32_t n_all, int32_t total, const uint32_t* __restrict__ ckey,
                   const int32_t* __restrict__ cpos, int32_t K, const int32_t* __restrict__ cand_map,
@@ -1505,6 +1506,131 @@ void k_topk_final(const float* __restrict__ scores, int32_t N, const int32_t* __
     }
   }
   for (uint32_t i = chosen + threadIdx.x; i < (uint32_t)K; i += NT) orow[i] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Group select for many long rows whose scores come with the maximum of every
+// run of 16 positions (the chunked-prefill score kernel writes both).  Take
+// the K best runs under the (run maximum, lower run) order: every position of
+// the row's Top-K lies in one of them.  (An entry x in any other run rho has
+// K runs each better than rho; each one's maximum beats x under the (score,
+// lower position) order, by a larger score or, at an equal score, by lying in
+// an earlier run, so x has K better entries.)  Any set of runs that holds
+// those K, such as every run whose maximum reaches some bound, serves as well.
+// One 512-thread work-group per row (K <= 512):
+//  1. a block select over the run maxima (in run order) marks the K best
+//     runs, or, when that takes fewer radix passes, every run at or above a
+//     digit boundary as long as they are at most 512; a run holding no
+//     visible position takes no part;
+//  2. the marked runs are listed in LDS in ascending order by one block scan;
+//  3. their positions (at most 8192), in ascending order, are the elements of
+//     a block select of the row's K largest under the (key, lower position)
+//     order, written out ascending as the final select does.
+// ---------------------------------------------------------------------------
+constexpr int kRunLen = 16;                              // positions per run
+constexpr int kGroupThreads = 512;
+constexpr int kGroupPT = 16;                             // gathered positions per thread
+constexpr int kGroupRuns = kGroupThreads * kGroupPT / kRunLen;   // runs one work-group gathers (512)
+
+// (512-thread work-groups at 8 waves per SIMD, as the register budgets then
+// allow: four rows share a compute unit, and one's loads and barriers
+// overlap the others' work)
+template <int PG>
+__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_topk_group(const float* __restrict__ scores, int32_t N, const float* __restrict__ gmax,
+                  const int32_t* __restrict__ n_valid, int32_t n_all, int32_t K,
+                  int32_t* __restrict__ out) {
+  constexpr int NT = kGroupThreads;
+  constexpr int GG = PG / 4;
+  constexpr int PT = kGroupPT;
+  constexpr int GT = PT / 4;
+  __shared__ BlockSelLdsT<NT> L;
+  __shared__ int32_t runs[kGroupRuns];
+  // rows 4 k .. 4 k + 3 share the 128-byte lines of run maxima: with R a
+  // multiple of 32 they go to work-groups w, w + 8, w + 16, w + 24, which the
+  // dispatch places on one XCD
+  const int R = gridDim.x, w = blockIdx.x;
+  const int row = (R & 31) ? w : 32 * (w >> 5) + 4 * (w & 7) + ((w >> 3) & 3);
+  const int tid = threadIdx.x;
+  const int32_t n = row_count(n_valid, n_all, row, N);
+  const int32_t nr = (n + kRunLen - 1) / kRunLen;        // runs holding a visible position
+
+  // 1. run maxima, run r = 4 NT u + 4 tid + j at [r / 8][row][r % 8]
+  uint32_t rk[PG];
+#pragma unroll
+  for (int u = 0; u < GG; ++u) {
+    const int32_t r = 4 * NT * u + 4 * tid;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < nr) v = *reinterpret_cast<const float4*>(gmax + ((size_t)(r >> 3) * R + row) * 8 + (r & 7));
+    rk[4 * u + 0] = r + 0 < nr ? score_key(v.x) : 0u;
+    rk[4 * u + 1] = r + 1 < nr ? score_key(v.y) : 0u;
+    rk[4 * u + 2] = r + 2 < nr ? score_key(v.z) : 0u;
+    rk[4 * u + 3] = r + 3 < nr ? score_key(v.w) : 0u;
+  }
+  bool top[PG];
+  int round = 0;
+  block_select<NT, PG>(rk, (uint32_t)K, (uint32_t)kGroupRuns, L, top, round);
+
+  // 2. the marked runs (at most kGroupRuns: the select keeps at most its
+  //    budget), listed in ascending order
+  uint32_t c[GG], pre[GG], tot[GG];
+#pragma unroll
+  for (int u = 0; u < GG; ++u) {
+    c[u] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[u] += top[4 * u + j] ? 1u : 0u;
+  }
+  scan_groups<NT, GG>(c, L.scan[round & 3], pre, tot);
+  ++round;
+  uint32_t nrun = 0;
+  {
+    uint32_t base = 0;
+#pragma unroll
+    for (int u = 0; u < GG; ++u) {
+      uint32_t o = base + pre[u];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (top[4 * u + j] && o < (uint32_t)kGroupRuns) runs[o++] = 4 * NT * u + 4 * tid + j;
+      base += tot[u];
+    }
+    nrun = base < (uint32_t)kGroupRuns ? base : (uint32_t)kGroupRuns;
+  }
+  __syncthreads();
+
+  // 3. element e = 4 NT u + 4 tid + j is position kRunLen runs[e / kRunLen] + e % kRunLen
+  const int32_t ne = (int32_t)nrun * kRunLen;
+  const float* sr = scores + (size_t)row * N;
+  auto position = [&](int32_t e) { return kRunLen * runs[e / kRunLen] + (e % kRunLen); };
+  uint32_t key[PT];
+#pragma unroll
+  for (int u = 0; u < GT; ++u) {
+    const int32_t e = 4 * NT * u + 4 * tid;
+    const int32_t p = e < ne ? position(e) : 0;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e < ne && p < n) v = *reinterpret_cast<const float4*>(sr + p);   // p + 3 < N: N is a multiple of 4
+    key[4 * u + 0] = e < ne && p + 0 < n ? score_key(v.x) : 0u;
+    key[4 * u + 1] = e < ne && p + 1 < n ? score_key(v.y) : 0u;
+    key[4 * u + 2] = e < ne && p + 2 < n ? score_key(v.z) : 0u;
+    key[4 * u + 3] = e < ne && p + 3 < n ? score_key(v.w) : 0u;
+  }
+  bool sel[PT];
+  const uint32_t chosen = block_select<NT, PT>(key, (uint32_t)K, (uint32_t)K, L, sel, round);
+  uint32_t oidx[PT];
+  kept_order<NT, PT>(sel, L, round, oidx);
+  int32_t* orow = out + (size_t)row * K;
+  int32_t* sp = reinterpret_cast<int32_t*>(&L.hist[0][0]);   // chosen <= K <= 2 kHistBins
+#pragma unroll
+  for (int u = 0; u < GT; ++u) {
+    const int32_t e = 4 * NT * u + 4 * tid;
+    if (e >= ne) continue;
+    const int32_t p = position(e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sel[4 * u + j]) sp[oidx[4 * u + j]] = p + j;
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < chosen; i += NT) orow[i] = sp[i];
+  for (uint32_t i = chosen + tid; i < (uint32_t)K; i += NT) orow[i] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1909,6 +2035,21 @@ hipError_t launch_topk_sliced(const float* scores, int32_t R, int32_t N,
   }
   return launch_final(dim3((unsigned)R), s, elems, scores, N, n_valid, n_all, total, ckey, cpos, K,
                       cand, out);
+}
+
+hipError_t launch_topk_group(const float* scores, const float* gmax, int32_t R, int32_t N,
+                             const int32_t* n_valid, int32_t n_all, int32_t K, int32_t* out,
+                             hipStream_t s) {
+  if (!topk_group_taken(N, K) || R <= 0 || (N & 3) || ((uintptr_t)scores & 15u) ||
+      ((uintptr_t)gmax & 15u))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)R), block(kGroupThreads);
+  const int32_t need = (N + kRunLen - 1) / kRunLen;
+  if (need <= 8 * kGroupThreads)
+    k_topk_group<8><<<grid, block, 0, s>>>(scores, N, gmax, n_valid, n_all, K, out);
+  else
+    k_topk_group<16><<<grid, block, 0, s>>>(scores, N, gmax, n_valid, n_all, K, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_score_topk(const uint8_t* key, int32_t B, int64_t M, const uint8_t* q_idx,

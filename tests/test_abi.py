@@ -35,6 +35,13 @@ def test_library_exports_every_declared_function():
     assert "gfx950" in C.csa2_version()
 
 
+def test_library_resolves_its_own_symbols():
+    """Every symbol of the library's own namespace is defined inside it (a
+    shared library links with undefined symbols, which would only fail at the
+    first call): loading with immediate binding resolves every one."""
+    ctypes.CDLL(C.LIB_PATH, mode=ctypes.RTLD_GLOBAL | os.RTLD_NOW)
+
+
 def test_status_strings():
     for s in range(8):
         assert C.csa2_status_string(s)
