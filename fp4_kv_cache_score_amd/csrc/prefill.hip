@@ -13,13 +13,15 @@
 //   each of the 8 indexer heads the E4M3 query and key slices (64 values per
 //   row) are staged in LDS as bf16 (exact: an E4M3 value has 4 significant
 //   bits and an exponent inside bf16's range), double-buffered so that the
-//   next head's loads are in flight during this head's math; each wave
-//   computes a 64 x 64 block with v_mfma_f32_32x32x16_bf16 (the products are
-//   exact in fp32), and the fp32 head result is folded into the score as
+//   next head's loads are in flight during this head's math; each of the
+//   8 waves computes a 64 x 32 block with v_mfma_f32_32x32x16_bf16 (the
+//   products are exact in fp32; at most 128 VGPRs, so two work-groups give a
+//   SIMD four waves, whose stores and loads overlap the others' math), and the
+//   fp32 head result is folded into the score as
 //   w_h * ReLU(.).  Entries a query cannot see yet are written as -inf.
 //   When asked, the kernel also writes the largest visible score of every
 //   run of 16 entries of each query: a run is one 16-lane row of the
-//   product's layout, reduced with four DPP rotations.
+//   product's layout, reduced by a DPP reduce-scatter.
 //   The FP8 matrix instruction is not used: measured on gfx950, its
 //   accumulation error reaches ~450 x 2^-24 of the sum of |products| (about
 //   2^-15 relative), against ~0.4 x 2^-24 for the bf16 instruction and for
@@ -44,7 +46,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kSQ = 128;                 // queries per work-group tile
 constexpr int kSE = 128;                 // pool entries per work-group tile
-constexpr int kSThreads = 256;
+constexpr int kSThreads = 512;             // 8 waves: 2 (query halves) x 4 (entry quarters)
 constexpr int kSRow = 128 + 16;          // LDS bytes per staged row (64 bf16 of one head + pad)
 
 // Entries query t sees: the first M (the sequence's length), within the causal limit.
@@ -95,7 +97,7 @@ __device__ __forceinline__ int32_t row16_max_scatter(const int32_t (&m)[16]) {
 // visible score of entries 128 t + 16 j .. + 15 of query q of sequence b
 // (-inf when it sees none); each work-group writes its tile's runs as whole
 // 128-byte lines.
-__global__ __launch_bounds__(kSThreads, 2)
+__global__ __launch_bounds__(kSThreads, 4)   // 4 waves per SIMD: two work-groups per CU
 void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
                      const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
                      int32_t Q, int64_t pos0, int32_t ratio, float* __restrict__ scores,
@@ -113,7 +115,7 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wq = wave & 1;                // 64-query half of the tile
-  const int we = wave >> 1;               // 64-entry half of the tile
+  const int we = wave >> 1;               // 32-entry quarter of the tile
   const uint8_t* qb = q_idx + (size_t)b * Q * kKeyRow;
   float* sb = scores + (size_t)b * Q * (size_t)N;
   const int64_t Ms = len ? (int64_t)len[b] : M;           // this sequence's entries
@@ -141,27 +143,23 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   }
   if (tid < kSQ) vis_s[tid] = (int32_t)visible(pos0, q0 + tid, ratio, Ms);   // one division per row
 
-  // staging: thread -> two (row, 16-byte part) pieces of each of Q and K.
+  // staging: thread -> one (row, 16-byte part) piece of each of Q and K.
   // Rows past Q or N load the last row instead (never written out), so the
   // loads are unconditional.
-  u32x4 rq[2], rk[2];
-  const uint8_t* qrow[2];
-  const uint8_t* krow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + i * kSThreads;
-    const int row = c >> 2, part = c & 3;
+  static_assert(kSQ * 4 == kSThreads && kSE * 4 == kSThreads, "one piece of Q and of K per thread");
+  u32x4 rq, rk;
+  const uint8_t* qrow;
+  const uint8_t* krow;
+  {
+    const int row = tid >> 2, part = tid & 3;
     const int t = q0 + row < Q ? q0 + row : Q - 1;
     const int64_t e = e0 + row < N ? e0 + row : N - 1;
-    qrow[i] = qb + (size_t)t * kKeyRow + part * 16;
-    krow[i] = key + (size_t)pool_row(map, b, e, M) * kKeyRow + part * 16;
+    qrow = qb + (size_t)t * kKeyRow + part * 16;
+    krow = key + (size_t)pool_row(map, b, e, M) * kKeyRow + part * 16;
   }
   auto load = [&](int h) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      rq[i] = *reinterpret_cast<const u32x4*>(qrow[i] + h * kDI);
-      rk[i] = *reinterpret_cast<const u32x4*>(krow[i] + h * kDI);
-    }
+    rq = *reinterpret_cast<const u32x4*>(qrow + h * kDI);
+    rk = *reinterpret_cast<const u32x4*>(krow + h * kDI);
   };
   // 16 E4M3 values -> 16 bf16 (two 16-byte pieces), exact
   auto widen = [](const u32x4& x, u32x4& lo, u32x4& hi) {
@@ -179,27 +177,22 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
     }
   };
   auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * kSThreads;
-      const int row = c >> 2, part = c & 3;
-      u32x4 lo, hi;
-      widen(rq[i], lo, hi);
-      *reinterpret_cast<u32x4*>(&qs[buf][row * kSRow + part * 32]) = lo;
-      *reinterpret_cast<u32x4*>(&qs[buf][row * kSRow + part * 32 + 16]) = hi;
-      widen(rk[i], lo, hi);
-      *reinterpret_cast<u32x4*>(&ks[buf][row * kSRow + part * 32]) = lo;
-      *reinterpret_cast<u32x4*>(&ks[buf][row * kSRow + part * 32 + 16]) = hi;
-    }
+    const int row = tid >> 2, part = tid & 3;
+    u32x4 lo, hi;
+    widen(rq, lo, hi);
+    *reinterpret_cast<u32x4*>(&qs[buf][row * kSRow + part * 32]) = lo;
+    *reinterpret_cast<u32x4*>(&qs[buf][row * kSRow + part * 32 + 16]) = hi;
+    widen(rk, lo, hi);
+    *reinterpret_cast<u32x4*>(&ks[buf][row * kSRow + part * 32]) = lo;
+    *reinterpret_cast<u32x4*>(&ks[buf][row * kSRow + part * 32 + 16]) = hi;
   };
 
-  f32x16 acc[2][2];
+  // acc[r]: queries 32 r .. of this wave's 64, its 32 entries
+  f32x16 acc[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[r][c][v] = 0.f;
+    for (int v = 0; v < 16; ++v) acc[r][v] = 0.f;
 
   // Per head: MFMA on the staged buffer, then the next head is staged from
   // the registers (loaded one head's compute earlier) and the head after it
@@ -214,22 +207,21 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   for (int h = 0; h < kHI; ++h) {
     const int buf = h & 1;
     // operands: lane holds 32 bf16 (4 k-steps of 8) of its row's half g
-    bf16x8 A[2][4], Bv[2][4];
+    bf16x8 A[2][4], Bv[4];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const uint8_t* src = &qs[buf][(64 * wq + 32 * r + lr) * kSRow + 64 * g];
 #pragma unroll
       for (int k = 0; k < 4; ++k) A[r][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * k));
     }
+    {
+      const uint8_t* src = &ks[buf][(32 * we + lr) * kSRow + 64 * g];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint8_t* src = &ks[buf][(64 * we + 32 * c + lr) * kSRow + 64 * g];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) Bv[c][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * k));
+      for (int k = 0; k < 4; ++k) Bv[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * k));
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      // head weights of the 16 query rows this lane holds in each block
+      // head weights of the 16 query rows this lane holds in the block
       float wv[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -239,17 +231,14 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
         wv[4 * j + 2] = w4.z;
         wv[4 * j + 3] = w4.w;
       }
+      f32x16 t = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f32x16 s = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < 4; ++k) t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][k], Bv[k], t, 0, 0, 0);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][k], Bv[c][k], s, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          // ReLU on the bit pattern: a signed max with 0 maps negatives and -0 to +0
-          const float rl = __int_as_float(max(__float_as_int(s[v]), 0));
-          acc[r][c][v] = fmaf(rl, wv[v], acc[r][c][v]);
-        }
+      for (int v = 0; v < 16; ++v) {
+        // ReLU on the bit pattern: a signed max with 0 maps negatives and -0 to +0
+        const float rl = __int_as_float(max(__float_as_int(t[v]), 0));
+        acc[r][v] = fmaf(rl, wv[v], acc[r][v]);
       }
     }
     if (h + 1 < kHI) store(buf ^ 1);
@@ -257,9 +246,9 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
     __syncthreads();
   }
 
-  // write: value v of block (r, c) is query row 8*(v/4) + 4*g + v%4, entry lr
-  const int32_t ea = (int32_t)e0 + 64 * we + lr;     // entries of blocks c = 0, 1
-  const int32_t eb = ea + 32;
+  // write: value v of block r is query row 8*(v/4) + 4*g + v%4 of the wave's
+  // 32 r .., entry lr of its 32
+  const int32_t ea = (int32_t)e0 + 32 * we + lr;
   const bool full = q0 + kSQ <= Q && e0 + kSE <= N && e0 + kSE <= (int64_t)vis_s[0];
   // A tile inside the chunk and the scanned entries, all of whose entries its
   // first (least-seeing) query sees: every value is stored, no test per value;
@@ -269,23 +258,16 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t off = o0 + (uint32_t)(32 * r + 8 * (v >> 2) + (v & 3)) * (uint32_t)N;
-        sb[off] = acc[r][0][v];
-        sb[off + 32] = acc[r][1][v];
-      }
-  } else {
-    const bool oka = ea < N, okb = eb < N;
+      for (int v = 0; v < 16; ++v)
+        sb[o0 + (uint32_t)(32 * r + 8 * (v >> 2) + (v & 3)) * (uint32_t)N] = acc[r][v];
+  } else if (ea < N) {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
         if (q0 + tr >= Q) continue;
-        const int32_t vis = vis_s[tr];
-        float* srow = sb + (size_t)(q0 + tr) * N;
-        if (oka) srow[ea] = ea < vis ? acc[r][0][v] : -INFINITY;
-        if (okb) srow[eb] = eb < vis ? acc[r][1][v] : -INFINITY;
+        sb[(size_t)(q0 + tr) * N + ea] = ea < vis_s[tr] ? acc[r][v] : -INFINITY;
       }
   }
   // the run maxima after the score stores are issued (their traffic drains
@@ -295,41 +277,40 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
     // maxima, [query][run] (128 x 8)
     float* gm_s = &ws[0][0];
     static_assert(kHI * kSQ == kSQ * (kSE / 16), "the run maxima fit the head weights' LDS");
-    static_assert(kSThreads == 2 * kSQ, "two threads write a query's runs");
-    // run maxima: block (r, c) holds 32 entries (one per lane of a half-wave)
-    // for 16 query rows; each 16-lane row of the wave is one run of one row
-    // per value, and after the reduction lane i of a row writes value i
+    // run maxima: block r holds the wave's 32 entries (one per lane of a
+    // half-wave) for 16 query rows; each 16-lane row of the wave is one run of
+    // one query row per value, and after the reduction lane i of a row holds
+    // value i's
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < 2; ++r) {
+      int32_t m[16];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int32_t e = c ? eb : ea;
-        int32_t m[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = acc[r][c][v];
-          if (!full) {
-            const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
-            x = e < N && e < vis_s[tr] ? x : -INFINITY;
-          }
-          m[v] = ord_i32(__float_as_int(x));
+      for (int v = 0; v < 16; ++v) {
+        float x = acc[r][v];
+        if (!full) {
+          const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
+          x = ea < N && ea < vis_s[tr] ? x : -INFINITY;
         }
-        const int32_t o = row16_max_scatter(m);
-        const int i = lane & 15;
-        const int ql = 64 * wq + 32 * r + 8 * (i >> 2) + 4 * g + (i & 3);
-        const int rl = 4 * we + 2 * c + ((lane >> 4) & 1);   // run of the tile (0 .. 7)
-        gm_s[ql * (kSE / 16) + rl] = __int_as_float(ord_i32(o));
+        m[v] = ord_i32(__float_as_int(x));
       }
+      const int32_t o = row16_max_scatter(m);
+      const int i = lane & 15;
+      const int ql = 64 * wq + 32 * r + 8 * (i >> 2) + 4 * g + (i & 3);
+      const int rl = 2 * we + ((lane >> 4) & 1);   // run of the tile (0 .. 7)
+      gm_s[ql * (kSE / 16) + rl] = __int_as_float(ord_i32(o));
+    }
     // a barrier ordering LDS only: the score stores stay in flight
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     // a query's 8 runs of the tile go out as two 16-byte pieces, the tile's
     // queries contiguous (runs past N hold -inf)
-    const int ql = tid >> 1, h = tid & 1;
-    if (q0 + ql < Q)
-      *reinterpret_cast<float4*>(gmax + (((size_t)(e0 >> 7) * gridDim.z + b) * Q + q0 + ql) * (kSE / 16) + 4 * h) =
-          *reinterpret_cast<const float4*>(&gm_s[ql * (kSE / 16) + 4 * h]);
+    if (tid < 2 * kSQ) {
+      const int ql = tid >> 1, hh = tid & 1;
+      if (q0 + ql < Q)
+        *reinterpret_cast<float4*>(gmax + (((size_t)(e0 >> 7) * gridDim.z + b) * Q + q0 + ql) * (kSE / 16) + 4 * hh) =
+            *reinterpret_cast<const float4*>(&gm_s[ql * (kSE / 16) + 4 * hh]);
+    }
   }
 }
 
