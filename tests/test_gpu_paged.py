@@ -3,8 +3,9 @@
 A paged pool holds the same entries as a contiguous one, only at other rows,
 so every result over it must be bit-identical to the contiguous run (which the
 other parity tests hold to the oracle): the decode schedule (flat,
-hierarchical, ragged), the scores, chunked prefill through the schedule and
-the write side (entries appended into pages land where the table says).
+hierarchical, ragged), the scores, chunked prefill through the schedule (short
+rows, and rows long enough for the group select) and the write side (entries
+appended into pages land where the table says).
 Pages are shuffled among spare ones, so a wrong row would read other data.
 """
 import sys
@@ -67,11 +68,15 @@ def test_paged_decode_equals_contiguous(ci, kw, lg2, lens):
     assert torch.equal(s0, s1)
 
 
-def test_paged_prefill_equals_contiguous():
+@pytest.mark.parametrize("kw", [
+    dict(Q=160, M=4096, K=96, chunk_pos=4 * 4096 - 3000),
+    # rows over 16384 entries on 256 rows: the group select from the run maxima
+    dict(Q=128, M=24576, K=512, chunk_pos=-1),
+], ids=["short_rows", "group_select"])
+def test_paged_prefill_equals_contiguous(kw):
     from fp4_kv_cache_score_amd.device import DeviceCase
-    cfg = CONFIGS[4].scaled(name="pgp", seed=81, B=2, Q=160, M=4096, K=96, W=40,
-                            modes=(FULL, REINDEX, REUSE), chunk_pos=4 * 4096 - 3000)
-    say("case: paged prefill Q=%d M=%d" % (cfg.Q, cfg.M))
+    cfg = CONFIGS[4].scaled(name="pgp", seed=81, B=2, W=40, modes=(FULL, REINDEX, REUSE), **kw)
+    say("case: paged prefill Q=%d M=%d K=%d" % (cfg.Q, cfg.M, cfg.K))
     case = synth.make_case(cfg)
     runs = []
     for paged in (False, True):
