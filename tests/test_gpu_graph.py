@@ -7,7 +7,8 @@ work that overwrites every output and a synchronisation; after the inputs are
 changed in place, a replay must equal a new eager call on the changed inputs.
 Two steps issued from two host threads onto two streams at once must give the
 results of the same steps run one after the other.  The chunked-prefill chain
-is captured and replayed the same way.
+is captured and replayed the same way, and so is csa2_prefill_layers on rows
+long enough for the group select (its run maxima recomputed on every replay).
 """
 import sys
 
@@ -172,3 +173,31 @@ def test_prefill_chain_graph_replay(M):
         torch.cuda.synchronize()
         for name, a, t in zip(("idx", "o", "lse"), want, outs):
             assert np.array_equal(a, t.cpu().numpy()), "replay %d: %s differs" % (rep, name)
+
+
+def test_prefill_layers_graph_replay_group_select():
+    """csa2_prefill_layers on rows long enough for the group select (256 tokens,
+    40000 entries: the score kernel writes run maxima, the select reads them)
+    captured into a graph: every replay, after the outputs and the whole
+    workspace (scores and run maxima) are overwritten, equals the eager call."""
+    from fp4_kv_cache_score_amd.device import DeviceCase
+    cfg = CONFIGS[4].scaled(name="graph_pfl", seed=57, B=1, Q=256, M=40000, K=512, W=64,
+                            modes=(FULL, REINDEX, REUSE))
+    say("case: prefill layers graph replay Q=%d M=%d (group select)" % (cfg.Q, cfg.M))
+    dc = DeviceCase(synth.make_case(cfg))
+    dc.prefill_layers()                      # eager; allocates the workspace
+    torch.cuda.synchronize()
+    want = dc.results()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dc.prefill_layers()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _clobber(dc)
+        dc.ws.fill_(0x7F)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(want, dc.results(), "replay %d" % rep)
