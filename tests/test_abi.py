@@ -70,6 +70,24 @@ def test_workspace_bytes():
     assert ws(99, 1, 1, 1, 1, 0, 0, 16) == 0
 
 
+def test_prefill_workspace_holds_the_run_maxima():
+    """A prefill chunk of 256 or more rows longer than 16384 entries with K <= 512
+    selects from run maxima: its workspace holds, beyond the scores and visible
+    counts, [ceil(M / 128)][B Q][8] floats of them (nothing for K > 512 or for
+    rows of at most 16384 entries)."""
+    ws = C.csa2_workspace_bytes
+    al = lambda x: (x + 255) // 256 * 256
+
+    def pf(B, Q, M, K):
+        return ws(C.CSA2_OP_PREFILL_LAYERS, B, Q, M, K, 0, 128, 16)
+    for B, Q, M in ((1, 256, 20000), (2, 128, 65536), (1, 2048, 65536)):
+        R = B * Q
+        runs = al(R * 8 * ((M + 127) // 128) * 4)
+        assert pf(B, Q, M, 512) - pf(B, Q, M, 513) == runs, (B, Q, M)
+        assert pf(B, Q, M, 512) == al(R * M * 4) + al(R * 4) + runs, (B, Q, M)
+    assert pf(1, 256, 16384, 512) == al(256 * 16384 * 4) + al(256 * 4)   # short rows: none
+
+
 def _pool(**kw):
     d = dict(latent=A, scale=A, idx_key=A, B=2, M=1024)
     d.update(kw)
