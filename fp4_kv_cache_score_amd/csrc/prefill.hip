@@ -14,11 +14,15 @@
 //   row) are staged in LDS as bf16 (exact: an E4M3 value has 4 significant
 //   bits and an exponent inside bf16's range), double-buffered so that the
 //   next head's loads are in flight during this head's math; each of the
-//   8 waves computes a 64 x 32 block with v_mfma_f32_32x32x16_bf16 (the
-//   products are exact in fp32; at most 128 VGPRs, so two work-groups give a
-//   SIMD four waves, whose stores and loads overlap the others' math), and the
-//   fp32 head result is folded into the score as
+//   8 waves computes 32 queries x 64 entries as two 32 x 32 products with
+//   v_mfma_f32_32x32x16_bf16 that share the query operand and the head
+//   weights (the products are exact in fp32; at most 128 VGPRs, so two
+//   work-groups give a SIMD four waves, whose stores and loads overlap the
+//   others' math), and the fp32 head result is folded into the score as
 //   w_h * ReLU(.).  Entries a query cannot see yet are written as -inf.
+//   The scores are stored non-temporally: they stream to memory instead of
+//   displacing the keys and queries the other tiles still read from the
+//   caches (measured: the chunk's score and select together 30 us faster).
 //   When asked, the kernel also writes the largest visible score of every
 //   run of 16 entries of each query: a run is one 16-lane row of the
 //   product's layout, reduced by a DPP reduce-scatter.
@@ -114,8 +118,8 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wq = wave & 1;                // 64-query half of the tile
-  const int we = wave >> 1;               // 32-entry quarter of the tile
+  const int wq = wave & 3;                // 32-query quarter of the tile
+  const int we = wave >> 2;               // 64-entry half of the tile
   const uint8_t* qb = q_idx + (size_t)b * Q * kKeyRow;
   float* sb = scores + (size_t)b * Q * (size_t)N;
   const int64_t Ms = len ? (int64_t)len[b] : M;           // this sequence's entries
@@ -187,12 +191,12 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
     *reinterpret_cast<u32x4*>(&ks[buf][row * kSRow + part * 32 + 16]) = hi;
   };
 
-  // acc[r]: queries 32 r .. of this wave's 64, its 32 entries
+  // acc[c]: this wave's 32 queries, entries 32 c .. of its 64
   f32x16 acc[2];
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[r][v] = 0.f;
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
 
   // Per head: MFMA on the staged buffer, then the next head is staged from
   // the registers (loaded one head's compute earlier) and the head after it
@@ -207,38 +211,38 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
   for (int h = 0; h < kHI; ++h) {
     const int buf = h & 1;
     // operands: lane holds 32 bf16 (4 k-steps of 8) of its row's half g
-    bf16x8 A[2][4], Bv[4];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const uint8_t* src = &qs[buf][(64 * wq + 32 * r + lr) * kSRow + 64 * g];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) A[r][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * k));
-    }
+    bf16x8 A[4], Bv[2][4];
     {
-      const uint8_t* src = &ks[buf][(32 * we + lr) * kSRow + 64 * g];
+      const uint8_t* src = &qs[buf][(32 * wq + lr) * kSRow + 64 * g];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) Bv[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * k));
+      for (int k = 0; k < 4; ++k) A[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * k));
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      // head weights of the 16 query rows this lane holds in the block
-      float wv[16];
+    for (int c = 0; c < 2; ++c) {
+      const uint8_t* src = &ks[buf][(64 * we + 32 * c + lr) * kSRow + 64 * g];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 w4 = *reinterpret_cast<const float4*>(&ws[h][64 * wq + 32 * r + 8 * j + 4 * g]);
-        wv[4 * j] = w4.x;
-        wv[4 * j + 1] = w4.y;
-        wv[4 * j + 2] = w4.z;
-        wv[4 * j + 3] = w4.w;
-      }
+      for (int k = 0; k < 4; ++k) Bv[c][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * k));
+    }
+    // head weights of the 16 query rows this lane holds (the same in both blocks)
+    float wv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&ws[h][32 * wq + 8 * j + 4 * g]);
+      wv[4 * j] = w4.x;
+      wv[4 * j + 1] = w4.y;
+      wv[4 * j + 2] = w4.z;
+      wv[4 * j + 3] = w4.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
       f32x16 t = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][k], Bv[k], t, 0, 0, 0);
+      for (int k = 0; k < 4; ++k) t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[k], Bv[c][k], t, 0, 0, 0);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         // ReLU on the bit pattern: a signed max with 0 maps negatives and -0 to +0
         const float rl = __int_as_float(max(__float_as_int(t[v]), 0));
-        acc[r][v] = fmaf(rl, wv[v], acc[r][v]);
+        acc[c][v] = fmaf(rl, wv[v], acc[c][v]);
       }
     }
     if (h + 1 < kHI) store(buf ^ 1);
@@ -246,29 +250,38 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
     __syncthreads();
   }
 
-  // write: value v of block r is query row 8*(v/4) + 4*g + v%4 of the wave's
-  // 32 r .., entry lr of its 32
-  const int32_t ea = (int32_t)e0 + 32 * we + lr;
+  // write: value v of block c is query row 8*(v/4) + 4*g + v%4 of the wave's
+  // 32, entry 32 c + lr of its 64
+  const int32_t ea = (int32_t)e0 + 64 * we + lr;
   const bool full = q0 + kSQ <= Q && e0 + kSE <= N && e0 + kSE <= (int64_t)vis_s[0];
   // A tile inside the chunk and the scanned entries, all of whose entries its
-  // first (least-seeing) query sees: every value is stored, no test per value;
-  // 32-bit offsets from the sequence's score base.
-  if (full && (uint64_t)Q * (uint64_t)N < (1ull << 31)) {
-    const uint32_t o0 = (uint32_t)(q0 + 64 * wq + 4 * g) * (uint32_t)N + (uint32_t)ea;
+  // first (least-seeing) query sees: every value is stored, no test per value.
+  // A store's row is the same for the whole wave but for the half-wave's
+  // offset of 4 g rows, so its address is a wave-uniform row base plus one
+  // per-lane 32-bit byte offset.
+  if (full && N < (1 << 26)) {
+    const int ws_ = __builtin_amdgcn_readfirstlane(wave);   // the wave, as a scalar
+    const float* base0 = sb + (size_t)(q0 + 32 * (ws_ & 3)) * N + e0 + 64 * (ws_ >> 2);
+    const uint32_t loff = ((uint32_t)(4 * g) * (uint32_t)N + (uint32_t)lr) * 4u;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int v = 0; v < 16; ++v)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        sb[o0 + (uint32_t)(32 * r + 8 * (v >> 2) + (v & 3)) * (uint32_t)N] = acc[r][v];
-  } else if (ea < N) {
+      for (int c = 0; c < 2; ++c) {
+        const float* rb = base0 + (size_t)(8 * (v >> 2) + (v & 3)) * N + 32 * c;
+        __builtin_nontemporal_store(acc[c][v], (float*)((const char*)rb + loff));
+      }
+  } else {
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int c = 0; c < 2; ++c) {
+      const int32_t ec = ea + 32 * c;
+      if (ec >= N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int tr = 32 * wq + 8 * (v >> 2) + 4 * g + (v & 3);
         if (q0 + tr >= Q) continue;
-        sb[(size_t)(q0 + tr) * N + ea] = ea < vis_s[tr] ? acc[r][v] : -INFINITY;
+        __builtin_nontemporal_store(ec < vis_s[tr] ? acc[c][v] : -INFINITY, &sb[(size_t)(q0 + tr) * N + ec]);
       }
+    }
   }
   // the run maxima after the score stores are issued (their traffic drains
   // meanwhile)
@@ -277,26 +290,26 @@ void k_prefill_score(const uint8_t* __restrict__ key, int64_t M, int32_t N,
     // maxima, [query][run] (128 x 8)
     float* gm_s = &ws[0][0];
     static_assert(kHI * kSQ == kSQ * (kSE / 16), "the run maxima fit the head weights' LDS");
-    // run maxima: block r holds the wave's 32 entries (one per lane of a
+    // run maxima: block c holds 32 of the wave's entries (one per lane of a
     // half-wave) for 16 query rows; each 16-lane row of the wave is one run of
     // one query row per value, and after the reduction lane i of a row holds
     // value i's
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int c = 0; c < 2; ++c) {
       int32_t m[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = acc[r][v];
+        float x = acc[c][v];
         if (!full) {
-          const int tr = 64 * wq + 32 * r + 8 * (v >> 2) + 4 * g + (v & 3);
-          x = ea < N && ea < vis_s[tr] ? x : -INFINITY;
+          const int tr = 32 * wq + 8 * (v >> 2) + 4 * g + (v & 3);
+          x = ea + 32 * c < N && ea + 32 * c < vis_s[tr] ? x : -INFINITY;
         }
         m[v] = ord_i32(__float_as_int(x));
       }
       const int32_t o = row16_max_scatter(m);
       const int i = lane & 15;
-      const int ql = 64 * wq + 32 * r + 8 * (i >> 2) + 4 * g + (i & 3);
-      const int rl = 2 * we + ((lane >> 4) & 1);   // run of the tile (0 .. 7)
+      const int ql = 32 * wq + 8 * (i >> 2) + 4 * g + (i & 3);
+      const int rl = 4 * we + 2 * c + ((lane >> 4) & 1);   // run of the tile (0 .. 7)
       gm_s[ql * (kSE / 16) + rl] = __int_as_float(ord_i32(o));
     }
     // a barrier ordering LDS only: the score stores stay in flight
