@@ -1607,7 +1607,11 @@ void k_topk_group(const float* __restrict__ scores, int32_t N, const float* __re
     const int32_t e = 4 * NT * u + 4 * tid;
     const int32_t p = e < ne ? position(e) : 0;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (e < ne && p < n) v = *reinterpret_cast<const float4*>(sr + p);   // p + 3 < N: N is a multiple of 4
+    // p is a multiple of 4; when N is not, the load is only 4-byte aligned
+    // and the last group of a row reads up to 3 values past it (masked
+    // below), still inside the workspace, whose visible counts follow the
+    // scores
+    if (e < ne && p < n) v = *reinterpret_cast<const float4*>(sr + p);
     key[4 * u + 0] = e < ne && p + 0 < n ? score_key(v.x) : 0u;
     key[4 * u + 1] = e < ne && p + 1 < n ? score_key(v.y) : 0u;
     key[4 * u + 2] = e < ne && p + 2 < n ? score_key(v.z) : 0u;
