@@ -645,7 +645,10 @@ void k_attn_dec(AttnArgs a, int32_t Cg, int32_t Cw, int32_t cps) {
   else        store_final<kQuarter>(a, row, p, ln, lg, O, m_run, L, a.o_in, a.lse_in);
 }
 
-// One work-group (128 lanes x 4 dims) per (head, query row).  The partial
+// One work-group (128 lanes x 4 dims) per (query row, head), the row index
+// fastest: with a row count that is a multiple of 8, a row's merges then run
+// on the XCD whose work-groups wrote its partials, and read them from that
+// L2 (measured: 0.5 us less per layer than head-first).  The partial
 // rows of up to kCombBatch splits are loaded together with every split's
 // (reference, sum) pair, so that the merge waits on one round trip to memory;
 // the weights are formed in LDS by the first wave, and the rows are summed in
@@ -659,8 +662,8 @@ void k_attn_combine(const float* __restrict__ opart, const float* __restrict__ m
                     float* lse) {
   __shared__ float wgt_s[kAttnMaxSplits + 1];
   __shared__ float L_s;
-  const int h = blockIdx.x;
-  const int row = blockIdx.y;
+  const int row = blockIdx.x;
+  const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int d0 = tid * 4;
   const float* src = opart + ((size_t)row * S * kH + h) * kD + d0;
@@ -792,7 +795,7 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
       else             k_attn_dec<false, true><<<grid, dim3(64 * kDecWaves), 0, s>>>(a, Cg, Cw, plan.cps);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      k_attn_combine<<<dim3((unsigned)kH, (unsigned)a.rows), dim3(kCombThreads), 0, s>>>(
+      k_attn_combine<<<dim3((unsigned)a.rows, (unsigned)kH), dim3(kCombThreads), 0, s>>>(
           a.opart, a.ml, S, a.o_in, a.lse_in, a.o, a.lse);
     } else {
       if (a.map.pages) k_attn_dec<true, false><<<grid, dim3(64 * kDecWaves), 0, s>>>(a, Cg, Cw, plan.cps);
